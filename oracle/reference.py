@@ -1,0 +1,274 @@
+"""fp64 reference of one tree-verification step (test infrastructure only).
+
+Inputs are the exact bf16 / fp16 / uint8 values the GPU receives, widened
+exactly to fp64; nothing is rounded inside.  See the package docstring for
+the passages each step follows.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+# ---------------------------------------------------------------- formats
+
+
+def bf16_to_f64(u16) -> np.ndarray:
+    """bf16 bit patterns -> fp64 (exact)."""
+    u16 = np.asarray(u16, dtype=np.uint16)
+    with np.errstate(invalid="ignore"):
+        return (u16.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def f16_to_f64(u16) -> np.ndarray:
+    """fp16 bit patterns -> fp64 (exact)."""
+    return np.asarray(u16, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+@dataclasses.dataclass(frozen=True)
+class Shape:
+    hidden: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    ffn: int
+    vocab: int
+    rms_eps: float = 1e-6
+    rope_base: float = 10000.0
+
+
+@dataclasses.dataclass
+class LayerWeights:
+    """One layer in logical form (codes ``q`` uint8, block scales ``d`` fp16 bits).
+
+    ``wqkv`` rows are [q heads; k heads; v heads], ``wgu`` rows are
+    [gate; up]; each ``(q, d)`` pair holds ``W[n, k] = d[n, k // 32] * (q[n, k] - 8)``.
+    """
+    attn_norm: np.ndarray  # bf16 bits [H]
+    ffn_norm: np.ndarray   # bf16 bits [H]
+    wqkv: tuple
+    wo: tuple
+    wgu: tuple
+    wd: tuple
+
+
+@dataclasses.dataclass
+class HeadWeights:
+    final_norm: np.ndarray  # bf16 bits [H]
+    lm: tuple               # (q [V, H], d [V, H/32])
+
+
+# ---------------------------------------------------------------- tree
+
+
+def tree_depths(parent: Sequence[int]) -> np.ndarray:
+    """depth[0] = 0, depth[i] = depth[parent[i]] + 1 (parents precede children)."""
+    parent = [int(p) for p in parent]
+    depth = np.zeros(len(parent), np.int64)
+    for i in range(1, len(parent)):
+        depth[i] = depth[parent[i]] + 1
+    return depth
+
+
+def tree_ancestors(parent: Sequence[int]) -> List[List[int]]:
+    """anc(i) = {i} plus anc(parent[i]), listed in increasing node index."""
+    out = []
+    for i in range(len(parent)):
+        chain = []
+        j = i
+        while j >= 0:
+            chain.append(j)
+            j = int(parent[j])
+        out.append(sorted(chain))
+    return out
+
+
+# ---------------------------------------------------------------- layer math
+
+
+def dequant_q4(q: np.ndarray, d: np.ndarray) -> np.ndarray:
+    """W[n, k] = d[n, k // 32] * (q[n, k] - 8), blocks of 32 along the input axis."""
+    q = np.asarray(q)
+    n_out, k_in = q.shape
+    scale = f16_to_f64(d).reshape(n_out, k_in // 32)
+    w = (q.astype(np.float64) - 8.0).reshape(n_out, k_in // 32, 32)
+    return (w * scale[:, :, None]).reshape(n_out, k_in)
+
+
+def linear_q4(x: np.ndarray, qd: tuple, row_chunk: int = 4096) -> np.ndarray:
+    """y = x @ W^T with W dequantised from (q, d); rows of W taken in chunks."""
+    q, d = qd
+    out = np.empty((x.shape[0], q.shape[0]), np.float64)
+    for r0 in range(0, q.shape[0], row_chunk):
+        w = dequant_q4(q[r0:r0 + row_chunk], d[r0:r0 + row_chunk])
+        out[:, r0:r0 + row_chunk] = x @ w.T
+    return out
+
+
+def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
+    """x / sqrt(mean(x^2) + eps) * g, per row; g multiplies (not 1 + g)."""
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * g
+
+
+def silu(a: np.ndarray) -> np.ndarray:
+    return a / (1.0 + np.exp(-a))
+
+
+def rope(x: np.ndarray, pos, base: float) -> np.ndarray:
+    """Rotate-half RoPE over the full head dim.
+
+    For j < d/2 the pair (x_j, x_{j+d/2}) turns by theta = pos * base^(-2j/d).
+    ``x`` is [..., d]; ``pos`` broadcasts against x[..., 0].
+    """
+    d = x.shape[-1]
+    h = d // 2
+    inv = base ** (-2.0 * np.arange(h, dtype=np.float64) / d)
+    th = np.asarray(pos, dtype=np.float64)[..., None] * inv
+    c, s = np.cos(th), np.sin(th)
+    a, b = x[..., :h], x[..., h:]
+    return np.concatenate([a * c - b * s, a * s + b * c], axis=-1)
+
+
+def tree_attention(q: np.ndarray, k_tree: np.ndarray, v_tree: np.ndarray,
+                   k_prefix: np.ndarray, v_prefix: np.ndarray,
+                   parent: Sequence[int]) -> np.ndarray:
+    """Tree-masked GQA attention.
+
+    q [N, Hq, d] and k_tree / v_tree [N, Hkv, d] are post-RoPE (values are
+    not rotated); k_prefix / v_prefix [Hkv, P, d] are used as stored.  Node i,
+    head h reads KV head g = h // (Hq / Hkv): all P prefix keys, then the tree
+    keys of anc(i) in index order; softmax of q.k / sqrt(d); weighted sum of
+    values.  Returns o [N, Hq, d].
+    """
+    N, Hq, d = q.shape
+    Hkv = k_tree.shape[1]
+    grp = Hq // Hkv
+    anc = tree_ancestors(parent)
+    o = np.zeros((N, Hq, d), np.float64)
+    for i in range(N):
+        a = anc[i]
+        for h in range(Hq):
+            g = h // grp
+            keys = np.concatenate([k_prefix[g], k_tree[a, g]], axis=0)
+            vals = np.concatenate([v_prefix[g], v_tree[a, g]], axis=0)
+            s = keys @ q[i, h] / np.sqrt(d)
+            p = np.exp(s - s.max())
+            p /= p.sum()
+            o[i, h] = p @ vals
+    return o
+
+
+def layer_forward(x: np.ndarray, w: LayerWeights, k_prefix: np.ndarray,
+                  v_prefix: np.ndarray, parent: Sequence[int], shape: Shape,
+                  prefix_len: Optional[int] = None):
+    """One pre-norm decoder layer over all tree nodes.
+
+    x [N, H] fp64 residual stream; k_prefix / v_prefix bf16 bits or fp64
+    [Hkv, P, d].  RoPE position of node i is prefix_len + depth(i).
+    Returns (x_out, k_tree, v_tree) with the tree K (post-RoPE) and V.
+    """
+    N, H = x.shape
+    Hq, Hkv, d = shape.n_q_heads, shape.n_kv_heads, shape.head_dim
+    kp = k_prefix if k_prefix.dtype == np.float64 else bf16_to_f64(k_prefix)
+    vp = v_prefix if v_prefix.dtype == np.float64 else bf16_to_f64(v_prefix)
+    P = kp.shape[1] if prefix_len is None else prefix_len
+    pos = P + tree_depths(parent)
+
+    u = rmsnorm(x, bf16_to_f64(w.attn_norm), shape.rms_eps)
+    qkv = linear_q4(u, w.wqkv)
+    q = qkv[:, :Hq * d].reshape(N, Hq, d)
+    k = qkv[:, Hq * d:(Hq + Hkv) * d].reshape(N, Hkv, d)
+    v = qkv[:, (Hq + Hkv) * d:].reshape(N, Hkv, d)
+    q = rope(q, pos[:, None], shape.rope_base)
+    k = rope(k, pos[:, None], shape.rope_base)
+
+    o = tree_attention(q, k, v, kp, vp, parent)
+    x = x + linear_q4(o.reshape(N, Hq * d), w.wo)
+
+    u2 = rmsnorm(x, bf16_to_f64(w.ffn_norm), shape.rms_eps)
+    gu = linear_q4(u2, w.wgu)
+    F = shape.ffn
+    m = silu(gu[:, :F]) * gu[:, F:]
+    x = x + linear_q4(m, w.wd)
+    return x, k, v
+
+
+def head_logits(x: np.ndarray, hw: HeadWeights, shape: Shape) -> np.ndarray:
+    """Final RMSNorm then the int4 lm_head: logits [N, V]."""
+    u = rmsnorm(x, bf16_to_f64(hw.final_norm), shape.rms_eps)
+    return linear_q4(u, hw.lm)
+
+
+def argmax_gap(logits: np.ndarray):
+    """Greedy token per row (lowest id on exact ties) and top1 - top2.
+
+    Duplicates count, so an exact tie at the top gives a gap of 0.
+    """
+    am = np.argmax(logits, axis=-1)  # numpy returns the first maximum
+    srt = np.sort(logits, axis=-1)
+    gap = srt[:, -1] - srt[:, -2] if logits.shape[-1] > 1 else np.full(len(logits), np.inf)
+    return am.astype(np.int64), gap
+
+
+def accept_path(parent: Sequence[int], token: Sequence[int], am: Sequence[int]):
+    """Greedy acceptance over the tree.
+
+    The root (node 0, the last accepted token) is accepted.  In index order,
+    node i is accepted when its parent is accepted and its drafted token equals
+    the target's greedy token at the parent.  The kept path ends at the
+    deepest accepted node (lowest index on ties); the committed tokens are the
+    accepted drafts on that path plus the target's greedy token at its end.
+    Returns (path, committed), both lists of ints.
+    """
+    N = len(parent)
+    depth = tree_depths(parent)
+    acc = [False] * N
+    acc[0] = True
+    for i in range(1, N):
+        p = int(parent[i])
+        acc[i] = acc[p] and int(token[i]) == int(am[p])
+    end = 0
+    for i in range(N):
+        if acc[i] and depth[i] > depth[end]:
+            end = i
+    path = []
+    j = end
+    while j >= 0:
+        path.append(j)
+        j = int(parent[j])
+    path.reverse()
+    committed = [int(token[i]) for i in path[1:]] + [int(am[end])]
+    return path, committed
+
+
+def verify_forward(x_in: np.ndarray, layers: Sequence[LayerWeights],
+                   kv: Sequence[tuple], head: Optional[HeadWeights],
+                   parent: Sequence[int], shape: Shape,
+                   token: Optional[Sequence[int]] = None, keep_hidden: bool = True):
+    """The whole step: all layers, final norm + lm_head, argmax/gap, walk.
+
+    x_in: bf16 bits [N, H] (per-node input hidden states) or fp64.
+    kv[l] = (k_prefix, v_prefix) for layer l; ``layers`` and ``kv`` may be
+    generators so a long stack is built one layer at a time.
+    Returns a dict with 'hidden' (list per layer, if kept), 'x', 'k_tree',
+    'v_tree' (last layer), 'logits', 'argmax', 'gap' and, if tokens are
+    given, 'path' and 'committed'.
+    """
+    x = x_in if np.asarray(x_in).dtype == np.float64 else bf16_to_f64(x_in)
+    hidden = []
+    kt = vt = None
+    for w, (kp, vp) in zip(layers, kv):
+        x, kt, vt = layer_forward(x, w, kp, vp, parent, shape)
+        if keep_hidden:
+            hidden.append(x.copy())
+    out = {"hidden": hidden, "x": x, "k_tree": kt, "v_tree": vt}
+    if head is not None:
+        logits = head_logits(x, head, shape)
+        am, gap = argmax_gap(logits)
+        out.update(logits=logits, argmax=am, gap=gap)
+        if token is not None:
+            path, committed = accept_path(parent, token, am)
+            out.update(path=path, committed=committed)
+    return out
