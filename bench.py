@@ -1,0 +1,204 @@
+"""Verify-step benchmark: latency, HBM GB/s and roofline fraction on one GPU.
+
+A step is one pass of the whole hot path over one draft tree: every layer's
+lucev_verify_layer, then lucev_accept_path (final norm, lm_head, greedy
+tokens, acceptance walk), replayed from one captured HIP graph with all
+inputs resident in HBM.  Prints one JSON line (rank 0).
+
+    python bench.py [--steps K] [--warmup W] [--config stack27b] [--gpus 1]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verify-step latency (ms) & HBM GB/s, 27B-class int4 stack, tree budget 22"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(cfg, nodes):
+    """Bytes the method must move per step: packed int4 weights once (18 B per
+    32 weights), the bf16 KV prefix once, norm gains, tree K/V writes, the
+    input / residual rows and the per-node outputs."""
+    H, Hkv, d = cfg.hidden, cfg.n_kv_heads, cfg.head_dim
+    w = (cfg.layers * cfg.layer_weight_count() + cfg.head_weight_count()) * 18 // 32
+    kv = cfg.layers * cfg.prefix * Hkv * d * 2 * 2
+    other = cfg.layers * (2 * H * 2 + 2 * nodes * Hkv * d * 2) + H * 2 + nodes * H * 4 * 2
+    return w, kv, other
+
+
+def attention_bytes(cfg, nodes):
+    Hq, Hkv, d = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    return (cfg.prefix * Hkv * d * 2 * 2 + 2 * nodes * Hq * d * 2 + 2 * nodes * Hkv * d * 2)
+
+
+def tokens_for(cfg, parent):
+    """Planted drafted tokens from the oracle's stored greedy tokens when the
+    golden file for this config exists, else uniform tokens (tokens only feed
+    the acceptance walk, which is the same work either way)."""
+    import numpy as np
+    import synth
+    gpath = os.path.join(ROOT, "tests", "golden", "%s.json" % cfg.name)
+    if os.path.exists(gpath):
+        with open(gpath) as fh:
+            g = json.load(fh)
+        runs = [r for r in g["runs"] if r["seed"] == cfg.seed]
+        if runs:
+            return np.array(runs[0]["tokens"], np.int32), "planted from the oracle's greedy tokens"
+    rng = np.random.default_rng(cfg.seed)
+    return rng.integers(0, cfg.vocab, len(parent)).astype(np.int32), "uniform random"
+
+
+def cpu_baseline(cfg, budget_s=30.0):
+    """The fp64 oracle, as it stands, on a bounded sample of the workload:
+    the first layer (full KV prefix) over the same tree."""
+    import numpy as np
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import oracle
+    import synth
+    import workload
+    parent = synth.tree_parents(cfg)
+    x = oracle.bf16_to_f64(synth.hidden_in(cfg))
+    lw = workload.layer_weights(cfg, 0)
+    kp, vp = synth.kv_prefix(cfg, 0)
+    shp = workload.shape(cfg)
+    t0 = time.perf_counter()
+    oracle.layer_forward(x, lw, kp, vp, parent, shp)
+    dt = time.perf_counter() - t0
+    layer_bytes = cfg.layer_weight_count() * 18 // 32 + cfg.prefix * cfg.n_kv_heads * cfg.head_dim * 4
+    try:
+        threads = len(os.sched_getaffinity(0))
+    except AttributeError:
+        threads = os.cpu_count()
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] + [1])
+    except Exception:
+        pass
+    return {"value": round(layer_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": "one full %s layer (%d-token prefix, %d-node tree) of the %d-layer step; "
+                      "GB/s over that layer's algorithmic bytes" % (cfg.name, cfg.prefix, cfg.nodes,
+                                                                  cfg.layers)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="stack27b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--attn-reps", type=int, default=20)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(got --gpus %d)" % args.gpus, flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import synth
+    import synth.device as sd
+    import tree_verify_amd as tv
+    from tree_verify_amd.runner import VerifyRunner
+
+    cfg = synth.get(args.config)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    wl = sd.Workload(cfg, device=dev)
+    torch.cuda.synchronize()
+    log("workload %s built on device in %.1f s" % (cfg.name, time.time() - t0))
+    shape = tv.make_shape(cfg.hidden, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ffn,
+                          cfg.vocab, cfg.rms_eps, cfg.rope_base)
+    r = VerifyRunner(shape, wl.layers, wl.head, cfg.nodes, wl.capacity, dev, keep_logits=False)
+    parent = synth.tree_parents(cfg)
+    tokens, tok_src = tokens_for(cfg, parent)
+    tree = tv.make_tree(parent, tokens)
+    x32 = wl.x_in_f32().contiguous()
+
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        r.step(tree, x32, cfg.prefix, with_logits=False)  # eager warm-up (and module loads)
+        stream.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            r.step(tree, x32, cfg.prefix, with_logits=False)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(args.steps):
+        graph.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    path = r.path.cpu().numpy()[: int(r.path_len.item())].tolist()
+    wb, kvb, ob = algorithmic_bytes(cfg, cfg.nodes)
+    total = wb + kvb + ob
+    gbs = total / (ms * 1e-3) / 1e9
+    log("step %.4f ms, %.1f GB/s (weights %.3f GB, KV %.3f GB, other %.4f GB), path %s" %
+        (ms, gbs, wb / 1e9, kvb / 1e9, ob / 1e9, path))
+
+    # dominant kernel by bytes: the tree attention of one layer (prefix split
+    # partial kernel + combine), timed alone on its own stream with HIP events
+    astream = torch.cuda.Stream()
+    Hq, Hkv, d, n = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.nodes
+    q = sd.flat_table("normal", synth.stream_key(cfg.seed, 90, 0), n * Hq * d, dev)
+    out = torch.zeros(n * Hq * d, dtype=torch.int16, device=dev)
+    kv0 = r.kv(0, cfg.prefix)
+    with torch.cuda.stream(astream):
+        st = astream.cuda_stream
+        for _ in range(3):
+            tv.lucev_tree_attention(shape, tree, kv0, q, r.k_tree[0], r.v_tree[0], out, r.ws,
+                                    r.ws_bytes, st)
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record(astream)
+        for i in range(args.attn_reps):
+            kvi = r.kv(i % cfg.layers, cfg.prefix)
+            tv.lucev_tree_attention(shape, tree, kvi, q, r.k_tree[0], r.v_tree[0], out, r.ws,
+                                    r.ws_bytes, st)
+        a1.record(astream)
+    torch.cuda.synchronize()
+    attn_ms = a0.elapsed_time(a1) / args.attn_reps
+    ab = attention_bytes(cfg, n)
+    attn_gbs = ab / (attn_ms * 1e-3) / 1e9
+    log("tree attention (one layer): %.2f us, %.1f GB/s" % (attn_ms * 1e3, attn_gbs))
+
+    line = {
+        "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int4 weights, f16/bf16 MFMA, f32 accumulate",
+        "data": "synthetic (seeded Philox draws with the pages' shapes; random-init weights)",
+        "config": {"workload": cfg.name, "layers": cfg.layers, "hidden": cfg.hidden,
+                   "heads": "%d/%d" % (cfg.n_q_heads, cfg.n_kv_heads), "head_dim": cfg.head_dim,
+                   "ffn": cfg.ffn, "vocab": cfg.vocab, "prefix": cfg.prefix, "tree_nodes": cfg.nodes,
+                   "algorithmic_bytes": total, "tokens": tok_src, "accepted_path": path},
+        "roofline": {"bound": "hbm", "kernel": "tree attention, one layer (partial + combine)",
+                     "achieved": round(attn_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": ab, "avg_launch_us": round(attn_ms * 1e3, 3)},
+        "step_roofline_frac": round(gbs / HBM_PEAK_GBS, 4),
+    }
+    if not args.no_cpu_baseline:
+        del wl, r, graph
+        torch.cuda.empty_cache()
+        line["cpu_baseline"] = cpu_baseline(cfg)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

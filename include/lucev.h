@@ -1,0 +1,207 @@
+/*
+ * lucev.h -- C ABI of the tree-verification forward on one MI355X (gfx950).
+ *
+ * One step of tree-based speculative decoding on the target model: a tree of
+ * drafted tokens is scored in ONE forward pass against a long KV cache, and
+ * greedy acceptance keeps the longest accepted root path.
+ *
+ * Passages this interface follows (page title, section):
+ *   - "Lucebox Hub", section "Speculative decoding 계층 (DFlash / DDTree /
+ *     DSpark)": the target verifies a tree of candidates in one forward
+ *     (verify_batch); the target adapter also projects hidden states through
+ *     its lm_head and keeps the KV cache so rejected tokens can be dropped.
+ *   - "Lucebox Hub", section "배경: 어떤 문제를 푸는가", item 1: decode reads
+ *     every weight once per forward, so one forward that checks many drafted
+ *     tokens amortises that read.
+ *   - "Lucebox: 추측 디코딩과 전용 커널로 ..." (discuss.pytorch.kr), section
+ *     "Lucebox 설치 및 실행": greedy decoding (temperature 0); tree budget 22
+ *     nodes on an RTX 3090 and 40 on an RTX 5090.
+ *
+ * The layer is a pre-norm decoder layer: RMSNorm, GQA attention with RoPE at
+ * position prefix_len + depth, SwiGLU FFN, all projections int4 block-32
+ * (w = d * (q - 8), fp16 d per 32 consecutive inputs).
+ *
+ * Conventions for every entry point
+ *   - Every tensor pointer is DEVICE memory owned by the caller and borrowed
+ *     until the stream reaches the end of the call.  The library never
+ *     allocates or frees device memory on these paths; scratch space is the
+ *     caller's workspace (lucev_workspace_bytes).
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL = default
+ *     stream) with no implicit synchronisation.  Calls are graph-capturable.
+ *   - Arguments are validated on the host BEFORE anything is launched.  On a
+ *     non-zero return nothing was enqueued (except LUCEV_ERR_HIP, which
+ *     reports a failed launch).  No C++ exception crosses the ABI.
+ *   - Same inputs give bit-identical outputs (no floating-point atomics).
+ *   - bf16 / fp16 tensors are passed as uint16_t bit patterns.
+ *   - Shapes: hidden, ffn and n_q_heads*head_dim multiples of 128;
+ *     head_dim in {64, 128}; n_q_heads a multiple of n_kv_heads;
+ *     vocab a multiple of 16; 1 <= tree nodes <= LUCEV_MAX_NODES.
+ */
+#ifndef LUCEV_H
+#define LUCEV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LUCEV_ABI_VERSION 1
+#define LUCEV_MAX_NODES 64
+
+/* status codes */
+#define LUCEV_OK 0
+#define LUCEV_ERR_NULL_ARG -1   /* a required pointer is NULL */
+#define LUCEV_ERR_BAD_SHAPE -2  /* unsupported dims (see conventions) */
+#define LUCEV_ERR_BAD_TREE -3   /* n outside [1,64], parent[0] != -1,
+                                   parent[i] outside [0,i), token outside [0,vocab) */
+#define LUCEV_ERR_WORKSPACE -4  /* workspace smaller than lucev_workspace_bytes */
+#define LUCEV_ERR_ALIGN -5      /* a pointer is not 16-byte aligned */
+#define LUCEV_ERR_HIP -6        /* a HIP call failed; see lucev_last_error() */
+#define LUCEV_ERR_DEVICE -7     /* current device is not gfx950 */
+#define LUCEV_ERR_BAD_KV -8     /* prefix_len < 0 or > capacity */
+
+/* Model shape shared by every layer. */
+typedef struct {
+  int32_t hidden;      /* H */
+  int32_t n_q_heads;   /* Hq */
+  int32_t n_kv_heads;  /* Hkv; query head h reads KV head h / (Hq / Hkv) */
+  int32_t head_dim;    /* d */
+  int32_t ffn;         /* F (SwiGLU inner width) */
+  int32_t vocab;       /* V */
+  float rms_eps;       /* added to mean(x^2) inside RMSNorm */
+  float rope_base;     /* RoPE: theta_j = pos * base^(-2j/d), rotate-half pairs (j, j+d/2) */
+} lucev_shape;
+
+/* One int4 matrix in the library's packed layout (lucev_q4_pack*).
+ * Logical form: W[n, k] = d[n, k/32] * (q[n, k] - 8), n < n_out, k < k_in. */
+typedef struct {
+  const void* packed;  /* device, lucev_q4_packed_bytes(n_out, k_in) bytes */
+  int64_t n_out;
+  int64_t k_in;
+} lucev_q4;
+
+/* Weights of one layer.  Norm gains are bf16 [H] and multiply (x*g).
+ *   wqkv: n_out = (Hq + 2 Hkv) d, k_in = H; logical rows [q heads; k heads; v heads]
+ *   wo  : n_out = H, k_in = Hq d
+ *   wgu : n_out = 2 F, k_in = H; logical rows [gate; up]
+ *   wd  : n_out = H, k_in = F                                                */
+typedef struct {
+  const uint16_t* attn_norm;
+  const uint16_t* ffn_norm;
+  lucev_q4 wqkv, wo, wgu, wd;
+} lucev_layer_w;
+
+/* Final RMSNorm gain (bf16 [H]) and the lm_head (n_out = V, k_in = H). */
+typedef struct {
+  const uint16_t* final_norm;
+  lucev_q4 lm_head;
+} lucev_head_w;
+
+/* One layer's bf16 KV cache for one sequence.
+ *   k: [Hkv][capacity][d]  keys stored after RoPE (token t rotated at position t)
+ *   v: [Hkv][d][capacity]  values stored dim-major (transposed), so the
+ *                          attention reads consecutive tokens of one dim
+ * Tokens 0 .. prefix_len-1 are the prefix every tree node attends to.        */
+typedef struct {
+  const uint16_t* k;
+  const uint16_t* v;
+  int32_t prefix_len;
+  int32_t capacity;
+} lucev_kv;
+
+/* The draft tree, in HOST memory, passed by value.  Node 0 is the root (the
+ * last accepted token, not yet in the cache); parent[i] < i.  The library
+ * derives depths, RoPE positions (prefix_len + depth) and ancestor masks into
+ * kernel arguments, so no host->device copy is needed.  token[i] is node i's
+ * drafted token (token[0] is not used by acceptance).                       */
+typedef struct {
+  int32_t n;
+  int32_t parent[LUCEV_MAX_NODES];
+  int32_t token[LUCEV_MAX_NODES];
+} lucev_tree;
+
+/* Matrix roles for packing (decides the library-private row order). */
+#define LUCEV_W_PLAIN 0 /* wo, wd, lm_head */
+#define LUCEV_W_QKV 1   /* needs head_dim (rotate-half pairs kept together) */
+#define LUCEV_W_GU 2    /* gate and up rows interleaved so SwiGLU pairs meet */
+
+/* ------------------------------------------------------------ helpers */
+
+int lucev_abi_version(void);
+const char* lucev_status_str(int status);
+/* Thread-local text of the last error on this thread ("" if none). */
+const char* lucev_last_error(void);
+
+/* Bytes of the packed layout: n_out * k_in * 9 / 16 (18 B per 32 weights).
+ * Returns 0 if n_out % 16 or k_in % 128 is non-zero. */
+size_t lucev_q4_packed_bytes(int64_t n_out, int64_t k_in);
+
+/* Pack logical codes q (uint8 [n_out][k_in], values 0..15) and scales d
+ * (fp16 bits [n_out][k_in/32]) into `dst`.  HOST pointers.  `kind` is one of
+ * LUCEV_W_*; head_dim is read only for LUCEV_W_QKV.  Returns LUCEV_OK,
+ * LUCEV_ERR_NULL_ARG, LUCEV_ERR_BAD_SHAPE or LUCEV_ERR_WORKSPACE (dst_bytes
+ * too small). */
+int lucev_q4_pack(int kind, int32_t head_dim, const uint8_t* q, const uint16_t* d,
+                  int64_t n_out, int64_t k_in, void* dst, size_t dst_bytes);
+
+/* Same packing with DEVICE pointers, enqueued on `stream`. */
+int lucev_q4_pack_device(int kind, int32_t head_dim, const uint8_t* q, const uint16_t* d,
+                         int64_t n_out, int64_t k_in, void* dst, size_t dst_bytes,
+                         void* stream);
+
+/* Workspace bytes needed by every entry point below for a tree of up to
+ * `n_nodes` nodes against a prefix of up to `prefix_len` tokens.  Returns 0
+ * for an unsupported shape. */
+size_t lucev_workspace_bytes(const lucev_shape* shape, int32_t n_nodes, int32_t prefix_len);
+
+/* Zero-fill a workspace (required once before its first use; every
+ * completed call leaves the workspace's counters zero again). */
+int lucev_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------ the step */
+
+/* One decoder layer over all tree nodes (RMSNorm, fused QKV projection, RoPE
+ * at prefix_len + depth, tree-masked GQA attention over the prefix and each
+ * node's ancestors, output projection + residual, RMSNorm, SwiGLU FFN +
+ * residual).
+ *   resid_io   : fp32 [n][H] residual stream, updated in place
+ *   k_tree_out : bf16 [n][Hkv][d] this layer's tree keys after RoPE
+ *   v_tree_out : bf16 [n][Hkv][d] this layer's tree values
+ * Attention inside uses the workspace; outputs must not alias inputs. */
+int lucev_verify_layer(const lucev_shape* shape, const lucev_layer_w* w, const lucev_tree* tree,
+                       const lucev_kv* kv, float* resid_io, uint16_t* k_tree_out,
+                       uint16_t* v_tree_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Tree-masked GQA attention alone.  Node i, query head h attends with scale
+ * 1/sqrt(d) to all prefix keys of KV head h/(Hq/Hkv) and to the tree keys of
+ * i's ancestors and itself.
+ *   q      : bf16 [n][Hq][d] after RoPE
+ *   k_tree : bf16 [n][Hkv][d] after RoPE;  v_tree : bf16 [n][Hkv][d]
+ *   out    : bf16 [n][Hq][d] */
+int lucev_tree_attention(const lucev_shape* shape, const lucev_tree* tree, const lucev_kv* kv,
+                         const uint16_t* q, const uint16_t* k_tree, const uint16_t* v_tree,
+                         uint16_t* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Final RMSNorm, lm_head, greedy token and top1-top2 gap per node (taken on
+ * the fp32 logits), then greedy acceptance over the tree: a node is accepted
+ * when its parent is accepted and its drafted token equals the parent's
+ * greedy token; the path ends at the deepest accepted node (lowest index on
+ * ties).  All outputs are DEVICE buffers:
+ *   resid         : fp32 [n][H] final residual stream (input)
+ *   logits_out    : bf16 [n][V] or NULL
+ *   argmax_out    : int32 [n]
+ *   gap_out       : fp32 [n] or NULL
+ *   path_out      : int32 [n]; path_len_out: int32 [1]
+ *   committed_out : int32 [n]: accepted drafted tokens along the path, then
+ *                   the greedy token at its end (path_len entries) */
+int lucev_accept_path(const lucev_shape* shape, const lucev_head_w* w, const lucev_tree* tree,
+                      const float* resid, uint16_t* logits_out, int32_t* argmax_out,
+                      float* gap_out, int32_t* path_out, int32_t* path_len_out,
+                      int32_t* committed_out, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LUCEV_H */

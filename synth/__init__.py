@@ -141,7 +141,8 @@ def philox_words(key, start: int, count: int) -> np.ndarray:
     ctr = (b0 - 1) & _MASK64
     ctr_words = [ctr, _MASK64 if b0 == 0 else 0, _MASK64 if b0 == 0 else 0,
                  _MASK64 if b0 == 0 else 0]
-    bg = np.random.Philox(key=[key[0], key[1]], counter=ctr_words)
+    bg = np.random.Philox(key=np.array([key[0], key[1]], dtype=np.uint64),
+                          counter=np.array(ctr_words, dtype=np.uint64))
     raw = bg.random_raw((b1 - b0) * 4).astype(np.uint64)
     words = raw.view(np.uint32)  # little-endian: low half first
     off = start - b0 * 8

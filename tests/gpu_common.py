@@ -1,0 +1,57 @@
+"""Helpers shared by the GPU tests: comparisons and oracle-side reference runs."""
+import numpy as np
+import pytest
+
+try:  # import early: the first import on a fresh machine is slow
+    import torch  # noqa: F401
+except ImportError:  # pragma: no cover
+    torch = None
+
+import oracle
+
+
+def need_gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import tree_verify_amd as tv
+    tv.lib()  # raises if the library is missing: no silent fallback
+    return torch
+
+
+def bf16_bits_to_f64(t):
+    """Device/host int16 tensor of bf16 bits -> fp64 numpy."""
+    a = t.detach().cpu().numpy().view(np.uint16)
+    return oracle.bf16_to_f64(a)
+
+
+def row_rel_err(got, ref):
+    """Per-row max |got - ref| / max |ref| (the inf-norm relative error)."""
+    got = np.asarray(got, np.float64).reshape(len(ref), -1)
+    ref = np.asarray(ref, np.float64).reshape(len(ref), -1)
+    return np.max(np.abs(got - ref), axis=1) / np.maximum(np.max(np.abs(ref), axis=1), 1e-30)
+
+
+def decisive_compare(parent, tokens, oracle_am, oracle_gap, gpu_am, gpu_path, gpu_len,
+                     gpu_committed, thr=0.05):
+    """Greedy tokens must match wherever the oracle's top1-top2 gap exceeds thr;
+    the path must match exactly when every oracle-accepted node is decisive.
+    Returns (n_decisive_tokens, path_decided)."""
+    dec = oracle_gap > thr
+    bad = [i for i in range(len(oracle_am)) if dec[i] and gpu_am[i] != oracle_am[i]]
+    assert not bad, "greedy token mismatch at decisive nodes %s" % bad
+    path, committed = oracle.accept_path(parent, tokens, oracle_am)
+    # nodes whose greedy token the acceptance actually consulted
+    acc_nodes = _accepted_nodes(parent, tokens, oracle_am)
+    decided = all(dec[i] for i in acc_nodes)
+    if decided:
+        assert list(gpu_path[:gpu_len]) == list(path)
+        assert list(gpu_committed[:gpu_len]) == list(committed)
+    return int(dec.sum()), decided
+
+
+def _accepted_nodes(parent, tokens, am):
+    acc = [True] + [False] * (len(parent) - 1)
+    for i in range(1, len(parent)):
+        acc[i] = acc[parent[i]] and int(tokens[i]) == int(am[parent[i]])
+    return [i for i in range(len(parent)) if acc[i]]

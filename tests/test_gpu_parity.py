@@ -1,0 +1,186 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Tolerances (from the arithmetic): logits, hidden states, tree
+K/V and attention outputs within a per-row inf-norm relative error of 2e-2;
+greedy tokens bit-exact wherever the oracle's top1-top2 gap exceeds 0.05 and
+accepted paths bit-exact whenever every accepted node is that decisive.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_common import (bf16_bits_to_f64, decisive_compare, need_gpu, row_rel_err)
+import workload
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+# ------------------------------------------------------------------ generator twin
+
+def test_device_generator_matches_cpu():
+    torch = need_gpu()
+    import synth.device as sd
+    for key in [(0, 0), synth.stream_key(1003, synth.T_K, 17), (2 ** 63 + 5, 2 ** 40 + 3)]:
+        for start, n in [(0, 100), (5, 37), (123456, 1000)]:
+            got = sd.raw_words(key, start, n, "cuda").cpu().numpy().view(np.uint32)
+            assert np.array_equal(got, synth.philox_words(key, start, n)), (key, start, n)
+    cfg = synth.get("tiny")
+    q, d = sd.logical_q4(cfg, "gu", 0, cfg.seed, "cuda")
+    q0, d0 = synth.weight_q4(cfg, "gu", 0)
+    assert np.array_equal(q.cpu().numpy(), q0)
+    assert np.array_equal(d.cpu().numpy().view(np.uint16), d0)
+    k, v = sd.kv_cache(cfg, 0, cfg.seed, 200, "cuda")
+    k0, v0 = synth.kv_prefix(cfg, 0)
+    kh = k.cpu().numpy().view(np.uint16)
+    vh = v.cpu().numpy().view(np.uint16)
+    assert np.array_equal(kh[:, :cfg.prefix], k0)
+    assert np.array_equal(vh[:, :, :cfg.prefix].transpose(0, 2, 1), v0)
+    assert not kh[:, cfg.prefix:].any() and not vh[:, :, cfg.prefix:].any()
+    g = sd.gain(cfg, "ffn", 0, cfg.seed, "cuda").cpu().numpy().view(np.uint16)
+    assert np.array_equal(g, synth.gain(cfg, "ffn", 0))
+    x = sd.hidden_in(cfg, cfg.seed, cfg.nodes, "cuda").cpu().numpy().view(np.uint16)
+    assert np.array_equal(x, synth.hidden_in(cfg))
+
+
+def test_device_packer_equals_host_packer():
+    torch = need_gpu()
+    import tree_verify_amd as tv
+    import synth.device as sd
+    cfg = synth.get("tiny")
+    for which, kind in [("qkv", tv.W_QKV), ("gu", tv.W_GU), ("o", tv.W_PLAIN), ("lm", tv.W_PLAIN)]:
+        n_out, k_in = synth.weight_dims(cfg, which)
+        q, d = synth.weight_q4(cfg, which, 0)
+        nb = tv.lucev_q4_packed_bytes(n_out, k_in)
+        host = np.zeros(nb, np.uint8)
+        tv.lucev_q4_pack(kind, cfg.head_dim, np.ascontiguousarray(q), np.ascontiguousarray(d),
+                         n_out, k_in, host, nb)
+        dev = sd.packed_q4(cfg, which, 0, cfg.seed, "cuda").cpu().numpy()
+        assert np.array_equal(dev, host), which
+
+
+# ------------------------------------------------------------------ attention alone
+
+ATTN_CASES = [
+    # (name, Hq, Hkv, d, P, parent-recipe, n)
+    ("tiny_shape", 4, 2, 64, 128, None, 8),
+    ("ragged_prefix", 8, 2, 128, 1000, None, 16),
+    ("27b_group", 48, 8, 128, 4100, (3, 8), 22),
+    ("wide_tree", 48, 8, 128, 2051, (4, 10), 40),
+    ("empty_prefix", 8, 2, 128, 0, None, 5),
+    ("single_node", 48, 8, 128, 777, None, 1),
+    ("max_nodes", 8, 2, 64, 300, None, 64),
+]
+
+
+@pytest.mark.parametrize("case", ATTN_CASES, ids=[c[0] for c in ATTN_CASES])
+def test_tree_attention_parity(case):
+    torch = need_gpu()
+    import tree_verify_amd as tv
+    import synth.device as sd
+    name, Hq, Hkv, d, P, rec, n = case
+    cfg = synth.Config("attn_" + name, layers=1, hidden=128, n_q_heads=Hq, n_kv_heads=Hkv,
+                       head_dim=d, ffn=128, vocab=64, prefix=P, nodes=n,
+                       max_children=rec[0] if rec else None, max_depth=rec[1] if rec else None,
+                       p_accept=0.7, seed=4242 + n)
+    say("attention case", name)
+    parent = synth.tree_parents(cfg)
+    cap = ((P + 7) // 8) * 8 + 8
+    k, v = sd.kv_cache(cfg, 0, cfg.seed, cap, "cuda")
+    tab = "normal"
+    q = sd.flat_table(tab, synth.stream_key(cfg.seed, 90, 0), n * Hq * d, "cuda")
+    kt = sd.flat_table(tab, synth.stream_key(cfg.seed, 91, 0), n * Hkv * d, "cuda")
+    vt = sd.flat_table(tab, synth.stream_key(cfg.seed, 92, 0), n * Hkv * d, "cuda")
+    out = torch.zeros(n * Hq * d, dtype=torch.int16, device="cuda")
+    shape = tv.make_shape(cfg.hidden, Hq, Hkv, d, cfg.ffn, cfg.vocab)
+    ws_bytes = tv.lucev_workspace_bytes(shape, n, P)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
+    tree = tv.make_tree(parent, [0] * n)
+    tv.lucev_tree_attention(shape, tree, tv.make_kv(k, v, P, cap), q, kt, vt, out, ws, ws_bytes,
+                            torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    kp, vp = synth.kv_prefix(cfg, 0)
+    ref = oracle.tree_attention(bf16_bits_to_f64(q).reshape(n, Hq, d),
+                                bf16_bits_to_f64(kt).reshape(n, Hkv, d),
+                                bf16_bits_to_f64(vt).reshape(n, Hkv, d),
+                                oracle.bf16_to_f64(kp), oracle.bf16_to_f64(vp), parent)
+    got = bf16_bits_to_f64(out).reshape(n * Hq, d)
+    err = row_rel_err(got, ref.reshape(n * Hq, d))
+    say("  max row rel err %.3e" % err.max())
+    assert err.max() < TOL
+
+
+# ------------------------------------------------------------------ whole steps
+
+def _run_gpu_step(cfg, seed, tokens, parent, layers=None, want_hidden=True):
+    torch = need_gpu()
+    import tree_verify_amd as tv
+    from tree_verify_amd.runner import VerifyRunner
+    import synth.device as sd
+    wl = sd.Workload(cfg, seed, "cuda", layers=layers)
+    shape = tv.make_shape(cfg.hidden, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ffn,
+                          cfg.vocab, cfg.rms_eps, cfg.rope_base)
+    r = VerifyRunner(shape, wl.layers, wl.head, cfg.nodes, wl.capacity, "cuda")
+    n = cfg.nodes
+    hid = [torch.zeros(n, cfg.hidden, dtype=torch.float32, device="cuda")
+           for _ in range(wl.n_layers)] if want_hidden else None
+    tree = tv.make_tree(parent, tokens)
+    r.step(tree, wl.x_in_f32(), cfg.prefix, hidden_out=hid)
+    torch.cuda.synchronize()
+    out = {
+        "hidden": [h.cpu().numpy().astype(np.float64) for h in hid] if hid else None,
+        "k_tree": bf16_bits_to_f64(r.k_tree[-1][:n]),
+        "v_tree": bf16_bits_to_f64(r.v_tree[-1][:n]),
+        "logits": bf16_bits_to_f64(r.logits[:n]),
+        "argmax": r.argmax[:n].cpu().numpy(),
+        "gap": r.gap[:n].cpu().numpy(),
+        "path": r.path[:n].cpu().numpy(),
+        "path_len": int(r.path_len.cpu().item()),
+        "committed": r.committed[:n].cpu().numpy(),
+    }
+    return out
+
+
+def _check_case(cfg, seed, layers=None):
+    ref = workload.planted_case(cfg, seed, layers=layers)
+    say("case", cfg.name, "seed", seed, "parent", list(ref["parent"]))
+    got = _run_gpu_step(cfg, seed, ref["tokens"], ref["parent"], layers=layers)
+    for l, (g, r) in enumerate(zip(got["hidden"], ref["hidden"])):
+        e = row_rel_err(g, r).max()
+        assert e < TOL, "hidden state of layer %d: rel err %.3e" % (l, e)
+    Hkv, d = cfg.n_kv_heads, cfg.head_dim
+    n = cfg.nodes
+    ek = row_rel_err(got["k_tree"].reshape(n * Hkv, d), ref["k_tree"].reshape(n * Hkv, d)).max()
+    ev = row_rel_err(got["v_tree"].reshape(n * Hkv, d), ref["v_tree"].reshape(n * Hkv, d)).max()
+    el = row_rel_err(got["logits"], ref["logits"]).max()
+    say("  rel err: k_tree %.2e v_tree %.2e logits %.2e hidden(last) %.2e" %
+        (ek, ev, el, row_rel_err(got["hidden"][-1], ref["hidden"][-1]).max()))
+    assert ek < TOL and ev < TOL and el < TOL
+    ndec, decided = decisive_compare(ref["parent"], ref["tokens"], ref["argmax"], ref["gap"],
+                                     got["argmax"], got["path"], got["path_len"], got["committed"])
+    # the gap the GPU reports is the fp32 top1-top2 difference
+    dec = ref["gap"] > 0.05
+    assert np.allclose(got["gap"][dec], ref["gap"][dec], rtol=0.05, atol=0.05)
+    say("  decisive nodes %d/%d, path decided %s, path %s" %
+        (ndec, n, decided, list(got["path"][:got["path_len"]])))
+    return decided
+
+
+@pytest.mark.parametrize("run", range(8))
+def test_tiny_config_parity(run):
+    cfg = synth.get("tiny")
+    _check_case(cfg, synth.run_seed(cfg, run))
+
+
+def test_tiny_decode_single_node():
+    cfg = synth.get("tiny").replace(nodes=1, name="tiny_decode")
+    _check_case(cfg, cfg.seed)

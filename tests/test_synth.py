@@ -17,6 +17,26 @@ def test_philox_known_answer_zero_key_zero_counter():
     assert [int(v) for v in w] == want
 
 
+def _philox_by_definition(ctr, key):
+    """Philox4x64-10 written out from the published round function."""
+    M = (1 << 64) - 1
+    c, (k0, k1) = list(ctr), key
+    for r in range(10):
+        if r:
+            k0, k1 = (k0 + 0x9E3779B97F4A7C15) & M, (k1 + 0xBB67AE8584CAA73B) & M
+        p0, p1 = 0xD2E7470EE14C6C93 * c[0], 0xCA5A826395121157 * c[2]
+        c = [(p1 >> 64) ^ c[1] ^ k0, p1 & M, (p0 >> 64) ^ c[3] ^ k1, p0 & M]
+    return c
+
+
+def test_stream_equals_round_function():
+    for key in [(0, 0), (1003, 12 << 32 | 5), (2 ** 63 + 5, 2 ** 40 + 3), (2 ** 64 - 1, 2 ** 64 - 1)]:
+        for b in (0, 1, 77, 2 ** 33 + 9):
+            w = synth.philox_words(key, 8 * b, 8)
+            got = [int(w[2 * i]) | (int(w[2 * i + 1]) << 32) for i in range(4)]
+            assert got == _philox_by_definition([b, 0, 0, 0], key), (key, b)
+
+
 def test_stream_random_access():
     key = synth.stream_key(1234, 12, 5)
     full = synth.philox_words(key, 0, 1000)

@@ -1,0 +1,455 @@
+// The C ABI of lucev (see include/lucev.h): host-side validation, tree
+// preparation, workspace carving and kernel dispatch.  Nothing here computes
+// model math; every step of the forward runs in the kernels.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/lucev.h"
+#include "internal.h"
+
+using namespace lucev;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(LUCEV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_shape(const lucev_shape* s) {
+  if (!s) return fail(LUCEV_ERR_NULL_ARG, "shape is NULL");
+  if (s->hidden <= 0 || s->n_q_heads <= 0 || s->n_kv_heads <= 0 || s->head_dim <= 0 ||
+      s->ffn <= 0 || s->vocab <= 0)
+    return fail(LUCEV_ERR_BAD_SHAPE, "non-positive dimension");
+  if (s->hidden % 128 || s->ffn % 128 || (s->n_q_heads * s->head_dim) % 128)
+    return fail(LUCEV_ERR_BAD_SHAPE, "hidden, ffn and n_q_heads*head_dim must be multiples of 128");
+  if (s->head_dim != 64 && s->head_dim != 128)
+    return fail(LUCEV_ERR_BAD_SHAPE, "head_dim must be 64 or 128 (got %d)", s->head_dim);
+  if (s->n_q_heads % s->n_kv_heads)
+    return fail(LUCEV_ERR_BAD_SHAPE, "n_q_heads must be a multiple of n_kv_heads");
+  if (s->vocab % 16) return fail(LUCEV_ERR_BAD_SHAPE, "vocab must be a multiple of 16");
+  if (!(s->rms_eps >= 0.f) || !(s->rope_base > 0.f))
+    return fail(LUCEV_ERR_BAD_SHAPE, "rms_eps must be >= 0 and rope_base > 0");
+  return LUCEV_OK;
+}
+
+// Depths, RoPE positions and ancestor masks of the draft tree.
+int prep_tree(const lucev_tree* t, int vocab, int prefix_len, TreeArgs* out) {
+  if (!t) return fail(LUCEV_ERR_NULL_ARG, "tree is NULL");
+  if (t->n < 1 || t->n > LUCEV_MAX_NODES)
+    return fail(LUCEV_ERR_BAD_TREE, "tree size %d outside [1, %d]", t->n, LUCEV_MAX_NODES);
+  if (t->parent[0] != -1) return fail(LUCEV_ERR_BAD_TREE, "parent[0] must be -1");
+  memset(out, 0, sizeof(*out));
+  out->n = t->n;
+  int depth[LUCEV_MAX_NODES];
+  for (int i = 0; i < t->n; ++i) {
+    const int p = t->parent[i];
+    if (i > 0 && (p < 0 || p >= i))
+      return fail(LUCEV_ERR_BAD_TREE, "parent[%d] = %d is not an earlier node", i, p);
+    if (t->token[i] < 0 || t->token[i] >= vocab)
+      return fail(LUCEV_ERR_BAD_TREE, "token[%d] = %d outside [0, vocab)", i, t->token[i]);
+    depth[i] = i == 0 ? 0 : depth[p] + 1;
+    out->parent[i] = p;
+    out->token[i] = t->token[i];
+    out->pos[i] = prefix_len + depth[i];
+    out->anc[i] = (i == 0 ? 0ull : out->anc[p]) | (1ull << i);
+  }
+  return LUCEV_OK;
+}
+
+int check_q4(const lucev_q4& w, int64_t n_out, int64_t k_in, const char* name) {
+  if (!w.packed) return fail(LUCEV_ERR_NULL_ARG, "%s.packed is NULL", name);
+  if (w.n_out != n_out || w.k_in != k_in)
+    return fail(LUCEV_ERR_BAD_SHAPE, "%s is [%lld, %lld], expected [%lld, %lld]", name,
+                (long long)w.n_out, (long long)w.k_in, (long long)n_out, (long long)k_in);
+  if (!aligned16(w.packed)) return fail(LUCEV_ERR_ALIGN, "%s.packed is not 16-byte aligned", name);
+  return LUCEV_OK;
+}
+
+int check_kv(const lucev_kv* kv) {
+  if (!kv) return fail(LUCEV_ERR_NULL_ARG, "kv is NULL");
+  if (kv->prefix_len < 0 || kv->capacity < 0 || kv->prefix_len > kv->capacity)
+    return fail(LUCEV_ERR_BAD_KV, "prefix_len %d / capacity %d invalid", kv->prefix_len, kv->capacity);
+  if (kv->capacity % 8) return fail(LUCEV_ERR_BAD_KV, "capacity must be a multiple of 8");
+  if (kv->prefix_len > 0 && (!kv->k || !kv->v)) return fail(LUCEV_ERR_NULL_ARG, "kv.k / kv.v is NULL");
+  if (!aligned16(kv->k) || !aligned16(kv->v)) return fail(LUCEV_ERR_ALIGN, "kv buffers must be 16-byte aligned");
+  return LUCEV_OK;
+}
+
+int check_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  static int cache[128];  // 0 unknown, 1 gfx950, -1 other
+  if (dev < 0 || dev >= 128) return fail(LUCEV_ERR_DEVICE, "device id %d out of range", dev);
+  if (cache[dev] == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+    cache[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+  }
+  if (cache[dev] != 1) return fail(LUCEV_ERR_DEVICE, "device %d is not gfx950", dev);
+  return LUCEV_OK;
+}
+
+struct Ws {
+  size_t counters, x, m, q, opart, ml, partials, cand, total;
+  int n_fg_lm;
+};
+
+constexpr int kCounters = 4096;
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int layer_gemm_partials(const lucev_shape* s, int n, size_t* floats) {
+  const int64_t H = s->hidden, F = s->ffn, Hq = s->n_q_heads, Hkv = s->n_kv_heads, d = s->head_dim;
+  const int64_t dims[5][2] = {{(Hq + 2 * Hkv) * d, H}, {H, Hq * d}, {2 * F, H}, {H, F}, {s->vocab, H}};
+  size_t best = 0;
+  for (int i = 0; i < 5; ++i) {
+    GemmPlan g = plan_gemm(dims[i][0], dims[i][1], n, 64);
+    if (g.ksplit > 1) {
+      if (g.fgroups > kCounters - 2) return -1;
+      const size_t f = (size_t)g.fgroups * g.ksplit * g.tile_floats;
+      if (f > best) best = f;
+    }
+  }
+  *floats = best;
+  return 0;
+}
+
+bool ws_layout(const lucev_shape* s, int nmax, int pmax, Ws* w) {
+  if (check_shape(s) != LUCEV_OK || nmax < 1 || nmax > LUCEV_MAX_NODES || pmax < 0) return false;
+  const int64_t H = s->hidden, F = s->ffn, Hq = s->n_q_heads, Hkv = s->n_kv_heads, d = s->head_dim;
+  size_t off = 0;
+  w->counters = off;
+  off = align256(off + kCounters * sizeof(uint32_t));
+  w->x = off;
+  off = align256(off + (size_t)nmax * (H > Hq * d ? H : Hq * d) * 2);
+  w->m = off;
+  off = align256(off + (size_t)nmax * F * 2);
+  w->q = off;
+  off = align256(off + (size_t)nmax * Hq * d * 2);
+  const int rows = nmax * (int)(Hq / Hkv);
+  const int chunks = attention_max_chunks((int)Hkv);
+  w->opart = off;
+  off = align256(off + (size_t)chunks * Hkv * rows * d * 2);
+  w->ml = off;
+  off = align256(off + (size_t)chunks * Hkv * rows * 2 * sizeof(float));
+  size_t pf = 0;
+  for (int n = 1; n <= nmax; ++n) {
+    size_t f;
+    if (layer_gemm_partials(s, n, &f)) return false;
+    if (f > pf) pf = f;
+  }
+  w->partials = off;
+  off = align256(off + pf * sizeof(float));
+  int fg_lm = 0;
+  for (int n = 1; n <= nmax; ++n) {
+    GemmPlan g = plan_gemm(s->vocab, H, n, 64);
+    if (g.fgroups > fg_lm) fg_lm = g.fgroups;
+  }
+  w->n_fg_lm = fg_lm;
+  w->cand = off;
+  off = align256(off + (size_t)fg_lm * nmax * sizeof(f32x4));
+  w->total = off;
+  (void)pmax;
+  return true;
+}
+
+int check_ws(const lucev_shape* s, int n, int prefix_len, void* ws, size_t ws_bytes, Ws* w) {
+  if (!ws) return fail(LUCEV_ERR_NULL_ARG, "workspace is NULL");
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+    return fail(LUCEV_ERR_ALIGN, "workspace must be 256-byte aligned");
+  if (!ws_layout(s, n, prefix_len, w)) return fail(LUCEV_ERR_BAD_SHAPE, "unsupported workspace shape");
+  if (ws_bytes < w->total)
+    return fail(LUCEV_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, w->total);
+  return LUCEV_OK;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+GemmParams gemm_params(const lucev_q4& w, const uint16_t* X, int ldx, int n, void* ws, const Ws& L) {
+  GemmPlan g = plan_gemm(w.n_out, w.k_in, n, 64);
+  GemmParams p;
+  p.X = X;
+  p.ldx = ldx;
+  p.n_nodes = n;
+  p.wq = static_cast<const uint8_t*>(w.packed);
+  p.wsc = reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(w.packed) + w.n_out * w.k_in / 2);
+  p.n_out = w.n_out;
+  p.n_tiles = g.n_tiles;
+  p.kgroups = g.kgroups;
+  p.fgroups = g.fgroups;
+  p.ksplit = g.ksplit;
+  p.gps = g.gps;
+  p.partials = at<float>(ws, L.partials);
+  p.counters = at<uint32_t>(ws, L.counters);
+  return p;
+}
+
+EpiArgs epi_blank() {
+  EpiArgs e;
+  memset(&e, 0, sizeof(e));
+  return e;
+}
+
+int run_attention(const lucev_shape* s, const TreeArgs& t, const lucev_kv* kv, const uint16_t* q,
+                  const uint16_t* k_tree, const uint16_t* v_tree, uint16_t* out, int out_f16,
+                  void* ws, const Ws& L, hipStream_t st) {
+  AttnPlan plan = plan_attention(t.n, s->n_q_heads, s->n_kv_heads, s->head_dim, kv->prefix_len);
+  AttnParams p;
+  p.q = q;
+  p.kc = kv->k;
+  p.vc = kv->v;
+  p.cap = kv->capacity;
+  p.prefix_len = kv->prefix_len;
+  p.chunk = plan.chunk;
+  p.n_chunks = plan.n_chunks;
+  p.n = t.n;
+  p.n_q_heads = s->n_q_heads;
+  p.n_kv_heads = s->n_kv_heads;
+  p.rows = plan.rows;
+  p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)s->head_dim));
+  p.o_part = at<uint16_t>(ws, L.opart);
+  p.ml_part = at<float>(ws, L.ml);
+  CombineParams c;
+  c.q = q;
+  c.k_tree = k_tree;
+  c.v_tree = v_tree;
+  c.o_part = p.o_part;
+  c.ml_part = p.ml_part;
+  c.n_chunks = plan.n_chunks;
+  c.n = t.n;
+  c.n_q_heads = s->n_q_heads;
+  c.n_kv_heads = s->n_kv_heads;
+  c.rows = plan.rows;
+  c.scale_log2 = p.scale_log2;
+  c.out = out;
+  c.out_f16 = out_f16;
+  hipError_t e = launch_attention(plan, s->head_dim, p, c, t, st);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return LUCEV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lucev_abi_version(void) { return LUCEV_ABI_VERSION; }
+
+const char* lucev_status_str(int status) {
+  switch (status) {
+    case LUCEV_OK: return "ok";
+    case LUCEV_ERR_NULL_ARG: return "null argument";
+    case LUCEV_ERR_BAD_SHAPE: return "unsupported shape";
+    case LUCEV_ERR_BAD_TREE: return "malformed tree";
+    case LUCEV_ERR_WORKSPACE: return "workspace too small";
+    case LUCEV_ERR_ALIGN: return "misaligned pointer";
+    case LUCEV_ERR_HIP: return "HIP error";
+    case LUCEV_ERR_DEVICE: return "device is not gfx950";
+    case LUCEV_ERR_BAD_KV: return "bad KV cache descriptor";
+    default: return "unknown status";
+  }
+}
+
+const char* lucev_last_error(void) { return g_err; }
+
+size_t lucev_q4_packed_bytes(int64_t n_out, int64_t k_in) {
+  if (n_out <= 0 || k_in <= 0 || n_out % 16 || k_in % 128) return 0;
+  return (size_t)(n_out * k_in / 32 * 18);
+}
+
+static int check_pack(int kind, int32_t head_dim, const void* q, const void* d, int64_t n_out,
+                      int64_t k_in, const void* dst, size_t dst_bytes) {
+  if (!q || !d || !dst) return fail(LUCEV_ERR_NULL_ARG, "pack: NULL pointer");
+  const size_t need = lucev_q4_packed_bytes(n_out, k_in);
+  if (!need) return fail(LUCEV_ERR_BAD_SHAPE, "pack: n_out %% 16 and k_in %% 128 must be 0");
+  if (kind < LUCEV_W_PLAIN || kind > LUCEV_W_GU) return fail(LUCEV_ERR_BAD_SHAPE, "pack: bad kind %d", kind);
+  if (kind == LUCEV_W_QKV && (head_dim % 16 || head_dim <= 0 || n_out % head_dim))
+    return fail(LUCEV_ERR_BAD_SHAPE, "pack: head_dim %d does not tile n_out", head_dim);
+  if (kind == LUCEV_W_GU && n_out % 32) return fail(LUCEV_ERR_BAD_SHAPE, "pack: gate/up needs n_out %% 32 == 0");
+  if (dst_bytes < need) return fail(LUCEV_ERR_WORKSPACE, "pack: dst %zu < %zu bytes", dst_bytes, need);
+  return LUCEV_OK;
+}
+
+int lucev_q4_pack(int kind, int32_t head_dim, const uint8_t* q, const uint16_t* d, int64_t n_out,
+                  int64_t k_in, void* dst, size_t dst_bytes) {
+  int rc = check_pack(kind, head_dim, q, d, n_out, k_in, dst, dst_bytes);
+  if (rc) return rc;
+  pack_q4_host(q, d, n_out, k_in, kind, head_dim, dst);
+  return LUCEV_OK;
+}
+
+int lucev_q4_pack_device(int kind, int32_t head_dim, const uint8_t* q, const uint16_t* d,
+                         int64_t n_out, int64_t k_in, void* dst, size_t dst_bytes, void* stream) {
+  int rc = check_pack(kind, head_dim, q, d, n_out, k_in, dst, dst_bytes);
+  if (rc) return rc;
+  if (!aligned16(dst) || !aligned16(q)) return fail(LUCEV_ERR_ALIGN, "pack: pointers must be 16-byte aligned");
+  if ((rc = check_device())) return rc;
+  hipError_t e = launch_pack_q4(q, d, n_out, k_in, kind, head_dim, dst, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "pack launch");
+  return LUCEV_OK;
+}
+
+size_t lucev_workspace_bytes(const lucev_shape* shape, int32_t n_nodes, int32_t prefix_len) {
+  Ws w;
+  if (!ws_layout(shape, n_nodes, prefix_len, &w)) return 0;
+  return w.total;
+}
+
+int lucev_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  if (!ws) return fail(LUCEV_ERR_NULL_ARG, "workspace is NULL");
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return fail(LUCEV_ERR_ALIGN, "workspace must be 256-byte aligned");
+  int rc = check_device();
+  if (rc) return rc;
+  hipError_t e = launch_zero(ws, ws_bytes & ~size_t(15), (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "zero launch");
+  return LUCEV_OK;
+}
+
+int lucev_tree_attention(const lucev_shape* shape, const lucev_tree* tree, const lucev_kv* kv,
+                         const uint16_t* q, const uint16_t* k_tree, const uint16_t* v_tree,
+                         uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (!q || !k_tree || !v_tree || !out) return fail(LUCEV_ERR_NULL_ARG, "tree_attention: NULL tensor");
+  if ((rc = check_kv(kv))) return rc;
+  TreeArgs t;
+  if ((rc = prep_tree(tree, shape->vocab, kv->prefix_len, &t))) return rc;
+  if (!aligned16(q) || !aligned16(k_tree) || !aligned16(v_tree) || !aligned16(out))
+    return fail(LUCEV_ERR_ALIGN, "tree_attention: tensors must be 16-byte aligned");
+  Ws L;
+  if ((rc = check_ws(shape, t.n, kv->prefix_len, ws, ws_bytes, &L))) return rc;
+  if ((rc = check_device())) return rc;
+  return run_attention(shape, t, kv, q, k_tree, v_tree, out, 0, ws, L, (hipStream_t)stream);
+}
+
+int lucev_verify_layer(const lucev_shape* shape, const lucev_layer_w* w, const lucev_tree* tree,
+                       const lucev_kv* kv, float* resid_io, uint16_t* k_tree_out,
+                       uint16_t* v_tree_out, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (!w || !resid_io || !k_tree_out || !v_tree_out || !w->attn_norm || !w->ffn_norm)
+    return fail(LUCEV_ERR_NULL_ARG, "verify_layer: NULL argument");
+  if ((rc = check_kv(kv))) return rc;
+  TreeArgs t;
+  if ((rc = prep_tree(tree, shape->vocab, kv->prefix_len, &t))) return rc;
+  const int64_t H = shape->hidden, F = shape->ffn, Hq = shape->n_q_heads, Hkv = shape->n_kv_heads,
+                d = shape->head_dim;
+  if ((rc = check_q4(w->wqkv, (Hq + 2 * Hkv) * d, H, "wqkv"))) return rc;
+  if ((rc = check_q4(w->wo, H, Hq * d, "wo"))) return rc;
+  if ((rc = check_q4(w->wgu, 2 * F, H, "wgu"))) return rc;
+  if ((rc = check_q4(w->wd, H, F, "wd"))) return rc;
+  if (!aligned16(resid_io) || !aligned16(k_tree_out) || !aligned16(v_tree_out))
+    return fail(LUCEV_ERR_ALIGN, "verify_layer: tensors must be 16-byte aligned");
+  Ws L;
+  if ((rc = check_ws(shape, t.n, kv->prefix_len, ws, ws_bytes, &L))) return rc;
+  if ((rc = check_device())) return rc;
+
+  hipStream_t st = (hipStream_t)stream;
+  const int n = t.n;
+  uint16_t* X = at<uint16_t>(ws, L.x);
+  uint16_t* M = at<uint16_t>(ws, L.m);
+  uint16_t* Q = at<uint16_t>(ws, L.q);
+  hipError_t e;
+
+  // attention half: RMSNorm -> QKV (+RoPE, tree K/V out) -> tree attention -> Wo + residual
+  if ((e = launch_rmsnorm(resid_io, n, (int)H, w->attn_norm, shape->rms_eps, X, (int)H, st)) != hipSuccess)
+    return hip_fail(e, "rmsnorm launch");
+  {
+    GemmParams p = gemm_params(w->wqkv, X, (int)H, n, ws, L);
+    EpiArgs ea = epi_blank();
+    ea.out16 = Q;
+    ea.k_out = k_tree_out;
+    ea.v_out = v_tree_out;
+    ea.n_q_heads = (int)Hq;
+    ea.n_kv_heads = (int)Hkv;
+    ea.head_dim = (int)d;
+    for (int i = 0; i < n; ++i) ea.pos[i] = t.pos[i];
+    for (int j = 0; j < d / 2; ++j) ea.inv_freq[j] = pow((double)shape->rope_base, -2.0 * j / (double)d);
+    if ((e = launch_gemm(EPI_QKV, p, ea, st)) != hipSuccess) return hip_fail(e, "qkv gemm launch");
+  }
+  if ((rc = run_attention(shape, t, kv, Q, k_tree_out, v_tree_out, X, 1, ws, L, st))) return rc;
+  {
+    GemmParams p = gemm_params(w->wo, X, (int)(Hq * d), n, ws, L);
+    EpiArgs ea = epi_blank();
+    ea.resid = resid_io;
+    ea.ld_out = (int)H;
+    if ((e = launch_gemm(EPI_RESID, p, ea, st)) != hipSuccess) return hip_fail(e, "wo gemm launch");
+  }
+  // FFN half: RMSNorm -> gate/up + SwiGLU -> down + residual
+  if ((e = launch_rmsnorm(resid_io, n, (int)H, w->ffn_norm, shape->rms_eps, X, (int)H, st)) != hipSuccess)
+    return hip_fail(e, "rmsnorm launch");
+  {
+    GemmParams p = gemm_params(w->wgu, X, (int)H, n, ws, L);
+    EpiArgs ea = epi_blank();
+    ea.out16 = M;
+    ea.ld_out = (int)F;
+    if ((e = launch_gemm(EPI_SWIGLU, p, ea, st)) != hipSuccess) return hip_fail(e, "gate/up gemm launch");
+  }
+  {
+    GemmParams p = gemm_params(w->wd, M, (int)F, n, ws, L);
+    EpiArgs ea = epi_blank();
+    ea.resid = resid_io;
+    ea.ld_out = (int)H;
+    if ((e = launch_gemm(EPI_RESID, p, ea, st)) != hipSuccess) return hip_fail(e, "down gemm launch");
+  }
+  return LUCEV_OK;
+}
+
+int lucev_accept_path(const lucev_shape* shape, const lucev_head_w* w, const lucev_tree* tree,
+                      const float* resid, uint16_t* logits_out, int32_t* argmax_out, float* gap_out,
+                      int32_t* path_out, int32_t* path_len_out, int32_t* committed_out, void* ws,
+                      size_t ws_bytes, void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (!w || !w->final_norm || !resid || !argmax_out || !path_out || !path_len_out || !committed_out)
+    return fail(LUCEV_ERR_NULL_ARG, "accept_path: NULL argument");
+  TreeArgs t;
+  if ((rc = prep_tree(tree, shape->vocab, 0, &t))) return rc;
+  if ((rc = check_q4(w->lm_head, shape->vocab, shape->hidden, "lm_head"))) return rc;
+  if (!aligned16(resid) || (logits_out && !aligned16(logits_out)))
+    return fail(LUCEV_ERR_ALIGN, "accept_path: tensors must be 16-byte aligned");
+  Ws L;
+  if ((rc = check_ws(shape, t.n, 0, ws, ws_bytes, &L))) return rc;
+  if ((rc = check_device())) return rc;
+
+  hipStream_t st = (hipStream_t)stream;
+  const int n = t.n;
+  const int H = shape->hidden;
+  uint16_t* X = at<uint16_t>(ws, L.x);
+  hipError_t e;
+  if ((e = launch_rmsnorm(resid, n, H, w->final_norm, shape->rms_eps, X, H, st)) != hipSuccess)
+    return hip_fail(e, "rmsnorm launch");
+  GemmParams p = gemm_params(w->lm_head, X, H, n, ws, L);
+  EpiArgs ea = epi_blank();
+  ea.out16 = logits_out;
+  ea.ld_out = shape->vocab;
+  ea.cand = at<f32x4>(ws, L.cand);
+  ea.cand_stride = n;
+  if ((e = launch_gemm(EPI_LOGITS, p, ea, st)) != hipSuccess) return hip_fail(e, "lm_head gemm launch");
+  uint32_t* counter = at<uint32_t>(ws, L.counters) + (kCounters - 1);
+  if ((e = launch_finalize(ea.cand, p.fgroups, n, t, argmax_out, gap_out, path_out, path_len_out,
+                           committed_out, counter, st)) != hipSuccess)
+    return hip_fail(e, "finalize launch");
+  return LUCEV_OK;
+}
+
+}  // extern "C"

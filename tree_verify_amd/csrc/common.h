@@ -1,0 +1,70 @@
+// Shared device-side definitions of the lucev kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lucev {
+
+typedef _Float16 f16;
+typedef f16 f16x2 __attribute__((ext_vector_type(2)));
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kMaxNodes = 64;
+constexpr int kWave = 64;
+
+// Tree facts derived on the host and passed by value as kernel arguments.
+struct TreeArgs {
+  int32_t n;
+  int32_t pos[kMaxNodes];     // prefix_len + depth
+  int32_t parent[kMaxNodes];  // parent[0] = -1
+  int32_t token[kMaxNodes];
+  uint64_t anc[kMaxNodes];    // bit j: node j is node i or one of its ancestors
+};
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);  // round to nearest even
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, (f16)x);  // round to nearest even
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
+  return (float)__builtin_bit_cast(f16, (uint16_t)b);
+}
+
+template <typename T>
+__device__ __forceinline__ T shfl_xor(T v, int mask) {
+  return __shfl_xor(v, mask, kWave);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += shfl_xor(v, m);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, shfl_xor(v, m));
+  return v;
+}
+
+// 16-byte global load / store helpers.
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void st16(void* p, u32x4 v) {
+  *reinterpret_cast<u32x4*>(p) = v;
+}
+
+}  // namespace lucev

@@ -1,0 +1,77 @@
+"""A verify step over a whole stack: device buffers plus the call sequence.
+
+Owns the workspace, the fp32 residual stream and the outputs, and issues
+``lucev_verify_layer`` for every layer followed by ``lucev_accept_path`` on one
+stream.  Orchestration only: all arithmetic runs in liblucev.so.
+"""
+from __future__ import annotations
+
+from typing import List, Optional, Sequence
+
+import torch
+
+import tree_verify_amd as tv
+
+
+class VerifyRunner:
+    def __init__(self, shape: tv.lucev_shape, layers: Sequence[dict], head: Optional[dict],
+                 n_max: int, capacity: int, device="cuda", keep_logits: bool = True):
+        self.shape = shape
+        self.layers = list(layers)
+        self.head = head
+        self.n_max = n_max
+        self.capacity = capacity
+        self.device = torch.device(device)
+        H, Hkv, d, V = shape.hidden, shape.n_kv_heads, shape.head_dim, shape.vocab
+        self.ws_bytes = tv.lucev_workspace_bytes(shape, n_max, capacity)
+        if self.ws_bytes == 0:
+            raise ValueError("unsupported shape for the workspace")
+        self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=self.device)
+        self.resid = torch.zeros(n_max, H, dtype=torch.float32, device=self.device)
+        self.k_tree = [torch.zeros(n_max, Hkv, d, dtype=torch.int16, device=self.device)
+                       for _ in self.layers]
+        self.v_tree = [torch.zeros(n_max, Hkv, d, dtype=torch.int16, device=self.device)
+                       for _ in self.layers]
+        self.logits = torch.zeros(n_max, V, dtype=torch.int16, device=self.device) if keep_logits else None
+        i32 = dict(dtype=torch.int32, device=self.device)
+        self.argmax = torch.zeros(n_max, **i32)
+        self.gap = torch.zeros(n_max, dtype=torch.float32, device=self.device)
+        self.path = torch.zeros(n_max, **i32)
+        self.path_len = torch.zeros(1, **i32)
+        self.committed = torch.zeros(n_max, **i32)
+        self._lw = [self._layer_struct(lw) for lw in self.layers]
+        self._hw = None
+        if head is not None:
+            self._hw = tv.lucev_head_w(head["final_norm"].data_ptr(),
+                                       tv.q4(head["lm"], V, H))
+
+    def _layer_struct(self, lw: dict) -> tv.lucev_layer_w:
+        s = self.shape
+        H, Hq, Hkv, d, F = s.hidden, s.n_q_heads, s.n_kv_heads, s.head_dim, s.ffn
+        return tv.lucev_layer_w(lw["attn_norm"].data_ptr(), lw["ffn_norm"].data_ptr(),
+                                tv.q4(lw["qkv"], (Hq + 2 * Hkv) * d, H), tv.q4(lw["o"], H, Hq * d),
+                                tv.q4(lw["gu"], 2 * F, H), tv.q4(lw["d"], H, F))
+
+    def kv(self, l: int, prefix_len: int) -> tv.lucev_kv:
+        lw = self.layers[l]
+        return tv.make_kv(lw["k"], lw["v"], prefix_len, self.capacity)
+
+    def step(self, tree: tv.lucev_tree, x_in_f32: torch.Tensor, prefix_len: int,
+             hidden_out: Optional[List[torch.Tensor]] = None, with_logits: bool = True,
+             stream=None) -> None:
+        """One verify step: residual <- x_in, every layer, then acceptance.
+
+        ``hidden_out``, if given, receives a copy of the residual after each layer.
+        """
+        n = tree.n
+        st = torch.cuda.current_stream().cuda_stream if stream is None else stream
+        self.resid[:n].copy_(x_in_f32[:n])
+        for l, lw in enumerate(self._lw):
+            tv.lucev_verify_layer(self.shape, lw, tree, self.kv(l, prefix_len), self.resid,
+                                  self.k_tree[l], self.v_tree[l], self.ws, self.ws_bytes, st)
+            if hidden_out is not None:
+                hidden_out[l].copy_(self.resid[:n])
+        if self._hw is not None:
+            tv.lucev_accept_path(self.shape, self._hw, tree, self.resid,
+                                 self.logits if with_logits else None, self.argmax, self.gap,
+                                 self.path, self.path_len, self.committed, self.ws, self.ws_bytes, st)
