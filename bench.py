@@ -126,6 +126,7 @@ def main():
     tokens, tok_src = tokens_for(cfg, parent)
     tree = tv.make_tree(parent, tokens)
     x32 = wl.x_in_f32().contiguous()
+    torch.cuda.synchronize()  # inputs were made on the default stream
 
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
@@ -158,6 +159,7 @@ def main():
     Hq, Hkv, d, n = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.nodes
     q = sd.flat_table("normal", synth.stream_key(cfg.seed, 90, 0), n * Hq * d, dev)
     out = torch.zeros(n * Hq * d, dtype=torch.int16, device=dev)
+    torch.cuda.synchronize()  # q / out were made on the default stream
     kv0 = r.kv(0, cfg.prefix)
     with torch.cuda.stream(astream):
         st = astream.cuda_stream

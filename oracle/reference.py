@@ -149,14 +149,14 @@ def tree_attention(q: np.ndarray, k_tree: np.ndarray, v_tree: np.ndarray,
     o = np.zeros((N, Hq, d), np.float64)
     for i in range(N):
         a = anc[i]
-        for h in range(Hq):
-            g = h // grp
+        for g in range(Hkv):
             keys = np.concatenate([k_prefix[g], k_tree[a, g]], axis=0)
             vals = np.concatenate([v_prefix[g], v_tree[a, g]], axis=0)
-            s = keys @ q[i, h] / np.sqrt(d)
-            p = np.exp(s - s.max())
-            p /= p.sum()
-            o[i, h] = p @ vals
+            for h in range(g * grp, (g + 1) * grp):
+                s = keys @ q[i, h] / np.sqrt(d)
+                p = np.exp(s - s.max())
+                p /= p.sum()
+                o[i, h] = p @ vals
     return o
 
 

@@ -155,6 +155,9 @@ class Workload:
             self.head = {"lm": packed_q4(cfg, "lm", 0, self.seed, self.device),
                          "final_norm": gain(cfg, "final", 0, self.seed, self.device)}
         self.x_in = hidden_in(cfg, self.seed, cfg.nodes, self.device)
+        # everything above was enqueued on the current stream; callers may run
+        # the step on another one
+        torch.cuda.synchronize(self.device)
 
     def x_in_f32(self) -> torch.Tensor:
         """Input hidden states widened exactly from bf16 to fp32."""

@@ -184,3 +184,28 @@ def test_tiny_config_parity(run):
 def test_tiny_decode_single_node():
     cfg = synth.get("tiny").replace(nodes=1, name="tiny_decode")
     _check_case(cfg, cfg.seed)
+
+
+# mid-size shape: every GEMM's feature groups are cut across blocks (the
+# split-K reduction path), 1 to 4 node tiles, ragged prefix
+MID = synth.Config("mid", layers=2, hidden=1024, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                   ffn=3584, vocab=32768, prefix=1000, nodes=22, max_children=3, max_depth=8,
+                   p_accept=0.7, seed=3100)
+
+
+@pytest.mark.parametrize("nodes,rec", [(22, (3, 8)), (40, (4, 10)), (64, (None, None)), (16, (None, None))])
+def test_midsize_parity(nodes, rec):
+    cfg = MID.replace(nodes=nodes, max_children=rec[0], max_depth=rec[1], name="mid%d" % nodes)
+    _check_case(cfg, cfg.seed + nodes)
+
+
+@pytest.mark.parametrize("run", range(2))
+def test_small_tree_config_parity(run):
+    cfg = synth.get("small_tree")
+    _check_case(cfg, synth.run_seed(cfg, run))
+
+
+@pytest.mark.parametrize("run", range(2))
+def test_small_decode_config_parity(run):
+    cfg = synth.get("small_decode")
+    _check_case(cfg, synth.run_seed(cfg, run))

@@ -107,64 +107,58 @@ int check_device() {
 }
 
 struct Ws {
-  size_t counters, x, m, q, opart, ml, partials, cand, total;
-  int n_fg_lm;
+  size_t counters, xhi, xlo, mhi, mlo, q32, k32, v32, opart, ml, partials, stats, ssq, cand, total;
+  int n_counters;
 };
-
-constexpr int kCounters = 4096;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-int layer_gemm_partials(const lucev_shape* s, int n, size_t* floats) {
+// every GEMM of a layer and the head, for a tree of n nodes
+void layer_gemms(const lucev_shape* s, int n, GemmPlan out[5]) {
   const int64_t H = s->hidden, F = s->ffn, Hq = s->n_q_heads, Hkv = s->n_kv_heads, d = s->head_dim;
   const int64_t dims[5][2] = {{(Hq + 2 * Hkv) * d, H}, {H, Hq * d}, {2 * F, H}, {H, F}, {s->vocab, H}};
-  size_t best = 0;
-  for (int i = 0; i < 5; ++i) {
-    GemmPlan g = plan_gemm(dims[i][0], dims[i][1], n, 64);
-    if (g.ksplit > 1) {
-      if (g.fgroups > kCounters - 2) return -1;
-      const size_t f = (size_t)g.fgroups * g.ksplit * g.tile_floats;
-      if (f > best) best = f;
-    }
-  }
-  *floats = best;
-  return 0;
+  for (int i = 0; i < 5; ++i) out[i] = plan_gemm(dims[i][0], dims[i][1], n);
 }
 
 bool ws_layout(const lucev_shape* s, int nmax, int pmax, Ws* w) {
   if (check_shape(s) != LUCEV_OK || nmax < 1 || nmax > LUCEV_MAX_NODES || pmax < 0) return false;
   const int64_t H = s->hidden, F = s->ffn, Hq = s->n_q_heads, Hkv = s->n_kv_heads, d = s->head_dim;
+  size_t part_floats = 0, ssq_floats = 0, cand = 0;
+  int counters = 0;
+  for (int n = 1; n <= nmax; ++n) {
+    GemmPlan g[5];
+    layer_gemms(s, n, g);
+    for (int i = 0; i < 5; ++i) {
+      const size_t pf = (size_t)g[i].blocks * 2 * g[i].tile_floats;
+      if (pf > part_floats) part_floats = pf;
+      if (g[i].fgroups > counters) counters = g[i].fgroups;
+    }
+    if ((size_t)g[1].fgroups * n > ssq_floats) ssq_floats = (size_t)g[1].fgroups * n;
+    if ((size_t)g[4].blocks * n > cand) cand = (size_t)g[4].blocks * n;
+  }
+  w->n_counters = counters;
   size_t off = 0;
-  w->counters = off;
-  off = align256(off + kCounters * sizeof(uint32_t));
-  w->x = off;
-  off = align256(off + (size_t)nmax * (H > Hq * d ? H : Hq * d) * 2);
-  w->m = off;
-  off = align256(off + (size_t)nmax * F * 2);
-  w->q = off;
-  off = align256(off + (size_t)nmax * Hq * d * 2);
+  auto take = [&](size_t bytes) {
+    const size_t at_ = off;
+    off = align256(off + bytes);
+    return at_;
+  };
+  w->counters = take((size_t)counters * sizeof(uint32_t));
+  w->xhi = take((size_t)nmax * Hq * d * 2);
+  w->xlo = take((size_t)nmax * Hq * d * 2);
+  w->mhi = take((size_t)nmax * F * 2);
+  w->mlo = take((size_t)nmax * F * 2);
+  w->q32 = take((size_t)nmax * Hq * d * 4);
+  w->k32 = take((size_t)nmax * Hkv * d * 4);
+  w->v32 = take((size_t)nmax * Hkv * d * 4);
   const int rows = nmax * (int)(Hq / Hkv);
   const int chunks = attention_max_chunks((int)Hkv);
-  w->opart = off;
-  off = align256(off + (size_t)chunks * Hkv * rows * d * 2);
-  w->ml = off;
-  off = align256(off + (size_t)chunks * Hkv * rows * 2 * sizeof(float));
-  size_t pf = 0;
-  for (int n = 1; n <= nmax; ++n) {
-    size_t f;
-    if (layer_gemm_partials(s, n, &f)) return false;
-    if (f > pf) pf = f;
-  }
-  w->partials = off;
-  off = align256(off + pf * sizeof(float));
-  int fg_lm = 0;
-  for (int n = 1; n <= nmax; ++n) {
-    GemmPlan g = plan_gemm(s->vocab, H, n, 64);
-    if (g.fgroups > fg_lm) fg_lm = g.fgroups;
-  }
-  w->n_fg_lm = fg_lm;
-  w->cand = off;
-  off = align256(off + (size_t)fg_lm * nmax * sizeof(f32x4));
+  w->opart = take((size_t)chunks * Hkv * rows * d * 4);
+  w->ml = take((size_t)chunks * Hkv * rows * 2 * sizeof(float));
+  w->partials = take(part_floats * sizeof(float));
+  w->stats = take((size_t)nmax * sizeof(float));
+  w->ssq = take(ssq_floats * sizeof(float));
+  w->cand = take(cand * sizeof(f32x4));
   w->total = off;
   (void)pmax;
   return true;
@@ -185,22 +179,38 @@ T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
 }
 
-GemmParams gemm_params(const lucev_q4& w, const uint16_t* X, int ldx, int n, void* ws, const Ws& L) {
-  GemmPlan g = plan_gemm(w.n_out, w.k_in, n, 64);
+// A_F16HL: X / Xlo are the fp16 planes; A_F32N: X is the fp32 residual, g the
+// gain and ssq the [ssq_groups][n] partial row sums of x^2
+GemmParams gemm_params(const lucev_q4& w, int a_mode, const void* X, const uint16_t* Xlo,
+                       const uint16_t* g, const float* ssq, int ssq_groups, int ldx, int n,
+                       float eps, void* ws, const Ws& L) {
+  GemmPlan pl = plan_gemm(w.n_out, w.k_in, n);
   GemmParams p;
-  p.X = X;
+  memset(&p, 0, sizeof(p));
+  p.a_mode = a_mode;
+  if (a_mode == A_F16HL) {
+    p.Xhi = static_cast<const uint16_t*>(X);
+    p.Xlo = Xlo;
+  } else {
+    p.Xf = static_cast<const float*>(X);
+    p.g = g;
+    p.ssq = ssq;
+    p.ssq_groups = ssq_groups;
+  }
   p.ldx = ldx;
   p.n_nodes = n;
   p.wq = static_cast<const uint8_t*>(w.packed);
   p.wsc = reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(w.packed) + w.n_out * w.k_in / 2);
   p.n_out = w.n_out;
-  p.n_tiles = g.n_tiles;
-  p.kgroups = g.kgroups;
-  p.fgroups = g.fgroups;
-  p.ksplit = g.ksplit;
-  p.gps = g.gps;
+  p.k_in = w.k_in;
+  p.n_tiles = pl.n_tiles;
+  p.kgroups = pl.kgroups;
+  p.fgroups = pl.fgroups;
+  p.blocks = pl.blocks;
+  p.units = pl.units;
   p.partials = at<float>(ws, L.partials);
   p.counters = at<uint32_t>(ws, L.counters);
+  p.rms_eps = eps;
   return p;
 }
 
@@ -210,12 +220,16 @@ EpiArgs epi_blank() {
   return e;
 }
 
+// q / k_tree / v_tree bf16 (always); q32 / k32 / v32 fp32 copies or NULL;
+// out bf16, or fp16 hi / lo planes when out_lo is set
 int run_attention(const lucev_shape* s, const TreeArgs& t, const lucev_kv* kv, const uint16_t* q,
-                  const uint16_t* k_tree, const uint16_t* v_tree, uint16_t* out, int out_f16,
-                  void* ws, const Ws& L, hipStream_t st) {
+                  const uint16_t* k_tree, const uint16_t* v_tree, const float* q32,
+                  const float* k32, const float* v32, uint16_t* out, uint16_t* out_lo, void* ws,
+                  const Ws& L, hipStream_t st) {
   AttnPlan plan = plan_attention(t.n, s->n_q_heads, s->n_kv_heads, s->head_dim, kv->prefix_len);
   AttnParams p;
   p.q = q;
+  p.q32 = q32;
   p.kc = kv->k;
   p.vc = kv->v;
   p.cap = kv->capacity;
@@ -227,12 +241,15 @@ int run_attention(const lucev_shape* s, const TreeArgs& t, const lucev_kv* kv, c
   p.n_kv_heads = s->n_kv_heads;
   p.rows = plan.rows;
   p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)s->head_dim));
-  p.o_part = at<uint16_t>(ws, L.opart);
+  p.o_part = at<float>(ws, L.opart);
   p.ml_part = at<float>(ws, L.ml);
   CombineParams c;
   c.q = q;
   c.k_tree = k_tree;
   c.v_tree = v_tree;
+  c.q32 = q32;
+  c.k32 = k32;
+  c.v32 = v32;
   c.o_part = p.o_part;
   c.ml_part = p.ml_part;
   c.n_chunks = plan.n_chunks;
@@ -242,7 +259,7 @@ int run_attention(const lucev_shape* s, const TreeArgs& t, const lucev_kv* kv, c
   c.rows = plan.rows;
   c.scale_log2 = p.scale_log2;
   c.out = out;
-  c.out_f16 = out_f16;
+  c.out_lo = out_lo;
   hipError_t e = launch_attention(plan, s->head_dim, p, c, t, st);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return LUCEV_OK;
@@ -338,7 +355,8 @@ int lucev_tree_attention(const lucev_shape* shape, const lucev_tree* tree, const
   Ws L;
   if ((rc = check_ws(shape, t.n, kv->prefix_len, ws, ws_bytes, &L))) return rc;
   if ((rc = check_device())) return rc;
-  return run_attention(shape, t, kv, q, k_tree, v_tree, out, 0, ws, L, (hipStream_t)stream);
+  return run_attention(shape, t, kv, q, k_tree, v_tree, nullptr, nullptr, nullptr, out, nullptr, ws,
+                       L, (hipStream_t)stream);
 }
 
 int lucev_verify_layer(const lucev_shape* shape, const lucev_layer_w* w, const lucev_tree* tree,
@@ -365,20 +383,30 @@ int lucev_verify_layer(const lucev_shape* shape, const lucev_layer_w* w, const l
 
   hipStream_t st = (hipStream_t)stream;
   const int n = t.n;
-  uint16_t* X = at<uint16_t>(ws, L.x);
-  uint16_t* M = at<uint16_t>(ws, L.m);
-  uint16_t* Q = at<uint16_t>(ws, L.q);
+  const float eps = shape->rms_eps;
+  uint16_t* Xhi = at<uint16_t>(ws, L.xhi);
+  uint16_t* Xlo = at<uint16_t>(ws, L.xlo);
+  uint16_t* Mhi = at<uint16_t>(ws, L.mhi);
+  uint16_t* Mlo = at<uint16_t>(ws, L.mlo);
+  float* q32 = at<float>(ws, L.q32);
+  float* k32 = at<float>(ws, L.k32);
+  float* v32 = at<float>(ws, L.v32);
+  float* stats = at<float>(ws, L.stats);
+  float* ssq = at<float>(ws, L.ssq);
   hipError_t e;
 
-  // attention half: RMSNorm -> QKV (+RoPE, tree K/V out) -> tree attention -> Wo + residual
-  if ((e = launch_rmsnorm(resid_io, n, (int)H, w->attn_norm, shape->rms_eps, X, (int)H, st)) != hipSuccess)
-    return hip_fail(e, "rmsnorm launch");
+  // attention half: RMSNorm (row statistic, then folded into the QKV operand)
+  // -> QKV + RoPE -> tree attention -> Wo + residual
+  if ((e = launch_row_ssq(resid_io, n, (int)H, stats, st)) != hipSuccess) return hip_fail(e, "row_ssq launch");
   {
-    GemmParams p = gemm_params(w->wqkv, X, (int)H, n, ws, L);
+    GemmParams p = gemm_params(w->wqkv, A_F32N, resid_io, nullptr, w->attn_norm, stats, 1, (int)H, n,
+                               eps, ws, L);
     EpiArgs ea = epi_blank();
-    ea.out16 = Q;
     ea.k_out = k_tree_out;
     ea.v_out = v_tree_out;
+    ea.q32 = q32;
+    ea.k32 = k32;
+    ea.v32 = v32;
     ea.n_q_heads = (int)Hq;
     ea.n_kv_heads = (int)Hkv;
     ea.head_dim = (int)d;
@@ -386,26 +414,31 @@ int lucev_verify_layer(const lucev_shape* shape, const lucev_layer_w* w, const l
     for (int j = 0; j < d / 2; ++j) ea.inv_freq[j] = pow((double)shape->rope_base, -2.0 * j / (double)d);
     if ((e = launch_gemm(EPI_QKV, p, ea, st)) != hipSuccess) return hip_fail(e, "qkv gemm launch");
   }
-  if ((rc = run_attention(shape, t, kv, Q, k_tree_out, v_tree_out, X, 1, ws, L, st))) return rc;
+  if ((rc = run_attention(shape, t, kv, nullptr, k_tree_out, v_tree_out, q32, k32, v32, Xhi, Xlo, ws,
+                          L, st)))
+    return rc;
+  GemmParams pwo = gemm_params(w->wo, A_F16HL, Xhi, Xlo, nullptr, nullptr, 0, (int)(Hq * d), n, eps,
+                               ws, L);
   {
-    GemmParams p = gemm_params(w->wo, X, (int)(Hq * d), n, ws, L);
+    // the residual update also emits per-group sums of x^2 for the FFN RMSNorm
     EpiArgs ea = epi_blank();
     ea.resid = resid_io;
     ea.ld_out = (int)H;
-    if ((e = launch_gemm(EPI_RESID, p, ea, st)) != hipSuccess) return hip_fail(e, "wo gemm launch");
+    ea.ssq_out = ssq;
+    if ((e = launch_gemm(EPI_RESID, pwo, ea, st)) != hipSuccess) return hip_fail(e, "wo gemm launch");
   }
-  // FFN half: RMSNorm -> gate/up + SwiGLU -> down + residual
-  if ((e = launch_rmsnorm(resid_io, n, (int)H, w->ffn_norm, shape->rms_eps, X, (int)H, st)) != hipSuccess)
-    return hip_fail(e, "rmsnorm launch");
+  // FFN half: RMSNorm folded into gate/up + SwiGLU -> down + residual
   {
-    GemmParams p = gemm_params(w->wgu, X, (int)H, n, ws, L);
+    GemmParams p = gemm_params(w->wgu, A_F32N, resid_io, nullptr, w->ffn_norm, ssq, pwo.fgroups,
+                               (int)H, n, eps, ws, L);
     EpiArgs ea = epi_blank();
-    ea.out16 = M;
+    ea.out16 = Mhi;
+    ea.out16_lo = Mlo;
     ea.ld_out = (int)F;
     if ((e = launch_gemm(EPI_SWIGLU, p, ea, st)) != hipSuccess) return hip_fail(e, "gate/up gemm launch");
   }
   {
-    GemmParams p = gemm_params(w->wd, M, (int)F, n, ws, L);
+    GemmParams p = gemm_params(w->wd, A_F16HL, Mhi, Mlo, nullptr, nullptr, 0, (int)F, n, eps, ws, L);
     EpiArgs ea = epi_blank();
     ea.resid = resid_io;
     ea.ld_out = (int)H;
@@ -434,20 +467,18 @@ int lucev_accept_path(const lucev_shape* shape, const lucev_head_w* w, const luc
   hipStream_t st = (hipStream_t)stream;
   const int n = t.n;
   const int H = shape->hidden;
-  uint16_t* X = at<uint16_t>(ws, L.x);
   hipError_t e;
-  if ((e = launch_rmsnorm(resid, n, H, w->final_norm, shape->rms_eps, X, H, st)) != hipSuccess)
-    return hip_fail(e, "rmsnorm launch");
-  GemmParams p = gemm_params(w->lm_head, X, H, n, ws, L);
+  float* stats = at<float>(ws, L.stats);
+  if ((e = launch_row_ssq(resid, n, H, stats, st)) != hipSuccess) return hip_fail(e, "row_ssq launch");
+  GemmParams p = gemm_params(w->lm_head, A_F32N, resid, nullptr, w->final_norm, stats, 1, H, n,
+                             shape->rms_eps, ws, L);
   EpiArgs ea = epi_blank();
   ea.out16 = logits_out;
   ea.ld_out = shape->vocab;
   ea.cand = at<f32x4>(ws, L.cand);
-  ea.cand_stride = n;
   if ((e = launch_gemm(EPI_LOGITS, p, ea, st)) != hipSuccess) return hip_fail(e, "lm_head gemm launch");
-  uint32_t* counter = at<uint32_t>(ws, L.counters) + (kCounters - 1);
-  if ((e = launch_finalize(ea.cand, p.fgroups, n, t, argmax_out, gap_out, path_out, path_len_out,
-                           committed_out, counter, st)) != hipSuccess)
+  if ((e = launch_finalize(ea.cand, p.blocks, t, argmax_out, gap_out, path_out, path_len_out,
+                           committed_out, st)) != hipSuccess)
     return hip_fail(e, "finalize launch");
   return LUCEV_OK;
 }

@@ -93,8 +93,10 @@ __global__ __launch_bounds__(QPW == 1 ? 1024 : 512) void attn_partial_kernel(Att
     }
   };
 
-  // query tiles of this wave; Q^T fragments stay in registers
+  // query tiles of this wave; Q^T fragments stay in registers as bf16 hi + lo
+  // (about 16 significant bits of q; the keys are exact bf16)
   bf16x8 qf[QPW][D / 32];
+  bf16x8 ql[QPW][D / 32];
   f32x4 O[QPW][D / 16];
   float m[QPW], l[QPW];
 #pragma unroll
@@ -109,15 +111,31 @@ __global__ __launch_bounds__(QPW == 1 ? 1024 : 512) void attn_partial_kernel(Att
     }
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) {
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (ok) v = ld16(p.q + ((int64_t)node * p.n_q_heads + head) * D + kk * 32 + lq * 8);
-      qf[i][kk] = __builtin_bit_cast(bf16x8, v);
+      const int64_t off = ((int64_t)node * p.n_q_heads + head) * D + kk * 32 + lq * 8;
+      if (p.q32) {
+        bf16x8 hv, lv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = ok ? p.q32[off + e] : 0.f;
+          const __bf16 hb = (__bf16)x;
+          hv[e] = hb;
+          lv[e] = (__bf16)(x - (float)hb);
+        }
+        qf[i][kk] = hv;
+        ql[i][kk] = lv;
+      } else {
+        u32x4 v = u32x4{0u, 0u, 0u, 0u};
+        if (ok) v = ld16(p.q + off);
+        qf[i][kk] = __builtin_bit_cast(bf16x8, v);
+        ql[i][kk] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+      }
     }
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) O[i][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     m[i] = -INFINITY;
     l[i] = 0.f;
   }
+  const bool q_lo = p.q32 != nullptr;
 
   gload(k_begin);
   sstore();
@@ -142,6 +160,7 @@ __global__ __launch_bounds__(QPW == 1 ? 1024 : 512) void attn_partial_kernel(Att
         for (int kk = 0; kk < D / 32; ++kk) {
           const bf16x8 a = *reinterpret_cast<const bf16x8*>(sK + key * KLD + kk * 32 + lq * 8);
           sacc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[i][kk], sacc[s], 0, 0, 0);
+          if (q_lo) sacc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[i][kk], sacc[s], 0, 0, 0);
         }
       }
       // this lane holds query lr, keys ks*32 + lq*8 + h*4 + ii
@@ -176,17 +195,23 @@ __global__ __launch_bounds__(QPW == 1 ? 1024 : 512) void attn_partial_kernel(Att
       for (int dt = 0; dt < D / 16; ++dt) O[i][dt] *= alpha;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        bf16x8 pb;
+        // P as bf16 hi + lo (about 16 significant bits)
+        bf16x8 pb, pl;
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
-          pb[ii] = (__bf16)sacc[2 * ks][ii];
-          pb[4 + ii] = (__bf16)sacc[2 * ks + 1][ii];
+          const __bf16 h0 = (__bf16)sacc[2 * ks][ii];
+          const __bf16 h1 = (__bf16)sacc[2 * ks + 1][ii];
+          pb[ii] = h0;
+          pb[4 + ii] = h1;
+          pl[ii] = (__bf16)(sacc[2 * ks][ii] - (float)h0);
+          pl[4 + ii] = (__bf16)(sacc[2 * ks + 1][ii] - (float)h1);
         }
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) {
           const bf16x8 a =
               *reinterpret_cast<const bf16x8*>(sV + (dt * 16 + lr) * VLD + ks * 32 + lq * 8);
           O[i][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, O[i][dt], 0, 0, 0);
+          O[i][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl, O[i][dt], 0, 0, 0);
         }
       }
     }
@@ -208,16 +233,11 @@ __global__ __launch_bounds__(QPW == 1 ? 1024 : 512) void attn_partial_kernel(Att
     if (row < p.rows) {
       const float inv = 1.0f / lt;
       const int64_t prow = ((int64_t)chunk * p.n_kv_heads + g) * p.rows + row;
-      uint16_t* dst = p.o_part + prow * D + lq * 4;
+      float* dst = p.o_part + prow * D + lq * 4;
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) {
+      for (int dt = 0; dt < D / 16; ++dt)
         // O^T layout: this lane holds query lr, dims dt*16 + 4*lq + ii
-        const uint32_t lo = (uint32_t)f32_to_f16_bits(O[i][dt][0] * inv) |
-                            ((uint32_t)f32_to_f16_bits(O[i][dt][1] * inv) << 16);
-        const uint32_t hi = (uint32_t)f32_to_f16_bits(O[i][dt][2] * inv) |
-                            ((uint32_t)f32_to_f16_bits(O[i][dt][3] * inv) << 16);
-        *reinterpret_cast<u32x2*>(dst + dt * 16) = u32x2{lo, hi};
-      }
+        *reinterpret_cast<f32x4*>(dst + dt * 16) = O[i][dt] * inv;
       if (lq == 0) {
         p.ml_part[prow * 2] = m[i];
         p.ml_part[prow * 2 + 1] = lt;
@@ -226,66 +246,105 @@ __global__ __launch_bounds__(QPW == 1 ? 1024 : 512) void attn_partial_kernel(Att
   }
 }
 
-template <int D>
-__device__ __forceinline__ float block_sum_d(float v, float* red) {
-  v = wave_sum(v);
-  if constexpr (D <= 64) {
-    return v;
-  } else {
-    const int wave = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) red[wave] = v;
-    __syncthreads();
-    float s = 0.f;
-#pragma unroll
-    for (int w = 0; w < D / 64; ++w) s += red[w];
-    __syncthreads();
-    return s;
-  }
-}
+constexpr int kMaxChunks = 512;
 
+// One block (256 threads) per (node, query head): log-sum-exp merge of the
+// prefix-chunk partials with the node's ancestor keys.
 template <int D>
-__global__ __launch_bounds__(D) void attn_combine_kernel(CombineParams c, TreeArgs t) {
-  __shared__ float red[4];
+__global__ __launch_bounds__(256) void attn_combine_kernel(CombineParams c, TreeArgs t) {
+  constexpr int PARTS = 256 / D;  // threads per output dim
+  constexpr int DPL = D / 64;     // dims per lane in the ancestor dot products
+  __shared__ float s_w[kMaxChunks];
   __shared__ float s_anc[kMaxNodes];
+  __shared__ float s_red[4];
+  __shared__ float s_acc[PARTS][D];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int node = blockIdx.x / c.n_q_heads;
   const int h = blockIdx.x - node * c.n_q_heads;
   const int G = c.n_q_heads / c.n_kv_heads;
   const int g = h / G;
   const int row = node * G + (h - g * G);
-  const int j = threadIdx.x;
-
-  const float qj = bf16_bits_to_f32(c.q[((int64_t)node * c.n_q_heads + h) * D + j]);
   const uint64_t anc = t.anc[node];
-  float M = -INFINITY;
-  int na = 0;
-  for (int a = 0; a < t.n; ++a) {
-    if (!((anc >> a) & 1ull)) continue;
-    const float kj = bf16_bits_to_f32(c.k_tree[((int64_t)a * c.n_kv_heads + g) * D + j]);
-    const float s = block_sum_d<D>(qj * kj, red) * c.scale_log2;
-    if (j == 0) s_anc[na] = s;
-    ++na;
-    M = fmaxf(M, s);
-  }
-  __syncthreads();
-  for (int ch = 0; ch < c.n_chunks; ++ch)
-    M = fmaxf(M, c.ml_part[(((int64_t)ch * c.n_kv_heads + g) * c.rows + row) * 2]);
 
-  float L = 0.f, acc = 0.f;
-  for (int ch = 0; ch < c.n_chunks; ++ch) {
+  // ancestor scores: wave w takes every 4th ancestor
+  {
+    float qv[DPL];
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) {
+      const int64_t o = ((int64_t)node * c.n_q_heads + h) * D + lane * DPL + i;
+      qv[i] = c.q32 ? c.q32[o] : bf16_bits_to_f32(c.q[o]);
+    }
+    int k = 0;
+    for (int a = 0; a < t.n; ++a) {
+      if (!((anc >> a) & 1ull)) continue;
+      if ((k & 3) == wave) {
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) {
+          const int64_t o = ((int64_t)a * c.n_kv_heads + g) * D + lane * DPL + i;
+          s += qv[i] * (c.k32 ? c.k32[o] : bf16_bits_to_f32(c.k_tree[o]));
+        }
+        s = wave_sum(s) * c.scale_log2;
+        if (lane == 0) s_anc[k] = s;
+      }
+      ++k;
+    }
+  }
+  const int na = __popcll(anc);
+  // running max over chunk maxima and ancestor scores
+  float mx = -INFINITY;
+  for (int ch = tid; ch < c.n_chunks; ch += 256)
+    mx = fmaxf(mx, c.ml_part[(((int64_t)ch * c.n_kv_heads + g) * c.rows + row) * 2]);
+  mx = wave_max(mx);
+  if (lane == 0) s_red[wave] = mx;
+  __syncthreads();
+  float M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  for (int k = 0; k < na; ++k) M = fmaxf(M, s_anc[k]);
+  __syncthreads();
+  float lsum = 0.f;
+  for (int ch = tid; ch < c.n_chunks; ch += 256) {
     const int64_t prow = ((int64_t)ch * c.n_kv_heads + g) * c.rows + row;
     const float w = __builtin_amdgcn_exp2f(c.ml_part[prow * 2] - M) * c.ml_part[prow * 2 + 1];
-    L += w;
-    acc += w * f16_bits_to_f32(c.o_part[prow * D + j]);
+    s_w[ch] = w;
+    lsum += w;
   }
-  na = 0;
-  for (int a = 0; a < t.n; ++a) {
-    if (!((anc >> a) & 1ull)) continue;
-    const float w = __builtin_amdgcn_exp2f(s_anc[na++] - M);
-    L += w;
-    acc += w * bf16_bits_to_f32(c.v_tree[((int64_t)a * c.n_kv_heads + g) * D + j]);
+  lsum = wave_sum(lsum);
+  if (lane == 0) s_red[wave] = lsum;
+  __syncthreads();
+  float L = (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
+  for (int k = 0; k < na; ++k) L += __builtin_amdgcn_exp2f(s_anc[k] - M);
+
+  // weighted sum of the chunk outputs: PARTS threads per dim, fixed order
+  const int j = tid % D, part = tid / D;
+  float acc = 0.f;
+#pragma unroll 8
+  for (int ch = part; ch < c.n_chunks; ch += PARTS) {
+    const int64_t prow = ((int64_t)ch * c.n_kv_heads + g) * c.rows + row;
+    acc += s_w[ch] * c.o_part[prow * D + j];
   }
-  const float o = acc / L;
-  c.out[((int64_t)node * c.n_q_heads + h) * D + j] = c.out_f16 ? f32_to_f16_bits(o) : f32_to_bf16_bits(o);
+  s_acc[part][j] = acc;
+  __syncthreads();
+  if (tid < D) {
+    float o = 0.f;
+#pragma unroll
+    for (int q = 0; q < PARTS; ++q) o += s_acc[q][j];
+    int k = 0;
+    for (int a = 0; a < t.n; ++a) {
+      if (!((anc >> a) & 1ull)) continue;
+      const int64_t vo = ((int64_t)a * c.n_kv_heads + g) * D + j;
+      o += __builtin_amdgcn_exp2f(s_anc[k++] - M) * (c.v32 ? c.v32[vo] : bf16_bits_to_f32(c.v_tree[vo]));
+    }
+    o /= L;
+    const int64_t oo = ((int64_t)node * c.n_q_heads + h) * D + j;
+    if (c.out_lo) {
+      const f16 hi = (f16)o;
+      c.out[oo] = __builtin_bit_cast(uint16_t, hi);
+      c.out_lo[oo] = f32_to_f16_bits(o - (float)hi);
+    } else {
+      c.out[oo] = f32_to_bf16_bits(o);
+    }
+  }
 }
 
 int attention_max_chunks(int n_kv_heads) { return (512 + n_kv_heads - 1) / n_kv_heads; }
@@ -340,9 +399,9 @@ hipError_t launch_attention(const AttnPlan& plan, int head_dim, const AttnParams
   }
   const int blocks = c.n * c.n_q_heads;
   if (head_dim == 128)
-    hipLaunchKernelGGL((attn_combine_kernel<128>), dim3(blocks), dim3(128), 0, s, c, t);
+    hipLaunchKernelGGL((attn_combine_kernel<128>), dim3(blocks), dim3(256), 0, s, c, t);
   else
-    hipLaunchKernelGGL((attn_combine_kernel<64>), dim3(blocks), dim3(64), 0, s, c, t);
+    hipLaunchKernelGGL((attn_combine_kernel<64>), dim3(blocks), dim3(256), 0, s, c, t);
   return hipGetLastError();
 }
 

@@ -6,9 +6,10 @@
 // item 1; section "Speculative decoding 계층"), so this kernel streams the
 // packed weights exactly once and reuses each dequantised weight for every
 // tree node.  With 16..64 nodes that reuse is a dense contraction, so the
-// MAC work goes to MFMA (v_mfma_f32_16x16x32_f16); the weights are
-// dequantised in registers (exponent-bias trick, exact q - 8, one fp16
-// rounding of d * (q - 8)) and never touch LDS.
+// MAC work goes to MFMA (v_mfma_f32_16x16x32_f16); the codes are expanded in
+// registers (exponent-bias trick: exact q - 8 as fp16), each 32-column block
+// is one MFMA K-step whose fp32 result takes the block's scale d, and the
+// weights never touch LDS.
 //
 // Packed layout (private to this library, written by lucev_q4_pack*):
 //   nibble region, per 16-row tile t and 128-column group c, 1024 bytes:
@@ -103,8 +104,8 @@ hipError_t launch_pack_q4(const uint8_t* q, const uint16_t* d, int64_t n_out, in
 
 // ------------------------------------------------------------ dequant
 
-// 8 codes of one dword -> 8 fp16 weights d * (q - 8) in column order.
-__device__ __forceinline__ f16x8 dequant8(uint32_t w, f16x2 s2) {
+// 8 codes of one dword -> the 8 exact values (q - 8) as fp16, column order.
+__device__ __forceinline__ f16x8 codes8(uint32_t w) {
   const uint32_t v0 = (w & 0x000F000Fu) | 0x64006400u;       // 1024 + q (cols 0, 1)
   const uint32_t v1 = (w & 0x00F000F0u) | 0x54005400u;       //   64 + q (cols 2, 3)
   const uint32_t w8 = w >> 8;
@@ -112,296 +113,463 @@ __device__ __forceinline__ f16x8 dequant8(uint32_t w, f16x2 s2) {
   const uint32_t v3 = (w8 & 0x00F000F0u) | 0x54005400u;      //   64 + q (cols 6, 7)
   const f16x2 b1032 = {(f16)1032.0f, (f16)1032.0f};
   const f16x2 b72 = {(f16)72.0f, (f16)72.0f};
-  f16x2 h0 = (__builtin_bit_cast(f16x2, v0) - b1032) * s2;
-  f16x2 h1 = (__builtin_bit_cast(f16x2, v1) - b72) * s2;
-  f16x2 h2 = (__builtin_bit_cast(f16x2, v2) - b1032) * s2;
-  f16x2 h3 = (__builtin_bit_cast(f16x2, v3) - b72) * s2;
+  const f16x2 h0 = __builtin_bit_cast(f16x2, v0) - b1032;
+  const f16x2 h1 = __builtin_bit_cast(f16x2, v1) - b72;
+  const f16x2 h2 = __builtin_bit_cast(f16x2, v2) - b1032;
+  const f16x2 h3 = __builtin_bit_cast(f16x2, v3) - b72;
   return f16x8{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
 }
 
-__device__ __forceinline__ f16x2 scale_pair(u32x2 s, int j) {
+// fp16 scale of block j (of 4) from the lane's 4 packed scales, as fp32
+__device__ __forceinline__ float scale_f32(u32x2 s, int j) {
   const uint32_t word = (j < 2) ? s[0] : s[1];
   const uint16_t bits = (uint16_t)((j & 1) ? (word >> 16) : (word & 0xFFFFu));
-  const f16 v = __builtin_bit_cast(f16, bits);
-  return f16x2{v, v};
+  return (float)__builtin_bit_cast(f16, bits);
 }
 
 // ------------------------------------------------------------ the GEMM
+//
+// Work: units (fg, c) = (FT-tile feature group, 128-column group), fg-major,
+// split into equal contiguous ranges, one per block (block-level stream-K:
+// every block gets the same number of weight bytes).  Inside a block the 4
+// waves take a segment's column groups round-robin; partial sums meet in LDS.
+// A feature group cut between blocks is finished by whichever contributor
+// arrives last: partial tiles are written with agent-scope stores, published
+// by a release increment of the group's counter, read back with agent-scope
+// loads and summed in block order, so results do not depend on timing.
+//
+// Precision: the activation operand is carried as two fp16 halves
+// (x = hi + lo, about 22 significant bits) and both go through the MFMA, and
+// the weights enter exactly, so rounding does not compound through a deep
+// stack.  The
+// normalised inputs of the QKV / gate-up / lm_head projections are formed
+// here from the fp32 residual: u = x * rsqrt(mean(x^2) + eps) * g, with the
+// row sums of x^2 produced by the previous kernel.
 
-template <int NT, int FT>
-struct Frag {
+template <int NT, int FT, int AM>
+struct Raw {
   u32x4 w[FT];
   u32x2 s[FT];
-  u32x4 x[NT][4];
+  u32x4 x[NT][4][2];                  // fp16 hi / lo planes, or fp32 x4 pairs
+  u32x4 g[AM == A_F32N ? 4 : 1];      // bf16 gain x8 per block
 };
 
 template <int NT, int FT>
-__device__ __forceinline__ void load_frag(const GemmParams& p, int c, int t0, int lane,
-                                          Frag<NT, FT>& f) {
+struct Ready {
+  u32x4 w[FT];
+  u32x2 s[FT];
+  f16x8 hi[NT][4];
+  f16x8 lo[NT][4];
+};
+
+template <int NT, int FT, int AM>
+__device__ __forceinline__ void load_raw(const GemmParams& p, int c, int t0, int lane,
+                                         Raw<NT, FT, AM>& r) {
   const int lr = lane & 15, lq = lane >> 4;
 #pragma unroll
   for (int ft = 0; ft < FT; ++ft) {
     int t = t0 + ft;
     t = t < p.n_tiles ? t : p.n_tiles - 1;  // ragged last group: re-read a valid tile
     const int64_t tg = (int64_t)t * p.kgroups + c;
-    f.w[ft] = ld16(p.wq + tg * 1024 + lane * 16);
-    f.s[ft] = *reinterpret_cast<const u32x2*>(p.wsc + tg * 64 + lr * 4);
+    r.w[ft] = ld16(p.wq + tg * 1024 + lane * 16);
+    r.s[ft] = *reinterpret_cast<const u32x2*>(p.wsc + tg * 64 + lr * 4);
+  }
+  if constexpr (AM == A_F32N) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r.g[j] = ld16(p.g + c * 128 + j * 32 + lq * 8);
   }
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int node = nt * 16 + lr;
+    const bool ok = node < p.n_nodes;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      if (node < p.n_nodes)
-        f.x[nt][j] = ld16(p.X + (int64_t)node * p.ldx + c * 128 + j * 32 + lq * 8);
-      else
-        f.x[nt][j] = u32x4{0u, 0u, 0u, 0u};
+      const int64_t off = (int64_t)node * p.ldx + c * 128 + j * 32 + lq * 8;
+      const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+      if constexpr (AM == A_F32N) {
+        r.x[nt][j][0] = ok ? ld16(p.Xf + off) : z;
+        r.x[nt][j][1] = ok ? ld16(p.Xf + off + 4) : z;
+      } else {
+        r.x[nt][j][0] = ok ? ld16(p.Xhi + off) : z;
+        r.x[nt][j][1] = ok ? ld16(p.Xlo + off) : z;
+      }
     }
   }
 }
 
+template <int NT, int FT, int AM>
+__device__ __forceinline__ void make_ready(const Raw<NT, FT, AM>& r, Ready<NT, FT>& q,
+                                           const float (&rinv)[NT]) {
+#pragma unroll
+  for (int ft = 0; ft < FT; ++ft) {
+    q.w[ft] = r.w[ft];
+    q.s[ft] = r.s[ft];
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if constexpr (AM == A_F32N) {
+      float gf[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        gf[2 * e] = __uint_as_float(r.g[j][e] << 16);
+        gf[2 * e + 1] = __uint_as_float(r.g[j][e] & 0xFFFF0000u);
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        f16x8 h, l;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float u = __uint_as_float(r.x[nt][j][e >> 2][e & 3]) * rinv[nt] * gf[e];
+          const f16 hh = (f16)u;
+          h[e] = hh;
+          l[e] = (f16)(u - (float)hh);
+        }
+        q.hi[nt][j] = h;
+        q.lo[nt][j] = l;
+      }
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        q.hi[nt][j] = __builtin_bit_cast(f16x8, r.x[nt][j][0]);
+        q.lo[nt][j] = __builtin_bit_cast(f16x8, r.x[nt][j][1]);
+      }
+    }
+  }
+}
+
+// Per 32-column block: MFMA of the exact codes against x_hi and x_lo, then
+// the block's fp16 scale d (the MFMA column = lane % 16 = this lane's
+// feature) is applied in fp32, so every weight enters as exactly d * (q - 8).
 template <int NT, int FT>
-__device__ __forceinline__ void mma_frag(const Frag<NT, FT>& f, f32x4 (&acc)[FT][NT]) {
+__device__ __forceinline__ void mma_ready(const Ready<NT, FT>& q, f32x4 (&acc)[FT][NT]) {
+  const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft) {
-      const f16x8 b = dequant8(f.w[ft][j], scale_pair(f.s[ft], j));
+      const f16x8 b = codes8(q.w[ft][j]);
+      const float dsc = scale_f32(q.s[ft], j);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const f16x8 a = __builtin_bit_cast(f16x8, f.x[nt][j]);
-        acc[ft][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[ft][nt], 0, 0, 0);
+        f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_f16(q.hi[nt][j], b, zero, 0, 0, 0);
+        t = __builtin_amdgcn_mfma_f32_16x16x32_f16(q.lo[nt][j], b, t, 0, 0, 0);
+        acc[ft][nt] += dsc * t;
       }
     }
   }
 }
 
-__device__ __forceinline__ void rope_pair_angle(int pos, int jj, int head_dim, const double* inv_freq,
-                                                float& cs, float& sn) {
+__device__ __forceinline__ void rope_pair_angle(int pos, int jj, const double* inv_freq, float& cs,
+                                                float& sn) {
   // angle in fp64, reduced to [-pi, pi] before the fp32 sin / cos
   const double th = (double)pos * inv_freq[jj];
   const double two_pi = 6.283185307179586476925286766559;
   const double r = th - two_pi * rint(th / two_pi);
-  const float rf = (float)r;
-  sincosf(rf, &sn, &cs);
+  sincosf((float)r, &sn, &cs);
 }
 
-template <int NT, int FT, int EPI>
+__device__ __forceinline__ void merge_top2(float& v1, int& i1, float& v2, float b1, int bi, float b2) {
+  if (b1 > v1 || (b1 == v1 && bi < i1)) {
+    v2 = fmaxf(v1, b2);
+    v1 = b1;
+    i1 = bi;
+  } else {
+    v2 = fmaxf(v2, b1);
+  }
+}
+
+__device__ __forceinline__ float ld_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// the block whose unit range holds unit u (ranges are [b*U/B, (b+1)*U/B))
+__device__ __forceinline__ int block_of(int64_t u, int64_t U, int B) {
+  return (int)(((u + 1) * B - 1) / U);
+}
+
+template <int NT, int FT, int AM, int EPI>
 __global__ __launch_bounds__(256) void gemm_q4_kernel(GemmParams p, EpiArgs e) {
   constexpr int TILE_F = FT * 16;
   constexpr int TILE_N = NT * 16;
+  constexpr int TILE = TILE_F * TILE_N;
   __shared__ float red[3][FT][NT][4][64];
   __shared__ float tile[TILE_F][TILE_N + 1];
-  __shared__ int is_last;
+  __shared__ float s_rinv[TILE_N];
+  __shared__ float best1[TILE_N], best2[TILE_N];
+  __shared__ int besti[TILE_N];
+  __shared__ int s_last;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int fg = blockIdx.x / p.ksplit;
-  const int ks = blockIdx.x - fg * p.ksplit;
-  const int t0 = fg * FT;
-  const int g_begin = ks * p.gps;
-  const int g_end = min(p.kgroups, g_begin + p.gps);
-
-  f32x4 acc[FT][NT];
-#pragma unroll
-  for (int ft = 0; ft < FT; ++ft)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc[ft][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // the 4 waves interleave over the block's column groups; loads of the next
-  // group are issued before the current one is consumed
-  Frag<NT, FT> fa, fb;
-  int c = g_begin + wave;
-  if (c < g_end) load_frag(p, c, t0, lane, fa);
-  while (c < g_end) {
-    int cn = c + 4;
-    if (cn < g_end) load_frag(p, cn, t0, lane, fb);
-    mma_frag(fa, acc);
-    c = cn;
-    if (c >= g_end) break;
-    cn = c + 4;
-    if (cn < g_end) load_frag(p, cn, t0, lane, fa);
-    mma_frag(fb, acc);
-    c = cn;
-  }
-
-  // cross-wave reduction in a fixed order (deterministic)
-  if (wave > 0) {
-#pragma unroll
-    for (int ft = 0; ft < FT; ++ft)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) red[wave - 1][ft][nt][i][lane] = acc[ft][nt][i];
-  }
-  __syncthreads();
-  if (wave == 0) {
-    const int lr = lane & 15, lq = lane >> 4;
-#pragma unroll
-    for (int ft = 0; ft < FT; ++ft)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = acc[ft][nt][i];
-          v += red[0][ft][nt][i][lane];
-          v += red[1][ft][nt][i][lane];
-          v += red[2][ft][nt][i][lane];
-          // D layout: column (feature) = lane % 16, row (node) = 4 * (lane / 16) + i
-          tile[ft * 16 + lr][nt * 16 + lq * 4 + i] = v;
-        }
-  }
-  __syncthreads();
-
-  if (p.ksplit > 1) {
-    // split-K: publish this block's partial tile; the last block of the
-    // feature group sums all partials in split order and runs the epilogue
-    float* part = p.partials + ((int64_t)fg * p.ksplit + ks) * (TILE_F * TILE_N);
-    for (int i = tid; i < TILE_F * TILE_N; i += 256) part[i] = tile[i / TILE_N][i % TILE_N];
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-      const unsigned prev = atomicAdd(&p.counters[fg], 1u);
-      is_last = (prev == (unsigned)(p.ksplit - 1));
-    }
-    __syncthreads();
-    if (!is_last) return;
-    __threadfence();
-    const float* base = p.partials + (int64_t)fg * p.ksplit * (TILE_F * TILE_N);
-    for (int i = tid; i < TILE_F * TILE_N; i += 256) {
-      float s = 0.f;
-      for (int k = 0; k < p.ksplit; ++k) s += __builtin_nontemporal_load(base + (int64_t)k * (TILE_F * TILE_N) + i);
-      tile[i / TILE_N][i % TILE_N] = s;
-    }
-    if (tid == 0) atomicExch(&p.counters[fg], 0u);
-    __syncthreads();
-  }
-
+  const int lr = lane & 15, lq = lane >> 4;
+  const int b = blockIdx.x;
+  const int B = p.blocks;
+  const int64_t U = p.units;
+  const int G = p.kgroups;
   const int nn = p.n_nodes;
-  if constexpr (EPI == EPI_RESID) {
-    // x += y (fp32 residual stream, plain row order)
-    for (int i = tid; i < TILE_F * nn; i += 256) {
-      const int n = i / TILE_F, fl = i - n * TILE_F;
-      const int64_t f = (int64_t)t0 * 16 + fl;
-      if (f < p.n_out) e.resid[(int64_t)n * e.ld_out + f] += tile[fl][n];
+  const int64_t u_begin = (int64_t)b * U / B;
+  const int64_t u_end = (int64_t)(b + 1) * U / B;
+
+  if constexpr (EPI == EPI_LOGITS) {
+    if (tid < TILE_N) {
+      best1[tid] = -INFINITY;
+      best2[tid] = -INFINITY;
+      besti[tid] = 0x7fffffff;
     }
-  } else if constexpr (EPI == EPI_SWIGLU) {
-    // packed tiles (2i, 2i+1) = (gate, up) rows [16i, 16i + 16)
-    for (int i = tid; i < (TILE_F / 2) * nn; i += 256) {
-      const int n = i / (TILE_F / 2), rl = i - n * (TILE_F / 2);
-      const int a = rl / 16, r = rl % 16;
-      const int64_t row = ((int64_t)t0 / 2 + a) * 16 + r;
-      if (2 * row < p.n_out) {
-        const float gt = tile[(2 * a) * 16 + r][n];
-        const float up = tile[(2 * a + 1) * 16 + r][n];
-        const float m = gt / (1.0f + expf(-gt)) * up;
-        e.out16[(int64_t)n * e.ld_out + row] = f32_to_f16_bits(m);
+  }
+  // 1/rms per row for the normalised input, from the producer's partial sums
+  if constexpr (AM == A_F32N) {
+    if (tid < TILE_N) {
+      float r = 0.f;
+      if (tid < nn) {
+        float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+        int i = 0;
+        for (; i + 4 <= p.ssq_groups; i += 4) {
+          s0 += p.ssq[(int64_t)i * nn + tid];
+          s1 += p.ssq[(int64_t)(i + 1) * nn + tid];
+          s2 += p.ssq[(int64_t)(i + 2) * nn + tid];
+          s3 += p.ssq[(int64_t)(i + 3) * nn + tid];
+        }
+        for (; i < p.ssq_groups; ++i) s0 += p.ssq[(int64_t)i * nn + tid];
+        r = 1.0f / sqrtf(((s0 + s1) + (s2 + s3)) / (float)p.k_in + p.rms_eps);
+      }
+      s_rinv[tid] = r;
+    }
+  }
+  __syncthreads();
+  float rinv[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) rinv[nt] = AM == A_F32N ? s_rinv[nt * 16 + lr] : 1.f;
+
+  for (int64_t u = u_begin; u < u_end;) {
+    const int fg = (int)(u / G);
+    const int c0 = (int)(u - (int64_t)fg * G);
+    const int c1 = (int)min((int64_t)G, (int64_t)c0 + (u_end - u));
+    u += c1 - c0;
+    const int t0 = fg * FT;
+
+    f32x4 acc[FT][NT];
+#pragma unroll
+    for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[ft][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    {
+      Raw<NT, FT, AM> raw;
+      Ready<NT, FT> rdy;
+      int c = c0 + wave;
+      if (c < c1) load_raw(p, c, t0, lane, raw);
+      while (c < c1) {
+        make_ready(raw, rdy, rinv);
+        const int cn = c + 4;
+        if (cn < c1) load_raw(p, cn, t0, lane, raw);
+        mma_ready(rdy, acc);
+        c = cn;
       }
     }
-  } else if constexpr (EPI == EPI_QKV) {
-    // rotate-half RoPE on q and k at pos = prefix_len + depth; v unrotated
-    const int hd = e.head_dim;
-    for (int i = tid; i < TILE_F * nn; i += 256) {
-      const int n = i / TILE_F, fl = i - n * TILE_F;
-      const int64_t prow = (int64_t)t0 * 16 + fl;
-      if (prow >= p.n_out) continue;
-      const int head = (int)(prow / hd);
-      const int r = (int)(prow % hd);
-      const int ti = r / 16, loc = r % 16;
-      const int j = loc < 8 ? 8 * ti + loc : hd / 2 + 8 * ti + (loc - 8);
-      float val = tile[fl][n];
-      if (head < e.n_q_heads + e.n_kv_heads) {
-        const float partner = tile[fl ^ 8][n];
-        float cs, sn;
-        const int jj = j < hd / 2 ? j : j - hd / 2;
-        rope_pair_angle(e.pos[n], jj, hd, e.inv_freq, cs, sn);
-        val = j < hd / 2 ? val * cs - partner * sn : partner * sn + val * cs;
-      }
-      uint16_t* dst;
-      if (head < e.n_q_heads)
-        dst = e.out16 + ((int64_t)n * e.n_q_heads + head) * hd + j;
-      else if (head < e.n_q_heads + e.n_kv_heads)
-        dst = e.k_out + ((int64_t)n * e.n_kv_heads + (head - e.n_q_heads)) * hd + j;
-      else
-        dst = e.v_out + ((int64_t)n * e.n_kv_heads + (head - e.n_q_heads - e.n_kv_heads)) * hd + j;
-      *dst = f32_to_bf16_bits(val);
+
+    // cross-wave reduction in a fixed order (deterministic)
+    if (wave > 0) {
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) red[wave - 1][ft][nt][i][lane] = acc[ft][nt][i];
     }
-  } else if constexpr (EPI == EPI_LOGITS) {
-    if (e.out16) {
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float v = acc[ft][nt][i];
+            v += red[0][ft][nt][i][lane];
+            v += red[1][ft][nt][i][lane];
+            v += red[2][ft][nt][i][lane];
+            // D layout: column (feature) = lane % 16, row (node) = 4 * (lane / 16) + i
+            tile[ft * 16 + lr][nt * 16 + lq * 4 + i] = v;
+          }
+    }
+    __syncthreads();
+
+    // a feature group cut between blocks: last contributor to arrive sums
+    const int bf = block_of((int64_t)fg * G, U, B);
+    const int bl = block_of((int64_t)fg * G + G - 1, U, B);
+    if (bf != bl) {
+      const int slot = (u_begin >= (int64_t)fg * G) ? 0 : 1;
+      float* part = p.partials + ((int64_t)b * 2 + slot) * TILE;
+      for (int i = tid; i < TILE; i += 256) st_coherent(part + i, tile[i / TILE_N][i % TILE_N]);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // every wave's stores done
+      __syncthreads();
+      if (tid == 0) {
+        // release: this block's partial stores are visible before the count
+        const unsigned prev = __hip_atomic_fetch_add(&p.counters[fg], 1u, __ATOMIC_RELEASE,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        s_last = prev == (unsigned)(bl - bf);
+      }
+      __syncthreads();
+      if (!s_last) continue;
+      for (int i = tid; i < TILE; i += 256) {
+        float s = 0.f;
+        for (int bb = bf; bb <= bl; ++bb) {
+          const int sl = ((int64_t)bb * U / B >= (int64_t)fg * G) ? 0 : 1;
+          s += ld_coherent(p.partials + ((int64_t)bb * 2 + sl) * TILE + i);
+        }
+        tile[i / TILE_N][i % TILE_N] = s;
+      }
+      if (tid == 0)
+        __hip_atomic_store(&p.counters[fg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+    }
+
+    // ---------------- epilogues on the finished tile [feature][node]
+    if constexpr (EPI == EPI_RESID) {
+      // x += y; the new rows' per-group sums of x^2 feed the next RMSNorm
       for (int i = tid; i < TILE_F * nn; i += 256) {
         const int n = i / TILE_F, fl = i - n * TILE_F;
         const int64_t f = (int64_t)t0 * 16 + fl;
-        if (f < p.n_out) e.out16[(int64_t)n * e.ld_out + f] = f32_to_bf16_bits(tile[fl][n]);
+        float xn = 0.f;
+        if (f < p.n_out) {
+          float* r = e.resid + (int64_t)n * e.ld_out + f;
+          xn = *r + tile[fl][n];
+          *r = xn;
+        }
+        tile[fl][n] = xn * xn;
       }
-    }
-    // per node: best, its index (lowest on ties) and runner-up of this group
-    if (tid < nn) {
-      float v1 = -INFINITY, v2 = -INFINITY;
-      int i1 = 0x7fffffff;
-      for (int fl = 0; fl < TILE_F; ++fl) {
-        const int64_t f = (int64_t)t0 * 16 + fl;
-        if (f >= p.n_out) break;
-        const float v = tile[fl][tid];
-        if (v > v1) {
-          v2 = v1;
-          v1 = v;
-          i1 = (int)f;
-        } else if (v > v2) {
-          v2 = v;
+      if (e.ssq_out) {
+        __syncthreads();
+        if (tid < nn) {
+          float s = 0.f;
+          for (int fl = 0; fl < TILE_F; ++fl) s += tile[fl][tid];
+          e.ssq_out[(int64_t)fg * nn + tid] = s;
         }
       }
-      e.cand[(int64_t)fg * e.cand_stride + tid] =
-          f32x4{v1, __int_as_float(i1), v2, 0.f};
+    } else if constexpr (EPI == EPI_SWIGLU) {
+      // packed tiles (2i, 2i+1) = (gate, up) rows [16i, 16i + 16); m as fp16 hi + lo
+      for (int i = tid; i < (TILE_F / 2) * nn; i += 256) {
+        const int n = i / (TILE_F / 2), rl = i - n * (TILE_F / 2);
+        const int a = rl / 16, r = rl % 16;
+        const int64_t row = ((int64_t)t0 / 2 + a) * 16 + r;
+        if (2 * row < p.n_out) {
+          const float gt = tile[(2 * a) * 16 + r][n];
+          const float up = tile[(2 * a + 1) * 16 + r][n];
+          const float m = gt / (1.0f + expf(-gt)) * up;
+          const f16 hi = (f16)m;
+          e.out16[(int64_t)n * e.ld_out + row] = __builtin_bit_cast(uint16_t, hi);
+          e.out16_lo[(int64_t)n * e.ld_out + row] = f32_to_f16_bits(m - (float)hi);
+        }
+      }
+    } else if constexpr (EPI == EPI_QKV) {
+      // rotate-half RoPE on q and k at pos = prefix_len + depth; v unrotated
+      const int hd = e.head_dim;
+      for (int i = tid; i < TILE_F * nn; i += 256) {
+        const int n = i / TILE_F, fl = i - n * TILE_F;
+        const int64_t prow = (int64_t)t0 * 16 + fl;
+        if (prow >= p.n_out) continue;
+        const int head = (int)(prow / hd);
+        const int r = (int)(prow % hd);
+        const int ti = r / 16, loc = r % 16;
+        const int j = loc < 8 ? 8 * ti + loc : hd / 2 + 8 * ti + (loc - 8);
+        float val = tile[fl][n];
+        if (head < e.n_q_heads + e.n_kv_heads) {
+          const float partner = tile[fl ^ 8][n];
+          float cs, sn;
+          const int jj = j < hd / 2 ? j : j - hd / 2;
+          rope_pair_angle(e.pos[n], jj, e.inv_freq, cs, sn);
+          val = j < hd / 2 ? val * cs - partner * sn : partner * sn + val * cs;
+        }
+        if (head < e.n_q_heads) {
+          const int64_t o = ((int64_t)n * e.n_q_heads + head) * hd + j;
+          e.q32[o] = val;
+          if (e.out16) e.out16[o] = f32_to_bf16_bits(val);
+        } else if (head < e.n_q_heads + e.n_kv_heads) {
+          const int64_t o = ((int64_t)n * e.n_kv_heads + (head - e.n_q_heads)) * hd + j;
+          e.k32[o] = val;
+          e.k_out[o] = f32_to_bf16_bits(val);
+        } else {
+          const int64_t o = ((int64_t)n * e.n_kv_heads + (head - e.n_q_heads - e.n_kv_heads)) * hd + j;
+          e.v32[o] = val;
+          e.v_out[o] = f32_to_bf16_bits(val);
+        }
+      }
+    } else if constexpr (EPI == EPI_LOGITS) {
+      if (e.out16) {
+        for (int i = tid; i < TILE_F * nn; i += 256) {
+          const int n = i / TILE_F, fl = i - n * TILE_F;
+          const int64_t f = (int64_t)t0 * 16 + fl;
+          if (f < p.n_out) e.out16[(int64_t)n * e.ld_out + f] = f32_to_bf16_bits(tile[fl][n]);
+        }
+      }
+      // this group's best / runner-up per node, merged into the block's running pair
+      if (tid < nn) {
+        float v1 = best1[tid], v2 = best2[tid];
+        int i1 = besti[tid];
+        for (int fl = 0; fl < TILE_F; ++fl) {
+          const int64_t f = (int64_t)t0 * 16 + fl;
+          if (f >= p.n_out) break;
+          merge_top2(v1, i1, v2, tile[fl][tid], (int)f, -INFINITY);
+        }
+        best1[tid] = v1;
+        best2[tid] = v2;
+        besti[tid] = i1;
+      }
     }
+    __syncthreads();  // LDS tiles are reused by the next segment
+  }
+
+  if constexpr (EPI == EPI_LOGITS) {
+    if (tid < nn) e.cand[(int64_t)b * nn + tid] = f32x4{best1[tid], __int_as_float(besti[tid]), best2[tid], 0.f};
   }
 }
 
-template <int NT, int FT, int EPI>
+template <int NT, int FT, int AM, int EPI>
 static hipError_t launch_t(const GemmParams& p, const EpiArgs& e, hipStream_t s) {
-  const int blocks = p.fgroups * p.ksplit;
-  hipLaunchKernelGGL((gemm_q4_kernel<NT, FT, EPI>), dim3(blocks), dim3(256), 0, s, p, e);
+  hipLaunchKernelGGL((gemm_q4_kernel<NT, FT, AM, EPI>), dim3(p.blocks), dim3(256), 0, s, p, e);
   return hipGetLastError();
 }
 
-template <int EPI>
+template <int AM, int EPI>
 static hipError_t launch_nt(const GemmParams& p, const EpiArgs& e, hipStream_t s) {
   const int nt = (p.n_nodes + 15) / 16;
   switch (nt) {
-    case 1: return launch_t<1, 4, EPI>(p, e, s);
-    case 2: return launch_t<2, 4, EPI>(p, e, s);
-    case 3: return launch_t<3, 2, EPI>(p, e, s);
-    default: return launch_t<4, 2, EPI>(p, e, s);
+    case 1: return launch_t<1, 4, AM, EPI>(p, e, s);
+    case 2: return launch_t<2, 4, AM, EPI>(p, e, s);
+    case 3: return launch_t<3, 2, AM, EPI>(p, e, s);
+    default: return launch_t<4, 2, AM, EPI>(p, e, s);
   }
 }
 
 int gemm_ft(int n_nodes) { return ((n_nodes + 15) / 16) <= 2 ? 4 : 2; }
 
-GemmPlan plan_gemm(int64_t n_out, int64_t k_in, int n_nodes, int max_ksplit) {
+GemmPlan plan_gemm(int64_t n_out, int64_t k_in, int n_nodes) {
   GemmPlan g;
   g.ft = gemm_ft(n_nodes);
   g.nt = (n_nodes + 15) / 16;
   g.n_tiles = (int)(n_out / 16);
   g.kgroups = (int)(k_in / 128);
   g.fgroups = (g.n_tiles + g.ft - 1) / g.ft;
-  // aim for ~2 blocks per CU; each wave should still own >= 2 column groups
-  int ks = (512 + g.fgroups - 1) / g.fgroups;
-  const int ks_cap = g.kgroups / 8 > 0 ? g.kgroups / 8 : 1;
-  if (ks > ks_cap) ks = ks_cap;
-  if (ks > max_ksplit) ks = max_ksplit;
-  if (ks < 1) ks = 1;
-  g.gps = (g.kgroups + ks - 1) / ks;
-  g.ksplit = (g.kgroups + g.gps - 1) / g.gps;
+  g.units = (int64_t)g.fgroups * g.kgroups;
+  // two resident blocks per CU on 256 CUs, never more blocks than units
+  g.blocks = (int)(g.units < 512 ? g.units : 512);
   g.tile_floats = g.ft * 16 * g.nt * 16;
   return g;
 }
 
 hipError_t launch_gemm(int epi, const GemmParams& p, const EpiArgs& e, hipStream_t s) {
-  switch (epi) {
-    case EPI_RESID: return launch_nt<EPI_RESID>(p, e, s);
-    case EPI_SWIGLU: return launch_nt<EPI_SWIGLU>(p, e, s);
-    case EPI_QKV: return launch_nt<EPI_QKV>(p, e, s);
-    default: return launch_nt<EPI_LOGITS>(p, e, s);
+  if (p.a_mode == A_F32N) {
+    switch (epi) {
+      case EPI_QKV: return launch_nt<A_F32N, EPI_QKV>(p, e, s);
+      case EPI_SWIGLU: return launch_nt<A_F32N, EPI_SWIGLU>(p, e, s);
+      default: return launch_nt<A_F32N, EPI_LOGITS>(p, e, s);
+    }
   }
+  return launch_nt<A_F16HL, EPI_RESID>(p, e, s);
 }
 
 }  // namespace lucev

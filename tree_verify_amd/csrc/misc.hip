@@ -1,33 +1,27 @@
-// RMSNorm, the greedy-acceptance finalisation and a fill kernel.
+// Greedy-acceptance finalisation and a fill kernel.
 #include "internal.h"
 
 namespace lucev {
 
-// u = x / sqrt(mean(x^2) + eps) * g, one block per row, fp16 output for the
-// next projection (pre-norm decoder layer).
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x, int hidden,
-                                                      const uint16_t* __restrict__ g, float eps,
-                                                      uint16_t* __restrict__ out, int ld_out) {
+// Row sums of x^2 (the statistic of RMSNorm), one block per row, fixed
+// reduction order.
+__global__ __launch_bounds__(256) void row_ssq_kernel(const float* __restrict__ x, int hidden,
+                                                      float* __restrict__ ssq) {
   __shared__ float red[4];
-  const int row = blockIdx.x;
-  const float* xr = x + (int64_t)row * hidden;
-  float ss = 0.f;
+  const float* xr = x + (int64_t)blockIdx.x * hidden;
+  float s = 0.f;
   for (int i = threadIdx.x * 4; i < hidden; i += 256 * 4) {
     const float4 v = *reinterpret_cast<const float4*>(xr + i);
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    s += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
   }
-  ss = wave_sum(ss);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  s = wave_sum(s);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
   __syncthreads();
-  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
-  const float rinv = 1.0f / sqrtf(tot / (float)hidden + eps);
-  for (int i = threadIdx.x; i < hidden; i += 256)
-    out[(int64_t)row * ld_out + i] = f32_to_f16_bits(xr[i] * rinv * bf16_bits_to_f32(g[i]));
+  if (threadIdx.x == 0) ssq[blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
 }
 
-hipError_t launch_rmsnorm(const float* x, int n, int hidden, const uint16_t* g, float eps,
-                          uint16_t* out_f16, int ld_out, hipStream_t s) {
-  hipLaunchKernelGGL(rmsnorm_kernel, dim3(n), dim3(256), 0, s, x, hidden, g, eps, out_f16, ld_out);
+hipError_t launch_row_ssq(const float* x, int n, int hidden, float* ssq, hipStream_t s) {
+  hipLaunchKernelGGL(row_ssq_kernel, dim3(n), dim3(256), 0, s, x, hidden, ssq);
   return hipGetLastError();
 }
 
@@ -43,81 +37,79 @@ __device__ __forceinline__ void merge_top2(float& v1, int& i1, float& v2, float 
   }
 }
 
-// One block per node reduces the lm_head candidates to the greedy token and
-// the top1 - top2 gap; the last block to finish walks the tree.  Acceptance
-// is greedy ("Lucebox: 추측 디코딩과 전용 커널로 ...", section "Lucebox 설치
-// 및 실행": temperature 0): node i is accepted when its parent is and its
-// drafted token equals the parent's greedy token; the kept path ends at the
-// deepest accepted node, lowest index on ties, and commits the accepted
-// drafts plus the greedy token at the path's end.
-__global__ __launch_bounds__(256) void finalize_kernel(const f32x4* __restrict__ cand, int n_fg,
-                                                       int stride, TreeArgs t, int32_t* argmax,
-                                                       float* gap, int32_t* path, int32_t* path_len,
-                                                       int32_t* committed, uint32_t* counter) {
-  __shared__ float s1[256], s2[256];
-  __shared__ int si[256];
-  __shared__ int is_last;
-  const int node = blockIdx.x;
+// One block: merge the lm_head blocks' candidates into the greedy token and
+// top1 - top2 gap of every node, then walk the tree in one wave (node i on
+// lane i).  Acceptance is greedy ("Lucebox: 추측 디코딩과 전용 커널로 ...",
+// section "Lucebox 설치 및 실행": temperature 0): a node is accepted when
+// every node on its root path drafted the greedy token of its parent; the kept
+// path ends at the deepest accepted node, lowest index on ties, and commits
+// the accepted drafts plus the greedy token at the path's end.
+__global__ __launch_bounds__(1024) void finalize_kernel(const f32x4* __restrict__ cand, int n_cand,
+                                                        TreeArgs t, int32_t* argmax, float* gap,
+                                                        int32_t* path, int32_t* path_len,
+                                                        int32_t* committed) {
+  __shared__ float s1[16][kMaxNodes], s2[16][kMaxNodes];
+  __shared__ int si[16][kMaxNodes];
   const int tid = threadIdx.x;
+  const int n = t.n;
+  const int node = tid & 63, part = tid >> 6;  // 16 parts of the candidate list
   float v1 = -INFINITY, v2 = -INFINITY;
   int i1 = 0x7fffffff;
-  for (int f = tid; f < n_fg; f += 256) {
-    const f32x4 c = cand[(int64_t)f * stride + node];
-    merge_top2(v1, i1, v2, c[0], __float_as_int(c[1]), c[2]);
-  }
-  s1[tid] = v1;
-  s2[tid] = v2;
-  si[tid] = i1;
-  __syncthreads();
-  for (int w = 128; w >= 1; w >>= 1) {
-    if (tid < w) {
-      float a1 = s1[tid], a2 = s2[tid];
-      int ai = si[tid];
-      merge_top2(a1, ai, a2, s1[tid + w], si[tid + w], s2[tid + w]);
-      s1[tid] = a1;
-      s2[tid] = a2;
-      si[tid] = ai;
+  if (node < n) {
+#pragma unroll 8
+    for (int c = part; c < n_cand; c += 16) {
+      const f32x4 v = cand[(int64_t)c * n + node];
+      merge_top2(v1, i1, v2, v[0], __float_as_int(v[1]), v[2]);
     }
-    __syncthreads();
   }
-  if (tid == 0) {
-    argmax[node] = si[0];
-    if (gap) gap[node] = s1[0] - s2[0];
-    __threadfence();
-    const unsigned prev = atomicAdd(counter, 1u);
-    is_last = prev == (unsigned)(t.n - 1);
-  }
+  s1[part][node] = v1;
+  s2[part][node] = v2;
+  si[part][node] = i1;
   __syncthreads();
-  if (!is_last || tid != 0) return;
-  __threadfence();
-  const int n = t.n;
-  bool acc[kMaxNodes];
-  int am[kMaxNodes];
-  for (int i = 0; i < n; ++i) am[i] = __hip_atomic_load(argmax + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  acc[0] = true;
-  int end = 0;
-  for (int i = 1; i < n; ++i) {
-    const int pr = t.parent[i];
-    acc[i] = acc[pr] && t.token[i] == am[pr];
-    if (acc[i] && t.pos[i] > t.pos[end]) end = i;  // pos = prefix_len + depth
+  if (tid >= 64) return;
+  const int lane = tid;
+  int am = 0;
+  if (lane < n) {
+    for (int q = 1; q < 16; ++q) merge_top2(v1, i1, v2, s1[q][lane], si[q][lane], s2[q][lane]);
+    am = i1;
+    argmax[lane] = am;
+    if (gap) gap[lane] = v1 - v2;
   }
-  int len = 0;
-  int rev[kMaxNodes];
-  for (int j = end; j >= 0; j = t.parent[j]) rev[len++] = j;
-  for (int k = 0; k < len; ++k) path[k] = rev[len - 1 - k];
-  for (int k = len; k < n; ++k) path[k] = -1;
-  for (int k = 1; k < len; ++k) committed[k - 1] = t.token[rev[len - 1 - k]];
-  committed[len - 1] = am[end];
-  for (int k = len; k < n; ++k) committed[k] = -1;
-  *path_len = len;
-  atomicExch(counter, 0u);
+  // acceptance walk
+  const int par = lane < n ? t.parent[lane] : 0;
+  const int tok = lane < n ? t.token[lane] : 0;
+  const int am_par = __shfl(am, par < 0 ? 0 : par, 64);
+  const bool match = lane == 0 || (lane < n && tok == am_par);
+  const uint64_t mm = __ballot(match);
+  const uint64_t anc = lane < n ? t.anc[lane] : 0ull;
+  const bool acc = lane < n && ((anc & ~mm) == 0ull);
+  const int depth = __popcll(anc) - 1;
+  int key = acc ? (depth << 8) | (255 - lane) : -1;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) key = max(key, __shfl_xor(key, m, 64));
+  const int end = 255 - (key & 255);
+  const uint64_t anc_end = __shfl(anc, end, 64);
+  const int am_end = __shfl(am, end, 64);
+  const int len = __popcll(anc_end);
+  // path position p holds the p-th ancestor of `end` in index order (on a
+  // root path, index order is depth order); every output written once
+  uint64_t x = anc_end;
+  for (int i = 0; i < lane && x; ++i) x &= x - 1ull;
+  const int nd = (lane < len && x) ? (__ffsll((long long)x) - 1) : 0;
+  const int nxt = __shfl(nd, lane < 63 ? lane + 1 : 63, 64);
+  const int tok_nxt = __shfl(tok, nxt, 64);
+  if (lane < n) {
+    path[lane] = lane < len ? nd : -1;
+    committed[lane] = lane + 1 < len ? tok_nxt : (lane + 1 == len ? am_end : -1);
+  }
+  if (lane == 0) *path_len = len;
 }
 
-hipError_t launch_finalize(const f32x4* cand, int n_fg, int cand_stride, const TreeArgs& t,
-                           int32_t* argmax, float* gap, int32_t* path, int32_t* path_len,
-                           int32_t* committed, uint32_t* counter, hipStream_t s) {
-  hipLaunchKernelGGL(finalize_kernel, dim3(t.n), dim3(256), 0, s, cand, n_fg, cand_stride, t,
-                     argmax, gap, path, path_len, committed, counter);
+hipError_t launch_finalize(const f32x4* cand, int n_cand, const TreeArgs& t, int32_t* argmax,
+                           float* gap, int32_t* path, int32_t* path_len, int32_t* committed,
+                           hipStream_t s) {
+  hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(1024), 0, s, cand, n_cand, t, argmax, gap,
+                     path, path_len, committed);
   return hipGetLastError();
 }
 

@@ -44,6 +44,9 @@ class VerifyRunner:
         if head is not None:
             self._hw = tv.lucev_head_w(head["final_norm"].data_ptr(),
                                        tv.q4(head["lm"], V, H))
+        # the buffers above were zero-filled on the current stream; the step
+        # may be issued on another one
+        torch.cuda.synchronize(self.device)
 
     def _layer_struct(self, lw: dict) -> tv.lucev_layer_w:
         s = self.shape
