@@ -134,9 +134,10 @@ __device__ __forceinline__ float scale_f32(u32x2 s, int j) {
 // every block gets the same number of weight bytes).  Inside a block the 4
 // waves take a segment's column groups round-robin; partial sums meet in LDS.
 // A feature group cut between blocks is finished by whichever contributor
-// arrives last: partial tiles are written with agent-scope stores, published
-// by a release increment of the group's counter, read back with agent-scope
-// loads and summed in block order, so results do not depend on timing.
+// arrives last: partial tiles are written through with agent-scope stores
+// that every wave waits for before the block counts in (no cache flush), read
+// back with agent-scope loads and summed in block order, so results do not
+// depend on timing.
 //
 // Precision: the activation operand is carried as two fp16 halves
 // (x = hi + lo, about 22 significant bits) and both go through the MFMA, and
@@ -408,20 +409,42 @@ __global__ __launch_bounds__(256) void gemm_q4_kernel(GemmParams p, EpiArgs e) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // every wave's stores done
       __syncthreads();
       if (tid == 0) {
-        // release: this block's partial stores are visible before the count
-        const unsigned prev = __hip_atomic_fetch_add(&p.counters[fg], 1u, __ATOMIC_RELEASE,
+        // the partials were written through (agent-scope stores) and every
+        // wave waited for them before the barrier, so a relaxed count suffices
+        const unsigned prev = __hip_atomic_fetch_add(&p.counters[fg], 1u, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT);
         s_last = prev == (unsigned)(bl - bf);
       }
       __syncthreads();
       if (!s_last) continue;
-      for (int i = tid; i < TILE; i += 256) {
-        float s = 0.f;
-        for (int bb = bf; bb <= bl; ++bb) {
-          const int sl = ((int64_t)bb * U / B >= (int64_t)fg * G) ? 0 : 1;
-          s += ld_coherent(p.partials + ((int64_t)bb * 2 + sl) * TILE + i);
+      // sum the contributors in block order; all loads of a batch of 8
+      // contributors are issued before any add so their latencies overlap
+      constexpr int PER = TILE / 256;
+      float acc_s[PER];
+#pragma unroll
+      for (int k = 0; k < PER; ++k) acc_s[k] = 0.f;
+      for (int b0 = bf; b0 <= bl; b0 += 8) {
+        float v[8][PER];
+#pragma unroll
+        for (int uu = 0; uu < 8; ++uu) {
+          const int bb = b0 + uu;
+          if (bb <= bl) {
+            const int sl = ((int64_t)bb * U / B >= (int64_t)fg * G) ? 0 : 1;
+            const float* src = p.partials + ((int64_t)bb * 2 + sl) * TILE + tid;
+#pragma unroll
+            for (int k = 0; k < PER; ++k) v[uu][k] = ld_coherent(src + k * 256);
+          }
         }
-        tile[i / TILE_N][i % TILE_N] = s;
+#pragma unroll
+        for (int uu = 0; uu < 8; ++uu)
+          if (b0 + uu <= bl)
+#pragma unroll
+            for (int k = 0; k < PER; ++k) acc_s[k] += v[uu][k];
+      }
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        const int i = tid + k * 256;
+        tile[i / TILE_N][i % TILE_N] = acc_s[k];
       }
       if (tid == 0)
         __hip_atomic_store(&p.counters[fg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
