@@ -107,7 +107,7 @@ int check_device() {
 }
 
 struct Ws {
-  size_t counters, xhi, xlo, mhi, mlo, q32, k32, v32, opart, ml, partials, stats, ssq, cand, total;
+  size_t counters, xa, xm, q32, k32, v32, opart, ml, partials, cand, total;
   int n_counters;
 };
 
@@ -123,7 +123,7 @@ void layer_gemms(const lucev_shape* s, int n, GemmPlan out[5]) {
 bool ws_layout(const lucev_shape* s, int nmax, int pmax, Ws* w) {
   if (check_shape(s) != LUCEV_OK || nmax < 1 || nmax > LUCEV_MAX_NODES || pmax < 0) return false;
   const int64_t H = s->hidden, F = s->ffn, Hq = s->n_q_heads, Hkv = s->n_kv_heads, d = s->head_dim;
-  size_t part_floats = 0, ssq_floats = 0, cand = 0;
+  size_t part_floats = 0, cand = 0;
   int counters = 0;
   for (int n = 1; n <= nmax; ++n) {
     GemmPlan g[5];
@@ -131,9 +131,8 @@ bool ws_layout(const lucev_shape* s, int nmax, int pmax, Ws* w) {
     for (int i = 0; i < 5; ++i) {
       const size_t pf = (size_t)g[i].blocks * 2 * g[i].tile_floats;
       if (pf > part_floats) part_floats = pf;
-      if (g[i].fgroups > counters) counters = g[i].fgroups;
+      if (g[i].panels > counters) counters = g[i].panels;
     }
-    if ((size_t)g[1].fgroups * n > ssq_floats) ssq_floats = (size_t)g[1].fgroups * n;
     if ((size_t)g[4].blocks * n > cand) cand = (size_t)g[4].blocks * n;
   }
   w->n_counters = counters;
@@ -144,10 +143,10 @@ bool ws_layout(const lucev_shape* s, int nmax, int pmax, Ws* w) {
     return at_;
   };
   w->counters = take((size_t)counters * sizeof(uint32_t));
-  w->xhi = take((size_t)nmax * Hq * d * 2);
-  w->xlo = take((size_t)nmax * Hq * d * 2);
-  w->mhi = take((size_t)nmax * F * 2);
-  w->mlo = take((size_t)nmax * F * 2);
+  // GEMM operands as fp16 hi/lo rows: normed inputs and the attention output
+  // (xa), the SwiGLU product (xm)
+  w->xa = take((size_t)2 * nmax * (H > Hq * d ? H : Hq * d) * 2);
+  w->xm = take((size_t)2 * nmax * F * 2);
   w->q32 = take((size_t)nmax * Hq * d * 4);
   w->k32 = take((size_t)nmax * Hkv * d * 4);
   w->v32 = take((size_t)nmax * Hkv * d * 4);
@@ -156,8 +155,6 @@ bool ws_layout(const lucev_shape* s, int nmax, int pmax, Ws* w) {
   w->opart = take((size_t)chunks * Hkv * rows * d * 4);
   w->ml = take((size_t)chunks * Hkv * rows * 2 * sizeof(float));
   w->partials = take(part_floats * sizeof(float));
-  w->stats = take((size_t)nmax * sizeof(float));
-  w->ssq = take(ssq_floats * sizeof(float));
   w->cand = take(cand * sizeof(f32x4));
   w->total = off;
   (void)pmax;
@@ -179,25 +176,12 @@ T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
 }
 
-// A_F16HL: X / Xlo are the fp16 planes; A_F32N: X is the fp32 residual, g the
-// gain and ssq the [ssq_groups][n] partial row sums of x^2
-GemmParams gemm_params(const lucev_q4& w, int a_mode, const void* X, const uint16_t* Xlo,
-                       const uint16_t* g, const float* ssq, int ssq_groups, int ldx, int n,
-                       float eps, void* ws, const Ws& L) {
+// X: the fp16 hi/lo operand rows [2n][k_in]
+GemmParams gemm_params(const lucev_q4& w, const uint16_t* X, int n, void* ws, const Ws& L) {
   GemmPlan pl = plan_gemm(w.n_out, w.k_in, n);
   GemmParams p;
   memset(&p, 0, sizeof(p));
-  p.a_mode = a_mode;
-  if (a_mode == A_F16HL) {
-    p.Xhi = static_cast<const uint16_t*>(X);
-    p.Xlo = Xlo;
-  } else {
-    p.Xf = static_cast<const float*>(X);
-    p.g = g;
-    p.ssq = ssq;
-    p.ssq_groups = ssq_groups;
-  }
-  p.ldx = ldx;
+  p.X = X;
   p.n_nodes = n;
   p.wq = static_cast<const uint8_t*>(w.packed);
   p.wsc = reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(w.packed) + w.n_out * w.k_in / 2);
@@ -205,12 +189,11 @@ GemmParams gemm_params(const lucev_q4& w, int a_mode, const void* X, const uint1
   p.k_in = w.k_in;
   p.n_tiles = pl.n_tiles;
   p.kgroups = pl.kgroups;
-  p.fgroups = pl.fgroups;
+  p.panels = pl.panels;
   p.blocks = pl.blocks;
   p.units = pl.units;
   p.partials = at<float>(ws, L.partials);
   p.counters = at<uint32_t>(ws, L.counters);
-  p.rms_eps = eps;
   return p;
 }
 
@@ -221,10 +204,10 @@ EpiArgs epi_blank() {
 }
 
 // q / k_tree / v_tree bf16 (always); q32 / k32 / v32 fp32 copies or NULL;
-// out bf16, or fp16 hi / lo planes when out_lo is set
+// out bf16 [n][Hq][d], or the Wo operand's fp16 hi/lo rows when out_hilo is set
 int run_attention(const lucev_shape* s, const TreeArgs& t, const lucev_kv* kv, const uint16_t* q,
                   const uint16_t* k_tree, const uint16_t* v_tree, const float* q32,
-                  const float* k32, const float* v32, uint16_t* out, uint16_t* out_lo, void* ws,
+                  const float* k32, const float* v32, uint16_t* out, int out_hilo, void* ws,
                   const Ws& L, hipStream_t st) {
   AttnPlan plan = plan_attention(t.n, s->n_q_heads, s->n_kv_heads, s->head_dim, kv->prefix_len);
   AttnParams p;
@@ -259,7 +242,7 @@ int run_attention(const lucev_shape* s, const TreeArgs& t, const lucev_kv* kv, c
   c.rows = plan.rows;
   c.scale_log2 = p.scale_log2;
   c.out = out;
-  c.out_lo = out_lo;
+  c.out_hilo = out_hilo;
   hipError_t e = launch_attention(plan, s->head_dim, p, c, t, st);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return LUCEV_OK;
@@ -355,8 +338,8 @@ int lucev_tree_attention(const lucev_shape* shape, const lucev_tree* tree, const
   Ws L;
   if ((rc = check_ws(shape, t.n, kv->prefix_len, ws, ws_bytes, &L))) return rc;
   if ((rc = check_device())) return rc;
-  return run_attention(shape, t, kv, q, k_tree, v_tree, nullptr, nullptr, nullptr, out, nullptr, ws,
-                       L, (hipStream_t)stream);
+  return run_attention(shape, t, kv, q, k_tree, v_tree, nullptr, nullptr, nullptr, out, 0, ws, L,
+                       (hipStream_t)stream);
 }
 
 int lucev_verify_layer(const lucev_shape* shape, const lucev_layer_w* w, const lucev_tree* tree,
@@ -384,23 +367,18 @@ int lucev_verify_layer(const lucev_shape* shape, const lucev_layer_w* w, const l
   hipStream_t st = (hipStream_t)stream;
   const int n = t.n;
   const float eps = shape->rms_eps;
-  uint16_t* Xhi = at<uint16_t>(ws, L.xhi);
-  uint16_t* Xlo = at<uint16_t>(ws, L.xlo);
-  uint16_t* Mhi = at<uint16_t>(ws, L.mhi);
-  uint16_t* Mlo = at<uint16_t>(ws, L.mlo);
+  uint16_t* xa = at<uint16_t>(ws, L.xa);
+  uint16_t* xm = at<uint16_t>(ws, L.xm);
   float* q32 = at<float>(ws, L.q32);
   float* k32 = at<float>(ws, L.k32);
   float* v32 = at<float>(ws, L.v32);
-  float* stats = at<float>(ws, L.stats);
-  float* ssq = at<float>(ws, L.ssq);
   hipError_t e;
 
-  // attention half: RMSNorm (row statistic, then folded into the QKV operand)
-  // -> QKV + RoPE -> tree attention -> Wo + residual
-  if ((e = launch_row_ssq(resid_io, n, (int)H, stats, st)) != hipSuccess) return hip_fail(e, "row_ssq launch");
+  // attention half: RMSNorm -> QKV + RoPE -> tree attention -> Wo + residual
+  if ((e = launch_norm_hilo(resid_io, n, (int)H, w->attn_norm, eps, xa, st)) != hipSuccess)
+    return hip_fail(e, "attention norm launch");
   {
-    GemmParams p = gemm_params(w->wqkv, A_F32N, resid_io, nullptr, w->attn_norm, stats, 1, (int)H, n,
-                               eps, ws, L);
+    GemmParams p = gemm_params(w->wqkv, xa, n, ws, L);
     EpiArgs ea = epi_blank();
     ea.k_out = k_tree_out;
     ea.v_out = v_tree_out;
@@ -412,37 +390,34 @@ int lucev_verify_layer(const lucev_shape* shape, const lucev_layer_w* w, const l
     ea.head_dim = (int)d;
     for (int i = 0; i < n; ++i) ea.pos[i] = t.pos[i];
     for (int j = 0; j < d / 2; ++j) ea.inv_freq[j] = pow((double)shape->rope_base, -2.0 * j / (double)d);
-    if ((e = launch_gemm(EPI_QKV, p, ea, st)) != hipSuccess) return hip_fail(e, "qkv gemm launch");
+    if ((e = launch_gemm(EPI_QKV, true, p, ea, st)) != hipSuccess) return hip_fail(e, "qkv gemm launch");
   }
-  if ((rc = run_attention(shape, t, kv, nullptr, k_tree_out, v_tree_out, q32, k32, v32, Xhi, Xlo, ws,
-                          L, st)))
+  if ((rc = run_attention(shape, t, kv, nullptr, k_tree_out, v_tree_out, q32, k32, v32, xa, 1, ws, L,
+                          st)))
     return rc;
-  GemmParams pwo = gemm_params(w->wo, A_F16HL, Xhi, Xlo, nullptr, nullptr, 0, (int)(Hq * d), n, eps,
-                               ws, L);
   {
-    // the residual update also emits per-group sums of x^2 for the FFN RMSNorm
+    GemmParams p = gemm_params(w->wo, xa, n, ws, L);
     EpiArgs ea = epi_blank();
     ea.resid = resid_io;
     ea.ld_out = (int)H;
-    ea.ssq_out = ssq;
-    if ((e = launch_gemm(EPI_RESID, pwo, ea, st)) != hipSuccess) return hip_fail(e, "wo gemm launch");
+    if ((e = launch_gemm(EPI_RESID, true, p, ea, st)) != hipSuccess) return hip_fail(e, "wo gemm launch");
   }
-  // FFN half: RMSNorm folded into gate/up + SwiGLU -> down + residual
+  // FFN half: RMSNorm -> gate/up + SwiGLU -> down + residual
+  if ((e = launch_norm_hilo(resid_io, n, (int)H, w->ffn_norm, eps, xa, st)) != hipSuccess)
+    return hip_fail(e, "ffn norm launch");
   {
-    GemmParams p = gemm_params(w->wgu, A_F32N, resid_io, nullptr, w->ffn_norm, ssq, pwo.fgroups,
-                               (int)H, n, eps, ws, L);
+    GemmParams p = gemm_params(w->wgu, xa, n, ws, L);
     EpiArgs ea = epi_blank();
-    ea.out16 = Mhi;
-    ea.out16_lo = Mlo;
+    ea.out16 = xm;
     ea.ld_out = (int)F;
-    if ((e = launch_gemm(EPI_SWIGLU, p, ea, st)) != hipSuccess) return hip_fail(e, "gate/up gemm launch");
+    if ((e = launch_gemm(EPI_SWIGLU, false, p, ea, st)) != hipSuccess) return hip_fail(e, "gate/up gemm launch");
   }
   {
-    GemmParams p = gemm_params(w->wd, A_F16HL, Mhi, Mlo, nullptr, nullptr, 0, (int)F, n, eps, ws, L);
+    GemmParams p = gemm_params(w->wd, xm, n, ws, L);
     EpiArgs ea = epi_blank();
     ea.resid = resid_io;
     ea.ld_out = (int)H;
-    if ((e = launch_gemm(EPI_RESID, p, ea, st)) != hipSuccess) return hip_fail(e, "down gemm launch");
+    if ((e = launch_gemm(EPI_RESID, false, p, ea, st)) != hipSuccess) return hip_fail(e, "down gemm launch");
   }
   return LUCEV_OK;
 }
@@ -468,15 +443,15 @@ int lucev_accept_path(const lucev_shape* shape, const lucev_head_w* w, const luc
   const int n = t.n;
   const int H = shape->hidden;
   hipError_t e;
-  float* stats = at<float>(ws, L.stats);
-  if ((e = launch_row_ssq(resid, n, H, stats, st)) != hipSuccess) return hip_fail(e, "row_ssq launch");
-  GemmParams p = gemm_params(w->lm_head, A_F32N, resid, nullptr, w->final_norm, stats, 1, H, n,
-                             shape->rms_eps, ws, L);
+  uint16_t* xa = at<uint16_t>(ws, L.xa);
+  if ((e = launch_norm_hilo(resid, n, H, w->final_norm, shape->rms_eps, xa, st)) != hipSuccess)
+    return hip_fail(e, "final norm launch");
+  GemmParams p = gemm_params(w->lm_head, xa, n, ws, L);
   EpiArgs ea = epi_blank();
   ea.out16 = logits_out;
   ea.ld_out = shape->vocab;
   ea.cand = at<f32x4>(ws, L.cand);
-  if ((e = launch_gemm(EPI_LOGITS, p, ea, st)) != hipSuccess) return hip_fail(e, "lm_head gemm launch");
+  if ((e = launch_gemm(EPI_LOGITS, true, p, ea, st)) != hipSuccess) return hip_fail(e, "lm_head gemm launch");
   if ((e = launch_finalize(ea.cand, p.blocks, t, argmax_out, gap_out, path_out, path_len_out,
                            committed_out, st)) != hipSuccess)
     return hip_fail(e, "finalize launch");

@@ -336,13 +336,15 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(CombineParams c, Tree
       o += __builtin_amdgcn_exp2f(s_anc[k++] - M) * (c.v32 ? c.v32[vo] : bf16_bits_to_f32(c.v_tree[vo]));
     }
     o /= L;
-    const int64_t oo = ((int64_t)node * c.n_q_heads + h) * D + j;
-    if (c.out_lo) {
+    if (c.out_hilo) {
+      // the Wo projection's operand: fp16 rows 2 node (hi) and 2 node + 1 (lo)
+      const int64_t width = (int64_t)c.n_q_heads * D;
+      const int64_t oo = (int64_t)(2 * node) * width + h * D + j;
       const f16 hi = (f16)o;
       c.out[oo] = __builtin_bit_cast(uint16_t, hi);
-      c.out_lo[oo] = f32_to_f16_bits(o - (float)hi);
+      c.out[oo + width] = f32_to_f16_bits(o - (float)hi);
     } else {
-      c.out[oo] = f32_to_bf16_bits(o);
+      c.out[((int64_t)node * c.n_q_heads + h) * D + j] = f32_to_bf16_bits(o);
     }
   }
 }

@@ -5,11 +5,10 @@
 // tokens in that one pass ("Lucebox Hub", section "배경: 어떤 문제를 푸는가",
 // item 1; section "Speculative decoding 계층"), so this kernel streams the
 // packed weights exactly once and reuses each dequantised weight for every
-// tree node.  With 16..64 nodes that reuse is a dense contraction, so the
-// MAC work goes to MFMA (v_mfma_f32_16x16x32_f16); the codes are expanded in
-// registers (exponent-bias trick: exact q - 8 as fp16), each 32-column block
-// is one MFMA K-step whose fp32 result takes the block's scale d, and the
-// weights never touch LDS.
+// tree node.  With 8..64 nodes that reuse is a dense contraction, so the MAC
+// work goes to MFMA (v_mfma_f32_16x16x32_f16); the codes are expanded in
+// registers (exponent-bias trick: exact q - 8 as fp16, then times the
+// block's fp16 scale), and the weights never touch LDS.
 //
 // Packed layout (private to this library, written by lucev_q4_pack*):
 //   nibble region, per 16-row tile t and 128-column group c, 1024 bytes:
@@ -104,13 +103,22 @@ hipError_t launch_pack_q4(const uint8_t* q, const uint16_t* d, int64_t n_out, in
 
 // ------------------------------------------------------------ dequant
 
+// v_bfi_b32: (a & mask) | (b & ~mask), one VALU op for a masked merge
+__device__ __forceinline__ uint32_t bfi(uint32_t mask, uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(mask), "v"(a), "v"(b));
+  return r;
+}
+
 // 8 codes of one dword -> the 8 exact values (q - 8) as fp16, column order.
+// A code placed in the low mantissa bits of 0x6400 (1024) reads 1024 + q; one
+// placed four bits higher under 0x5400 (64) reads 64 + q.
 __device__ __forceinline__ f16x8 codes8(uint32_t w) {
-  const uint32_t v0 = (w & 0x000F000Fu) | 0x64006400u;       // 1024 + q (cols 0, 1)
-  const uint32_t v1 = (w & 0x00F000F0u) | 0x54005400u;       //   64 + q (cols 2, 3)
   const uint32_t w8 = w >> 8;
-  const uint32_t v2 = (w8 & 0x000F000Fu) | 0x64006400u;      // 1024 + q (cols 4, 5)
-  const uint32_t v3 = (w8 & 0x00F000F0u) | 0x54005400u;      //   64 + q (cols 6, 7)
+  const uint32_t v0 = bfi(0x000F000Fu, w, 0x64006400u);   // 1024 + q (cols 0, 1)
+  const uint32_t v1 = bfi(0x00F000F0u, w, 0x54005400u);   //   64 + q (cols 2, 3)
+  const uint32_t v2 = bfi(0x000F000Fu, w8, 0x64006400u);  // 1024 + q (cols 4, 5)
+  const uint32_t v3 = bfi(0x00F000F0u, w8, 0x54005400u);  //   64 + q (cols 6, 7)
   const f16x2 b1032 = {(f16)1032.0f, (f16)1032.0f};
   const f16x2 b72 = {(f16)72.0f, (f16)72.0f};
   const f16x2 h0 = __builtin_bit_cast(f16x2, v0) - b1032;
@@ -120,144 +128,39 @@ __device__ __forceinline__ f16x8 codes8(uint32_t w) {
   return f16x8{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
 }
 
-// fp16 scale of block j (of 4) from the lane's 4 packed scales, as fp32
-__device__ __forceinline__ float scale_f32(u32x2 s, int j) {
+// 8 codes of one dword times the block scale: fp16 d * (q - 8), column order
+__device__ __forceinline__ f16x8 dequant8(uint32_t w, f16x2 dd) {
+  const f16x8 c = codes8(w);
+  const f16x2 a = f16x2{c[0], c[1]} * dd;
+  const f16x2 b = f16x2{c[2], c[3]} * dd;
+  const f16x2 cc = f16x2{c[4], c[5]} * dd;
+  const f16x2 d = f16x2{c[6], c[7]} * dd;
+  return f16x8{a[0], a[1], b[0], b[1], cc[0], cc[1], d[0], d[1]};
+}
+
+// The same product split exactly: hi = fp16(d * (q - 8)) and lo = d * (q - 8)
+// - hi.  d has 11 significant bits and q - 8 at most 3, so the residual has at
+// most 3 bits, is a multiple of ulp(d) >= 2^-19 and fits fp16; the fused
+// multiply-add forms it without rounding.
+__device__ __forceinline__ void dequant8_split(uint32_t w, f16x2 dd, f16x8& hi, f16x8& lo) {
+  const f16x8 c = codes8(w);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f16x2 ci = f16x2{c[2 * i], c[2 * i + 1]};
+    const f16x2 h = ci * dd;
+    const f16x2 l = __builtin_elementwise_fma(ci, dd, -h);
+    hi[2 * i] = h[0];
+    hi[2 * i + 1] = h[1];
+    lo[2 * i] = l[0];
+    lo[2 * i + 1] = l[1];
+  }
+}
+
+// the block-j scale of this lane's row, splatted to both fp16 halves
+__device__ __forceinline__ f16x2 scale_pair(u32x2 s, int j) {
   const uint32_t word = (j < 2) ? s[0] : s[1];
-  const uint16_t bits = (uint16_t)((j & 1) ? (word >> 16) : (word & 0xFFFFu));
-  return (float)__builtin_bit_cast(f16, bits);
-}
-
-// ------------------------------------------------------------ the GEMM
-//
-// Work: units (fg, c) = (FT-tile feature group, 128-column group), fg-major,
-// split into equal contiguous ranges, one per block (block-level stream-K:
-// every block gets the same number of weight bytes).  Inside a block the 4
-// waves take a segment's column groups round-robin; partial sums meet in LDS.
-// A feature group cut between blocks is finished by whichever contributor
-// arrives last: partial tiles are written through with agent-scope stores
-// that every wave waits for before the block counts in (no cache flush), read
-// back with agent-scope loads and summed in block order, so results do not
-// depend on timing.
-//
-// Precision: the activation operand is carried as two fp16 halves
-// (x = hi + lo, about 22 significant bits) and both go through the MFMA, and
-// the weights enter exactly, so rounding does not compound through a deep
-// stack.  The
-// normalised inputs of the QKV / gate-up / lm_head projections are formed
-// here from the fp32 residual: u = x * rsqrt(mean(x^2) + eps) * g, with the
-// row sums of x^2 produced by the previous kernel.
-
-template <int NT, int FT, int AM>
-struct Raw {
-  u32x4 w[FT];
-  u32x2 s[FT];
-  u32x4 x[NT][4][2];                  // fp16 hi / lo planes, or fp32 x4 pairs
-  u32x4 g[AM == A_F32N ? 4 : 1];      // bf16 gain x8 per block
-};
-
-template <int NT, int FT>
-struct Ready {
-  u32x4 w[FT];
-  u32x2 s[FT];
-  f16x8 hi[NT][4];
-  f16x8 lo[NT][4];
-};
-
-template <int NT, int FT, int AM>
-__device__ __forceinline__ void load_raw(const GemmParams& p, int c, int t0, int lane,
-                                         Raw<NT, FT, AM>& r) {
-  const int lr = lane & 15, lq = lane >> 4;
-#pragma unroll
-  for (int ft = 0; ft < FT; ++ft) {
-    int t = t0 + ft;
-    t = t < p.n_tiles ? t : p.n_tiles - 1;  // ragged last group: re-read a valid tile
-    const int64_t tg = (int64_t)t * p.kgroups + c;
-    r.w[ft] = ld16(p.wq + tg * 1024 + lane * 16);
-    r.s[ft] = *reinterpret_cast<const u32x2*>(p.wsc + tg * 64 + lr * 4);
-  }
-  if constexpr (AM == A_F32N) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) r.g[j] = ld16(p.g + c * 128 + j * 32 + lq * 8);
-  }
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int node = nt * 16 + lr;
-    const bool ok = node < p.n_nodes;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t off = (int64_t)node * p.ldx + c * 128 + j * 32 + lq * 8;
-      const u32x4 z = u32x4{0u, 0u, 0u, 0u};
-      if constexpr (AM == A_F32N) {
-        r.x[nt][j][0] = ok ? ld16(p.Xf + off) : z;
-        r.x[nt][j][1] = ok ? ld16(p.Xf + off + 4) : z;
-      } else {
-        r.x[nt][j][0] = ok ? ld16(p.Xhi + off) : z;
-        r.x[nt][j][1] = ok ? ld16(p.Xlo + off) : z;
-      }
-    }
-  }
-}
-
-template <int NT, int FT, int AM>
-__device__ __forceinline__ void make_ready(const Raw<NT, FT, AM>& r, Ready<NT, FT>& q,
-                                           const float (&rinv)[NT]) {
-#pragma unroll
-  for (int ft = 0; ft < FT; ++ft) {
-    q.w[ft] = r.w[ft];
-    q.s[ft] = r.s[ft];
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if constexpr (AM == A_F32N) {
-      float gf[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        gf[2 * e] = __uint_as_float(r.g[j][e] << 16);
-        gf[2 * e + 1] = __uint_as_float(r.g[j][e] & 0xFFFF0000u);
-      }
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        f16x8 h, l;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float u = __uint_as_float(r.x[nt][j][e >> 2][e & 3]) * rinv[nt] * gf[e];
-          const f16 hh = (f16)u;
-          h[e] = hh;
-          l[e] = (f16)(u - (float)hh);
-        }
-        q.hi[nt][j] = h;
-        q.lo[nt][j] = l;
-      }
-    } else {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        q.hi[nt][j] = __builtin_bit_cast(f16x8, r.x[nt][j][0]);
-        q.lo[nt][j] = __builtin_bit_cast(f16x8, r.x[nt][j][1]);
-      }
-    }
-  }
-}
-
-// Per 32-column block: MFMA of the exact codes against x_hi and x_lo, then
-// the block's fp16 scale d (the MFMA column = lane % 16 = this lane's
-// feature) is applied in fp32, so every weight enters as exactly d * (q - 8).
-template <int NT, int FT>
-__device__ __forceinline__ void mma_ready(const Ready<NT, FT>& q, f32x4 (&acc)[FT][NT]) {
-  const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-#pragma unroll
-    for (int ft = 0; ft < FT; ++ft) {
-      const f16x8 b = codes8(q.w[ft][j]);
-      const float dsc = scale_f32(q.s[ft], j);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_f16(q.hi[nt][j], b, zero, 0, 0, 0);
-        t = __builtin_amdgcn_mfma_f32_16x16x32_f16(q.lo[nt][j], b, t, 0, 0, 0);
-        acc[ft][nt] += dsc * t;
-      }
-    }
-  }
+  const uint32_t h = (j & 1) ? (word >> 16) : (word & 0xFFFFu);
+  return __builtin_bit_cast(f16x2, h | (h << 16));
 }
 
 __device__ __forceinline__ void rope_pair_angle(int pos, int jj, const double* inv_freq, float& cs,
@@ -286,19 +189,50 @@ __device__ __forceinline__ void st_coherent(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// the block whose unit range holds unit u (ranges are [b*U/B, (b+1)*U/B))
-__device__ __forceinline__ int block_of(int64_t u, int64_t U, int B) {
-  return (int)(((u + 1) * B - 1) / U);
+
+// Block barrier that orders LDS only: outstanding global loads (the weight
+// prefetch) stay in flight across it, unlike __syncthreads().
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-template <int NT, int FT, int AM, int EPI>
-__global__ __launch_bounds__(256) void gemm_q4_kernel(GemmParams p, EpiArgs e) {
-  constexpr int TILE_F = FT * 16;
-  constexpr int TILE_N = NT * 16;
+template <int UG, int FT>
+struct WRegs {
+  u32x4 w[UG][FT];  // per column group and tile: 4 blocks x 8 codes of this lane's row
+  u32x2 s[UG][FT];  // the row's 4 block scales
+};
+
+template <int UG>
+constexpr int gemm_xld() { return UG * 128 + 8; }  // staged activation row (fp16), padded
+
+// Unit u of the flat list [0, U) lives in block block_of_unit(u): blocks take
+// contiguous ranges of whole unit pairs, [2 floor(b P / B), 2 floor((b+1) P / B))
+// with P = ceil(U / 2) pairs, so every range starts on an even unit.
+__device__ __forceinline__ int64_t range_start(int b, int64_t U, int B) {
+  const int64_t P = (U + 1) / 2;
+  const int64_t s = 2 * ((int64_t)b * P / B);
+  return s < U ? s : U;
+}
+__device__ __forceinline__ int block_of_unit(int64_t u, int64_t U, int B) {
+  const int64_t P = (U + 1) / 2;
+  return (int)(((u / 2 + 1) * B - 1) / P);
+}
+
+template <int WAVES, int FT, int NTX, int UG, int EPI, bool EXACT>
+__global__ __launch_bounds__(WAVES * 64) void gemm_q4_kernel(GemmParams p, EpiArgs e) {
+  constexpr int NTH = WAVES * 64;
+  constexpr int PT = WAVES * FT;   // tiles per panel
+  constexpr int TILE_F = PT * 16;
+  constexpr int XR = NTX * 16;     // staged hi/lo rows
+  constexpr int XLD = gemm_xld<UG>();
+  constexpr int XCPR = UG * 16;    // 16-byte chunks per staged row
+  constexpr int XCH = (XR * XCPR + NTH - 1) / NTH;  // staging chunks per thread
+  constexpr int TILE_N = NTX * 8;  // nodes
   constexpr int TILE = TILE_F * TILE_N;
-  __shared__ float red[3][FT][NT][4][64];
+  __shared__ __attribute__((aligned(16))) uint16_t sx[2 * XR * XLD];
   __shared__ float tile[TILE_F][TILE_N + 1];
-  __shared__ float s_rinv[TILE_N];
   __shared__ float best1[TILE_N], best2[TILE_N];
   __shared__ int besti[TILE_N];
   __shared__ int s_last;
@@ -309,10 +243,12 @@ __global__ __launch_bounds__(256) void gemm_q4_kernel(GemmParams p, EpiArgs e) {
   const int b = blockIdx.x;
   const int B = p.blocks;
   const int64_t U = p.units;
-  const int G = p.kgroups;
+  const int G = p.kgroups;   // 128-column groups
+  const int GU = G / UG;     // units per panel
   const int nn = p.n_nodes;
-  const int64_t u_begin = (int64_t)b * U / B;
-  const int64_t u_end = (int64_t)(b + 1) * U / B;
+  const int64_t K = p.k_in;
+  const int64_t u_begin = range_start(b, U, B);
+  const int64_t u_end = range_start(b + 1, U, B);
 
   if constexpr (EPI == EPI_LOGITS) {
     if (tid < TILE_N) {
@@ -321,179 +257,206 @@ __global__ __launch_bounds__(256) void gemm_q4_kernel(GemmParams p, EpiArgs e) {
       besti[tid] = 0x7fffffff;
     }
   }
-  // 1/rms per row for the normalised input, from the producer's partial sums
-  if constexpr (AM == A_F32N) {
-    if (tid < TILE_N) {
-      float r = 0.f;
-      if (tid < nn) {
-        float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-        int i = 0;
-        for (; i + 4 <= p.ssq_groups; i += 4) {
-          s0 += p.ssq[(int64_t)i * nn + tid];
-          s1 += p.ssq[(int64_t)(i + 1) * nn + tid];
-          s2 += p.ssq[(int64_t)(i + 2) * nn + tid];
-          s3 += p.ssq[(int64_t)(i + 3) * nn + tid];
-        }
-        for (; i < p.ssq_groups; ++i) s0 += p.ssq[(int64_t)i * nn + tid];
-        r = 1.0f / sqrtf(((s0 + s1) + (s2 + s3)) / (float)p.k_in + p.rms_eps);
-      }
-      s_rinv[tid] = r;
+
+  // A unit as (panel, unit within the panel), advanced without divisions.
+  struct Cur {
+    int pnl, c;
+  };
+  auto cur_of = [&](int64_t u) { return Cur{(int)(u / GU), (int)(u % GU)}; };
+  auto advance = [&](Cur& k) {
+    if (++k.c == GU) {
+      k.c = 0;
+      ++k.pnl;
     }
-  }
-  __syncthreads();
-  float rinv[NT];
+  };
+  // the weights are read once: non-temporal loads keep them from evicting
+  // the activation rows, which every block re-reads, from L2
+  auto wload = [&](Cur k, WRegs<UG, FT>& r) {
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) rinv[nt] = AM == A_F32N ? s_rinv[nt * 16 + lr] : 1.f;
+    for (int g = 0; g < UG; ++g)
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft) {
+        int t = k.pnl * PT + wave * FT + ft;
+        t = t < p.n_tiles ? t : p.n_tiles - 1;  // ragged last panel: re-read a valid tile
+        const int64_t tg = (int64_t)t * G + k.c * UG + g;
+        r.w[g][ft] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.wq + tg * 1024 + lane * 16));
+        r.s[g][ft] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p.wsc + tg * 64 + lr * 4));
+      }
+  };
+  // activation slice of a unit: XR rows x UG * 128 columns, in 16-byte chunks
+  // (every lane loads from a valid row and zeroes what lies past the 2n rows,
+  // so the load count does not depend on the lane)
+  auto xload = [&](Cur k, u32x4 (&xr)[XCH]) {
+    const int col0 = k.c * UG * 128;
+#pragma unroll
+    for (int i = 0; i < XCH; ++i) {
+      const int id = tid + NTH * i;
+      const int row = id / XCPR, part = id % XCPR;
+      const bool ok = id < XR * XCPR && row < 2 * nn;
+      const u32x4 v = ld16(p.X + (ok ? row : 0) * K + col0 + part * 8);
+      xr[i] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto xstore = [&](int buf, const u32x4 (&xr)[XCH]) {
+#pragma unroll
+    for (int i = 0; i < XCH; ++i) {
+      const int id = tid + NTH * i;
+      const int row = id / XCPR, part = id % XCPR;
+      if (id < XR * XCPR) *reinterpret_cast<u32x4*>(&sx[(buf * XR + row) * XLD + part * 8]) = xr[i];
+    }
+  };
 
-  for (int64_t u = u_begin; u < u_end;) {
-    const int fg = (int)(u / G);
-    const int c0 = (int)(u - (int64_t)fg * G);
-    const int c1 = (int)min((int64_t)G, (int64_t)c0 + (u_end - u));
-    u += c1 - c0;
-    const int t0 = fg * FT;
+  f32x4 acc[FT][NTX];
+#pragma unroll
+  for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+    for (int nt = 0; nt < NTX; ++nt) acc[ft][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    f32x4 acc[FT][NT];
+  auto compute = [&](int buf, const WRegs<UG, FT>& r) {
+    const uint16_t* xs = sx + (buf * XR + lr) * XLD + lq * 8;
+#pragma unroll
+    for (int g = 0; g < UG; ++g)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f16x8 xa[NTX];
+#pragma unroll
+        for (int nt = 0; nt < NTX; ++nt)
+          xa[nt] = *reinterpret_cast<const f16x8*>(xs + nt * 16 * XLD + g * 128 + j * 32);
+#pragma unroll
+        for (int ft = 0; ft < FT; ++ft) {
+          if constexpr (EXACT) {
+            // d * (q - 8) split exactly into fp16 hi + lo, both through the MFMA
+            f16x8 wh, wl;
+            dequant8_split(r.w[g][ft][j], scale_pair(r.s[g][ft], j), wh, wl);
+#pragma unroll
+            for (int nt = 0; nt < NTX; ++nt) {
+              acc[ft][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[nt], wh, acc[ft][nt], 0, 0, 0);
+              acc[ft][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[nt], wl, acc[ft][nt], 0, 0, 0);
+            }
+          } else {
+            const f16x8 wb = dequant8(r.w[g][ft][j], scale_pair(r.s[g][ft], j));
+#pragma unroll
+            for (int nt = 0; nt < NTX; ++nt)
+              acc[ft][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[nt], wb, acc[ft][nt], 0, 0, 0);
+          }
+        }
+      }
+  };
+
+  // finish panel pnl: hi/lo rows merged into the LDS tile [feature][node],
+  // split panels reduced across blocks, then the epilogue
+  auto flush = [&](int64_t pnl) {
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc[ft][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    {
-      Raw<NT, FT, AM> raw;
-      Ready<NT, FT> rdy;
-      int c = c0 + wave;
-      if (c < c1) load_raw(p, c, t0, lane, raw);
-      while (c < c1) {
-        make_ready(raw, rdy, rinv);
-        const int cn = c + 4;
-        if (cn < c1) load_raw(p, cn, t0, lane, raw);
-        mma_ready(rdy, acc);
-        c = cn;
+      for (int nt = 0; nt < NTX; ++nt) {
+        // D layout: column (feature) = lane % 16, rows 4 * (lane / 16) + i =
+        // hi/lo rows of nodes nt * 8 + 2 * (lane / 16) + {0, 1}
+        const int fl = (wave * FT + ft) * 16 + lr;
+        const int n0 = nt * 8 + 2 * lq;
+        tile[fl][n0] = acc[ft][nt][0] + acc[ft][nt][1];
+        tile[fl][n0 + 1] = acc[ft][nt][2] + acc[ft][nt][3];
+        acc[ft][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-    }
+    lds_barrier();
 
-    // cross-wave reduction in a fixed order (deterministic)
-    if (wave > 0) {
-#pragma unroll
-      for (int ft = 0; ft < FT; ++ft)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) red[wave - 1][ft][nt][i][lane] = acc[ft][nt][i];
-    }
-    __syncthreads();
-    if (wave == 0) {
-#pragma unroll
-      for (int ft = 0; ft < FT; ++ft)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float v = acc[ft][nt][i];
-            v += red[0][ft][nt][i][lane];
-            v += red[1][ft][nt][i][lane];
-            v += red[2][ft][nt][i][lane];
-            // D layout: column (feature) = lane % 16, row (node) = 4 * (lane / 16) + i
-            tile[ft * 16 + lr][nt * 16 + lq * 4 + i] = v;
-          }
-    }
-    __syncthreads();
-
-    // a feature group cut between blocks: last contributor to arrive sums
-    const int bf = block_of((int64_t)fg * G, U, B);
-    const int bl = block_of((int64_t)fg * G + G - 1, U, B);
+    const int64_t first = pnl * GU, last = pnl * GU + GU - 1;
+    const int bf = block_of_unit(first, U, B);
+    const int bl = block_of_unit(last, U, B);
     if (bf != bl) {
-      const int slot = (u_begin >= (int64_t)fg * G) ? 0 : 1;
+      constexpr int PER = (TILE + NTH - 1) / NTH;
+      const int slot = (u_begin >= first) ? 0 : 1;
       float* part = p.partials + ((int64_t)b * 2 + slot) * TILE;
-      for (int i = tid; i < TILE; i += 256) st_coherent(part + i, tile[i / TILE_N][i % TILE_N]);
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        const int i = tid + k * NTH;
+        if (i < TILE) st_coherent(part + i, tile[i / TILE_N][i % TILE_N]);
+      }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // every wave's stores done
-      __syncthreads();
+      lds_barrier();
       if (tid == 0) {
         // the partials were written through (agent-scope stores) and every
         // wave waited for them before the barrier, so a relaxed count suffices
-        const unsigned prev = __hip_atomic_fetch_add(&p.counters[fg], 1u, __ATOMIC_RELAXED,
+        const unsigned prev = __hip_atomic_fetch_add(&p.counters[pnl], 1u, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT);
         s_last = prev == (unsigned)(bl - bf);
       }
-      __syncthreads();
-      if (!s_last) continue;
-      // sum the contributors in block order; all loads of a batch of 8
-      // contributors are issued before any add so their latencies overlap
-      constexpr int PER = TILE / 256;
-      float acc_s[PER];
+      lds_barrier();
+      if (!s_last) return;
+      // sum the contributors in block order, CB at a time with all their
+      // loads in flight together
+      constexpr int CB = PER <= 12 ? 6 : 3;
+      float sum[PER];
 #pragma unroll
-      for (int k = 0; k < PER; ++k) acc_s[k] = 0.f;
-      for (int b0 = bf; b0 <= bl; b0 += 8) {
-        float v[8][PER];
+      for (int k = 0; k < PER; ++k) sum[k] = 0.f;
+      for (int b0 = bf; b0 <= bl; b0 += CB) {
+        float v[CB][PER];
 #pragma unroll
-        for (int uu = 0; uu < 8; ++uu) {
-          const int bb = b0 + uu;
-          if (bb <= bl) {
-            const int sl = ((int64_t)bb * U / B >= (int64_t)fg * G) ? 0 : 1;
-            const float* src = p.partials + ((int64_t)bb * 2 + sl) * TILE + tid;
+        for (int uu = 0; uu < CB; ++uu) {
+          const int bb = min(b0 + uu, bl);  // past the last contributor: re-read it, unused
+          const int sl = (range_start(bb, U, B) >= first) ? 0 : 1;
+          const float* src = p.partials + ((int64_t)bb * 2 + sl) * TILE + tid;
 #pragma unroll
-            for (int k = 0; k < PER; ++k) v[uu][k] = ld_coherent(src + k * 256);
-          }
+          for (int k = 0; k < PER; ++k)
+            v[uu][k] = (tid + k * NTH < TILE) ? ld_coherent(src + k * NTH) : 0.f;
         }
 #pragma unroll
-        for (int uu = 0; uu < 8; ++uu)
+        for (int uu = 0; uu < CB; ++uu)
           if (b0 + uu <= bl)
 #pragma unroll
-            for (int k = 0; k < PER; ++k) acc_s[k] += v[uu][k];
+            for (int k = 0; k < PER; ++k) sum[k] += v[uu][k];
       }
 #pragma unroll
       for (int k = 0; k < PER; ++k) {
-        const int i = tid + k * 256;
-        tile[i / TILE_N][i % TILE_N] = acc_s[k];
+        const int i = tid + k * NTH;
+        if (i < TILE) tile[i / TILE_N][i % TILE_N] = sum[k];
       }
       if (tid == 0)
-        __hip_atomic_store(&p.counters[fg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __syncthreads();
+        __hip_atomic_store(&p.counters[pnl], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      lds_barrier();
     }
 
+    const int64_t t0 = pnl * PT;
     // ---------------- epilogues on the finished tile [feature][node]
     if constexpr (EPI == EPI_RESID) {
-      // x += y; the new rows' per-group sums of x^2 feed the next RMSNorm
-      for (int i = tid; i < TILE_F * nn; i += 256) {
+      // x += y: all of this thread's residual loads are issued before any store
+      constexpr int EPT = (TILE_F * TILE_N + NTH - 1) / NTH;
+      float xv[EPT];
+#pragma unroll
+      for (int k = 0; k < EPT; ++k) {
+        const int i = tid + k * NTH;
         const int n = i / TILE_F, fl = i - n * TILE_F;
-        const int64_t f = (int64_t)t0 * 16 + fl;
-        float xn = 0.f;
-        if (f < p.n_out) {
-          float* r = e.resid + (int64_t)n * e.ld_out + f;
-          xn = *r + tile[fl][n];
-          *r = xn;
-        }
-        tile[fl][n] = xn * xn;
+        const int64_t f = t0 * 16 + fl;
+        xv[k] = (n < nn && f < p.n_out) ? e.resid[(int64_t)n * e.ld_out + f] : 0.f;
       }
-      if (e.ssq_out) {
-        __syncthreads();
-        if (tid < nn) {
-          float s = 0.f;
-          for (int fl = 0; fl < TILE_F; ++fl) s += tile[fl][tid];
-          e.ssq_out[(int64_t)fg * nn + tid] = s;
-        }
+#pragma unroll
+      for (int k = 0; k < EPT; ++k) {
+        const int i = tid + k * NTH;
+        const int n = i / TILE_F, fl = i - n * TILE_F;
+        const int64_t f = t0 * 16 + fl;
+        if (n < nn && f < p.n_out) e.resid[(int64_t)n * e.ld_out + f] = xv[k] + tile[fl][n];
       }
     } else if constexpr (EPI == EPI_SWIGLU) {
-      // packed tiles (2i, 2i+1) = (gate, up) rows [16i, 16i + 16); m as fp16 hi + lo
-      for (int i = tid; i < (TILE_F / 2) * nn; i += 256) {
+      // packed tiles (2i, 2i+1) = (gate, up) rows [16i, 16i + 16); m as hi/lo rows
+      for (int i = tid; i < (TILE_F / 2) * nn; i += NTH) {
         const int n = i / (TILE_F / 2), rl = i - n * (TILE_F / 2);
         const int a = rl / 16, r = rl % 16;
-        const int64_t row = ((int64_t)t0 / 2 + a) * 16 + r;
+        const int64_t row = (t0 / 2 + a) * 16 + r;
         if (2 * row < p.n_out) {
           const float gt = tile[(2 * a) * 16 + r][n];
           const float up = tile[(2 * a + 1) * 16 + r][n];
           const float m = gt / (1.0f + expf(-gt)) * up;
           const f16 hi = (f16)m;
-          e.out16[(int64_t)n * e.ld_out + row] = __builtin_bit_cast(uint16_t, hi);
-          e.out16_lo[(int64_t)n * e.ld_out + row] = f32_to_f16_bits(m - (float)hi);
+          e.out16[(int64_t)(2 * n) * e.ld_out + row] = __builtin_bit_cast(uint16_t, hi);
+          e.out16[(int64_t)(2 * n + 1) * e.ld_out + row] = f32_to_f16_bits(m - (float)hi);
         }
       }
     } else if constexpr (EPI == EPI_QKV) {
       // rotate-half RoPE on q and k at pos = prefix_len + depth; v unrotated
       const int hd = e.head_dim;
-      for (int i = tid; i < TILE_F * nn; i += 256) {
+      for (int i = tid; i < TILE_F * nn; i += NTH) {
         const int n = i / TILE_F, fl = i - n * TILE_F;
-        const int64_t prow = (int64_t)t0 * 16 + fl;
+        const int64_t prow = t0 * 16 + fl;
         if (prow >= p.n_out) continue;
         const int head = (int)(prow / hd);
         const int r = (int)(prow % hd);
@@ -523,18 +486,18 @@ __global__ __launch_bounds__(256) void gemm_q4_kernel(GemmParams p, EpiArgs e) {
       }
     } else if constexpr (EPI == EPI_LOGITS) {
       if (e.out16) {
-        for (int i = tid; i < TILE_F * nn; i += 256) {
+        for (int i = tid; i < TILE_F * nn; i += NTH) {
           const int n = i / TILE_F, fl = i - n * TILE_F;
-          const int64_t f = (int64_t)t0 * 16 + fl;
+          const int64_t f = t0 * 16 + fl;
           if (f < p.n_out) e.out16[(int64_t)n * e.ld_out + f] = f32_to_bf16_bits(tile[fl][n]);
         }
       }
-      // this group's best / runner-up per node, merged into the block's running pair
+      // this panel's best / runner-up per node, merged into the block's running pair
       if (tid < nn) {
         float v1 = best1[tid], v2 = best2[tid];
         int i1 = besti[tid];
         for (int fl = 0; fl < TILE_F; ++fl) {
-          const int64_t f = (int64_t)t0 * 16 + fl;
+          const int64_t f = t0 * 16 + fl;
           if (f >= p.n_out) break;
           merge_top2(v1, i1, v2, tile[fl][tid], (int)f, -INFINITY);
         }
@@ -543,7 +506,79 @@ __global__ __launch_bounds__(256) void gemm_q4_kernel(GemmParams p, EpiArgs e) {
         besti[tid] = i1;
       }
     }
-    __syncthreads();  // LDS tiles are reused by the next segment
+    lds_barrier();  // the LDS tile is reused by the next panel
+  };
+
+  // One unit u: load the activation slice of unit u + 2, MFMA unit u from
+  // LDS, refill this weight slot with unit u + 2, publish the slice of unit
+  // u + 1 (loaded one unit earlier) to the other LDS buffer.  Prefetches past
+  // the block's last unit re-read that unit, so every path issues the same
+  // loads and the loop body is straight-line: the compiler then keeps the
+  // prefetch in flight instead of draining it with a conservative wait.
+  int xb = 0;
+  const int64_t u_last = u_end - 1;
+  Cur pf;            // the unit being prefetched
+  int64_t pf_u = 0;
+  auto step = [&](WRegs<UG, FT>& r, u32x4 (&xr_store)[XCH], u32x4 (&xr_load)[XCH]) {
+    xload(pf, xr_load);
+    compute(xb, r);
+    wload(pf, r);
+    xstore(xb ^ 1, xr_store);
+    lds_barrier();
+    xb ^= 1;
+    if (pf_u < u_last) {
+      ++pf_u;
+      advance(pf);
+    }
+  };
+
+  if (u_begin < u_end) {
+    // weights: r0 / r1 hold units u / u + 1 at the top of the loop; slices:
+    // x1 holds unit u + 1, x0 receives unit u + 2
+    WRegs<UG, FT> r0, r1;
+    u32x4 x0[XCH], x1[XCH];
+    {
+      Cur k = cur_of(u_begin);
+      wload(k, r0);
+      xload(k, x0);
+      pf_u = u_begin;
+      if (pf_u < u_last) {
+        ++pf_u;
+        advance(k);
+      }
+      wload(k, r1);
+      xload(k, x1);
+      if (pf_u < u_last) {
+        ++pf_u;
+        advance(k);
+      }
+      pf = k;
+      xstore(0, x0);
+    }
+    lds_barrier();
+    int64_t u = u_begin;
+    while (u < u_end) {
+      const int64_t pnl = u / GU;
+      const int64_t s_end = min((pnl + 1) * GU, u_end);
+      for (; u + 2 <= s_end; u += 2) {
+        step(r0, x1, x0);
+        step(r1, x0, x1);
+      }
+      if (u < s_end) {  // odd segment: one more unit, then the rings turn by one
+        step(r0, x1, x0);
+        const WRegs<UG, FT> t = r0;
+        r0 = r1;
+        r1 = t;
+#pragma unroll
+        for (int i = 0; i < XCH; ++i) {
+          const u32x4 tx = x0[i];
+          x0[i] = x1[i];
+          x1[i] = tx;
+        }
+        u += 1;
+      }
+      flush(pnl);
+    }
   }
 
   if constexpr (EPI == EPI_LOGITS) {
@@ -551,48 +586,69 @@ __global__ __launch_bounds__(256) void gemm_q4_kernel(GemmParams p, EpiArgs e) {
   }
 }
 
-template <int NT, int FT, int AM, int EPI>
+template <int FT, int NTX, int EPI, bool EXACT>
 static hipError_t launch_t(const GemmParams& p, const EpiArgs& e, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_q4_kernel<NT, FT, AM, EPI>), dim3(p.blocks), dim3(256), 0, s, p, e);
+  bool two = false;
+  if constexpr (NTX <= 4) two = gemm_ug(p.kgroups, NTX) == 2;
+  if constexpr (NTX <= 4) {
+    if (two) {
+      hipLaunchKernelGGL((gemm_q4_kernel<kGemmWaves, FT, NTX, 2, EPI, EXACT>), dim3(p.blocks),
+                         dim3(kGemmWaves * 64), 0, s, p, e);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((gemm_q4_kernel<kGemmWaves, FT, NTX, 1, EPI, EXACT>), dim3(p.blocks),
+                     dim3(kGemmWaves * 64), 0, s, p, e);
   return hipGetLastError();
 }
 
-template <int AM, int EPI>
-static hipError_t launch_nt(const GemmParams& p, const EpiArgs& e, hipStream_t s) {
-  const int nt = (p.n_nodes + 15) / 16;
-  switch (nt) {
-    case 1: return launch_t<1, 4, AM, EPI>(p, e, s);
-    case 2: return launch_t<2, 4, AM, EPI>(p, e, s);
-    case 3: return launch_t<3, 2, AM, EPI>(p, e, s);
-    default: return launch_t<4, 2, AM, EPI>(p, e, s);
+template <int EPI, bool EXACT>
+static hipError_t launch_ntx(const GemmParams& p, const EpiArgs& e, hipStream_t s) {
+  switch (gemm_ntx(p.n_nodes)) {
+    case 1: return launch_t<gemm_ft_for(1), 1, EPI, EXACT>(p, e, s);
+    case 2: return launch_t<gemm_ft_for(2), 2, EPI, EXACT>(p, e, s);
+    case 3: return launch_t<gemm_ft_for(3), 3, EPI, EXACT>(p, e, s);
+    case 4: return launch_t<gemm_ft_for(4), 4, EPI, EXACT>(p, e, s);
+    case 5: return launch_t<gemm_ft_for(5), 5, EPI, EXACT>(p, e, s);
+    case 6: return launch_t<gemm_ft_for(6), 6, EPI, EXACT>(p, e, s);
+    case 7: return launch_t<gemm_ft_for(7), 7, EPI, EXACT>(p, e, s);
+    default: return launch_t<gemm_ft_for(8), 8, EPI, EXACT>(p, e, s);
   }
 }
 
-int gemm_ft(int n_nodes) { return ((n_nodes + 15) / 16) <= 2 ? 4 : 2; }
+int gemm_ntx(int n_nodes) { return (2 * n_nodes + 15) / 16; }
+
+// column groups per unit: two (256 inputs) when k_in allows it and the LDS
+// staging of two groups fits beside the tile
+int gemm_ug(int kgroups, int ntx) { return (kgroups % 2 == 0 && ntx <= 4) ? 2 : 1; }
 
 GemmPlan plan_gemm(int64_t n_out, int64_t k_in, int n_nodes) {
   GemmPlan g;
-  g.ft = gemm_ft(n_nodes);
-  g.nt = (n_nodes + 15) / 16;
+  g.ntx = gemm_ntx(n_nodes);
+  g.ft = gemm_ft_for(g.ntx);
   g.n_tiles = (int)(n_out / 16);
   g.kgroups = (int)(k_in / 128);
-  g.fgroups = (g.n_tiles + g.ft - 1) / g.ft;
-  g.units = (int64_t)g.fgroups * g.kgroups;
-  // two resident blocks per CU on 256 CUs, never more blocks than units
-  g.blocks = (int)(g.units < 512 ? g.units : 512);
-  g.tile_floats = g.ft * 16 * g.nt * 16;
+  const int pt = kGemmWaves * g.ft;
+  g.panels = (g.n_tiles + pt - 1) / pt;
+  g.ug = gemm_ug(g.kgroups, g.ntx);
+  g.units = (int64_t)g.panels * (g.kgroups / g.ug);
+  // kGemmBlocksPerCU resident blocks on each of the 256 CUs; blocks take
+  // whole pairs of units
+  const int64_t pairs = (g.units + 1) / 2;
+  const int64_t target = 256 * kGemmBlocksPerCU;
+  g.blocks = (int)(pairs < target ? pairs : target);
+  g.tile_floats = pt * 16 * g.ntx * 8;
   return g;
 }
 
-hipError_t launch_gemm(int epi, const GemmParams& p, const EpiArgs& e, hipStream_t s) {
-  if (p.a_mode == A_F32N) {
-    switch (epi) {
-      case EPI_QKV: return launch_nt<A_F32N, EPI_QKV>(p, e, s);
-      case EPI_SWIGLU: return launch_nt<A_F32N, EPI_SWIGLU>(p, e, s);
-      default: return launch_nt<A_F32N, EPI_LOGITS>(p, e, s);
-    }
+hipError_t launch_gemm(int epi, bool exact, const GemmParams& p, const EpiArgs& e, hipStream_t s) {
+  switch (epi) {
+    case EPI_QKV: return launch_ntx<EPI_QKV, true>(p, e, s);
+    case EPI_SWIGLU: return launch_ntx<EPI_SWIGLU, false>(p, e, s);
+    case EPI_LOGITS: return launch_ntx<EPI_LOGITS, true>(p, e, s);
+    default:
+      return exact ? launch_ntx<EPI_RESID, true>(p, e, s) : launch_ntx<EPI_RESID, false>(p, e, s);
   }
-  return launch_nt<A_F16HL, EPI_RESID>(p, e, s);
 }
 
 }  // namespace lucev

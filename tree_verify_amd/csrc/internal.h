@@ -7,40 +7,45 @@ namespace lucev {
 
 enum { W_PLAIN = 0, W_QKV = 1, W_GU = 2 };  // same values as LUCEV_W_*
 enum { EPI_RESID = 0, EPI_SWIGLU = 1, EPI_QKV = 2, EPI_LOGITS = 3 };
-enum { A_F16HL = 0, A_F32N = 1 };
 
-// GEMM partition: a flat list of units (4-tile feature group fg, 128-column
-// group c), fg-major, split evenly over the blocks (block-level stream-K).
+// GEMM partition: blocks of kGemmWaves waves own panels of kGemmWaves *
+// kGemmFT 16-row tiles; the flat list of units (panel, one or two 128-column
+// groups), panel-major, is split evenly over the blocks (block-level
+// stream-K).
+#ifndef LUCEV_GEMM_WAVES
+#define LUCEV_GEMM_WAVES 8
+#endif
+#ifndef LUCEV_GEMM_FT
+#define LUCEV_GEMM_FT 2
+#endif
+#ifndef LUCEV_GEMM_BPC
+#define LUCEV_GEMM_BPC 1
+#endif
+constexpr int kGemmWaves = LUCEV_GEMM_WAVES;     // waves per block
+constexpr int kGemmFT = LUCEV_GEMM_FT;           // 16-row tiles per wave
+constexpr int kGemmBlocksPerCU = LUCEV_GEMM_BPC;  // grid = 256 CUs x this (at most)
+
 struct GemmPlan {
-  int ft, nt, n_tiles, kgroups, fgroups, blocks, tile_floats;
+  int ft, ntx, ug, n_tiles, kgroups, panels, blocks, tile_floats;
   int64_t units;
 };
 
 struct GemmParams {
-  int a_mode;               // A_F16HL or A_F32N
-  const uint16_t* Xhi;      // A_F16HL: fp16 high / low planes [n_nodes][ldx], x = hi + lo
-  const uint16_t* Xlo;
-  const float* Xf;          // A_F32N: fp32 residual [n_nodes][ldx]
-  const uint16_t* g;        // A_F32N: bf16 RMSNorm gain [k_in]
-  const float* ssq;         // A_F32N: row sums of x^2 as [ssq_groups][n_nodes] partials
-  int ssq_groups;
-  int ldx;
+  const uint16_t* X;        // fp16 [2 * n_nodes][k_in]: row 2i = hi(x_i), row 2i+1 = lo(x_i)
   int n_nodes;
   const uint8_t* wq;        // nibble region of the packed matrix
   const uint16_t* wsc;      // scale region (fp16 bits)
   int64_t n_out, k_in;
-  int n_tiles, kgroups, fgroups, blocks;
+  int n_tiles, kgroups, panels, blocks;
   int64_t units;
-  float* partials;          // [blocks][2][tile]: split-segment partial tiles
-  uint32_t* counters;       // [fgroups], zero between calls
-  float rms_eps;
+  float* partials;          // [blocks][2][tile]: split-panel partial tiles
+  uint32_t* counters;       // [panels], zero between calls
 };
 
 struct EpiArgs {
   float* resid;             // EPI_RESID: fp32 [n][ld_out], updated in place
-  float* ssq_out;           // EPI_RESID: per feature group sum of x_new^2, [fgroups][n], or NULL
-  uint16_t* out16;          // bf16 q / logits (may be NULL) / fp16 high plane of SwiGLU m
-  uint16_t* out16_lo;       // fp16 low plane of SwiGLU m
+  uint16_t* out16;          // bf16 q (EPI_QKV, may be NULL) / bf16 logits (EPI_LOGITS, may be
+                            // NULL) / fp16 hi/lo rows [2n][ld_out] of SwiGLU m (EPI_SWIGLU)
   int ld_out;
   uint16_t* k_out;          // EPI_QKV: bf16 [n][Hkv][d]
   uint16_t* v_out;
@@ -53,8 +58,14 @@ struct EpiArgs {
   double inv_freq[kMaxNodes];  // base^(-2j/d), j < d/2
 };
 
+int gemm_ntx(int n_nodes);  // 16-row MFMA tiles of the 2n hi/lo rows
+int gemm_ug(int kgroups, int ntx);  // 128-column groups per unit
+// tiles per wave: fewer when many node tiles already fill the registers
+constexpr int gemm_ft_for(int ntx) { return ntx <= 4 ? kGemmFT : (kGemmFT > 1 ? kGemmFT / 2 : 1); }
 GemmPlan plan_gemm(int64_t n_out, int64_t k_in, int n_nodes);
-hipError_t launch_gemm(int epi, const GemmParams& p, const EpiArgs& e, hipStream_t s);
+// exact: weights enter as an exact fp16 hi + lo pair (QKV, lm_head always;
+// for EPI_RESID as asked), else rounded once to fp16
+hipError_t launch_gemm(int epi, bool exact, const GemmParams& p, const EpiArgs& e, hipStream_t s);
 hipError_t launch_pack_q4(const uint8_t* q, const uint16_t* d, int64_t n_out, int64_t k_in,
                           int kind, int head_dim, void* dst, hipStream_t s);
 void pack_q4_host(const uint8_t* q, const uint16_t* d, int64_t n_out, int64_t k_in, int kind,
@@ -93,8 +104,8 @@ struct CombineParams {
   const float* ml_part;
   int n_chunks, n, n_q_heads, n_kv_heads, rows;
   float scale_log2;
-  uint16_t* out;      // [n][Hq][d]: bf16, or the fp16 high plane when out_lo is set
-  uint16_t* out_lo;   // fp16 low plane (o = hi + lo) or NULL
+  uint16_t* out;      // bf16 [n][Hq][d], or fp16 hi/lo rows [2n][Hq * d] when out_hilo
+  int out_hilo;
 };
 
 AttnPlan plan_attention(int n_nodes, int n_q_heads, int n_kv_heads, int head_dim, int prefix_len);
@@ -104,7 +115,10 @@ hipError_t launch_attention(const AttnPlan& plan, int head_dim, const AttnParams
 
 // ---------------------------------------------------------------- small kernels
 
-hipError_t launch_row_ssq(const float* x, int n, int hidden, float* ssq, hipStream_t s);
+// RMSNorm of each row into the GEMM operand: u = x / sqrt(mean(x^2) + eps) * g
+// as fp16 hi/lo rows [2n][hidden]
+hipError_t launch_norm_hilo(const float* x, int n, int hidden, const uint16_t* g, float eps,
+                            uint16_t* out, hipStream_t s);
 hipError_t launch_finalize(const f32x4* cand, int n_cand, const TreeArgs& t, int32_t* argmax,
                            float* gap, int32_t* path, int32_t* path_len, int32_t* committed,
                            hipStream_t s);

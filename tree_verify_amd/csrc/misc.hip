@@ -1,14 +1,17 @@
-// Greedy-acceptance finalisation and a fill kernel.
+// RMSNorm into the GEMM operand, greedy-acceptance finalisation and a fill kernel.
 #include "internal.h"
 
 namespace lucev {
 
-// Row sums of x^2 (the statistic of RMSNorm), one block per row, fixed
-// reduction order.
-__global__ __launch_bounds__(256) void row_ssq_kernel(const float* __restrict__ x, int hidden,
-                                                      float* __restrict__ ssq) {
+// RMSNorm of one row per block into the GEMM operand: u = x * g / sqrt(mean(x^2)
+// + eps), written as fp16 rows 2i (hi) and 2i+1 (lo = u - hi).  The sum of
+// squares is reduced in a fixed order.
+__global__ __launch_bounds__(256) void norm_hilo_kernel(const float* __restrict__ x, int hidden,
+                                                        const uint16_t* __restrict__ g, float eps,
+                                                        uint16_t* __restrict__ out) {
   __shared__ float red[4];
-  const float* xr = x + (int64_t)blockIdx.x * hidden;
+  const int row = blockIdx.x;
+  const float* xr = x + (int64_t)row * hidden;
   float s = 0.f;
   for (int i = threadIdx.x * 4; i < hidden; i += 256 * 4) {
     const float4 v = *reinterpret_cast<const float4*>(xr + i);
@@ -17,11 +20,29 @@ __global__ __launch_bounds__(256) void row_ssq_kernel(const float* __restrict__ 
   s = wave_sum(s);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
   __syncthreads();
-  if (threadIdx.x == 0) ssq[blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
+  const float rinv = 1.0f / sqrtf(((red[0] + red[1]) + (red[2] + red[3])) / (float)hidden + eps);
+  uint16_t* hi = out + (int64_t)(2 * row) * hidden;
+  uint16_t* lo = hi + hidden;
+  for (int i = threadIdx.x * 4; i < hidden; i += 256 * 4) {
+    const float4 v = *reinterpret_cast<const float4*>(xr + i);
+    const uint2 gw = *reinterpret_cast<const uint2*>(g + i);
+    const float u[4] = {v.x * rinv * bf16_bits_to_f32(gw.x & 0xFFFFu), v.y * rinv * bf16_bits_to_f32(gw.x >> 16),
+                        v.z * rinv * bf16_bits_to_f32(gw.y & 0xFFFFu), v.w * rinv * bf16_bits_to_f32(gw.y >> 16)};
+    uint16_t h[4], l[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const f16 hh = (f16)u[k];
+      h[k] = __builtin_bit_cast(uint16_t, hh);
+      l[k] = f32_to_f16_bits(u[k] - (float)hh);
+    }
+    *reinterpret_cast<uint2*>(hi + i) = make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
+    *reinterpret_cast<uint2*>(lo + i) = make_uint2(l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16));
+  }
 }
 
-hipError_t launch_row_ssq(const float* x, int n, int hidden, float* ssq, hipStream_t s) {
-  hipLaunchKernelGGL(row_ssq_kernel, dim3(n), dim3(256), 0, s, x, hidden, ssq);
+hipError_t launch_norm_hilo(const float* x, int n, int hidden, const uint16_t* g, float eps,
+                            uint16_t* out, hipStream_t s) {
+  hipLaunchKernelGGL(norm_hilo_kernel, dim3(n), dim3(256), 0, s, x, hidden, g, eps, out);
   return hipGetLastError();
 }
 
