@@ -19,26 +19,59 @@
 //             row): max and sum in log2 units and the chunk-normalised O.
 //   combine: one block per (node, query head): merges the chunk partials and
 //             the (at most 64) ancestor keys with a log-sum-exp merge.
+#include <type_traits>
+
 #include "internal.h"
 
 namespace lucev {
 
 constexpr int KT = 64;  // tokens per LDS tile
 
-// Blocks have at least 512 threads (8 waves); with one query tile per wave
-// up to 16 waves share the LDS tiles, with more tiles per wave 8 waves do.
-template <int D, int QPW>
-__global__ __launch_bounds__(QPW == 1 ? 1024 : 512) void attn_partial_kernel(AttnParams p) {
-  constexpr int KLD = D + 8;   // padded K row (elements): spreads LDS banks
-  constexpr int VLD = KT + 8;  // padded V^T row
-  constexpr int KCH = KT * D / 8;  // 16-byte chunks of a K tile
-  constexpr int VCH = D * KT / 8;
-  constexpr int MAXC = (KCH + VCH) / 512;
-  __shared__ __attribute__((aligned(16))) uint16_t sK[KT * KLD];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[D * VLD];
+// Block barrier that orders LDS only: the next tiles' global loads stay in
+// flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Waves per block for a query-tile count and tiles per wave.
+constexpr int attn_max_waves(int qpw) { return qpw == 1 ? 12 : 8; }
+
+// wait until at most n of this wave's vector-memory operations are in
+// flight (vmcnt only; LDS and export counters left alone)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// One block per (prefix chunk, KV head), one wave per QPW query tiles (waves
+// past the last query tile only load).  K and V^T tiles of 64 tokens go
+// straight from HBM into a ring of three LDS buffers with 16-byte
+// direct-to-LDS loads, two tiles ahead of the MFMAs; every wave issues the
+// same number of them per tile (padded with loads into a scratch area), so a
+// fixed vmcnt wait plus one barrier per tile publishes a tile.  A load
+// instruction fills 1 KB of LDS, 16 bytes per lane in lane order, so the bank
+// swizzles are applied on the global side: LDS chunk c of K row `key` holds
+// the row's 16-byte chunk c ^ ((key & 3) | ((key >> 3) & 3) << 2), and chunk
+// c of V^T row `dim` holds chunk c ^ ((dim >> 1) & 7); the 16 rows one
+// 16-lane group reads at once then fall in 16 different bank groups.  The
+// ragged last tile of the prefix goes through registers so tokens past it
+// are zero.
+template <int D, int QPW, bool QLO>
+__global__ __launch_bounds__(attn_max_waves(QPW) * 64) void attn_partial_kernel(AttnParams p) {
+  constexpr int WAVES = attn_max_waves(QPW);
+  constexpr int KCPR = D / 8;                   // 16-byte chunks per K row
+  constexpr int KROWS = 64 / KCPR;              // K rows per 1 KB load
+  constexpr int KBYTES = KT * D * 2;            // one K tile
+  constexpr int VBYTES = D * KT * 2;            // one V^T tile (rows of 128 bytes)
+  constexpr int NLD = (KBYTES + VBYTES) / 1024; // 1 KB loads per tile
+  constexpr int LPW = (NLD + WAVES - 1) / WAVES;  // loads per wave per tile
+  constexpr int BUF = KBYTES + VBYTES;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[3 * BUF + 1024];
 
   const int tid = threadIdx.x;
-  const int nth = blockDim.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lq = lane >> 4;
   const int chunk = blockIdx.x;
@@ -47,48 +80,56 @@ __global__ __launch_bounds__(QPW == 1 ? 1024 : 512) void attn_partial_kernel(Att
   const int RT = (p.rows + 15) / 16;
   const int k_begin = chunk * p.chunk;
   const int k_end = min(p.prefix_len, k_begin + p.chunk);
+  const int n_tiles = (k_end - k_begin + KT - 1) / KT;
 
   const uint16_t* kbase = p.kc + (int64_t)g * p.cap * D;
   const uint16_t* vbase = p.vc + (int64_t)g * D * p.cap;
 
-  u32x4 pre[MAXC];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int r = 0; r < MAXC; ++r) {
-      const int cid = tid + r * nth;
-      u32x4 val = u32x4{0u, 0u, 0u, 0u};
-      if (cid < KCH) {
-        const int key = cid / (D / 8), part = cid % (D / 8);
-        const int gk = k0 + key;
-        if (gk < k_end) val = ld16(kbase + (int64_t)gk * D + part * 8);
-      } else if (cid < KCH + VCH) {
-        const int v = cid - KCH;
-        const int dim = v / (KT / 8), part = v % (KT / 8);
-        const int gk = k0 + part * 8;
-        if (gk < k_end) {
-          val = ld16(vbase + (int64_t)dim * p.cap + gk);
-          const int valid = k_end - gk;
-          if (valid < 8) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (e >= valid) val[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-          }
-        }
-      }
-      pre[r] = val;
+  // Load j of a tile (j < NLD): K rows for j < KBYTES / 1024, else V^T rows.
+  // This lane's global element offset at token 0 and its LDS byte offset.
+  auto load_slot = [&](int j, int64_t& goff, int& loff, int& tok, bool& is_v) {
+    if (j < KBYTES / 1024) {
+      const int key = j * KROWS + lane / KCPR, pc = lane % KCPR;
+      const int sw = ((key & 3) | (((key >> 3) & 3) << 2)) & (KCPR - 1);
+      goff = (int64_t)key * D + (pc ^ sw) * 8;
+      loff = j * 1024;
+      tok = key;
+      is_v = false;
+    } else {
+      const int dim = (j - KBYTES / 1024) * 8 + lane / 8, pc = lane % 8;
+      goff = (int64_t)dim * p.cap + (pc ^ ((dim >> 1) & 7)) * 8;
+      loff = j * 1024;
+      tok = (pc ^ ((dim >> 1) & 7)) * 8;
+      is_v = true;
     }
   };
-  auto sstore = [&]() {
+  // issue this wave's loads of tile t (clamped to the last tile) into buffer b
+  auto issue = [&](int t, int b) {
+    const int k0 = k_begin + min(t, n_tiles - 1) * KT;
+    const bool ragged = k0 + KT > k_end;
 #pragma unroll
-    for (int r = 0; r < MAXC; ++r) {
-      const int cid = tid + r * nth;
-      if (cid < KCH) {
-        const int key = cid / (D / 8), part = cid % (D / 8);
-        *reinterpret_cast<u32x4*>(sK + key * KLD + part * 8) = pre[r];
-      } else if (cid < KCH + VCH) {
-        const int v = cid - KCH;
-        const int dim = v / (KT / 8), part = v % (KT / 8);
-        *reinterpret_cast<u32x4*>(sV + dim * VLD + part * 8) = pre[r];
+    for (int r = 0; r < LPW; ++r) {
+      const int j = wave + r * WAVES;
+      uint8_t* dst = lds + (j < NLD ? b * BUF + j * 1024 : 3 * BUF);  // past NLD: scratch area
+      int64_t goff = 0;
+      int loff = 0, tok = 0;
+      bool is_v = false;
+      if (j < NLD) load_slot(j, goff, loff, tok, is_v);
+      const uint16_t* src = j < NLD ? (is_v ? vbase + goff + k0 : kbase + goff + (int64_t)k0 * D) : kbase;
+      if (!ragged || j >= NLD) {
+        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+      } else {
+        // tokens past the prefix are zero: through registers
+        const int gk = k0 + tok;
+        u32x4 val = u32x4{0u, 0u, 0u, 0u};
+        if (gk < k_end) val = ld16(src);
+        const int valid = k_end - gk;
+        if (is_v && valid < 8) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (e >= valid) val[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+        }
+        *reinterpret_cast<u32x4*>(dst + lane * 16) = val;
       }
     }
   };
@@ -109,24 +150,36 @@ __global__ __launch_bounds__(QPW == 1 ? 1024 : 512) void attn_partial_kernel(Att
       node = row / G;
       head = g * G + (row - node * G);
     }
+    // all of this lane's q loads are issued before any is used
+    const int64_t qoff = ((int64_t)node * p.n_q_heads + head) * D + lq * 8;
+    if constexpr (QLO) {
+      u32x4 raw[D / 32][2];
 #pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) {
-      const int64_t off = ((int64_t)node * p.n_q_heads + head) * D + kk * 32 + lq * 8;
-      if (p.q32) {
+      for (int kk = 0; kk < D / 32; ++kk) {
+        raw[kk][0] = ld16(p.q32 + qoff + kk * 32);
+        raw[kk][1] = ld16(p.q32 + qoff + kk * 32 + 4);
+      }
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk) {
         bf16x8 hv, lv;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float x = ok ? p.q32[off + e] : 0.f;
+          // scores come out in log2 units: q carries log2(e) / sqrt(d)
+          const float x = ok ? __uint_as_float(raw[kk][e >> 2][e & 3]) * p.scale_log2 : 0.f;
           const __bf16 hb = (__bf16)x;
           hv[e] = hb;
           lv[e] = (__bf16)(x - (float)hb);
         }
         qf[i][kk] = hv;
         ql[i][kk] = lv;
-      } else {
-        u32x4 v = u32x4{0u, 0u, 0u, 0u};
-        if (ok) v = ld16(p.q + off);
-        qf[i][kk] = __builtin_bit_cast(bf16x8, v);
+      }
+    } else {
+      u32x4 raw[D / 32];
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk) raw[kk] = ld16(p.q + qoff + kk * 32);
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk) {
+        qf[i][kk] = __builtin_bit_cast(bf16x8, ok ? raw[kk] : u32x4{0u, 0u, 0u, 0u});
         ql[i][kk] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
       }
     }
@@ -135,91 +188,137 @@ __global__ __launch_bounds__(QPW == 1 ? 1024 : 512) void attn_partial_kernel(Att
     m[i] = -INFINITY;
     l[i] = 0.f;
   }
-  const bool q_lo = p.q32 != nullptr;
+  // Scores of one 32-key half (keys ks*32 ..) for query tile i, as two 16-key
+  // MFMA tiles.  With the hi/lo q (already scaled to log2 units) the
+  // accumulators start at -bias, so they come out relative to the running
+  // max; bias is the reference the scores were taken against.
+  auto scores = [&](const uint16_t* K, int i, int ks, f32x4 (&sc)[2], float& bias) {
+    bias = m[i] == -INFINITY ? 0.f : m[i];
+    const float init = QLO ? -bias : 0.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      f32x4 a4 = f32x4{init, init, init, init};
+      // this lane's key row (order permuted for the PV operand); its swizzle is
+      // lr, so d chunk kk*4 + lq sits at (kk*4 + lq) ^ lr
+      const int key = ks * 32 + (lr >> 2) * 8 + h * 4 + (lr & 3);
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk) {
+        const bf16x8 a =
+            *reinterpret_cast<const bf16x8*>(K + key * D + (((kk * 4 + lq) ^ lr) & (KCPR - 1)) * 8);
+        a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[i][kk], a4, 0, 0, 0);
+        if constexpr (QLO) a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[i][kk], a4, 0, 0, 0);
+      }
+      sc[h] = a4;
+    }
+    if constexpr (!QLO) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) sc[h] = sc[h] * p.scale_log2 - bias;
+    }
+  };
 
-  gload(k_begin);
-  sstore();
-  __syncthreads();
+  // Online softmax of one half and its PV product.  The reference max only
+  // moves when some row's scores exceed it by more than 8 (log2 units): the
+  // exponentials stay below 2^8, the final division by l is unchanged, and
+  // most halves skip the rescale.  Returns by how much the reference moved.
+  auto softmax_pv = [&](const uint16_t* V, int i, int ks, f32x4 (&sc)[2], float bias, int k0,
+                        auto masked) -> float {
+    if constexpr (decltype(masked)::value) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+          if (k0 + ks * 32 + lq * 8 + h * 4 + ii >= k_end) sc[h][ii] = -INFINITY;
+    }
+    // this lane holds query lr, keys ks*32 + lq*8 + h*4 + ii
+    float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+    mx = fmaxf(mx, shfl_xor(mx, 16));
+    mx = fmaxf(mx, shfl_xor(mx, 32));
+    float moved = 0.f;
+    if (__builtin_amdgcn_ballot_w64(bias + mx > m[i] + 8.f) != 0) {
+      const float m_new = fmaxf(m[i], bias + mx);
+      const float alpha = __builtin_amdgcn_exp2f(m[i] - m_new);
+      moved = m_new - bias;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) sc[h] -= moved;
+      l[i] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) O[i][dt] *= alpha;
+      m[i] = m_new;
+    }
+    float psum = 0.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const float pv = __builtin_amdgcn_exp2f(sc[h][ii]);
+        sc[h][ii] = pv;
+        psum += pv;
+      }
+    l[i] += psum;
+    // P as bf16 hi + lo (about 16 significant bits)
+    bf16x8 pb, pl;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const __bf16 h0 = (__bf16)sc[0][ii];
+      const __bf16 h1 = (__bf16)sc[1][ii];
+      pb[ii] = h0;
+      pb[4 + ii] = h1;
+      pl[ii] = (__bf16)(sc[0][ii] - (float)h0);
+      pl[4 + ii] = (__bf16)(sc[1][ii] - (float)h1);
+    }
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      // V^T row dt*16 + lr (swizzle (lr >> 1) & 7), keys ks*32 + lq*8 ..
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+          V + (dt * 16 + lr) * KT + (((ks * 4 + lq) ^ ((lr >> 1) & 7)) * 8));
+      O[i][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, O[i][dt], 0, 0, 0);
+      O[i][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl, O[i][dt], 0, 0, 0);
+    }
+    // relative to m after this half, scores taken against bias sit lower by:
+    return m[i] - bias;
+  };
 
-  for (int k0 = k_begin; k0 < k_end; k0 += KT) {
-    const bool more = k0 + KT < k_end;
-    if (more) gload(k0 + KT);
-
+  // one 64-key tile: both halves' scores first, so the second half's MFMAs
+  // can overlap the first half's softmax
+  auto compute = [&](int buf, int k0, auto masked) {
+    const uint16_t* K = reinterpret_cast<const uint16_t*>(lds + buf * BUF);
+    const uint16_t* V = reinterpret_cast<const uint16_t*>(lds + buf * BUF + KBYTES);
 #pragma unroll
     for (int i = 0; i < QPW; ++i) {
       const int qt = wave * QPW + i;
       if (qt >= RT) continue;
-      // S^T tiles: subtile s = 2*ks + h covers keys ks*32 + 8*(r/4) + 4*h + r%4
-      f32x4 sacc[4];
+      f32x4 s0[2], s1[2];
+      float b0, b1;
+      scores(K, i, 0, s0, b0);
+      scores(K, i, 1, s1, b1);
+      softmax_pv(V, i, 0, s0, b0, k0, masked);
+      // the first half may have moved the reference: rebase the second
+      const float shift = m[i] == -INFINITY ? 0.f : m[i] - b1;
+      if (__builtin_amdgcn_ballot_w64(shift != 0.f) != 0) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        sacc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int ks = s >> 1, h = s & 1;
-        const int key = ks * 32 + (lr >> 2) * 8 + h * 4 + (lr & 3);
-#pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sK + key * KLD + kk * 32 + lq * 8);
-          sacc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[i][kk], sacc[s], 0, 0, 0);
-          if (q_lo) sacc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[i][kk], sacc[s], 0, 0, 0);
-        }
+        for (int h = 0; h < 2; ++h) s1[h] -= shift;
+        b1 += shift;
       }
-      // this lane holds query lr, keys ks*32 + lq*8 + h*4 + ii
-      float mx = -INFINITY;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int ks = s >> 1, h = s & 1;
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          float v = sacc[s][ii] * p.scale_log2;
-          if (k0 + ks * 32 + lq * 8 + h * 4 + ii >= k_end) v = -INFINITY;
-          sacc[s][ii] = v;
-          mx = fmaxf(mx, v);
-        }
-      }
-      mx = fmaxf(mx, shfl_xor(mx, 16));
-      mx = fmaxf(mx, shfl_xor(mx, 32));
-      const float m_new = fmaxf(m[i], mx);
-      const float alpha = __builtin_amdgcn_exp2f(m[i] - m_new);
-      float psum = 0.f;
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const float pv = __builtin_amdgcn_exp2f(sacc[s][ii] - m_new);
-          sacc[s][ii] = pv;
-          psum += pv;
-        }
-      l[i] = l[i] * alpha + psum;
-      m[i] = m_new;
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) O[i][dt] *= alpha;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        // P as bf16 hi + lo (about 16 significant bits)
-        bf16x8 pb, pl;
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const __bf16 h0 = (__bf16)sacc[2 * ks][ii];
-          const __bf16 h1 = (__bf16)sacc[2 * ks + 1][ii];
-          pb[ii] = h0;
-          pb[4 + ii] = h1;
-          pl[ii] = (__bf16)(sacc[2 * ks][ii] - (float)h0);
-          pl[4 + ii] = (__bf16)(sacc[2 * ks + 1][ii] - (float)h1);
-        }
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-          const bf16x8 a =
-              *reinterpret_cast<const bf16x8*>(sV + (dt * 16 + lr) * VLD + ks * 32 + lq * 8);
-          O[i][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, O[i][dt], 0, 0, 0);
-          O[i][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl, O[i][dt], 0, 0, 0);
-        }
-      }
+      softmax_pv(V, i, 1, s1, b1, k0, masked);
     }
+  };
+  auto compute_tile = [&](int buf, int t) {
+    const int k0 = k_begin + t * KT;
+    if (k0 + KT <= k_end)
+      compute(buf, k0, std::integral_constant<bool, false>());
+    else
+      compute(buf, k0, std::integral_constant<bool, true>());
+  };
 
-    __syncthreads();
-    if (more) {
-      sstore();
-      __syncthreads();
+  if (n_tiles > 0) {
+    issue(0, 0);
+    issue(1, 1);
+    for (int t = 0; t < n_tiles; ++t) {
+      wait_vmcnt<LPW>();  // this wave's part of tile t has landed
+      lds_barrier();      // every part has; every wave is done with tile t - 1
+      issue(t + 2, (t + 2) % 3);
+      compute_tile(t % 3, t);
     }
   }
 
@@ -349,22 +448,17 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(CombineParams c, Tree
   }
 }
 
-int attention_max_chunks(int n_kv_heads) { return (512 + n_kv_heads - 1) / n_kv_heads; }
+int attention_max_chunks(int n_kv_heads) { return (256 + n_kv_heads - 1) / n_kv_heads; }
 
 AttnPlan plan_attention(int n_nodes, int n_q_heads, int n_kv_heads, int head_dim, int prefix_len) {
   (void)head_dim;
   AttnPlan a;
   a.rows = n_nodes * (n_q_heads / n_kv_heads);
   const int rt = (a.rows + 15) / 16;
-  if (rt <= 16) {
-    a.qpw = 1;
-    a.waves = rt < 8 ? 8 : rt;
-  } else {
-    a.qpw = (rt + 7) / 8;
-    a.waves = 8;
-  }
-  // ~512 blocks over (chunk, KV head), chunks a multiple of the LDS tile
-  int chunk = (int)(((int64_t)prefix_len * n_kv_heads + 511) / 512);
+  a.qpw = rt <= attn_max_waves(1) ? 1 : (rt + attn_max_waves(2) - 1) / attn_max_waves(2);
+  a.waves = attn_max_waves(a.qpw);
+  // one block per CU over (chunk, KV head): chunks a multiple of the LDS tile
+  int chunk = (int)(((int64_t)prefix_len * n_kv_heads + 255) / 256);
   chunk = ((chunk + KT - 1) / KT) * KT;
   if (chunk < KT) chunk = KT;
   a.chunk = chunk;
@@ -374,8 +468,12 @@ AttnPlan plan_attention(int n_nodes, int n_q_heads, int n_kv_heads, int head_dim
 
 template <int D, int QPW>
 static void launch_partial(const AttnPlan& plan, const AttnParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((attn_partial_kernel<D, QPW>), dim3(plan.n_chunks, p.n_kv_heads),
-                     dim3(64 * plan.waves), 0, s, p);
+  if (p.q32)
+    hipLaunchKernelGGL((attn_partial_kernel<D, QPW, true>), dim3(plan.n_chunks, p.n_kv_heads),
+                       dim3(64 * attn_max_waves(QPW)), 0, s, p);
+  else
+    hipLaunchKernelGGL((attn_partial_kernel<D, QPW, false>), dim3(plan.n_chunks, p.n_kv_heads),
+                       dim3(64 * attn_max_waves(QPW)), 0, s, p);
 }
 
 hipError_t launch_attention(const AttnPlan& plan, int head_dim, const AttnParams& p,
