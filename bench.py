@@ -91,6 +91,44 @@ def cpu_baseline(cfg, budget_s=30.0):
                                                                   cfg.layers)}
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "tree_attention_stack27b_traffic.txt")
+ATTN_SOURCE = os.path.join(ROOT, "tree_verify_amd", "csrc", "attention.hip")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the tree attention from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary, or None when the kernel source changed
+    since those counters were taken."""
+    import hashlib
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    fields = {}
+    with open(TRAFFIC_FILE) as fh:
+        for line in fh:
+            if ":" in line:
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    with open(ATTN_SOURCE, "rb") as fh:
+        digest = hashlib.sha256(fh.read()).hexdigest()
+    if fields.get("source_sha256") != digest or "hbm_bytes_per_launch" not in fields:
+        return None
+    return int(float(fields["hbm_bytes_per_launch"]))
+
+
+def copy_calibration(nbytes):
+    """One device-to-device copy of nbytes: the reference kernel for scaling
+    the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    dev = torch.device("cuda:0")
+    a = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    b = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -99,7 +137,12 @@ def main():
     ap.add_argument("--config", default="stack27b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--attn-reps", type=int, default=20)
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run one device copy of this many bytes (counter calibration)")
     args = ap.parse_args()
+    if args.copy_bytes:
+        copy_calibration(args.copy_bytes)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(got --gpus %d)" % args.gpus, flush=True)
@@ -191,7 +234,7 @@ def main():
                    "algorithmic_bytes": total, "tokens": tok_src, "accepted_path": path},
         "roofline": {"bound": "hbm", "kernel": "tree attention, one layer (partial + combine)",
                      "achieved": round(attn_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "bytes_per_launch": ab, "avg_launch_us": round(attn_ms * 1e3, 3)},
         "step_roofline_frac": round(gbs / HBM_PEAK_GBS, 4),
     }
