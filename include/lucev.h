@@ -33,7 +33,7 @@
  *     reports a failed launch).  No C++ exception crosses the ABI.
  *   - Same inputs give bit-identical outputs (no floating-point atomics).
  *   - bf16 / fp16 tensors are passed as uint16_t bit patterns.
- *   - Shapes: hidden, ffn and n_q_heads*head_dim multiples of 128;
+ *   - Shapes: hidden, ffn and n_q_heads*head_dim multiples of 128; hidden <= 8192;
  *     head_dim in {64, 128}; n_q_heads a multiple of n_kv_heads;
  *     vocab a multiple of 16; 1 <= tree nodes <= LUCEV_MAX_NODES.
  */

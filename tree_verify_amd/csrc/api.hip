@@ -37,6 +37,7 @@ int check_shape(const lucev_shape* s) {
     return fail(LUCEV_ERR_BAD_SHAPE, "non-positive dimension");
   if (s->hidden % 128 || s->ffn % 128 || (s->n_q_heads * s->head_dim) % 128)
     return fail(LUCEV_ERR_BAD_SHAPE, "hidden, ffn and n_q_heads*head_dim must be multiples of 128");
+  if (s->hidden > 8192) return fail(LUCEV_ERR_BAD_SHAPE, "hidden must be at most 8192 (got %d)", s->hidden);
   if (s->head_dim != 64 && s->head_dim != 128)
     return fail(LUCEV_ERR_BAD_SHAPE, "head_dim must be 64 or 128 (got %d)", s->head_dim);
   if (s->n_q_heads % s->n_kv_heads)

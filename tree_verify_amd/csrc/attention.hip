@@ -348,11 +348,14 @@ __global__ __launch_bounds__(attn_max_waves(QPW) * 64) void attn_partial_kernel(
 constexpr int kMaxChunks = 512;
 
 // One block (256 threads) per (node, query head): log-sum-exp merge of the
-// prefix-chunk partials with the node's ancestor keys.
+// prefix-chunk partials with the node's ancestor keys.  The chunk maxima and
+// sums and the first chunk outputs are loaded before the ancestor scores are
+// formed, so their latency overlaps.
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(CombineParams c, TreeArgs t) {
   constexpr int PARTS = 256 / D;  // threads per output dim
   constexpr int DPL = D / 64;     // dims per lane in the ancestor dot products
+  constexpr int PRE = 16;         // chunk outputs per thread loaded up front
   __shared__ float s_w[kMaxChunks];
   __shared__ float s_anc[kMaxNodes];
   __shared__ float s_red[4];
@@ -365,6 +368,22 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(CombineParams c, Tree
   const int g = h / G;
   const int row = node * G + (h - g * G);
   const uint64_t anc = t.anc[node];
+  const int j = tid % D, part = tid / D;
+  auto prow = [&](int ch) { return ((int64_t)ch * c.n_kv_heads + g) * c.rows + row; };
+
+  // chunk statistics (one chunk per thread, more in a loop) and the first
+  // PRE chunk outputs of this thread's dim
+  float cm = -INFINITY, cl = 0.f;
+  if (tid < c.n_chunks) {
+    cm = c.ml_part[prow(tid) * 2];
+    cl = c.ml_part[prow(tid) * 2 + 1];
+  }
+  float ov[PRE];
+#pragma unroll
+  for (int r = 0; r < PRE; ++r) {
+    const int ch = part + r * PARTS;
+    ov[r] = ch < c.n_chunks ? c.o_part[prow(ch) * D + j] : 0.f;
+  }
 
   // ancestor scores: wave w takes every 4th ancestor
   {
@@ -378,23 +397,22 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(CombineParams c, Tree
     for (int a = 0; a < t.n; ++a) {
       if (!((anc >> a) & 1ull)) continue;
       if ((k & 3) == wave) {
-        float s = 0.f;
+        float sdot = 0.f;
 #pragma unroll
         for (int i = 0; i < DPL; ++i) {
           const int64_t o = ((int64_t)a * c.n_kv_heads + g) * D + lane * DPL + i;
-          s += qv[i] * (c.k32 ? c.k32[o] : bf16_bits_to_f32(c.k_tree[o]));
+          sdot += qv[i] * (c.k32 ? c.k32[o] : bf16_bits_to_f32(c.k_tree[o]));
         }
-        s = wave_sum(s) * c.scale_log2;
-        if (lane == 0) s_anc[k] = s;
+        sdot = wave_sum(sdot) * c.scale_log2;
+        if (lane == 0) s_anc[k] = sdot;
       }
       ++k;
     }
   }
   const int na = __popcll(anc);
   // running max over chunk maxima and ancestor scores
-  float mx = -INFINITY;
-  for (int ch = tid; ch < c.n_chunks; ch += 256)
-    mx = fmaxf(mx, c.ml_part[(((int64_t)ch * c.n_kv_heads + g) * c.rows + row) * 2]);
+  float mx = cm;
+  for (int ch = tid + 256; ch < c.n_chunks; ch += 256) mx = fmaxf(mx, c.ml_part[prow(ch) * 2]);
   mx = wave_max(mx);
   if (lane == 0) s_red[wave] = mx;
   __syncthreads();
@@ -402,9 +420,13 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(CombineParams c, Tree
   for (int k = 0; k < na; ++k) M = fmaxf(M, s_anc[k]);
   __syncthreads();
   float lsum = 0.f;
-  for (int ch = tid; ch < c.n_chunks; ch += 256) {
-    const int64_t prow = ((int64_t)ch * c.n_kv_heads + g) * c.rows + row;
-    const float w = __builtin_amdgcn_exp2f(c.ml_part[prow * 2] - M) * c.ml_part[prow * 2 + 1];
+  if (tid < c.n_chunks) {
+    const float w = __builtin_amdgcn_exp2f(cm - M) * cl;
+    s_w[tid] = w;
+    lsum = w;
+  }
+  for (int ch = tid + 256; ch < c.n_chunks; ch += 256) {
+    const float w = __builtin_amdgcn_exp2f(c.ml_part[prow(ch) * 2] - M) * c.ml_part[prow(ch) * 2 + 1];
     s_w[ch] = w;
     lsum += w;
   }
@@ -415,13 +437,13 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(CombineParams c, Tree
   for (int k = 0; k < na; ++k) L += __builtin_amdgcn_exp2f(s_anc[k] - M);
 
   // weighted sum of the chunk outputs: PARTS threads per dim, fixed order
-  const int j = tid % D, part = tid / D;
   float acc = 0.f;
-#pragma unroll 8
-  for (int ch = part; ch < c.n_chunks; ch += PARTS) {
-    const int64_t prow = ((int64_t)ch * c.n_kv_heads + g) * c.rows + row;
-    acc += s_w[ch] * c.o_part[prow * D + j];
+#pragma unroll
+  for (int r = 0; r < PRE; ++r) {
+    const int ch = part + r * PARTS;
+    if (ch < c.n_chunks) acc += s_w[ch] * ov[r];
   }
+  for (int ch = part + PRE * PARTS; ch < c.n_chunks; ch += PARTS) acc += s_w[ch] * c.o_part[prow(ch) * D + j];
   s_acc[part][j] = acc;
   __syncthreads();
   if (tid < D) {

@@ -4,36 +4,54 @@
 namespace lucev {
 
 // RMSNorm of one row per block into the GEMM operand: u = x * g / sqrt(mean(x^2)
-// + eps), written as fp16 rows 2i (hi) and 2i+1 (lo = u - hi).  The sum of
+// + eps), written as fp16 rows 2i (hi) and 2i+1 (lo = u - hi).  The row is
+// read once into registers (all loads in flight together); the sum of
 // squares is reduced in a fixed order.
-__global__ __launch_bounds__(256) void norm_hilo_kernel(const float* __restrict__ x, int hidden,
-                                                        const uint16_t* __restrict__ g, float eps,
-                                                        uint16_t* __restrict__ out) {
-  __shared__ float red[4];
+constexpr int kNormThreads = 512;
+constexpr int kNormMaxPer = 4;  // float4 per thread: rows up to 512 * 16 = 8192 wide
+
+__global__ __launch_bounds__(kNormThreads) void norm_hilo_kernel(const float* __restrict__ x, int hidden,
+                                                                 const uint16_t* __restrict__ g, float eps,
+                                                                 uint16_t* __restrict__ out) {
+  __shared__ float red[kNormThreads / 64];
   const int row = blockIdx.x;
+  const int tid = threadIdx.x;
   const float* xr = x + (int64_t)row * hidden;
-  float s = 0.f;
-  for (int i = threadIdx.x * 4; i < hidden; i += 256 * 4) {
-    const float4 v = *reinterpret_cast<const float4*>(xr + i);
-    s += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  float4 v[kNormMaxPer];
+  uint2 gw[kNormMaxPer];
+#pragma unroll
+  for (int k = 0; k < kNormMaxPer; ++k) {
+    const int i = (tid + k * kNormThreads) * 4;
+    const bool ok = i < hidden;
+    v[k] = ok ? *reinterpret_cast<const float4*>(xr + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+    gw[k] = ok ? *reinterpret_cast<const uint2*>(g + i) : make_uint2(0u, 0u);
   }
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < kNormMaxPer; ++k) s += v[k].x * v[k].x + v[k].y * v[k].y + v[k].z * v[k].z + v[k].w * v[k].w;
   s = wave_sum(s);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+  if ((tid & 63) == 0) red[tid >> 6] = s;
   __syncthreads();
-  const float rinv = 1.0f / sqrtf(((red[0] + red[1]) + (red[2] + red[3])) / (float)hidden + eps);
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < kNormThreads / 64; ++w) tot += red[w];
+  const float rinv = 1.0f / sqrtf(tot / (float)hidden + eps);
   uint16_t* hi = out + (int64_t)(2 * row) * hidden;
   uint16_t* lo = hi + hidden;
-  for (int i = threadIdx.x * 4; i < hidden; i += 256 * 4) {
-    const float4 v = *reinterpret_cast<const float4*>(xr + i);
-    const uint2 gw = *reinterpret_cast<const uint2*>(g + i);
-    const float u[4] = {v.x * rinv * bf16_bits_to_f32(gw.x & 0xFFFFu), v.y * rinv * bf16_bits_to_f32(gw.x >> 16),
-                        v.z * rinv * bf16_bits_to_f32(gw.y & 0xFFFFu), v.w * rinv * bf16_bits_to_f32(gw.y >> 16)};
+#pragma unroll
+  for (int k = 0; k < kNormMaxPer; ++k) {
+    const int i = (tid + k * kNormThreads) * 4;
+    if (i >= hidden) break;
+    const float u[4] = {v[k].x * rinv * bf16_bits_to_f32(gw[k].x & 0xFFFFu),
+                        v[k].y * rinv * bf16_bits_to_f32(gw[k].x >> 16),
+                        v[k].z * rinv * bf16_bits_to_f32(gw[k].y & 0xFFFFu),
+                        v[k].w * rinv * bf16_bits_to_f32(gw[k].y >> 16)};
     uint16_t h[4], l[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const f16 hh = (f16)u[k];
-      h[k] = __builtin_bit_cast(uint16_t, hh);
-      l[k] = f32_to_f16_bits(u[k] - (float)hh);
+    for (int e = 0; e < 4; ++e) {
+      const f16 hh = (f16)u[e];
+      h[e] = __builtin_bit_cast(uint16_t, hh);
+      l[e] = f32_to_f16_bits(u[e] - (float)hh);
     }
     *reinterpret_cast<uint2*>(hi + i) = make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
     *reinterpret_cast<uint2*>(lo + i) = make_uint2(l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16));
@@ -42,7 +60,7 @@ __global__ __launch_bounds__(256) void norm_hilo_kernel(const float* __restrict_
 
 hipError_t launch_norm_hilo(const float* x, int n, int hidden, const uint16_t* g, float eps,
                             uint16_t* out, hipStream_t s) {
-  hipLaunchKernelGGL(norm_hilo_kernel, dim3(n), dim3(256), 0, s, x, hidden, g, eps, out);
+  hipLaunchKernelGGL(norm_hilo_kernel, dim3(n), dim3(kNormThreads), 0, s, x, hidden, g, eps, out);
   return hipGetLastError();
 }
 
