@@ -5,7 +5,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["api.hip", "gemm_q4.hip", "attention.hip", "misc.hip"]
+SOURCES = ["api.hip", "gemm_q4.hip", "attention.hip", "misc.hip", "split.hip"]
 LIB = os.path.join(HERE, "liblucev.so")
 
 # Packed-fp32 VALU forms are kept out of the generated code on purpose.

@@ -108,7 +108,7 @@ int check_device() {
 }
 
 struct Ws {
-  size_t counters, xa, xm, q32, k32, v32, opart, ml, partials, cand, total;
+  size_t counters, xa, xm, q32, k32, v32, opart, ml, partials, split, cand, total;
   int n_counters;
 };
 
@@ -124,7 +124,7 @@ void layer_gemms(const lucev_shape* s, int n, GemmPlan out[5]) {
 bool ws_layout(const lucev_shape* s, int nmax, int pmax, Ws* w) {
   if (check_shape(s) != LUCEV_OK || nmax < 1 || nmax > LUCEV_MAX_NODES || pmax < 0) return false;
   const int64_t H = s->hidden, F = s->ffn, Hq = s->n_q_heads, Hkv = s->n_kv_heads, d = s->head_dim;
-  size_t part_floats = 0, cand = 0;
+  size_t part_floats = 0, split_floats = 0, cand = 0;
   int counters = 0;
   for (int n = 1; n <= nmax; ++n) {
     GemmPlan g[5];
@@ -133,6 +133,8 @@ bool ws_layout(const lucev_shape* s, int nmax, int pmax, Ws* w) {
       const size_t pf = (size_t)g[i].blocks * 2 * g[i].tile_floats;
       if (pf > part_floats) part_floats = pf;
       if (g[i].panels > counters) counters = g[i].panels;
+      const size_t sf = (size_t)g[i].panels * g[i].c_max * g[i].tile_floats;
+      if (i < 4 && sf > split_floats) split_floats = sf;  // the layer GEMMs run split
     }
     if ((size_t)g[4].blocks * n > cand) cand = (size_t)g[4].blocks * n;
   }
@@ -156,6 +158,7 @@ bool ws_layout(const lucev_shape* s, int nmax, int pmax, Ws* w) {
   w->opart = take((size_t)chunks * Hkv * rows * d * 4);
   w->ml = take((size_t)chunks * Hkv * rows * 2 * sizeof(float));
   w->partials = take(part_floats * sizeof(float));
+  w->split = take(split_floats * sizeof(float));
   w->cand = take(cand * sizeof(f32x4));
   w->total = off;
   (void)pmax;
@@ -195,6 +198,16 @@ GemmParams gemm_params(const lucev_q4& w, const uint16_t* X, int n, void* ws, co
   p.units = pl.units;
   p.partials = at<float>(ws, L.partials);
   p.counters = at<uint32_t>(ws, L.counters);
+  p.c_max = pl.c_max;
+  return p;
+}
+
+// the same GEMM writing its per-block partial tiles into the split area
+GemmParams gemm_params_split(const lucev_q4& w, const uint16_t* X, int n, void* ws, const Ws& L,
+                             SplitOut* so) {
+  GemmParams p = gemm_params(w, X, n, ws, L);
+  p.partials = at<float>(ws, L.split);
+  *so = split_out(plan_gemm(w.n_out, w.k_in, n), p.partials);
   return p;
 }
 
@@ -375,11 +388,14 @@ int lucev_verify_layer(const lucev_shape* shape, const lucev_layer_w* w, const l
   float* v32 = at<float>(ws, L.v32);
   hipError_t e;
 
-  // attention half: RMSNorm -> QKV + RoPE -> tree attention -> Wo + residual
+  // attention half: RMSNorm -> QKV (split) -> RoPE -> tree attention -> Wo (split)
   if ((e = launch_norm_hilo(resid_io, n, (int)H, w->attn_norm, eps, xa, st)) != hipSuccess)
     return hip_fail(e, "attention norm launch");
+  SplitOut so;
   {
-    GemmParams p = gemm_params(w->wqkv, xa, n, ws, L);
+    GemmParams p = gemm_params_split(w->wqkv, xa, n, ws, L, &so);
+    if ((e = launch_gemm(EPI_PARTIAL, true, p, epi_blank(), st)) != hipSuccess)
+      return hip_fail(e, "qkv gemm launch");
     EpiArgs ea = epi_blank();
     ea.k_out = k_tree_out;
     ea.v_out = v_tree_out;
@@ -391,34 +407,32 @@ int lucev_verify_layer(const lucev_shape* shape, const lucev_layer_w* w, const l
     ea.head_dim = (int)d;
     for (int i = 0; i < n; ++i) ea.pos[i] = t.pos[i];
     for (int j = 0; j < d / 2; ++j) ea.inv_freq[j] = pow((double)shape->rope_base, -2.0 * j / (double)d);
-    if ((e = launch_gemm(EPI_QKV, true, p, ea, st)) != hipSuccess) return hip_fail(e, "qkv gemm launch");
+    if ((e = launch_qkv_finish(so, ea, n, st)) != hipSuccess) return hip_fail(e, "qkv finish launch");
   }
   if ((rc = run_attention(shape, t, kv, nullptr, k_tree_out, v_tree_out, q32, k32, v32, xa, 1, ws, L,
                           st)))
     return rc;
   {
-    GemmParams p = gemm_params(w->wo, xa, n, ws, L);
-    EpiArgs ea = epi_blank();
-    ea.resid = resid_io;
-    ea.ld_out = (int)H;
-    if ((e = launch_gemm(EPI_RESID, true, p, ea, st)) != hipSuccess) return hip_fail(e, "wo gemm launch");
+    GemmParams p = gemm_params_split(w->wo, xa, n, ws, L, &so);
+    if ((e = launch_gemm(EPI_PARTIAL, true, p, epi_blank(), st)) != hipSuccess)
+      return hip_fail(e, "wo gemm launch");
+    // residual += attention output projection, then the FFN RMSNorm
+    if ((e = launch_resid_finish(so, resid_io, (int)H, n, w->ffn_norm, eps, xa, st)) != hipSuccess)
+      return hip_fail(e, "wo finish launch");
   }
-  // FFN half: RMSNorm -> gate/up + SwiGLU -> down + residual
-  if ((e = launch_norm_hilo(resid_io, n, (int)H, w->ffn_norm, eps, xa, st)) != hipSuccess)
-    return hip_fail(e, "ffn norm launch");
+  // FFN half: gate/up (split) -> SwiGLU -> down (split) -> residual
   {
-    GemmParams p = gemm_params(w->wgu, xa, n, ws, L);
-    EpiArgs ea = epi_blank();
-    ea.out16 = xm;
-    ea.ld_out = (int)F;
-    if ((e = launch_gemm(EPI_SWIGLU, false, p, ea, st)) != hipSuccess) return hip_fail(e, "gate/up gemm launch");
+    GemmParams p = gemm_params_split(w->wgu, xa, n, ws, L, &so);
+    if ((e = launch_gemm(EPI_PARTIAL, false, p, epi_blank(), st)) != hipSuccess)
+      return hip_fail(e, "gate/up gemm launch");
+    if ((e = launch_swiglu_finish(so, xm, (int)F, n, st)) != hipSuccess) return hip_fail(e, "swiglu launch");
   }
   {
-    GemmParams p = gemm_params(w->wd, xm, n, ws, L);
-    EpiArgs ea = epi_blank();
-    ea.resid = resid_io;
-    ea.ld_out = (int)H;
-    if ((e = launch_gemm(EPI_RESID, false, p, ea, st)) != hipSuccess) return hip_fail(e, "down gemm launch");
+    GemmParams p = gemm_params_split(w->wd, xm, n, ws, L, &so);
+    if ((e = launch_gemm(EPI_PARTIAL, false, p, epi_blank(), st)) != hipSuccess)
+      return hip_fail(e, "down gemm launch");
+    if ((e = launch_resid_finish(so, resid_io, (int)H, n, nullptr, eps, nullptr, st)) != hipSuccess)
+      return hip_fail(e, "down finish launch");
   }
   return LUCEV_OK;
 }

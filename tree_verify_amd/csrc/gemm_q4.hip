@@ -207,19 +207,6 @@ struct WRegs {
 template <int UG>
 constexpr int gemm_xld() { return UG * 128 + 8; }  // staged activation row (fp16), padded
 
-// Unit u of the flat list [0, U) lives in block block_of_unit(u): blocks take
-// contiguous ranges of whole unit pairs, [2 floor(b P / B), 2 floor((b+1) P / B))
-// with P = ceil(U / 2) pairs, so every range starts on an even unit.
-__device__ __forceinline__ int64_t range_start(int b, int64_t U, int B) {
-  const int64_t P = (U + 1) / 2;
-  const int64_t s = 2 * ((int64_t)b * P / B);
-  return s < U ? s : U;
-}
-__device__ __forceinline__ int block_of_unit(int64_t u, int64_t U, int B) {
-  const int64_t P = (U + 1) / 2;
-  return (int)(((u / 2 + 1) * B - 1) / P);
-}
-
 template <int WAVES, int FT, int NTX, int UG, int EPI, bool EXACT>
 __global__ __launch_bounds__(WAVES * 64) void gemm_q4_kernel(GemmParams p, EpiArgs e) {
   constexpr int NTH = WAVES * 64;
@@ -363,6 +350,18 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_q4_kernel(GemmParams p, EpiAr
     const int64_t first = pnl * GU, last = pnl * GU + GU - 1;
     const int bf = block_of_unit(first, U, B);
     const int bl = block_of_unit(last, U, B);
+    if constexpr (EPI == EPI_PARTIAL) {
+      // this block's share of the panel, node-major; a later kernel sums
+      // the contributors and applies the epilogue (plain stores: that kernel
+      // starts after this one has finished)
+      float* dst = p.partials + ((int64_t)pnl * p.c_max + (b - bf)) * TILE;
+      for (int i = tid; i < TILE; i += NTH) {
+        const int n = i / TILE_F, fl = i - n * TILE_F;
+        dst[i] = tile[fl][n];
+      }
+      lds_barrier();  // the LDS tile is reused by the next panel
+      return;
+    }
     if (bf != bl) {
       constexpr int PER = (TILE + NTH - 1) / NTH;
       const int slot = (u_begin >= first) ? 0 : 1;
@@ -638,11 +637,33 @@ GemmPlan plan_gemm(int64_t n_out, int64_t k_in, int n_nodes) {
   const int64_t target = 256 * kGemmBlocksPerCU;
   g.blocks = (int)(pairs < target ? pairs : target);
   g.tile_floats = pt * 16 * g.ntx * 8;
+  const int gu = g.kgroups / g.ug;
+  g.c_max = 1;
+  for (int pnl = 0; pnl < g.panels; ++pnl) {
+    const int c = block_of_unit((int64_t)pnl * gu + gu - 1, g.units, g.blocks) -
+                  block_of_unit((int64_t)pnl * gu, g.units, g.blocks) + 1;
+    if (c > g.c_max) g.c_max = c;
+  }
   return g;
+}
+
+SplitOut split_out(const GemmPlan& g, const float* part) {
+  SplitOut so;
+  so.part = part;
+  so.units = g.units;
+  so.blocks = g.blocks;
+  so.gu = g.kgroups / g.ug;
+  so.c_max = g.c_max;
+  so.tile_f = kGemmWaves * g.ft * 16;
+  so.tile_n = g.ntx * 8;
+  so.panels = g.panels;
+  return so;
 }
 
 hipError_t launch_gemm(int epi, bool exact, const GemmParams& p, const EpiArgs& e, hipStream_t s) {
   switch (epi) {
+    case EPI_PARTIAL:
+      return exact ? launch_ntx<EPI_PARTIAL, true>(p, e, s) : launch_ntx<EPI_PARTIAL, false>(p, e, s);
     case EPI_QKV: return launch_ntx<EPI_QKV, true>(p, e, s);
     case EPI_SWIGLU: return launch_ntx<EPI_SWIGLU, false>(p, e, s);
     case EPI_LOGITS: return launch_ntx<EPI_LOGITS, true>(p, e, s);

@@ -6,7 +6,7 @@
 namespace lucev {
 
 enum { W_PLAIN = 0, W_QKV = 1, W_GU = 2 };  // same values as LUCEV_W_*
-enum { EPI_RESID = 0, EPI_SWIGLU = 1, EPI_QKV = 2, EPI_LOGITS = 3 };
+enum { EPI_RESID = 0, EPI_SWIGLU = 1, EPI_QKV = 2, EPI_LOGITS = 3, EPI_PARTIAL = 4 };
 
 // GEMM partition: blocks of kGemmWaves waves own panels of kGemmWaves *
 // kGemmFT 16-row tiles; the flat list of units (panel, one or two 128-column
@@ -28,6 +28,30 @@ constexpr int kGemmBlocksPerCU = LUCEV_GEMM_BPC;  // grid = 256 CUs x this (at m
 struct GemmPlan {
   int ft, ntx, ug, n_tiles, kgroups, panels, blocks, tile_floats;
   int64_t units;
+  int c_max;  // most blocks sharing one panel (partial-tile slots per panel)
+};
+
+// Blocks take contiguous ranges of whole unit pairs of the flat unit list
+// [0, U): block b starts at 2 floor(b P / B), P = ceil(U / 2) pairs.
+__host__ __device__ inline int64_t range_start(int b, int64_t U, int B) {
+  const int64_t P = (U + 1) / 2;
+  const int64_t s = 2 * ((int64_t)b * P / B);
+  return s < U ? s : U;
+}
+__host__ __device__ inline int block_of_unit(int64_t u, int64_t U, int B) {
+  const int64_t P = (U + 1) / 2;
+  return (int)(((u / 2 + 1) * B - 1) / P);
+}
+
+// Where a GEMM run with EPI_PARTIAL left its partial tiles: panel p's
+// contributors are blocks bf..bl (bf = block_of_unit(p * gu), bl =
+// block_of_unit(p * gu + gu - 1)); contributor c = b - bf wrote fp32
+// [tile_n][tile_f] at part + (p * c_max + c) * tile_n * tile_f.  Output
+// feature f of the GEMM is panel f / tile_f, column f % tile_f.
+struct SplitOut {
+  const float* part;
+  int64_t units;
+  int blocks, gu, c_max, tile_f, tile_n, panels;
 };
 
 struct GemmParams {
@@ -38,8 +62,10 @@ struct GemmParams {
   int64_t n_out, k_in;
   int n_tiles, kgroups, panels, blocks;
   int64_t units;
-  float* partials;          // [blocks][2][tile]: split-panel partial tiles
+  float* partials;          // [blocks][2][tile] split-panel tiles (last-arriver reduction), or
+                            // the EPI_PARTIAL slots (see SplitOut)
   uint32_t* counters;       // [panels], zero between calls
+  int c_max;                // EPI_PARTIAL: slots per panel
 };
 
 struct EpiArgs {
@@ -114,6 +140,20 @@ hipError_t launch_attention(const AttnPlan& plan, int head_dim, const AttnParams
                             const CombineParams& c, const TreeArgs& t, hipStream_t s);
 
 // ---------------------------------------------------------------- small kernels
+
+// ---------------------------------------------------------------- split-K consumers
+// Each sums a GEMM's EPI_PARTIAL tiles in contributor order and applies what
+// the GEMM epilogue would have.
+SplitOut split_out(const GemmPlan& g, const float* part);
+// QKV: RoPE (rotate-half pairs sit 8 rows apart in one tile) -> fp32 q/k/v
+// and bf16 tree K/V, as EPI_QKV
+hipError_t launch_qkv_finish(const SplitOut& so, const EpiArgs& e, int n, hipStream_t s);
+// gate/up: silu(gate) * up -> fp16 hi/lo rows [2n][ffn], as EPI_SWIGLU
+hipError_t launch_swiglu_finish(const SplitOut& so, uint16_t* m, int ffn, int n, hipStream_t s);
+// residual: resid[n][hidden] += y; with g set, then the RMSNorm of the new rows
+// into the GEMM operand (as norm_hilo)
+hipError_t launch_resid_finish(const SplitOut& so, float* resid, int hidden, int n, const uint16_t* g,
+                               float eps, uint16_t* out_hilo, hipStream_t s);
 
 // RMSNorm of each row into the GEMM operand: u = x / sqrt(mean(x^2) + eps) * g
 // as fp16 hi/lo rows [2n][hidden]

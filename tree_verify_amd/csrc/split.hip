@@ -1,0 +1,194 @@
+// Split-K consumers: the int4 GEMM (EPI_PARTIAL) leaves each block's share of
+// a panel as a partial tile; these kernels add the shares of every output in
+// contributor order (deterministic) and apply the epilogue the projection
+// needs.  Doing the reduction here, after the GEMM has finished, needs no
+// synchronisation between the GEMM's blocks.
+#include "internal.h"
+
+namespace lucev {
+
+// Sum of the contributors of output feature column fl (of panel pnl) for
+// node n: up to 16 contributors' loads are issued before any is added, then
+// they are added in contributor order.
+__device__ __forceinline__ float split_sum(const SplitOut& so, int pnl, int fl, int n) {
+  const int bf = block_of_unit((int64_t)pnl * so.gu, so.units, so.blocks);
+  const int bl = block_of_unit((int64_t)pnl * so.gu + so.gu - 1, so.units, so.blocks);
+  const int64_t tile = (int64_t)so.tile_n * so.tile_f;
+  const float* __restrict__ src = so.part + (int64_t)pnl * so.c_max * tile + (int64_t)n * so.tile_f + fl;
+  const int nc = bl - bf + 1;
+  float v[16];
+#pragma unroll
+  for (int c = 0; c < 16; ++c) v[c] = c < nc ? src[c * tile] : 0.f;
+  float y = 0.f;
+#pragma unroll
+  for (int c = 0; c < 16; ++c) y += v[c];
+  for (int c = 16; c < nc; ++c) y += src[c * tile];
+  return y;
+}
+
+// ------------------------------------------------------------ QKV + RoPE
+// One block per (panel, node), one thread per panel row (at most 256).  Packed rows of a
+// head tile 16i..16i+15 hold dims [8i, 8i+8) and [d/2 + 8i, d/2 + 8i + 8), so
+// a rotate-half RoPE pair is rows fl and fl ^ 8 of the same tile.
+__global__ __launch_bounds__(256) void qkv_finish_kernel(SplitOut so, EpiArgs e) {
+  __shared__ float s_y[256];
+  const int pnl = blockIdx.x, n = blockIdx.y;
+  const int fl = threadIdx.x;
+  const int hd = e.head_dim;
+  const int64_t n_out = (int64_t)(e.n_q_heads + 2 * e.n_kv_heads) * hd;
+  const int64_t prow = (int64_t)pnl * so.tile_f + fl;
+  const bool ok = prow < n_out;
+  s_y[fl] = ok ? split_sum(so, pnl, fl, n) : 0.f;
+  __syncthreads();
+  if (!ok) return;
+  const int head = (int)(prow / hd);
+  const int r = (int)(prow % hd);
+  const int ti = r / 16, loc = r % 16;
+  const int j = loc < 8 ? 8 * ti + loc : hd / 2 + 8 * ti + (loc - 8);
+  float val = s_y[fl];
+  if (head < e.n_q_heads + e.n_kv_heads) {
+    const float partner = s_y[fl ^ 8];
+    const int jj = j < hd / 2 ? j : j - hd / 2;
+    // angle in fp64, reduced to [-pi, pi] before the fp32 sin / cos
+    const double th = (double)e.pos[n] * e.inv_freq[jj];
+    const double two_pi = 6.283185307179586476925286766559;
+    const double rr = th - two_pi * rint(th / two_pi);
+    float cs, sn;
+    sincosf((float)rr, &sn, &cs);
+    val = j < hd / 2 ? val * cs - partner * sn : partner * sn + val * cs;
+  }
+  if (head < e.n_q_heads) {
+    const int64_t o = ((int64_t)n * e.n_q_heads + head) * hd + j;
+    e.q32[o] = val;
+    if (e.out16) e.out16[o] = f32_to_bf16_bits(val);
+  } else if (head < e.n_q_heads + e.n_kv_heads) {
+    const int64_t o = ((int64_t)n * e.n_kv_heads + (head - e.n_q_heads)) * hd + j;
+    e.k32[o] = val;
+    e.k_out[o] = f32_to_bf16_bits(val);
+  } else {
+    const int64_t o = ((int64_t)n * e.n_kv_heads + (head - e.n_q_heads - e.n_kv_heads)) * hd + j;
+    e.v32[o] = val;
+    e.v_out[o] = f32_to_bf16_bits(val);
+  }
+}
+
+hipError_t launch_qkv_finish(const SplitOut& so, const EpiArgs& e, int n, hipStream_t s) {
+  if (so.tile_f > 256 || so.tile_f % 32) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(qkv_finish_kernel, dim3(so.panels, n), dim3(so.tile_f), 0, s, so, e);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ SwiGLU
+// One block per (panel, group of nodes).  Packed tiles (2i, 2i+1) of a panel
+// are the gate and up rows [16i, 16i + 16) of the same FFN unit.
+constexpr int kSwiNodes = 4;  // nodes per block
+
+__global__ __launch_bounds__(256) void swiglu_finish_kernel(SplitOut so, uint16_t* __restrict__ m, int ffn, int n) {
+  __shared__ float s_y[kSwiNodes][256];
+  const int pnl = blockIdx.x, n0 = blockIdx.y * kSwiNodes;
+  const int fl = threadIdx.x;
+  const int64_t n_out = 2 * (int64_t)ffn;
+  const bool ok = (int64_t)pnl * so.tile_f + fl < n_out;
+#pragma unroll
+  for (int k = 0; k < kSwiNodes; ++k) s_y[k][fl] = (ok && n0 + k < n) ? split_sum(so, pnl, fl, n0 + k) : 0.f;
+  __syncthreads();
+  // thread fl < tile_f / 2 forms row fl of the panel's FFN units for every node
+  if (fl >= so.tile_f / 2) return;
+  const int a = fl / 16, r = fl % 16;
+  const int64_t row = ((int64_t)pnl * (so.tile_f / 32) + a) * 16 + r;
+  if (2 * row >= n_out) return;
+#pragma unroll
+  for (int k = 0; k < kSwiNodes; ++k) {
+    const int node = n0 + k;
+    if (node >= n) break;
+    const float gt = s_y[k][(2 * a) * 16 + r];
+    const float up = s_y[k][(2 * a + 1) * 16 + r];
+    const float mv = gt / (1.0f + expf(-gt)) * up;
+    const f16 hi = (f16)mv;
+    m[(int64_t)(2 * node) * ffn + row] = __builtin_bit_cast(uint16_t, hi);
+    m[(int64_t)(2 * node + 1) * ffn + row] = f32_to_f16_bits(mv - (float)hi);
+  }
+}
+
+hipError_t launch_swiglu_finish(const SplitOut& so, uint16_t* m, int ffn, int n, hipStream_t s) {
+  if (so.tile_f > 256 || so.tile_f % 32) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(swiglu_finish_kernel, dim3(so.panels, (n + kSwiNodes - 1) / kSwiNodes), dim3(so.tile_f), 0, s,
+                     so, m, ffn, n);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ residual
+// Without a gain: one block per (panel, node), x += y.
+__global__ __launch_bounds__(256) void resid_finish_kernel(SplitOut so, float* resid, int hidden) {
+  const int pnl = blockIdx.x, n = blockIdx.y;
+  const int fl = threadIdx.x;
+  const int64_t f = (int64_t)pnl * so.tile_f + fl;
+  if (f >= hidden) return;
+  const float y = split_sum(so, pnl, fl, n);
+  float* r = resid + (int64_t)n * hidden + f;
+  *r = *r + y;
+}
+
+// With a gain: one block per node row, x += y over the whole row, then the
+// RMSNorm of the new row into the GEMM operand (fp16 rows 2n hi, 2n+1 lo),
+// sums of squares in a fixed order.
+constexpr int kFinThreads = 1024;
+constexpr int kFinPer = 8;  // features per thread: rows up to 8192 wide
+
+__global__ __launch_bounds__(kFinThreads) void resid_norm_finish_kernel(SplitOut so, float* __restrict__ resid,
+                                                                        int hidden, const uint16_t* __restrict__ g,
+                                                                        float eps, uint16_t* __restrict__ out) {
+  __shared__ float red[kFinThreads / 64];
+  const int n = blockIdx.x;
+  const int tid = threadIdx.x;
+  float* xr = resid + (int64_t)n * hidden;
+  float xv[kFinPer], yv[kFinPer];
+#pragma unroll
+  for (int k = 0; k < kFinPer; ++k) {
+    const int f = tid + k * kFinThreads;
+    const bool ok = f < hidden;
+    xv[k] = ok ? xr[f] : 0.f;
+    yv[k] = ok ? split_sum(so, f / so.tile_f, f % so.tile_f, n) : 0.f;
+  }
+  float ssq = 0.f;
+#pragma unroll
+  for (int k = 0; k < kFinPer; ++k) {
+    const int f = tid + k * kFinThreads;
+    xv[k] += yv[k];
+    if (f < hidden) xr[f] = xv[k];
+    ssq += xv[k] * xv[k];
+  }
+  ssq = wave_sum(ssq);
+  if ((tid & 63) == 0) red[tid >> 6] = ssq;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < kFinThreads / 64; ++w) tot += red[w];
+  const float rinv = 1.0f / sqrtf(tot / (float)hidden + eps);
+  uint16_t* hi = out + (int64_t)(2 * n) * hidden;
+  uint16_t* lo = hi + hidden;
+#pragma unroll
+  for (int k = 0; k < kFinPer; ++k) {
+    const int f = tid + k * kFinThreads;
+    if (f >= hidden) break;
+    const float u = xv[k] * rinv * bf16_bits_to_f32(g[f]);
+    const f16 hh = (f16)u;
+    hi[f] = __builtin_bit_cast(uint16_t, hh);
+    lo[f] = f32_to_f16_bits(u - (float)hh);
+  }
+}
+
+hipError_t launch_resid_finish(const SplitOut& so, float* resid, int hidden, int n, const uint16_t* g,
+                               float eps, uint16_t* out_hilo, hipStream_t s) {
+  if (g) {
+    if (hidden > kFinThreads * kFinPer) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(resid_norm_finish_kernel, dim3(n), dim3(kFinThreads), 0, s, so, resid, hidden, g, eps,
+                       out_hilo);
+  } else {
+    if (so.tile_f > 256) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(resid_finish_kernel, dim3(so.panels, n), dim3(so.tile_f), 0, s, so, resid, hidden);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace lucev
