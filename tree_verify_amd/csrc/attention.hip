@@ -27,24 +27,8 @@ namespace lucev {
 
 constexpr int KT = 64;  // tokens per LDS tile
 
-// Block barrier that orders LDS only: the next tiles' global loads stay in
-// flight across it.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // Waves per block for a query-tile count and tiles per wave.
 constexpr int attn_max_waves(int qpw) { return qpw == 1 ? 12 : 8; }
-
-// wait until at most n of this wave's vector-memory operations are in
-// flight (vmcnt only; LDS and export counters left alone)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
 
 // One block per (prefix chunk, KV head), one wave per QPW query tiles (waves
 // past the last query tile only load).  K and V^T tiles of 64 tokens go

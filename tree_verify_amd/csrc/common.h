@@ -59,6 +59,32 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Block barrier that orders LDS only: global loads in flight (prefetches)
+// stay in flight across it, unlike __syncthreads().
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Block barrier after direct-to-LDS loads, which the caller has waited for
+// with wait_vmcnt: no release fence (one would make the compiler wait for
+// every outstanding direct-to-LDS load, including later prefetches); the
+// acquire fence keeps the LDS reads that follow below the barrier.
+__device__ __forceinline__ void dma_barrier() {
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// wait until at most N of this wave's vector-memory operations are in
+// flight (vmcnt only; LDS and export counters left alone).  Direct-to-LDS
+// loads count here and are not waited for by the compiler.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 // 16-byte global load / store helpers.
 __device__ __forceinline__ u32x4 ld16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);

@@ -138,38 +138,12 @@ __device__ __forceinline__ f16x8 dequant8(uint32_t w, f16x2 dd) {
   return f16x8{a[0], a[1], b[0], b[1], cc[0], cc[1], d[0], d[1]};
 }
 
-// The same product split exactly: hi = fp16(d * (q - 8)) and lo = d * (q - 8)
-// - hi.  d has 11 significant bits and q - 8 at most 3, so the residual has at
-// most 3 bits, is a multiple of ulp(d) >= 2^-19 and fits fp16; the fused
-// multiply-add forms it without rounding.
-__device__ __forceinline__ void dequant8_split(uint32_t w, f16x2 dd, f16x8& hi, f16x8& lo) {
-  const f16x8 c = codes8(w);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const f16x2 ci = f16x2{c[2 * i], c[2 * i + 1]};
-    const f16x2 h = ci * dd;
-    const f16x2 l = __builtin_elementwise_fma(ci, dd, -h);
-    hi[2 * i] = h[0];
-    hi[2 * i + 1] = h[1];
-    lo[2 * i] = l[0];
-    lo[2 * i + 1] = l[1];
-  }
-}
-
-// the block-j scale of this lane's row, splatted to both fp16 halves
+// the block-j scale of this lane's row, splatted to both fp16 halves (a
+// shuffle of the scale word, which the packed multiply takes as its operand
+// select rather than as separate instructions)
 __device__ __forceinline__ f16x2 scale_pair(u32x2 s, int j) {
-  const uint32_t word = (j < 2) ? s[0] : s[1];
-  const uint32_t h = (j & 1) ? (word >> 16) : (word & 0xFFFFu);
-  return __builtin_bit_cast(f16x2, h | (h << 16));
-}
-
-__device__ __forceinline__ void rope_pair_angle(int pos, int jj, const double* inv_freq, float& cs,
-                                                float& sn) {
-  // angle in fp64, reduced to [-pi, pi] before the fp32 sin / cos
-  const double th = (double)pos * inv_freq[jj];
-  const double two_pi = 6.283185307179586476925286766559;
-  const double r = th - two_pi * rint(th / two_pi);
-  sincosf((float)r, &sn, &cs);
+  const f16x2 w = __builtin_bit_cast(f16x2, (j < 2) ? s[0] : s[1]);
+  return (j & 1) ? __builtin_shufflevector(w, w, 1, 1) : __builtin_shufflevector(w, w, 0, 0);
 }
 
 __device__ __forceinline__ void merge_top2(float& v1, int& i1, float& v2, float b1, int bi, float b2) {
@@ -190,13 +164,6 @@ __device__ __forceinline__ void st_coherent(float* p, float v) {
 }
 
 
-// Block barrier that orders LDS only: outstanding global loads (the weight
-// prefetch) stay in flight across it, unlike __syncthreads().
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 template <int UG, int FT>
 struct WRegs {
@@ -204,21 +171,34 @@ struct WRegs {
   u32x2 s[UG][FT];  // the row's 4 block scales
 };
 
-template <int UG>
-constexpr int gemm_xld() { return UG * 128 + 8; }  // staged activation row (fp16), padded
+// 16-byte buffer load straight into LDS: this lane's bytes land at
+// lds + 16 * lane.  (A function of its own: called from a lambda inside the
+// kernel template, the builtin keeps the host pass from emitting the
+// kernel's launch stub.)
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rsrc, uint8_t* lds, uint32_t voff,
+                                                  uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
 
 template <int WAVES, int FT, int NTX, int UG, int EPI, bool EXACT>
-__global__ __launch_bounds__(WAVES * 64) void gemm_q4_kernel(GemmParams p, EpiArgs e) {
+__global__ __launch_bounds__(WAVES * 64, 2) void gemm_q4_kernel(GemmParams p, EpiArgs e) {
   constexpr int NTH = WAVES * 64;
   constexpr int PT = WAVES * FT;   // tiles per panel
   constexpr int TILE_F = PT * 16;
   constexpr int XR = NTX * 16;     // staged hi/lo rows
-  constexpr int XLD = gemm_xld<UG>();
-  constexpr int XCPR = UG * 16;    // 16-byte chunks per staged row
-  constexpr int XCH = (XR * XCPR + NTH - 1) / NTH;  // staging chunks per thread
+  constexpr int RB = UG * 256;     // bytes of a staged row (UG * 128 fp16)
+  constexpr int XBUF = XR * RB;    // bytes of one staged slice
+  constexpr int XI = XBUF / 1024;  // 1 KB direct-to-LDS loads per slice
+  constexpr int XIW = (XI + WAVES - 1) / WAVES;  // of them per wave
   constexpr int TILE_N = NTX * 8;  // nodes
   constexpr int TILE = TILE_F * TILE_N;
-  __shared__ __attribute__((aligned(16))) uint16_t sx[2 * XR * XLD];
+  static_assert(XBUF % 1024 == 0, "a staged slice is whole 1 KB loads");
+  // three slice buffers as separate arrays: the compiler can then tell a
+  // direct-to-LDS load into one from operand reads of another, and does not
+  // wait for it
+  __shared__ __attribute__((aligned(1024))) uint8_t sx0[XBUF];
+  __shared__ __attribute__((aligned(1024))) uint8_t sx1[XBUF];
+  __shared__ __attribute__((aligned(1024))) uint8_t sx2[XBUF];
   __shared__ float tile[TILE_F][TILE_N + 1];
   __shared__ float best1[TILE_N], best2[TILE_N];
   __shared__ int besti[TILE_N];
@@ -256,40 +236,59 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_q4_kernel(GemmParams p, EpiAr
       ++k.pnl;
     }
   };
+  // Load addresses: a wave-uniform base (scalar registers, advanced per
+  // unit with scalar arithmetic) plus a per-lane offset fixed for the whole
+  // kernel, so the loads cost no vector address arithmetic.
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t w_off = (uint32_t)lane * 16u;  // bytes into a 1 KB tile-group
+  const uint32_t s_off = (uint32_t)lr * 8u;     // bytes into its 128-byte scale group
   // the weights are read once: non-temporal loads keep them from evicting
   // the activation rows, which every block re-reads, from L2
+  auto wload_one = [&](Cur k, WRegs<UG, FT>& r, int g, int ft) {
+    // ragged last panel: re-read a valid tile (a wave-uniform clamp)
+    const int t = min(k.pnl * PT + wave_s * FT + ft, p.n_tiles - 1);
+    const int64_t tg = (int64_t)t * G + k.c * UG + g;
+    const uint8_t* wb = p.wq + tg * 1024;
+    const uint8_t* sb = reinterpret_cast<const uint8_t*>(p.wsc) + tg * 128;
+    r.w[g][ft] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wb + w_off));
+    r.s[g][ft] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(sb + s_off));
+  };
   auto wload = [&](Cur k, WRegs<UG, FT>& r) {
 #pragma unroll
     for (int g = 0; g < UG; ++g)
 #pragma unroll
-      for (int ft = 0; ft < FT; ++ft) {
-        int t = k.pnl * PT + wave * FT + ft;
-        t = t < p.n_tiles ? t : p.n_tiles - 1;  // ragged last panel: re-read a valid tile
-        const int64_t tg = (int64_t)t * G + k.c * UG + g;
-        r.w[g][ft] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.wq + tg * 1024 + lane * 16));
-        r.s[g][ft] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p.wsc + tg * 64 + lr * 4));
-      }
+      for (int ft = 0; ft < FT; ++ft) wload_one(k, r, g, ft);
   };
-  // activation slice of a unit: XR rows x UG * 128 columns, in 16-byte chunks
-  // (every lane loads from a valid row and zeroes what lies past the 2n rows,
-  // so the load count does not depend on the lane)
-  auto xload = [&](Cur k, u32x4 (&xr)[XCH]) {
-    const int col0 = k.c * UG * 128;
+  // Activation slice of a unit: XR rows x UG * 128 columns, loaded straight
+  // into LDS (16 bytes a lane, 1 KB a wave instruction, no registers).  A
+  // load fills RB-byte rows in lane order; the lane at 16-byte position p of
+  // row r fetches chunk p ^ (r % 16) of that row, so chunk c of row r sits at
+  // position c ^ (r % 16) and the MFMA operand reads (16 rows, one chunk)
+  // fall in 16 different bank groups.  Rows past the 2n operand rows re-read
+  // row 0: they only feed accumulator rows of padding nodes, which no
+  // epilogue or consumer reads.  A wave's loads past the slice's last repeat
+  // it (same bytes to the same place).
+  uint32_t x_off[XIW];  // bytes from the slice's first column, per load of this wave
 #pragma unroll
-    for (int i = 0; i < XCH; ++i) {
-      const int id = tid + NTH * i;
-      const int row = id / XCPR, part = id % XCPR;
-      const bool ok = id < XR * XCPR && row < 2 * nn;
-      const u32x4 v = ld16(p.X + (ok ? row : 0) * K + col0 + part * 8);
-      xr[i] = ok ? v : u32x4{0u, 0u, 0u, 0u};
-    }
-  };
-  auto xstore = [&](int buf, const u32x4 (&xr)[XCH]) {
+  for (int q = 0; q < XIW; ++q) {
+    const int ins = min(wave + WAVES * q, XI - 1);
+    const int row = ins * (1024 / RB) + lane / (RB / 16);
+    const int pos = lane % (RB / 16);
+    const int src_row = row < 2 * nn ? row : 0;
+    x_off[q] = (uint32_t)((src_row * K + (pos ^ (row & 15)) * 8) * 2);
+  }
+  // Buffer loads: the per-lane offset is a register fixed for the whole
+  // kernel (a per-unit address register would have to outlive the load, which
+  // reads it late) and the unit's column offset a scalar; the descriptor's
+  // range is the operand rows, so a stray offset reads zeros.
+  const __amdgpu_buffer_rsrc_t x_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.X, (short)0, (int)(2 * nn * K * 2), 0x00020000);
+  auto xload = [&](Cur k, uint8_t* dst) {
+    const uint32_t col_bytes = (uint32_t)(k.c * UG * 256);
 #pragma unroll
-    for (int i = 0; i < XCH; ++i) {
-      const int id = tid + NTH * i;
-      const int row = id / XCPR, part = id % XCPR;
-      if (id < XR * XCPR) *reinterpret_cast<u32x4*>(&sx[(buf * XR + row) * XLD + part * 8]) = xr[i];
+    for (int q = 0; q < XIW; ++q) {
+      const int ins = min(wave_s + WAVES * q, XI - 1);
+      buffer_load_lds16(x_rsrc, dst + ins * 1024, x_off[q], col_bytes);
     }
   };
 
@@ -299,26 +298,45 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_q4_kernel(GemmParams p, EpiAr
 #pragma unroll
     for (int nt = 0; nt < NTX; ++nt) acc[ft][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int buf, const WRegs<UG, FT>& r) {
-    const uint16_t* xs = sx + (buf * XR + lr) * XLD + lq * 8;
+  // this lane's A-operand chunk (row lr, chunk 4j + lq of a 128-column
+  // group) in a staged slice, per j
+  uint32_t a_off[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) a_off[j] = (uint32_t)(lr * RB + (((j * 4 + lq) ^ lr) * 16));
+  // The weight prefetch of unit pf (into slot rf) is spread over the MFMA
+  // iterations, one tile-group per iteration, so the block's waves do not all
+  // queue their loads at the memory pipeline at the same moment.  The
+  // scheduling fence keeps each load at its site while the arithmetic moves
+  // freely around it.
+  constexpr int kLoads = UG * FT;
+  auto prefetch = [&](int q, Cur pf, WRegs<UG, FT>& rf) {
+    if (q < kLoads) wload_one(pf, rf, q / FT, q % FT);
+  };
+  auto compute = [&](const uint8_t* xs, const WRegs<UG, FT>& r, Cur pf, WRegs<UG, FT>& rf) {
 #pragma unroll
     for (int g = 0; g < UG; ++g)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
+        prefetch(g * 4 + j, pf, rf);
+        __builtin_amdgcn_sched_barrier(kGemmSchedMask);
         f16x8 xa[NTX];
 #pragma unroll
         for (int nt = 0; nt < NTX; ++nt)
-          xa[nt] = *reinterpret_cast<const f16x8*>(xs + nt * 16 * XLD + g * 128 + j * 32);
+          xa[nt] = *reinterpret_cast<const f16x8*>(xs + a_off[j] + nt * 16 * RB + g * 256);
 #pragma unroll
         for (int ft = 0; ft < FT; ++ft) {
           if constexpr (EXACT) {
-            // d * (q - 8) split exactly into fp16 hi + lo, both through the MFMA
-            f16x8 wh, wl;
-            dequant8_split(r.w[g][ft][j], scale_pair(r.s[g][ft], j), wh, wl);
+            // The exact codes q - 8 go through the MFMA, whose 32-deep sum
+            // covers exactly one scale block; the block scale then multiplies
+            // the fp32 sum.  Output column = lane % 16 = the row whose scale
+            // this lane holds, so one scale serves all four outputs.
+            const f16x8 cq = codes8(r.w[g][ft][j]);
+            const float dj = (float)scale_pair(r.s[g][ft], j)[0];
 #pragma unroll
             for (int nt = 0; nt < NTX; ++nt) {
-              acc[ft][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[nt], wh, acc[ft][nt], 0, 0, 0);
-              acc[ft][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[nt], wl, acc[ft][nt], 0, 0, 0);
+              const f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[nt], cq, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) acc[ft][nt][i] = __builtin_fmaf(t[i], dj, acc[ft][nt][i]);
             }
           } else {
             const f16x8 wb = dequant8(r.w[g][ft][j], scale_pair(r.s[g][ft], j));
@@ -328,6 +346,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_q4_kernel(GemmParams p, EpiAr
           }
         }
       }
+#pragma unroll
+    for (int q = UG * 4; q < kLoads; ++q) prefetch(q, pf, rf);
   };
 
   // finish panel pnl: hi/lo rows merged into the LDS tile [feature][node],
@@ -354,8 +374,13 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_q4_kernel(GemmParams p, EpiAr
       // this block's share of the panel, node-major; a later kernel sums
       // the contributors and applies the epilogue (plain stores: that kernel
       // starts after this one has finished)
+      // (a fixed store count per thread, so the loads still in flight keep
+      // exact wait counts across the flush)
+      static_assert(TILE % NTH == 0, "partial tile must split evenly over the threads");
       float* dst = p.partials + ((int64_t)pnl * p.c_max + (b - bf)) * TILE;
-      for (int i = tid; i < TILE; i += NTH) {
+#pragma unroll
+      for (int k = 0; k < TILE / NTH; ++k) {
+        const int i = tid + k * NTH;
         const int n = i / TILE_F, fl = i - n * TILE_F;
         dst[i] = tile[fl][n];
       }
@@ -416,74 +441,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_q4_kernel(GemmParams p, EpiAr
     }
 
     const int64_t t0 = pnl * PT;
-    // ---------------- epilogues on the finished tile [feature][node]
-    if constexpr (EPI == EPI_RESID) {
-      // x += y: all of this thread's residual loads are issued before any store
-      constexpr int EPT = (TILE_F * TILE_N + NTH - 1) / NTH;
-      float xv[EPT];
-#pragma unroll
-      for (int k = 0; k < EPT; ++k) {
-        const int i = tid + k * NTH;
-        const int n = i / TILE_F, fl = i - n * TILE_F;
-        const int64_t f = t0 * 16 + fl;
-        xv[k] = (n < nn && f < p.n_out) ? e.resid[(int64_t)n * e.ld_out + f] : 0.f;
-      }
-#pragma unroll
-      for (int k = 0; k < EPT; ++k) {
-        const int i = tid + k * NTH;
-        const int n = i / TILE_F, fl = i - n * TILE_F;
-        const int64_t f = t0 * 16 + fl;
-        if (n < nn && f < p.n_out) e.resid[(int64_t)n * e.ld_out + f] = xv[k] + tile[fl][n];
-      }
-    } else if constexpr (EPI == EPI_SWIGLU) {
-      // packed tiles (2i, 2i+1) = (gate, up) rows [16i, 16i + 16); m as hi/lo rows
-      for (int i = tid; i < (TILE_F / 2) * nn; i += NTH) {
-        const int n = i / (TILE_F / 2), rl = i - n * (TILE_F / 2);
-        const int a = rl / 16, r = rl % 16;
-        const int64_t row = (t0 / 2 + a) * 16 + r;
-        if (2 * row < p.n_out) {
-          const float gt = tile[(2 * a) * 16 + r][n];
-          const float up = tile[(2 * a + 1) * 16 + r][n];
-          const float m = gt / (1.0f + expf(-gt)) * up;
-          const f16 hi = (f16)m;
-          e.out16[(int64_t)(2 * n) * e.ld_out + row] = __builtin_bit_cast(uint16_t, hi);
-          e.out16[(int64_t)(2 * n + 1) * e.ld_out + row] = f32_to_f16_bits(m - (float)hi);
-        }
-      }
-    } else if constexpr (EPI == EPI_QKV) {
-      // rotate-half RoPE on q and k at pos = prefix_len + depth; v unrotated
-      const int hd = e.head_dim;
-      for (int i = tid; i < TILE_F * nn; i += NTH) {
-        const int n = i / TILE_F, fl = i - n * TILE_F;
-        const int64_t prow = t0 * 16 + fl;
-        if (prow >= p.n_out) continue;
-        const int head = (int)(prow / hd);
-        const int r = (int)(prow % hd);
-        const int ti = r / 16, loc = r % 16;
-        const int j = loc < 8 ? 8 * ti + loc : hd / 2 + 8 * ti + (loc - 8);
-        float val = tile[fl][n];
-        if (head < e.n_q_heads + e.n_kv_heads) {
-          const float partner = tile[fl ^ 8][n];
-          float cs, sn;
-          const int jj = j < hd / 2 ? j : j - hd / 2;
-          rope_pair_angle(e.pos[n], jj, e.inv_freq, cs, sn);
-          val = j < hd / 2 ? val * cs - partner * sn : partner * sn + val * cs;
-        }
-        if (head < e.n_q_heads) {
-          const int64_t o = ((int64_t)n * e.n_q_heads + head) * hd + j;
-          e.q32[o] = val;
-          if (e.out16) e.out16[o] = f32_to_bf16_bits(val);
-        } else if (head < e.n_q_heads + e.n_kv_heads) {
-          const int64_t o = ((int64_t)n * e.n_kv_heads + (head - e.n_q_heads)) * hd + j;
-          e.k32[o] = val;
-          e.k_out[o] = f32_to_bf16_bits(val);
-        } else {
-          const int64_t o = ((int64_t)n * e.n_kv_heads + (head - e.n_q_heads - e.n_kv_heads)) * hd + j;
-          e.v32[o] = val;
-          e.v_out[o] = f32_to_bf16_bits(val);
-        }
-      }
-    } else if constexpr (EPI == EPI_LOGITS) {
+    // ---------------- epilogue on the finished tile [feature][node]
+    if constexpr (EPI == EPI_LOGITS) {
       if (e.out16) {
         for (int i = tid; i < TILE_F * nn; i += NTH) {
           const int n = i / TILE_F, fl = i - n * TILE_F;
@@ -508,76 +467,69 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_q4_kernel(GemmParams p, EpiAr
     lds_barrier();  // the LDS tile is reused by the next panel
   };
 
-  // One unit u: load the activation slice of unit u + 2, MFMA unit u from
-  // LDS, refill this weight slot with unit u + 2, publish the slice of unit
-  // u + 1 (loaded one unit earlier) to the other LDS buffer.  Prefetches past
+  // One unit u: load the activation slice of unit u + 2 into the LDS buffer
+  // unit u - 1 used (which every wave has finished), MFMA unit u while
+  // loading the weights of unit u + 2 into the register slot unit u - 1 used,
+  // wait for this wave's part of the slice of unit u + 1 (loaded one unit
+  // earlier; only the loads issued after it may still be in flight), and
+  // finish the panel when u ends a segment.  Unit u uses slice buffer and
+  // weight slot u % 3 (counted from the block's first unit).  Prefetches past
   // the block's last unit re-read that unit, so every path issues the same
-  // loads and the loop body is straight-line: the compiler then keeps the
-  // prefetch in flight instead of draining it with a conservative wait.
-  int xb = 0;
+  // loads.
   const int64_t u_last = u_end - 1;
-  Cur pf;            // the unit being prefetched
-  int64_t pf_u = 0;
-  auto step = [&](WRegs<UG, FT>& r, u32x4 (&xr_store)[XCH], u32x4 (&xr_load)[XCH]) {
-    xload(pf, xr_load);
-    compute(xb, r);
-    wload(pf, r);
-    xstore(xb ^ 1, xr_store);
-    lds_barrier();
-    xb ^= 1;
-    if (pf_u < u_last) {
-      ++pf_u;
-      advance(pf);
-    }
-  };
-
   if (u_begin < u_end) {
-    // weights: r0 / r1 hold units u / u + 1 at the top of the loop; slices:
-    // x1 holds unit u + 1, x0 receives unit u + 2
-    WRegs<UG, FT> r0, r1;
-    u32x4 x0[XCH], x1[XCH];
-    {
-      Cur k = cur_of(u_begin);
-      wload(k, r0);
-      xload(k, x0);
-      pf_u = u_begin;
-      if (pf_u < u_last) {
-        ++pf_u;
-        advance(k);
-      }
-      wload(k, r1);
-      xload(k, x1);
-      if (pf_u < u_last) {
-        ++pf_u;
-        advance(k);
-      }
-      pf = k;
-      xstore(0, x0);
-    }
-    lds_barrier();
+    WRegs<UG, FT> r0, r1, r2;
+    Cur pf = cur_of(u_begin);  // next unit to prefetch
+    int64_t pf_u = u_begin;
+    // (selects, not branches: with a branch the compiler may reuse an earlier
+    // load's registers on the path that does not advance, which makes every
+    // later wait drain the queue)
+    auto next = [&](Cur& k, int64_t& ku) {
+      const int adv = ku < u_last ? 1 : 0;
+      ku += adv;
+      const int c = k.c + adv;
+      k.pnl += c == GU ? 1 : 0;
+      k.c = c == GU ? 0 : c;
+    };
+    // loads issued after a slice's, until the wait for it
+    constexpr int kAfterSlice = 2 * (2 * UG * FT) + XIW;
+    xload(pf, sx0);
+    __builtin_amdgcn_sched_barrier(0);
+    wload(pf, r0);
+    next(pf, pf_u);
+    __builtin_amdgcn_sched_barrier(0);
+    xload(pf, sx1);
+    __builtin_amdgcn_sched_barrier(0);
+    wload(pf, r1);
+    next(pf, pf_u);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<2 * UG * FT + XIW + 2 * UG * FT>();  // slice of the first unit has landed
+    dma_barrier();
     int64_t u = u_begin;
-    while (u < u_end) {
-      const int64_t pnl = u / GU;
-      const int64_t s_end = min((pnl + 1) * GU, u_end);
-      for (; u + 2 <= s_end; u += 2) {
-        step(r0, x1, x0);
-        step(r1, x0, x1);
-      }
-      if (u < s_end) {  // odd segment: one more unit, then the rings turn by one
-        step(r0, x1, x0);
-        const WRegs<UG, FT> t = r0;
-        r0 = r1;
-        r1 = t;
-#pragma unroll
-        for (int i = 0; i < XCH; ++i) {
-          const u32x4 tx = x0[i];
-          x0[i] = x1[i];
-          x1[i] = tx;
-        }
-        u += 1;
-      }
-      flush(pnl);
+    Cur cu = cur_of(u_begin);
+    auto step = [&](const uint8_t* xs, uint8_t* xfill, WRegs<UG, FT>& r, WRegs<UG, FT>& rf) {
+      xload(pf, xfill);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(xs, r, pf, rf);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<kAfterSlice>();  // this wave's part of the next unit's slice has landed
+      dma_barrier();
+      next(pf, pf_u);
+      if (cu.c == GU - 1 || u == u_last) flush(cu.pnl);
+      advance(cu);
+      ++u;
+    };
+    // a counted loop with the remainder after it: no exit from the middle of
+    // the loop body, whose paths would make the load waits conservative
+    const int64_t n_units = u_end - u_begin;
+    int64_t k = 0;
+    for (; k + 3 <= n_units; k += 3) {
+      step(sx0, sx2, r0, r2);
+      step(sx1, sx0, r1, r0);
+      step(sx2, sx1, r2, r1);
     }
+    if (k < n_units) step(sx0, sx2, r0, r2);
+    if (k + 1 < n_units) step(sx1, sx0, r1, r0);
   }
 
   if constexpr (EPI == EPI_LOGITS) {
@@ -588,8 +540,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_q4_kernel(GemmParams p, EpiAr
 template <int FT, int NTX, int EPI, bool EXACT>
 static hipError_t launch_t(const GemmParams& p, const EpiArgs& e, hipStream_t s) {
   bool two = false;
-  if constexpr (NTX <= 4) two = gemm_ug(p.kgroups, NTX) == 2;
-  if constexpr (NTX <= 4) {
+  if constexpr (NTX <= 3) two = gemm_ug(p.kgroups, NTX) == 2;
+  if constexpr (NTX <= 3) {
     if (two) {
       hipLaunchKernelGGL((gemm_q4_kernel<kGemmWaves, FT, NTX, 2, EPI, EXACT>), dim3(p.blocks),
                          dim3(kGemmWaves * 64), 0, s, p, e);
@@ -617,9 +569,9 @@ static hipError_t launch_ntx(const GemmParams& p, const EpiArgs& e, hipStream_t 
 
 int gemm_ntx(int n_nodes) { return (2 * n_nodes + 15) / 16; }
 
-// column groups per unit: two (256 inputs) when k_in allows it and the LDS
-// staging of two groups fits beside the tile
-int gemm_ug(int kgroups, int ntx) { return (kgroups % 2 == 0 && ntx <= 4) ? 2 : 1; }
+// column groups per unit: two (256 inputs) when k_in allows it and the
+// registers hold two groups' weights beside the accumulators of ntx tiles
+int gemm_ug(int kgroups, int ntx) { return (kgroups % 2 == 0 && ntx <= 3) ? 2 : 1; }
 
 GemmPlan plan_gemm(int64_t n_out, int64_t k_in, int n_nodes) {
   GemmPlan g;
@@ -631,11 +583,10 @@ GemmPlan plan_gemm(int64_t n_out, int64_t k_in, int n_nodes) {
   g.panels = (g.n_tiles + pt - 1) / pt;
   g.ug = gemm_ug(g.kgroups, g.ntx);
   g.units = (int64_t)g.panels * (g.kgroups / g.ug);
-  // kGemmBlocksPerCU resident blocks on each of the 256 CUs; blocks take
-  // whole pairs of units
-  const int64_t pairs = (g.units + 1) / 2;
+  // kGemmBlocksPerCU resident blocks on each of the 256 CUs, at least one
+  // unit each
   const int64_t target = 256 * kGemmBlocksPerCU;
-  g.blocks = (int)(pairs < target ? pairs : target);
+  g.blocks = (int)(g.units < target ? g.units : target);
   g.tile_floats = pt * 16 * g.ntx * 8;
   const int gu = g.kgroups / g.ug;
   g.c_max = 1;
@@ -664,11 +615,8 @@ hipError_t launch_gemm(int epi, bool exact, const GemmParams& p, const EpiArgs& 
   switch (epi) {
     case EPI_PARTIAL:
       return exact ? launch_ntx<EPI_PARTIAL, true>(p, e, s) : launch_ntx<EPI_PARTIAL, false>(p, e, s);
-    case EPI_QKV: return launch_ntx<EPI_QKV, true>(p, e, s);
-    case EPI_SWIGLU: return launch_ntx<EPI_SWIGLU, false>(p, e, s);
     case EPI_LOGITS: return launch_ntx<EPI_LOGITS, true>(p, e, s);
-    default:
-      return exact ? launch_ntx<EPI_RESID, true>(p, e, s) : launch_ntx<EPI_RESID, false>(p, e, s);
+    default: return hipErrorInvalidValue;
   }
 }
 

@@ -6,7 +6,9 @@
 namespace lucev {
 
 enum { W_PLAIN = 0, W_QKV = 1, W_GU = 2 };  // same values as LUCEV_W_*
-enum { EPI_RESID = 0, EPI_SWIGLU = 1, EPI_QKV = 2, EPI_LOGITS = 3, EPI_PARTIAL = 4 };
+// GEMM epilogues: per-block partial tiles summed by a later kernel, or the
+// lm_head's in-kernel split-K sum and per-node top-2
+enum { EPI_LOGITS = 3, EPI_PARTIAL = 4 };
 
 // GEMM partition: blocks of kGemmWaves waves own panels of kGemmWaves *
 // kGemmFT 16-row tiles; the flat list of units (panel, one or two 128-column
@@ -24,6 +26,12 @@ enum { EPI_RESID = 0, EPI_SWIGLU = 1, EPI_QKV = 2, EPI_LOGITS = 3, EPI_PARTIAL =
 constexpr int kGemmWaves = LUCEV_GEMM_WAVES;     // waves per block
 constexpr int kGemmFT = LUCEV_GEMM_FT;           // 16-row tiles per wave
 constexpr int kGemmBlocksPerCU = LUCEV_GEMM_BPC;  // grid = 256 CUs x this (at most)
+// What the GEMM's scheduling fences let the compiler move across them (the
+// sched_barrier mask): all but the vector-memory loads they pin in place.
+#ifndef LUCEV_GEMM_SCHED_MASK
+#define LUCEV_GEMM_SCHED_MASK 0x78F
+#endif
+constexpr int kGemmSchedMask = LUCEV_GEMM_SCHED_MASK;
 
 struct GemmPlan {
   int ft, ntx, ug, n_tiles, kgroups, panels, blocks, tile_floats;
@@ -31,16 +39,14 @@ struct GemmPlan {
   int c_max;  // most blocks sharing one panel (partial-tile slots per panel)
 };
 
-// Blocks take contiguous ranges of whole unit pairs of the flat unit list
-// [0, U): block b starts at 2 floor(b P / B), P = ceil(U / 2) pairs.
+// Blocks take contiguous ranges of the flat unit list [0, U): block b starts
+// at floor(b U / B), so range lengths differ by at most one unit (B <= U).
 __host__ __device__ inline int64_t range_start(int b, int64_t U, int B) {
-  const int64_t P = (U + 1) / 2;
-  const int64_t s = 2 * ((int64_t)b * P / B);
-  return s < U ? s : U;
+  return (int64_t)b * U / B;
 }
+// the block whose range holds unit u: the largest b with floor(b U / B) <= u
 __host__ __device__ inline int block_of_unit(int64_t u, int64_t U, int B) {
-  const int64_t P = (U + 1) / 2;
-  return (int)(((u / 2 + 1) * B - 1) / P);
+  return (int)(((u + 1) * B - 1) / U);
 }
 
 // Where a GEMM run with EPI_PARTIAL left its partial tiles: panel p's
@@ -68,14 +74,14 @@ struct GemmParams {
   int c_max;                // EPI_PARTIAL: slots per panel
 };
 
+// Epilogue arguments: the lm_head GEMM (EPI_LOGITS) and the QKV consumer
+// (RoPE, q/k/v outputs).
 struct EpiArgs {
-  float* resid;             // EPI_RESID: fp32 [n][ld_out], updated in place
-  uint16_t* out16;          // bf16 q (EPI_QKV, may be NULL) / bf16 logits (EPI_LOGITS, may be
-                            // NULL) / fp16 hi/lo rows [2n][ld_out] of SwiGLU m (EPI_SWIGLU)
+  uint16_t* out16;          // bf16 q (QKV consumer, may be NULL) / bf16 logits (EPI_LOGITS, may be NULL)
   int ld_out;
-  uint16_t* k_out;          // EPI_QKV: bf16 [n][Hkv][d]
+  uint16_t* k_out;          // QKV consumer: bf16 [n][Hkv][d]
   uint16_t* v_out;
-  float* q32;               // EPI_QKV: fp32 q [n][Hq][d], k and v [n][Hkv][d]
+  float* q32;               // QKV consumer: fp32 q [n][Hq][d], k and v [n][Hkv][d]
   float* k32;
   float* v32;
   int n_q_heads, n_kv_heads, head_dim;
@@ -89,8 +95,7 @@ int gemm_ug(int kgroups, int ntx);  // 128-column groups per unit
 // tiles per wave: fewer when many node tiles already fill the registers
 constexpr int gemm_ft_for(int ntx) { return ntx <= 4 ? kGemmFT : (kGemmFT > 1 ? kGemmFT / 2 : 1); }
 GemmPlan plan_gemm(int64_t n_out, int64_t k_in, int n_nodes);
-// exact: weights enter as an exact fp16 hi + lo pair (QKV, lm_head always;
-// for EPI_RESID as asked), else rounded once to fp16
+// exact: weights enter exactly (QKV, Wo, lm_head), else rounded once to fp16
 hipError_t launch_gemm(int epi, bool exact, const GemmParams& p, const EpiArgs& e, hipStream_t s);
 hipError_t launch_pack_q4(const uint8_t* q, const uint16_t* d, int64_t n_out, int64_t k_in,
                           int kind, int head_dim, void* dst, hipStream_t s);
@@ -146,9 +151,9 @@ hipError_t launch_attention(const AttnPlan& plan, int head_dim, const AttnParams
 // the GEMM epilogue would have.
 SplitOut split_out(const GemmPlan& g, const float* part);
 // QKV: RoPE (rotate-half pairs sit 8 rows apart in one tile) -> fp32 q/k/v
-// and bf16 tree K/V, as EPI_QKV
+// and bf16 tree K/V
 hipError_t launch_qkv_finish(const SplitOut& so, const EpiArgs& e, int n, hipStream_t s);
-// gate/up: silu(gate) * up -> fp16 hi/lo rows [2n][ffn], as EPI_SWIGLU
+// gate/up: silu(gate) * up -> fp16 hi/lo rows [2n][ffn]
 hipError_t launch_swiglu_finish(const SplitOut& so, uint16_t* m, int ffn, int n, hipStream_t s);
 // residual: resid[n][hidden] += y; with g set, then the RMSNorm of the new rows
 // into the GEMM operand (as norm_hilo)
