@@ -263,8 +263,8 @@ __global__ __launch_bounds__(attn_max_waves(QPW) * 64) void attn_partial_kernel(
     return m[i] - bias;
   };
 
-  // one 64-key tile: both halves' scores first, so the second half's MFMAs
-  // can overlap the first half's softmax
+  // one 64-key tile, half after half (the second half's scores are taken
+  // against the reference the first half left)
   auto compute = [&](int buf, int k0, auto masked) {
     const uint16_t* K = reinterpret_cast<const uint16_t*>(lds + buf * BUF);
     const uint16_t* V = reinterpret_cast<const uint16_t*>(lds + buf * BUF + KBYTES);
@@ -272,19 +272,13 @@ __global__ __launch_bounds__(attn_max_waves(QPW) * 64) void attn_partial_kernel(
     for (int i = 0; i < QPW; ++i) {
       const int qt = wave * QPW + i;
       if (qt >= RT) continue;
-      f32x4 s0[2], s1[2];
-      float b0, b1;
-      scores(K, i, 0, s0, b0);
-      scores(K, i, 1, s1, b1);
-      softmax_pv(V, i, 0, s0, b0, k0, masked);
-      // the first half may have moved the reference: rebase the second
-      const float shift = m[i] == -INFINITY ? 0.f : m[i] - b1;
-      if (__builtin_amdgcn_ballot_w64(shift != 0.f) != 0) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) s1[h] -= shift;
-        b1 += shift;
+      for (int ks = 0; ks < 2; ++ks) {
+        f32x4 sc[2];
+        float bias;
+        scores(K, i, ks, sc, bias);
+        softmax_pv(V, i, ks, sc, bias, k0, masked);
       }
-      softmax_pv(V, i, 1, s1, b1, k0, masked);
     }
   };
   auto compute_tile = [&](int buf, int t) {

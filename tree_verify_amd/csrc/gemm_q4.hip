@@ -493,6 +493,10 @@ __global__ __launch_bounds__(WAVES * 64, 2) void gemm_q4_kernel(GemmParams p, Ep
     };
     // loads issued after a slice's, until the wait for it
     constexpr int kAfterSlice = 2 * (2 * UG * FT) + XIW;
+    // The prologue asks for the first unit's weights alone: every block's
+    // requests reach memory at once, and the first unit's arrive sooner
+    // without the second's queued beside them; the second unit's weights
+    // are requested at the start of the first step.
     xload(pf, sx0);
     __builtin_amdgcn_sched_barrier(0);
     wload(pf, r0);
@@ -500,10 +504,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void gemm_q4_kernel(GemmParams p, Ep
     __builtin_amdgcn_sched_barrier(0);
     xload(pf, sx1);
     __builtin_amdgcn_sched_barrier(0);
-    wload(pf, r1);
-    next(pf, pf_u);
-    __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt<2 * UG * FT + XIW + 2 * UG * FT>();  // slice of the first unit has landed
+    wait_vmcnt<2 * UG * FT + XIW>();  // slice of the first unit has landed
     dma_barrier();
     int64_t u = u_begin;
     Cur cu = cur_of(u_begin);
@@ -519,17 +520,22 @@ __global__ __launch_bounds__(WAVES * 64, 2) void gemm_q4_kernel(GemmParams p, Ep
       advance(cu);
       ++u;
     };
+    // first unit: the second unit's weights, then the regular step
+    wload(pf, r1);
+    next(pf, pf_u);
+    __builtin_amdgcn_sched_barrier(0);
+    step(sx0, sx2, r0, r2);
     // a counted loop with the remainder after it: no exit from the middle of
     // the loop body, whose paths would make the load waits conservative
     const int64_t n_units = u_end - u_begin;
-    int64_t k = 0;
+    int64_t k = 1;
     for (; k + 3 <= n_units; k += 3) {
-      step(sx0, sx2, r0, r2);
       step(sx1, sx0, r1, r0);
       step(sx2, sx1, r2, r1);
+      step(sx0, sx2, r0, r2);
     }
-    if (k < n_units) step(sx0, sx2, r0, r2);
-    if (k + 1 < n_units) step(sx1, sx0, r1, r0);
+    if (k < n_units) step(sx1, sx0, r1, r0);
+    if (k + 1 < n_units) step(sx2, sx1, r2, r1);
   }
 
   if constexpr (EPI == EPI_LOGITS) {
