@@ -199,6 +199,7 @@ GemmParams gemm_params(const lucev_q4& w, const uint16_t* X, int n, void* ws, co
   p.partials = at<float>(ws, L.partials);
   p.counters = at<uint32_t>(ws, L.counters);
   p.c_max = pl.c_max;
+  p.ug = pl.ug;
   return p;
 }
 

@@ -199,6 +199,8 @@ __global__ __launch_bounds__(WAVES * 64, 2) void gemm_q4_kernel(GemmParams p, Ep
   __shared__ __attribute__((aligned(1024))) uint8_t sx0[XBUF];
   __shared__ __attribute__((aligned(1024))) uint8_t sx1[XBUF];
   __shared__ __attribute__((aligned(1024))) uint8_t sx2[XBUF];
+  // target of a wave's loads past a slice's last (every wave issues XIW)
+  __shared__ __attribute__((aligned(1024))) uint8_t sx_pad[XI % WAVES ? 1024 : 16];
   __shared__ float tile[TILE_F][TILE_N + 1];
   __shared__ float best1[TILE_N], best2[TILE_N];
   __shared__ int besti[TILE_N];
@@ -266,8 +268,8 @@ __global__ __launch_bounds__(WAVES * 64, 2) void gemm_q4_kernel(GemmParams p, Ep
   // position c ^ (r % 16) and the MFMA operand reads (16 rows, one chunk)
   // fall in 16 different bank groups.  Rows past the 2n operand rows re-read
   // row 0: they only feed accumulator rows of padding nodes, which no
-  // epilogue or consumer reads.  A wave's loads past the slice's last repeat
-  // it (same bytes to the same place).
+  // epilogue or consumer reads.  A wave's loads past the slice's last go to a
+  // pad area nothing reads.
   uint32_t x_off[XIW];  // bytes from the slice's first column, per load of this wave
 #pragma unroll
   for (int q = 0; q < XIW; ++q) {
@@ -287,8 +289,8 @@ __global__ __launch_bounds__(WAVES * 64, 2) void gemm_q4_kernel(GemmParams p, Ep
     const uint32_t col_bytes = (uint32_t)(k.c * UG * 256);
 #pragma unroll
     for (int q = 0; q < XIW; ++q) {
-      const int ins = min(wave_s + WAVES * q, XI - 1);
-      buffer_load_lds16(x_rsrc, dst + ins * 1024, x_off[q], col_bytes);
+      const int ins = wave_s + WAVES * q;
+      buffer_load_lds16(x_rsrc, ins < XI ? dst + ins * 1024 : sx_pad, x_off[q], col_bytes);
     }
   };
 
@@ -546,7 +548,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void gemm_q4_kernel(GemmParams p, Ep
 template <int FT, int NTX, int EPI, bool EXACT>
 static hipError_t launch_t(const GemmParams& p, const EpiArgs& e, hipStream_t s) {
   bool two = false;
-  if constexpr (NTX <= 3) two = gemm_ug(p.kgroups, NTX) == 2;
+  if constexpr (NTX <= 3) two = p.ug == 2;
   if constexpr (NTX <= 3) {
     if (two) {
       hipLaunchKernelGGL((gemm_q4_kernel<kGemmWaves, FT, NTX, 2, EPI, EXACT>), dim3(p.blocks),
@@ -577,6 +579,8 @@ int gemm_ntx(int n_nodes) { return (2 * n_nodes + 15) / 16; }
 
 // column groups per unit: two (256 inputs) when k_in allows it and the
 // registers hold two groups' weights beside the accumulators of ntx tiles
+// (one-group units measured slower inside the verify step, also for the
+// projections whose weights spread thinly over the blocks)
 int gemm_ug(int kgroups, int ntx) { return (kgroups % 2 == 0 && ntx <= 3) ? 2 : 1; }
 
 GemmPlan plan_gemm(int64_t n_out, int64_t k_in, int n_nodes) {

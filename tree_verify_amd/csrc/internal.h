@@ -72,6 +72,7 @@ struct GemmParams {
                             // the EPI_PARTIAL slots (see SplitOut)
   uint32_t* counters;       // [panels], zero between calls
   int c_max;                // EPI_PARTIAL: slots per panel
+  int ug;                   // 128-column groups per unit (the plan's)
 };
 
 // Epilogue arguments: the lm_head GEMM (EPI_LOGITS) and the QKV consumer
