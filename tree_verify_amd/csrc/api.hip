@@ -417,9 +417,13 @@ int lucev_verify_layer(const lucev_shape* shape, const lucev_layer_w* w, const l
     GemmParams p = gemm_params_split(w->wo, xa, n, ws, L, &so);
     if ((e = launch_gemm(EPI_PARTIAL, true, p, epi_blank(), st)) != hipSuccess)
       return hip_fail(e, "wo gemm launch");
-    // residual += attention output projection, then the FFN RMSNorm
-    if ((e = launch_resid_finish(so, resid_io, (int)H, n, w->ffn_norm, eps, xa, st)) != hipSuccess)
+    // residual += attention output projection, then the FFN RMSNorm (two
+    // kernels: a fused one with one block per row, or with a cross-block
+    // handoff of the row's sum of squares, measured slower)
+    if ((e = launch_resid_finish(so, resid_io, (int)H, n, st)) != hipSuccess)
       return hip_fail(e, "wo finish launch");
+    if ((e = launch_norm_hilo(resid_io, n, (int)H, w->ffn_norm, eps, xa, st)) != hipSuccess)
+      return hip_fail(e, "ffn norm launch");
   }
   // FFN half: gate/up (split) -> SwiGLU -> down (split) -> residual
   {
@@ -432,7 +436,7 @@ int lucev_verify_layer(const lucev_shape* shape, const lucev_layer_w* w, const l
     GemmParams p = gemm_params_split(w->wd, xm, n, ws, L, &so);
     if ((e = launch_gemm(EPI_PARTIAL, false, p, epi_blank(), st)) != hipSuccess)
       return hip_fail(e, "down gemm launch");
-    if ((e = launch_resid_finish(so, resid_io, (int)H, n, nullptr, eps, nullptr, st)) != hipSuccess)
+    if ((e = launch_resid_finish(so, resid_io, (int)H, n, st)) != hipSuccess)
       return hip_fail(e, "down finish launch");
   }
   return LUCEV_OK;

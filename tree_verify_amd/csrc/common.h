@@ -59,6 +59,15 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Device-coherent (agent-scope) fp32 load / store, for data one block
+// writes and another block of the same launch reads.
+__device__ __forceinline__ float ld_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Block barrier that orders LDS only: global loads in flight (prefetches)
 // stay in flight across it, unlike __syncthreads().
 __device__ __forceinline__ void lds_barrier() {

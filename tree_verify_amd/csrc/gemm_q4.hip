@@ -156,12 +156,6 @@ __device__ __forceinline__ void merge_top2(float& v1, int& i1, float& v2, float 
   }
 }
 
-__device__ __forceinline__ float ld_coherent(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_coherent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 
 

@@ -156,10 +156,8 @@ SplitOut split_out(const GemmPlan& g, const float* part);
 hipError_t launch_qkv_finish(const SplitOut& so, const EpiArgs& e, int n, hipStream_t s);
 // gate/up: silu(gate) * up -> fp16 hi/lo rows [2n][ffn]
 hipError_t launch_swiglu_finish(const SplitOut& so, uint16_t* m, int ffn, int n, hipStream_t s);
-// residual: resid[n][hidden] += y; with g set, then the RMSNorm of the new rows
-// into the GEMM operand (as norm_hilo)
-hipError_t launch_resid_finish(const SplitOut& so, float* resid, int hidden, int n, const uint16_t* g,
-                               float eps, uint16_t* out_hilo, hipStream_t s);
+// residual: resid[n][hidden] += y
+hipError_t launch_resid_finish(const SplitOut& so, float* resid, int hidden, int n, hipStream_t s);
 
 // RMSNorm of each row into the GEMM operand: u = x / sqrt(mean(x^2) + eps) * g
 // as fp16 hi/lo rows [2n][hidden]

@@ -8,22 +8,36 @@
 namespace lucev {
 
 // Sum of the contributors of output feature column fl (of panel pnl) for
-// node n: up to 16 contributors' loads are issued before any is added, then
-// they are added in contributor order.
-__device__ __forceinline__ float split_sum(const SplitOut& so, int pnl, int fl, int n) {
+// node n, added in contributor order.  The first 16 contributors' loads are
+// unconditional (past the last contributor they re-read it and the value is
+// dropped by a select), so a caller's loads for several columns can all be
+// in flight before the first sum.
+struct SplitLoads {
+  float v[16];
+  const float* src;
+  int nc;
+  int64_t tile;
+};
+__device__ __forceinline__ void split_issue(const SplitOut& so, int pnl, int fl, int n, SplitLoads& l) {
   const int bf = block_of_unit((int64_t)pnl * so.gu, so.units, so.blocks);
   const int bl = block_of_unit((int64_t)pnl * so.gu + so.gu - 1, so.units, so.blocks);
-  const int64_t tile = (int64_t)so.tile_n * so.tile_f;
-  const float* __restrict__ src = so.part + (int64_t)pnl * so.c_max * tile + (int64_t)n * so.tile_f + fl;
-  const int nc = bl - bf + 1;
-  float v[16];
+  l.tile = (int64_t)so.tile_n * so.tile_f;
+  l.src = so.part + (int64_t)pnl * so.c_max * l.tile + (int64_t)n * so.tile_f + fl;
+  l.nc = bl - bf + 1;
 #pragma unroll
-  for (int c = 0; c < 16; ++c) v[c] = c < nc ? src[c * tile] : 0.f;
+  for (int c = 0; c < 16; ++c) l.v[c] = l.src[min(c, l.nc - 1) * l.tile];
+}
+__device__ __forceinline__ float split_finish(const SplitLoads& l) {
   float y = 0.f;
 #pragma unroll
-  for (int c = 0; c < 16; ++c) y += v[c];
-  for (int c = 16; c < nc; ++c) y += src[c * tile];
+  for (int c = 0; c < 16; ++c) y += c < l.nc ? l.v[c] : 0.f;
+  for (int c = 16; c < l.nc; ++c) y += l.src[c * l.tile];
   return y;
+}
+__device__ __forceinline__ float split_sum(const SplitOut& so, int pnl, int fl, int n) {
+  SplitLoads l;
+  split_issue(so, pnl, fl, n, l);
+  return split_finish(l);
 }
 
 // ------------------------------------------------------------ QKV + RoPE
@@ -89,8 +103,11 @@ __global__ __launch_bounds__(256) void swiglu_finish_kernel(SplitOut so, uint16_
   const int fl = threadIdx.x;
   const int64_t n_out = 2 * (int64_t)ffn;
   const bool ok = (int64_t)pnl * so.tile_f + fl < n_out;
+  SplitLoads ld[kSwiNodes];
 #pragma unroll
-  for (int k = 0; k < kSwiNodes; ++k) s_y[k][fl] = (ok && n0 + k < n) ? split_sum(so, pnl, fl, n0 + k) : 0.f;
+  for (int k = 0; k < kSwiNodes; ++k) split_issue(so, pnl, fl, min(n0 + k, n - 1), ld[k]);
+#pragma unroll
+  for (int k = 0; k < kSwiNodes; ++k) s_y[k][fl] = (ok && n0 + k < n) ? split_finish(ld[k]) : 0.f;
   __syncthreads();
   // thread fl < tile_f / 2 forms row fl of the panel's FFN units for every node
   if (fl >= so.tile_f / 2) return;
@@ -118,76 +135,22 @@ hipError_t launch_swiglu_finish(const SplitOut& so, uint16_t* m, int ffn, int n,
 }
 
 // ------------------------------------------------------------ residual
-// Without a gain: one block per (panel, node), x += y.
+// One block per (panel, node), x += y.
 __global__ __launch_bounds__(256) void resid_finish_kernel(SplitOut so, float* resid, int hidden) {
   const int pnl = blockIdx.x, n = blockIdx.y;
   const int fl = threadIdx.x;
   const int64_t f = (int64_t)pnl * so.tile_f + fl;
   if (f >= hidden) return;
-  const float y = split_sum(so, pnl, fl, n);
   float* r = resid + (int64_t)n * hidden + f;
-  *r = *r + y;
+  SplitLoads ld;
+  split_issue(so, pnl, fl, n, ld);
+  const float x = *r;
+  *r = x + split_finish(ld);
 }
 
-// With a gain: one block per node row, x += y over the whole row, then the
-// RMSNorm of the new row into the GEMM operand (fp16 rows 2n hi, 2n+1 lo),
-// sums of squares in a fixed order.
-constexpr int kFinThreads = 1024;
-constexpr int kFinPer = 8;  // features per thread: rows up to 8192 wide
-
-__global__ __launch_bounds__(kFinThreads) void resid_norm_finish_kernel(SplitOut so, float* __restrict__ resid,
-                                                                        int hidden, const uint16_t* __restrict__ g,
-                                                                        float eps, uint16_t* __restrict__ out) {
-  __shared__ float red[kFinThreads / 64];
-  const int n = blockIdx.x;
-  const int tid = threadIdx.x;
-  float* xr = resid + (int64_t)n * hidden;
-  float xv[kFinPer], yv[kFinPer];
-#pragma unroll
-  for (int k = 0; k < kFinPer; ++k) {
-    const int f = tid + k * kFinThreads;
-    const bool ok = f < hidden;
-    xv[k] = ok ? xr[f] : 0.f;
-    yv[k] = ok ? split_sum(so, f / so.tile_f, f % so.tile_f, n) : 0.f;
-  }
-  float ssq = 0.f;
-#pragma unroll
-  for (int k = 0; k < kFinPer; ++k) {
-    const int f = tid + k * kFinThreads;
-    xv[k] += yv[k];
-    if (f < hidden) xr[f] = xv[k];
-    ssq += xv[k] * xv[k];
-  }
-  ssq = wave_sum(ssq);
-  if ((tid & 63) == 0) red[tid >> 6] = ssq;
-  __syncthreads();
-  float tot = 0.f;
-#pragma unroll
-  for (int w = 0; w < kFinThreads / 64; ++w) tot += red[w];
-  const float rinv = 1.0f / sqrtf(tot / (float)hidden + eps);
-  uint16_t* hi = out + (int64_t)(2 * n) * hidden;
-  uint16_t* lo = hi + hidden;
-#pragma unroll
-  for (int k = 0; k < kFinPer; ++k) {
-    const int f = tid + k * kFinThreads;
-    if (f >= hidden) break;
-    const float u = xv[k] * rinv * bf16_bits_to_f32(g[f]);
-    const f16 hh = (f16)u;
-    hi[f] = __builtin_bit_cast(uint16_t, hh);
-    lo[f] = f32_to_f16_bits(u - (float)hh);
-  }
-}
-
-hipError_t launch_resid_finish(const SplitOut& so, float* resid, int hidden, int n, const uint16_t* g,
-                               float eps, uint16_t* out_hilo, hipStream_t s) {
-  if (g) {
-    if (hidden > kFinThreads * kFinPer) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(resid_norm_finish_kernel, dim3(n), dim3(kFinThreads), 0, s, so, resid, hidden, g, eps,
-                       out_hilo);
-  } else {
-    if (so.tile_f > 256) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(resid_finish_kernel, dim3(so.panels, n), dim3(so.tile_f), 0, s, so, resid, hidden);
-  }
+hipError_t launch_resid_finish(const SplitOut& so, float* resid, int hidden, int n, hipStream_t s) {
+  if (so.tile_f > 256) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(resid_finish_kernel, dim3(so.panels, n), dim3(so.tile_f), 0, s, so, resid, hidden);
   return hipGetLastError();
 }
 
