@@ -156,8 +156,8 @@ int lucev_q4_pack_device(int kind, int32_t head_dim, const uint8_t* q, const uin
  * for an unsupported shape. */
 size_t lucev_workspace_bytes(const lucev_shape* shape, int32_t n_nodes, int32_t prefix_len);
 
-/* Zero-fill a workspace (required once before its first use; every
- * completed call leaves the workspace's counters zero again). */
+/* Zero-fill a workspace (once before its first use; no call depends on
+ * what an earlier call left in it). */
 int lucev_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------ the step */

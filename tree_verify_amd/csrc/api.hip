@@ -108,8 +108,7 @@ int check_device() {
 }
 
 struct Ws {
-  size_t counters, xa, xm, q32, k32, v32, opart, ml, partials, split, cand, total;
-  int n_counters;
+  size_t xa, xm, q32, k32, v32, opart, ml, split, cand, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -124,28 +123,22 @@ void layer_gemms(const lucev_shape* s, int n, GemmPlan out[5]) {
 bool ws_layout(const lucev_shape* s, int nmax, int pmax, Ws* w) {
   if (check_shape(s) != LUCEV_OK || nmax < 1 || nmax > LUCEV_MAX_NODES || pmax < 0) return false;
   const int64_t H = s->hidden, F = s->ffn, Hq = s->n_q_heads, Hkv = s->n_kv_heads, d = s->head_dim;
-  size_t part_floats = 0, split_floats = 0, cand = 0;
-  int counters = 0;
+  size_t split_floats = 0, cand = 0;
   for (int n = 1; n <= nmax; ++n) {
     GemmPlan g[5];
     layer_gemms(s, n, g);
     for (int i = 0; i < 5; ++i) {
-      const size_t pf = (size_t)g[i].blocks * 2 * g[i].tile_floats;
-      if (pf > part_floats) part_floats = pf;
-      if (g[i].panels > counters) counters = g[i].panels;
       const size_t sf = (size_t)g[i].panels * g[i].c_max * g[i].tile_floats;
-      if (i < 4 && sf > split_floats) split_floats = sf;  // the layer GEMMs run split
+      if (sf > split_floats) split_floats = sf;
     }
-    if ((size_t)g[4].blocks * n > cand) cand = (size_t)g[4].blocks * n;
+    if ((size_t)g[4].panels * n > cand) cand = (size_t)g[4].panels * n;
   }
-  w->n_counters = counters;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at_ = off;
     off = align256(off + bytes);
     return at_;
   };
-  w->counters = take((size_t)counters * sizeof(uint32_t));
   // GEMM operands as fp16 hi/lo rows: normed inputs and the attention output
   // (xa), the SwiGLU product (xm)
   w->xa = take((size_t)2 * nmax * (H > Hq * d ? H : Hq * d) * 2);
@@ -157,7 +150,6 @@ bool ws_layout(const lucev_shape* s, int nmax, int pmax, Ws* w) {
   const int chunks = attention_max_chunks((int)Hkv);
   w->opart = take((size_t)chunks * Hkv * rows * d * 4);
   w->ml = take((size_t)chunks * Hkv * rows * 2 * sizeof(float));
-  w->partials = take(part_floats * sizeof(float));
   w->split = take(split_floats * sizeof(float));
   w->cand = take(cand * sizeof(f32x4));
   w->total = off;
@@ -196,8 +188,7 @@ GemmParams gemm_params(const lucev_q4& w, const uint16_t* X, int n, void* ws, co
   p.panels = pl.panels;
   p.blocks = pl.blocks;
   p.units = pl.units;
-  p.partials = at<float>(ws, L.partials);
-  p.counters = at<uint32_t>(ws, L.counters);
+  p.partials = at<float>(ws, L.split);
   p.c_max = pl.c_max;
   p.ug = pl.ug;
   return p;
@@ -395,7 +386,7 @@ int lucev_verify_layer(const lucev_shape* shape, const lucev_layer_w* w, const l
   SplitOut so;
   {
     GemmParams p = gemm_params_split(w->wqkv, xa, n, ws, L, &so);
-    if ((e = launch_gemm(EPI_PARTIAL, true, p, epi_blank(), st)) != hipSuccess)
+    if ((e = launch_gemm(true, p, st)) != hipSuccess)
       return hip_fail(e, "qkv gemm launch");
     EpiArgs ea = epi_blank();
     ea.k_out = k_tree_out;
@@ -415,7 +406,7 @@ int lucev_verify_layer(const lucev_shape* shape, const lucev_layer_w* w, const l
     return rc;
   {
     GemmParams p = gemm_params_split(w->wo, xa, n, ws, L, &so);
-    if ((e = launch_gemm(EPI_PARTIAL, true, p, epi_blank(), st)) != hipSuccess)
+    if ((e = launch_gemm(true, p, st)) != hipSuccess)
       return hip_fail(e, "wo gemm launch");
     // residual += attention output projection, then the FFN RMSNorm (two
     // kernels: a fused one with one block per row, or with a cross-block
@@ -428,13 +419,13 @@ int lucev_verify_layer(const lucev_shape* shape, const lucev_layer_w* w, const l
   // FFN half: gate/up (split) -> SwiGLU -> down (split) -> residual
   {
     GemmParams p = gemm_params_split(w->wgu, xa, n, ws, L, &so);
-    if ((e = launch_gemm(EPI_PARTIAL, false, p, epi_blank(), st)) != hipSuccess)
+    if ((e = launch_gemm(false, p, st)) != hipSuccess)
       return hip_fail(e, "gate/up gemm launch");
     if ((e = launch_swiglu_finish(so, xm, (int)F, n, st)) != hipSuccess) return hip_fail(e, "swiglu launch");
   }
   {
     GemmParams p = gemm_params_split(w->wd, xm, n, ws, L, &so);
-    if ((e = launch_gemm(EPI_PARTIAL, false, p, epi_blank(), st)) != hipSuccess)
+    if ((e = launch_gemm(false, p, st)) != hipSuccess)
       return hip_fail(e, "down gemm launch");
     if ((e = launch_resid_finish(so, resid_io, (int)H, n, st)) != hipSuccess)
       return hip_fail(e, "down finish launch");
@@ -466,13 +457,13 @@ int lucev_accept_path(const lucev_shape* shape, const lucev_head_w* w, const luc
   uint16_t* xa = at<uint16_t>(ws, L.xa);
   if ((e = launch_norm_hilo(resid, n, H, w->final_norm, shape->rms_eps, xa, st)) != hipSuccess)
     return hip_fail(e, "final norm launch");
-  GemmParams p = gemm_params(w->lm_head, xa, n, ws, L);
-  EpiArgs ea = epi_blank();
-  ea.out16 = logits_out;
-  ea.ld_out = shape->vocab;
-  ea.cand = at<f32x4>(ws, L.cand);
-  if ((e = launch_gemm(EPI_LOGITS, true, p, ea, st)) != hipSuccess) return hip_fail(e, "lm_head gemm launch");
-  if ((e = launch_finalize(ea.cand, p.blocks, t, argmax_out, gap_out, path_out, path_len_out,
+  SplitOut so;
+  GemmParams p = gemm_params_split(w->lm_head, xa, n, ws, L, &so);
+  f32x4* cand = at<f32x4>(ws, L.cand);
+  if ((e = launch_gemm(true, p, st)) != hipSuccess) return hip_fail(e, "lm_head gemm launch");
+  if ((e = launch_logits_finish(so, logits_out, shape->vocab, cand, n, st)) != hipSuccess)
+    return hip_fail(e, "lm_head finish launch");
+  if ((e = launch_finalize(cand, so.panels, t, argmax_out, gap_out, path_out, path_len_out,
                            committed_out, st)) != hipSuccess)
     return hip_fail(e, "finalize launch");
   return LUCEV_OK;

@@ -334,8 +334,10 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(CombineParams c, Tree
   constexpr int PARTS = 256 / D;  // threads per output dim
   constexpr int DPL = D / 64;     // dims per lane in the ancestor dot products
   constexpr int PRE = 16;         // chunk outputs per thread loaded up front
+  constexpr int kAncRound = 4;    // ancestors per wave per round of key loads
   __shared__ float s_w[kMaxChunks];
   __shared__ float s_anc[kMaxNodes];
+  __shared__ int s_alist[kMaxNodes];
   __shared__ float s_red[4];
   __shared__ float s_acc[PARTS][D];
   const int tid = threadIdx.x;
@@ -363,7 +365,18 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(CombineParams c, Tree
     ov[r] = ch < c.n_chunks ? c.o_part[prow(ch) * D + j] : 0.f;
   }
 
-  // ancestor scores: wave w takes every 4th ancestor
+  // the node's ancestors (itself included), in increasing order
+  const int na = __popcll(anc);
+  if (tid == 0) {
+    uint64_t m = anc;
+    for (int k = 0; k < na; ++k) {
+      s_alist[k] = __builtin_ctzll(m);
+      m &= m - 1;
+    }
+  }
+  __syncthreads();
+  // ancestor scores: wave w takes ancestors w, w + 4, ..., kAncRound of them
+  // per round with every key load of the round in flight at once
   {
     float qv[DPL];
 #pragma unroll
@@ -371,23 +384,32 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(CombineParams c, Tree
       const int64_t o = ((int64_t)node * c.n_q_heads + h) * D + lane * DPL + i;
       qv[i] = c.q32 ? c.q32[o] : bf16_bits_to_f32(c.q[o]);
     }
-    int k = 0;
-    for (int a = 0; a < t.n; ++a) {
-      if (!((anc >> a) & 1ull)) continue;
-      if ((k & 3) == wave) {
-        float sdot = 0.f;
+    // (one loop per key precision, so no load sits behind a branch)
+    auto rounds = [&](auto kload) {
+      for (int k0 = wave; k0 < na; k0 += 4 * kAncRound) {
+        float kv[kAncRound][DPL];
 #pragma unroll
-        for (int i = 0; i < DPL; ++i) {
-          const int64_t o = ((int64_t)a * c.n_kv_heads + g) * D + lane * DPL + i;
-          sdot += qv[i] * (c.k32 ? c.k32[o] : bf16_bits_to_f32(c.k_tree[o]));
+        for (int r = 0; r < kAncRound; ++r) {
+          const int a = s_alist[min(k0 + 4 * r, na - 1)];
+#pragma unroll
+          for (int i = 0; i < DPL; ++i) kv[r][i] = kload(((int64_t)a * c.n_kv_heads + g) * D + lane * DPL + i);
         }
-        sdot = wave_sum(sdot) * c.scale_log2;
-        if (lane == 0) s_anc[k] = sdot;
+#pragma unroll
+        for (int r = 0; r < kAncRound; ++r) {
+          if (k0 + 4 * r >= na) break;
+          float sdot = 0.f;
+#pragma unroll
+          for (int i = 0; i < DPL; ++i) sdot += qv[i] * kv[r][i];
+          sdot = wave_sum(sdot) * c.scale_log2;
+          if (lane == 0) s_anc[k0 + 4 * r] = sdot;
+        }
       }
-      ++k;
-    }
+    };
+    if (c.k32)
+      rounds([&](int64_t o) { return c.k32[o]; });
+    else
+      rounds([&](int64_t o) { return bf16_bits_to_f32(c.k_tree[o]); });
   }
-  const int na = __popcll(anc);
   // running max over chunk maxima and ancestor scores
   float mx = cm;
   for (int ch = tid + 256; ch < c.n_chunks; ch += 256) mx = fmaxf(mx, c.ml_part[prow(ch) * 2]);
@@ -428,12 +450,27 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(CombineParams c, Tree
     float o = 0.f;
 #pragma unroll
     for (int q = 0; q < PARTS; ++q) o += s_acc[q][j];
-    int k = 0;
-    for (int a = 0; a < t.n; ++a) {
-      if (!((anc >> a) & 1ull)) continue;
-      const int64_t vo = ((int64_t)a * c.n_kv_heads + g) * D + j;
-      o += __builtin_amdgcn_exp2f(s_anc[k++] - M) * (c.v32 ? c.v32[vo] : bf16_bits_to_f32(c.v_tree[vo]));
-    }
+    // the ancestors' values, kAncRound * 4 loads in flight per round, added in
+    // ancestor order
+    auto rounds = [&](auto vload) {
+      for (int k0 = 0; k0 < na; k0 += 4 * kAncRound) {
+        float vv[4 * kAncRound];
+#pragma unroll
+        for (int r = 0; r < 4 * kAncRound; ++r)
+          vv[r] = vload(((int64_t)s_alist[min(k0 + r, na - 1)] * c.n_kv_heads + g) * D + j);
+        // a select, not a break: every load above is then used, and none is
+        // moved down behind a branch
+#pragma unroll
+        for (int r = 0; r < 4 * kAncRound; ++r) {
+          const float w = k0 + r < na ? __builtin_amdgcn_exp2f(s_anc[min(k0 + r, na - 1)] - M) : 0.f;
+          o += w * vv[r];
+        }
+      }
+    };
+    if (c.v32)
+      rounds([&](int64_t vo) { return c.v32[vo]; });
+    else
+      rounds([&](int64_t vo) { return bf16_bits_to_f32(c.v_tree[vo]); });
     o /= L;
     if (c.out_hilo) {
       // the Wo projection's operand: fp16 rows 2 node (hi) and 2 node + 1 (lo)

@@ -68,6 +68,19 @@ __device__ __forceinline__ void st_coherent(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Top-2 merge: best value, its index (lowest on exact ties) and the runner-up
+// (a tie at the top makes the runner-up equal to the best).  Associative and
+// commutative, so any fixed merge tree gives the same result.
+__device__ __forceinline__ void merge_top2(float& v1, int& i1, float& v2, float b1, int bi, float b2) {
+  if (b1 > v1 || (b1 == v1 && bi < i1)) {
+    v2 = fmaxf(v1, b2);
+    v1 = b1;
+    i1 = bi;
+  } else {
+    v2 = fmaxf(v2, b1);
+  }
+}
+
 // Block barrier that orders LDS only: global loads in flight (prefetches)
 // stay in flight across it, unlike __syncthreads().
 __device__ __forceinline__ void lds_barrier() {

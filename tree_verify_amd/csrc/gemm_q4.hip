@@ -146,19 +146,6 @@ __device__ __forceinline__ f16x2 scale_pair(u32x2 s, int j) {
   return (j & 1) ? __builtin_shufflevector(w, w, 1, 1) : __builtin_shufflevector(w, w, 0, 0);
 }
 
-__device__ __forceinline__ void merge_top2(float& v1, int& i1, float& v2, float b1, int bi, float b2) {
-  if (b1 > v1 || (b1 == v1 && bi < i1)) {
-    v2 = fmaxf(v1, b2);
-    v1 = b1;
-    i1 = bi;
-  } else {
-    v2 = fmaxf(v2, b1);
-  }
-}
-
-
-
-
 template <int UG, int FT>
 struct WRegs {
   u32x4 w[UG][FT];  // per column group and tile: 4 blocks x 8 codes of this lane's row
@@ -174,8 +161,8 @@ __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rsrc, u
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
 }
 
-template <int WAVES, int FT, int NTX, int UG, int EPI, bool EXACT>
-__global__ __launch_bounds__(WAVES * 64, 2) void gemm_q4_kernel(GemmParams p, EpiArgs e) {
+template <int WAVES, int FT, int NTX, int UG, bool EXACT>
+__global__ __launch_bounds__(WAVES * 64, 2) void gemm_q4_kernel(GemmParams p) {
   constexpr int NTH = WAVES * 64;
   constexpr int PT = WAVES * FT;   // tiles per panel
   constexpr int TILE_F = PT * 16;
@@ -196,9 +183,6 @@ __global__ __launch_bounds__(WAVES * 64, 2) void gemm_q4_kernel(GemmParams p, Ep
   // target of a wave's loads past a slice's last (every wave issues XIW)
   __shared__ __attribute__((aligned(1024))) uint8_t sx_pad[XI % WAVES ? 1024 : 16];
   __shared__ float tile[TILE_F][TILE_N + 1];
-  __shared__ float best1[TILE_N], best2[TILE_N];
-  __shared__ int besti[TILE_N];
-  __shared__ int s_last;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -213,13 +197,6 @@ __global__ __launch_bounds__(WAVES * 64, 2) void gemm_q4_kernel(GemmParams p, Ep
   const int64_t u_begin = range_start(b, U, B);
   const int64_t u_end = range_start(b + 1, U, B);
 
-  if constexpr (EPI == EPI_LOGITS) {
-    if (tid < TILE_N) {
-      best1[tid] = -INFINITY;
-      best2[tid] = -INFINITY;
-      besti[tid] = 0x7fffffff;
-    }
-  }
 
   // A unit as (panel, unit within the panel), advanced without divisions.
   struct Cur {
@@ -363,102 +340,18 @@ __global__ __launch_bounds__(WAVES * 64, 2) void gemm_q4_kernel(GemmParams p, Ep
       }
     lds_barrier();
 
-    const int64_t first = pnl * GU, last = pnl * GU + GU - 1;
-    const int bf = block_of_unit(first, U, B);
-    const int bl = block_of_unit(last, U, B);
-    if constexpr (EPI == EPI_PARTIAL) {
-      // this block's share of the panel, node-major; a later kernel sums
-      // the contributors and applies the epilogue (plain stores: that kernel
-      // starts after this one has finished)
-      // (a fixed store count per thread, so the loads still in flight keep
-      // exact wait counts across the flush)
-      static_assert(TILE % NTH == 0, "partial tile must split evenly over the threads");
-      float* dst = p.partials + ((int64_t)pnl * p.c_max + (b - bf)) * TILE;
+    // this block's share of the panel, node-major; a later kernel sums the
+    // contributors and applies the epilogue (plain stores: that kernel starts
+    // after this one has finished).  A fixed store count per thread keeps
+    // exact wait counts for the loads still in flight across the flush.
+    const int bf = block_of_unit(pnl * GU, U, B);
+    static_assert(TILE % NTH == 0, "partial tile must split evenly over the threads");
+    float* dst = p.partials + ((int64_t)pnl * p.c_max + (b - bf)) * TILE;
 #pragma unroll
-      for (int k = 0; k < TILE / NTH; ++k) {
-        const int i = tid + k * NTH;
-        const int n = i / TILE_F, fl = i - n * TILE_F;
-        dst[i] = tile[fl][n];
-      }
-      lds_barrier();  // the LDS tile is reused by the next panel
-      return;
-    }
-    if (bf != bl) {
-      constexpr int PER = (TILE + NTH - 1) / NTH;
-      const int slot = (u_begin >= first) ? 0 : 1;
-      float* part = p.partials + ((int64_t)b * 2 + slot) * TILE;
-#pragma unroll
-      for (int k = 0; k < PER; ++k) {
-        const int i = tid + k * NTH;
-        if (i < TILE) st_coherent(part + i, tile[i / TILE_N][i % TILE_N]);
-      }
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // every wave's stores done
-      lds_barrier();
-      if (tid == 0) {
-        // the partials were written through (agent-scope stores) and every
-        // wave waited for them before the barrier, so a relaxed count suffices
-        const unsigned prev = __hip_atomic_fetch_add(&p.counters[pnl], 1u, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-        s_last = prev == (unsigned)(bl - bf);
-      }
-      lds_barrier();
-      if (!s_last) return;
-      // sum the contributors in block order, CB at a time with all their
-      // loads in flight together
-      constexpr int CB = PER <= 12 ? 6 : 3;
-      float sum[PER];
-#pragma unroll
-      for (int k = 0; k < PER; ++k) sum[k] = 0.f;
-      for (int b0 = bf; b0 <= bl; b0 += CB) {
-        float v[CB][PER];
-#pragma unroll
-        for (int uu = 0; uu < CB; ++uu) {
-          const int bb = min(b0 + uu, bl);  // past the last contributor: re-read it, unused
-          const int sl = (range_start(bb, U, B) >= first) ? 0 : 1;
-          const float* src = p.partials + ((int64_t)bb * 2 + sl) * TILE + tid;
-#pragma unroll
-          for (int k = 0; k < PER; ++k)
-            v[uu][k] = (tid + k * NTH < TILE) ? ld_coherent(src + k * NTH) : 0.f;
-        }
-#pragma unroll
-        for (int uu = 0; uu < CB; ++uu)
-          if (b0 + uu <= bl)
-#pragma unroll
-            for (int k = 0; k < PER; ++k) sum[k] += v[uu][k];
-      }
-#pragma unroll
-      for (int k = 0; k < PER; ++k) {
-        const int i = tid + k * NTH;
-        if (i < TILE) tile[i / TILE_N][i % TILE_N] = sum[k];
-      }
-      if (tid == 0)
-        __hip_atomic_store(&p.counters[pnl], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      lds_barrier();
-    }
-
-    const int64_t t0 = pnl * PT;
-    // ---------------- epilogue on the finished tile [feature][node]
-    if constexpr (EPI == EPI_LOGITS) {
-      if (e.out16) {
-        for (int i = tid; i < TILE_F * nn; i += NTH) {
-          const int n = i / TILE_F, fl = i - n * TILE_F;
-          const int64_t f = t0 * 16 + fl;
-          if (f < p.n_out) e.out16[(int64_t)n * e.ld_out + f] = f32_to_bf16_bits(tile[fl][n]);
-        }
-      }
-      // this panel's best / runner-up per node, merged into the block's running pair
-      if (tid < nn) {
-        float v1 = best1[tid], v2 = best2[tid];
-        int i1 = besti[tid];
-        for (int fl = 0; fl < TILE_F; ++fl) {
-          const int64_t f = t0 * 16 + fl;
-          if (f >= p.n_out) break;
-          merge_top2(v1, i1, v2, tile[fl][tid], (int)f, -INFINITY);
-        }
-        best1[tid] = v1;
-        best2[tid] = v2;
-        besti[tid] = i1;
-      }
+    for (int k = 0; k < TILE / NTH; ++k) {
+      const int i = tid + k * NTH;
+      const int n = i / TILE_F, fl = i - n * TILE_F;
+      dst[i] = tile[fl][n];
     }
     lds_barrier();  // the LDS tile is reused by the next panel
   };
@@ -533,39 +426,34 @@ __global__ __launch_bounds__(WAVES * 64, 2) void gemm_q4_kernel(GemmParams p, Ep
     if (k < n_units) step(sx1, sx0, r1, r0);
     if (k + 1 < n_units) step(sx2, sx1, r2, r1);
   }
-
-  if constexpr (EPI == EPI_LOGITS) {
-    if (tid < nn) e.cand[(int64_t)b * nn + tid] = f32x4{best1[tid], __int_as_float(besti[tid]), best2[tid], 0.f};
-  }
 }
 
-template <int FT, int NTX, int EPI, bool EXACT>
-static hipError_t launch_t(const GemmParams& p, const EpiArgs& e, hipStream_t s) {
+template <int FT, int NTX, bool EXACT>
+static hipError_t launch_t(const GemmParams& p, hipStream_t s) {
   bool two = false;
   if constexpr (NTX <= 3) two = p.ug == 2;
   if constexpr (NTX <= 3) {
     if (two) {
-      hipLaunchKernelGGL((gemm_q4_kernel<kGemmWaves, FT, NTX, 2, EPI, EXACT>), dim3(p.blocks),
-                         dim3(kGemmWaves * 64), 0, s, p, e);
+      hipLaunchKernelGGL((gemm_q4_kernel<kGemmWaves, FT, NTX, 2, EXACT>), dim3(p.blocks), dim3(kGemmWaves * 64), 0, s,
+                         p);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((gemm_q4_kernel<kGemmWaves, FT, NTX, 1, EPI, EXACT>), dim3(p.blocks),
-                     dim3(kGemmWaves * 64), 0, s, p, e);
+  hipLaunchKernelGGL((gemm_q4_kernel<kGemmWaves, FT, NTX, 1, EXACT>), dim3(p.blocks), dim3(kGemmWaves * 64), 0, s, p);
   return hipGetLastError();
 }
 
-template <int EPI, bool EXACT>
-static hipError_t launch_ntx(const GemmParams& p, const EpiArgs& e, hipStream_t s) {
+template <bool EXACT>
+static hipError_t launch_ntx(const GemmParams& p, hipStream_t s) {
   switch (gemm_ntx(p.n_nodes)) {
-    case 1: return launch_t<gemm_ft_for(1), 1, EPI, EXACT>(p, e, s);
-    case 2: return launch_t<gemm_ft_for(2), 2, EPI, EXACT>(p, e, s);
-    case 3: return launch_t<gemm_ft_for(3), 3, EPI, EXACT>(p, e, s);
-    case 4: return launch_t<gemm_ft_for(4), 4, EPI, EXACT>(p, e, s);
-    case 5: return launch_t<gemm_ft_for(5), 5, EPI, EXACT>(p, e, s);
-    case 6: return launch_t<gemm_ft_for(6), 6, EPI, EXACT>(p, e, s);
-    case 7: return launch_t<gemm_ft_for(7), 7, EPI, EXACT>(p, e, s);
-    default: return launch_t<gemm_ft_for(8), 8, EPI, EXACT>(p, e, s);
+    case 1: return launch_t<gemm_ft_for(1), 1, EXACT>(p, s);
+    case 2: return launch_t<gemm_ft_for(2), 2, EXACT>(p, s);
+    case 3: return launch_t<gemm_ft_for(3), 3, EXACT>(p, s);
+    case 4: return launch_t<gemm_ft_for(4), 4, EXACT>(p, s);
+    case 5: return launch_t<gemm_ft_for(5), 5, EXACT>(p, s);
+    case 6: return launch_t<gemm_ft_for(6), 6, EXACT>(p, s);
+    case 7: return launch_t<gemm_ft_for(7), 7, EXACT>(p, s);
+    default: return launch_t<gemm_ft_for(8), 8, EXACT>(p, s);
   }
 }
 
@@ -615,13 +503,8 @@ SplitOut split_out(const GemmPlan& g, const float* part) {
   return so;
 }
 
-hipError_t launch_gemm(int epi, bool exact, const GemmParams& p, const EpiArgs& e, hipStream_t s) {
-  switch (epi) {
-    case EPI_PARTIAL:
-      return exact ? launch_ntx<EPI_PARTIAL, true>(p, e, s) : launch_ntx<EPI_PARTIAL, false>(p, e, s);
-    case EPI_LOGITS: return launch_ntx<EPI_LOGITS, true>(p, e, s);
-    default: return hipErrorInvalidValue;
-  }
+hipError_t launch_gemm(bool exact, const GemmParams& p, hipStream_t s) {
+  return exact ? launch_ntx<true>(p, s) : launch_ntx<false>(p, s);
 }
 
 }  // namespace lucev

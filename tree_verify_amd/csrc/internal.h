@@ -6,9 +6,6 @@
 namespace lucev {
 
 enum { W_PLAIN = 0, W_QKV = 1, W_GU = 2 };  // same values as LUCEV_W_*
-// GEMM epilogues: per-block partial tiles summed by a later kernel, or the
-// lm_head's in-kernel split-K sum and per-node top-2
-enum { EPI_LOGITS = 3, EPI_PARTIAL = 4 };
 
 // GEMM partition: blocks of kGemmWaves waves own panels of kGemmWaves *
 // kGemmFT 16-row tiles; the flat list of units (panel, one or two 128-column
@@ -49,7 +46,7 @@ __host__ __device__ inline int block_of_unit(int64_t u, int64_t U, int B) {
   return (int)(((u + 1) * B - 1) / U);
 }
 
-// Where a GEMM run with EPI_PARTIAL left its partial tiles: panel p's
+// Where a GEMM left its partial tiles: panel p's
 // contributors are blocks bf..bl (bf = block_of_unit(p * gu), bl =
 // block_of_unit(p * gu + gu - 1)); contributor c = b - bf wrote fp32
 // [tile_n][tile_f] at part + (p * c_max + c) * tile_n * tile_f.  Output
@@ -68,25 +65,20 @@ struct GemmParams {
   int64_t n_out, k_in;
   int n_tiles, kgroups, panels, blocks;
   int64_t units;
-  float* partials;          // [blocks][2][tile] split-panel tiles (last-arriver reduction), or
-                            // the EPI_PARTIAL slots (see SplitOut)
-  uint32_t* counters;       // [panels], zero between calls
-  int c_max;                // EPI_PARTIAL: slots per panel
+  float* partials;          // per-block partial tiles (see SplitOut)
+  int c_max;                // partial-tile slots per panel
   int ug;                   // 128-column groups per unit (the plan's)
 };
 
-// Epilogue arguments: the lm_head GEMM (EPI_LOGITS) and the QKV consumer
-// (RoPE, q/k/v outputs).
+// Arguments of the QKV consumer (RoPE, q/k/v outputs).
 struct EpiArgs {
-  uint16_t* out16;          // bf16 q (QKV consumer, may be NULL) / bf16 logits (EPI_LOGITS, may be NULL)
-  int ld_out;
+  uint16_t* out16;          // bf16 q, may be NULL
   uint16_t* k_out;          // QKV consumer: bf16 [n][Hkv][d]
   uint16_t* v_out;
   float* q32;               // QKV consumer: fp32 q [n][Hq][d], k and v [n][Hkv][d]
   float* k32;
   float* v32;
   int n_q_heads, n_kv_heads, head_dim;
-  f32x4* cand;              // EPI_LOGITS: per (block, node) {best, idx, second, 0}
   int32_t pos[kMaxNodes];
   double inv_freq[kMaxNodes];  // base^(-2j/d), j < d/2
 };
@@ -96,8 +88,10 @@ int gemm_ug(int kgroups, int ntx);  // 128-column groups per unit
 // tiles per wave: fewer when many node tiles already fill the registers
 constexpr int gemm_ft_for(int ntx) { return ntx <= 4 ? kGemmFT : (kGemmFT > 1 ? kGemmFT / 2 : 1); }
 GemmPlan plan_gemm(int64_t n_out, int64_t k_in, int n_nodes);
-// exact: weights enter exactly (QKV, Wo, lm_head), else rounded once to fp16
-hipError_t launch_gemm(int epi, bool exact, const GemmParams& p, const EpiArgs& e, hipStream_t s);
+// Every block writes its share of each panel it touches as a partial tile;
+// a consumer kernel sums them.  exact: weights enter exactly (QKV, Wo,
+// lm_head), else rounded once to fp16.
+hipError_t launch_gemm(bool exact, const GemmParams& p, hipStream_t s);
 hipError_t launch_pack_q4(const uint8_t* q, const uint16_t* d, int64_t n_out, int64_t k_in,
                           int kind, int head_dim, void* dst, hipStream_t s);
 void pack_q4_host(const uint8_t* q, const uint16_t* d, int64_t n_out, int64_t k_in, int kind,
@@ -148,8 +142,8 @@ hipError_t launch_attention(const AttnPlan& plan, int head_dim, const AttnParams
 // ---------------------------------------------------------------- small kernels
 
 // ---------------------------------------------------------------- split-K consumers
-// Each sums a GEMM's EPI_PARTIAL tiles in contributor order and applies what
-// the GEMM epilogue would have.
+// Each sums a GEMM's partial tiles in contributor order and applies the
+// projection's epilogue.
 SplitOut split_out(const GemmPlan& g, const float* part);
 // QKV: RoPE (rotate-half pairs sit 8 rows apart in one tile) -> fp32 q/k/v
 // and bf16 tree K/V
@@ -158,6 +152,10 @@ hipError_t launch_qkv_finish(const SplitOut& so, const EpiArgs& e, int n, hipStr
 hipError_t launch_swiglu_finish(const SplitOut& so, uint16_t* m, int ffn, int n, hipStream_t s);
 // residual: resid[n][hidden] += y
 hipError_t launch_resid_finish(const SplitOut& so, float* resid, int hidden, int n, hipStream_t s);
+// lm_head: bf16 logits [n][vocab] (if logits is not NULL) and each panel's
+// top-2 per node, cand[panel][node] = {best, index bits, second, 0}
+hipError_t launch_logits_finish(const SplitOut& so, uint16_t* logits, int64_t vocab, f32x4* cand, int n,
+                                hipStream_t s);
 
 // RMSNorm of each row into the GEMM operand: u = x / sqrt(mean(x^2) + eps) * g
 // as fp16 hi/lo rows [2n][hidden]

@@ -64,19 +64,7 @@ hipError_t launch_norm_hilo(const float* x, int n, int hidden, const uint16_t* g
   return hipGetLastError();
 }
 
-// Top-2 merge: best value, its index (lowest on exact ties) and the runner-up
-// (a tie at the top makes the runner-up equal to the best).
-__device__ __forceinline__ void merge_top2(float& v1, int& i1, float& v2, float b1, int bi, float b2) {
-  if (b1 > v1 || (b1 == v1 && bi < i1)) {
-    v2 = fmaxf(v1, b2);
-    v1 = b1;
-    i1 = bi;
-  } else {
-    v2 = fmaxf(v2, b1);
-  }
-}
-
-// One block: merge the lm_head blocks' candidates into the greedy token and
+// One block: merge the lm_head panels' candidates into the greedy token and
 // top1 - top2 gap of every node, then walk the tree in one wave (node i on
 // lane i).  Acceptance is greedy ("Lucebox: 추측 디코딩과 전용 커널로 ...",
 // section "Lucebox 설치 및 실행": temperature 0): a node is accepted when

@@ -1,4 +1,4 @@
-// Split-K consumers: the int4 GEMM (EPI_PARTIAL) leaves each block's share of
+// Split-K consumers: the int4 GEMM leaves each block's share of
 // a panel as a partial tile; these kernels add the shares of every output in
 // contributor order (deterministic) and apply the epilogue the projection
 // needs.  Doing the reduction here, after the GEMM has finished, needs no
@@ -151,6 +151,56 @@ __global__ __launch_bounds__(256) void resid_finish_kernel(SplitOut so, float* r
 hipError_t launch_resid_finish(const SplitOut& so, float* resid, int hidden, int n, hipStream_t s) {
   if (so.tile_f > 256) return hipErrorInvalidValue;
   hipLaunchKernelGGL(resid_finish_kernel, dim3(so.panels, n), dim3(so.tile_f), 0, s, so, resid, hidden);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ lm_head
+// One block per (panel, group of nodes), one thread per panel row: the
+// logits (bf16, if asked for) and the panel's top-2 per node, reduced
+// lane-pairwise in each wave and then over the waves in wave order.
+constexpr int kLogNodes = 4;  // nodes per block
+
+__global__ __launch_bounds__(256) void logits_finish_kernel(SplitOut so, uint16_t* __restrict__ logits,
+                                                            int64_t vocab, f32x4* __restrict__ cand, int n) {
+  __shared__ float s_v1[kLogNodes][4], s_v2[kLogNodes][4];
+  __shared__ int s_i1[kLogNodes][4];
+  const int pnl = blockIdx.x, n0 = blockIdx.y * kLogNodes;
+  const int fl = threadIdx.x, lane = fl & 63, wave = fl >> 6;
+  const int64_t f = (int64_t)pnl * so.tile_f + fl;
+  const bool ok = f < vocab;
+  SplitLoads ld[kLogNodes];
+#pragma unroll
+  for (int k = 0; k < kLogNodes; ++k) split_issue(so, pnl, fl, min(n0 + k, n - 1), ld[k]);
+#pragma unroll
+  for (int k = 0; k < kLogNodes; ++k) {
+    const int node = n0 + k;
+    const float y = split_finish(ld[k]);
+    if (logits && ok && node < n) logits[(int64_t)node * vocab + f] = f32_to_bf16_bits(y);
+    float v1 = ok ? y : -INFINITY, v2 = -INFINITY;
+    int i1 = ok ? (int)f : 0x7fffffff;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1)
+      merge_top2(v1, i1, v2, shfl_xor(v1, m), __shfl_xor(i1, m, 64), shfl_xor(v2, m));
+    if (lane == 0) {
+      s_v1[k][wave] = v1;
+      s_v2[k][wave] = v2;
+      s_i1[k][wave] = i1;
+    }
+  }
+  __syncthreads();
+  if (fl < kLogNodes && n0 + fl < n) {
+    float v1 = s_v1[fl][0], v2 = s_v2[fl][0];
+    int i1 = s_i1[fl][0];
+    for (int w = 1; w < (int)(blockDim.x >> 6); ++w) merge_top2(v1, i1, v2, s_v1[fl][w], s_i1[fl][w], s_v2[fl][w]);
+    cand[(int64_t)pnl * n + n0 + fl] = f32x4{v1, __int_as_float(i1), v2, 0.f};
+  }
+}
+
+hipError_t launch_logits_finish(const SplitOut& so, uint16_t* logits, int64_t vocab, f32x4* cand, int n,
+                                hipStream_t s) {
+  if (so.tile_f > 256 || so.tile_f % 64) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(logits_finish_kernel, dim3(so.panels, (n + kLogNodes - 1) / kLogNodes), dim3(so.tile_f), 0, s,
+                     so, logits, vocab, cand, n);
   return hipGetLastError();
 }
 
