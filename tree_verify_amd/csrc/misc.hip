@@ -75,29 +75,35 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const f32x4* __restrict_
                                                         TreeArgs t, int32_t* argmax, float* gap,
                                                         int32_t* path, int32_t* path_len,
                                                         int32_t* committed) {
-  __shared__ float s1[16][kMaxNodes], s2[16][kMaxNodes];
-  __shared__ int si[16][kMaxNodes];
+  // the candidate list of every node split over 1024 / n parts, so all
+  // threads load (a few candidates each, all in flight) before merging
+  __shared__ float s1[1024], s2[1024];
+  __shared__ int si[1024];
   const int tid = threadIdx.x;
   const int n = t.n;
-  const int node = tid & 63, part = tid >> 6;  // 16 parts of the candidate list
+  const int parts = 1024 / n;
+  const int node = tid % n, part = tid / n;
   float v1 = -INFINITY, v2 = -INFINITY;
   int i1 = 0x7fffffff;
-  if (node < n) {
-#pragma unroll 8
-    for (int c = part; c < n_cand; c += 16) {
+  if (part < parts) {
+#pragma unroll 16
+    for (int c = part; c < n_cand; c += parts) {
       const f32x4 v = cand[(int64_t)c * n + node];
       merge_top2(v1, i1, v2, v[0], __float_as_int(v[1]), v[2]);
     }
+    s1[part * n + node] = v1;
+    s2[part * n + node] = v2;
+    si[part * n + node] = i1;
   }
-  s1[part][node] = v1;
-  s2[part][node] = v2;
-  si[part][node] = i1;
   __syncthreads();
   if (tid >= 64) return;
   const int lane = tid;
   int am = 0;
   if (lane < n) {
-    for (int q = 1; q < 16; ++q) merge_top2(v1, i1, v2, s1[q][lane], si[q][lane], s2[q][lane]);
+    v1 = s1[lane];
+    v2 = s2[lane];
+    i1 = si[lane];
+    for (int q = 1; q < parts; ++q) merge_top2(v1, i1, v2, s1[q * n + lane], si[q * n + lane], s2[q * n + lane]);
     am = i1;
     argmax[lane] = am;
     if (gap) gap[lane] = v1 - v2;

@@ -8,42 +8,53 @@
 namespace lucev {
 
 // Sum of the contributors of output feature column fl (of panel pnl) for
-// node n, added in contributor order.  The first 16 contributors' loads are
+// node n, added in contributor order.  The first CM contributors' loads are
 // unconditional (past the last contributor they re-read it and the value is
 // dropped by a select), so a caller's loads for several columns can all be
-// in flight before the first sum.
+// in flight before the first sum; CM is the GEMM's most contributors per
+// panel rounded up to 4, 8 or 16 (kernels are instantiated per CM).
+template <int CM>
 struct SplitLoads {
-  float v[16];
+  float v[CM];
   const float* src;
   int nc;
   int64_t tile;
 };
-__device__ __forceinline__ void split_issue(const SplitOut& so, int pnl, int fl, int n, SplitLoads& l) {
+template <int CM>
+__device__ __forceinline__ void split_issue(const SplitOut& so, int pnl, int fl, int n, SplitLoads<CM>& l) {
   const int bf = block_of_unit((int64_t)pnl * so.gu, so.units, so.blocks);
   const int bl = block_of_unit((int64_t)pnl * so.gu + so.gu - 1, so.units, so.blocks);
   l.tile = (int64_t)so.tile_n * so.tile_f;
   l.src = so.part + (int64_t)pnl * so.c_max * l.tile + (int64_t)n * so.tile_f + fl;
   l.nc = bl - bf + 1;
 #pragma unroll
-  for (int c = 0; c < 16; ++c) l.v[c] = l.src[min(c, l.nc - 1) * l.tile];
+  for (int c = 0; c < CM; ++c) l.v[c] = l.src[min(c, l.nc - 1) * l.tile];
 }
-__device__ __forceinline__ float split_finish(const SplitLoads& l) {
+template <int CM>
+__device__ __forceinline__ float split_finish(const SplitLoads<CM>& l) {
   float y = 0.f;
 #pragma unroll
-  for (int c = 0; c < 16; ++c) y += c < l.nc ? l.v[c] : 0.f;
-  for (int c = 16; c < l.nc; ++c) y += l.src[c * l.tile];
+  for (int c = 0; c < CM; ++c) y += c < l.nc ? l.v[c] : 0.f;
+  for (int c = CM; c < l.nc; ++c) y += l.src[c * l.tile];
   return y;
 }
-__device__ __forceinline__ float split_sum(const SplitOut& so, int pnl, int fl, int n) {
-  SplitLoads l;
-  split_issue(so, pnl, fl, n, l);
-  return split_finish(l);
-}
+
+// launch a consumer kernel template instantiated for the GEMM's contributor count
+#define LUCEV_SPLIT_LAUNCH(KERNEL, GRID, BLOCK, SO, ...)                                        \
+  do {                                                                                         \
+    if ((SO).c_max <= 4)                                                                       \
+      hipLaunchKernelGGL(KERNEL<4>, GRID, BLOCK, 0, s, SO, __VA_ARGS__);                       \
+    else if ((SO).c_max <= 8)                                                                  \
+      hipLaunchKernelGGL(KERNEL<8>, GRID, BLOCK, 0, s, SO, __VA_ARGS__);                       \
+    else                                                                                       \
+      hipLaunchKernelGGL(KERNEL<16>, GRID, BLOCK, 0, s, SO, __VA_ARGS__);                      \
+  } while (0)
 
 // ------------------------------------------------------------ QKV + RoPE
 // One block per (panel, node), one thread per panel row (at most 256).  Packed rows of a
 // head tile 16i..16i+15 hold dims [8i, 8i+8) and [d/2 + 8i, d/2 + 8i + 8), so
 // a rotate-half RoPE pair is rows fl and fl ^ 8 of the same tile.
+template <int CM>
 __global__ __launch_bounds__(256) void qkv_finish_kernel(SplitOut so, EpiArgs e) {
   __shared__ float s_y[256];
   const int pnl = blockIdx.x, n = blockIdx.y;
@@ -52,7 +63,9 @@ __global__ __launch_bounds__(256) void qkv_finish_kernel(SplitOut so, EpiArgs e)
   const int64_t n_out = (int64_t)(e.n_q_heads + 2 * e.n_kv_heads) * hd;
   const int64_t prow = (int64_t)pnl * so.tile_f + fl;
   const bool ok = prow < n_out;
-  s_y[fl] = ok ? split_sum(so, pnl, fl, n) : 0.f;
+  SplitLoads<CM> ld;
+  split_issue(so, pnl, fl, n, ld);
+  s_y[fl] = ok ? split_finish(ld) : 0.f;
   __syncthreads();
   if (!ok) return;
   const int head = (int)(prow / hd);
@@ -88,7 +101,7 @@ __global__ __launch_bounds__(256) void qkv_finish_kernel(SplitOut so, EpiArgs e)
 
 hipError_t launch_qkv_finish(const SplitOut& so, const EpiArgs& e, int n, hipStream_t s) {
   if (so.tile_f > 256 || so.tile_f % 32) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(qkv_finish_kernel, dim3(so.panels, n), dim3(so.tile_f), 0, s, so, e);
+  LUCEV_SPLIT_LAUNCH(qkv_finish_kernel, dim3(so.panels, n), dim3(so.tile_f), so, e);
   return hipGetLastError();
 }
 
@@ -97,13 +110,14 @@ hipError_t launch_qkv_finish(const SplitOut& so, const EpiArgs& e, int n, hipStr
 // are the gate and up rows [16i, 16i + 16) of the same FFN unit.
 constexpr int kSwiNodes = 4;  // nodes per block
 
+template <int CM>
 __global__ __launch_bounds__(256) void swiglu_finish_kernel(SplitOut so, uint16_t* __restrict__ m, int ffn, int n) {
   __shared__ float s_y[kSwiNodes][256];
   const int pnl = blockIdx.x, n0 = blockIdx.y * kSwiNodes;
   const int fl = threadIdx.x;
   const int64_t n_out = 2 * (int64_t)ffn;
   const bool ok = (int64_t)pnl * so.tile_f + fl < n_out;
-  SplitLoads ld[kSwiNodes];
+  SplitLoads<CM> ld[kSwiNodes];
 #pragma unroll
   for (int k = 0; k < kSwiNodes; ++k) split_issue(so, pnl, fl, min(n0 + k, n - 1), ld[k]);
 #pragma unroll
@@ -129,20 +143,21 @@ __global__ __launch_bounds__(256) void swiglu_finish_kernel(SplitOut so, uint16_
 
 hipError_t launch_swiglu_finish(const SplitOut& so, uint16_t* m, int ffn, int n, hipStream_t s) {
   if (so.tile_f > 256 || so.tile_f % 32) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(swiglu_finish_kernel, dim3(so.panels, (n + kSwiNodes - 1) / kSwiNodes), dim3(so.tile_f), 0, s,
-                     so, m, ffn, n);
+  LUCEV_SPLIT_LAUNCH(swiglu_finish_kernel, dim3(so.panels, (n + kSwiNodes - 1) / kSwiNodes), dim3(so.tile_f), so, m,
+                     ffn, n);
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------ residual
 // One block per (panel, node), x += y.
+template <int CM>
 __global__ __launch_bounds__(256) void resid_finish_kernel(SplitOut so, float* resid, int hidden) {
   const int pnl = blockIdx.x, n = blockIdx.y;
   const int fl = threadIdx.x;
   const int64_t f = (int64_t)pnl * so.tile_f + fl;
   if (f >= hidden) return;
   float* r = resid + (int64_t)n * hidden + f;
-  SplitLoads ld;
+  SplitLoads<CM> ld;
   split_issue(so, pnl, fl, n, ld);
   const float x = *r;
   *r = x + split_finish(ld);
@@ -150,7 +165,7 @@ __global__ __launch_bounds__(256) void resid_finish_kernel(SplitOut so, float* r
 
 hipError_t launch_resid_finish(const SplitOut& so, float* resid, int hidden, int n, hipStream_t s) {
   if (so.tile_f > 256) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(resid_finish_kernel, dim3(so.panels, n), dim3(so.tile_f), 0, s, so, resid, hidden);
+  LUCEV_SPLIT_LAUNCH(resid_finish_kernel, dim3(so.panels, n), dim3(so.tile_f), so, resid, hidden);
   return hipGetLastError();
 }
 
@@ -160,6 +175,7 @@ hipError_t launch_resid_finish(const SplitOut& so, float* resid, int hidden, int
 // lane-pairwise in each wave and then over the waves in wave order.
 constexpr int kLogNodes = 4;  // nodes per block
 
+template <int CM>
 __global__ __launch_bounds__(256) void logits_finish_kernel(SplitOut so, uint16_t* __restrict__ logits,
                                                             int64_t vocab, f32x4* __restrict__ cand, int n) {
   __shared__ float s_v1[kLogNodes][4], s_v2[kLogNodes][4];
@@ -168,7 +184,7 @@ __global__ __launch_bounds__(256) void logits_finish_kernel(SplitOut so, uint16_
   const int fl = threadIdx.x, lane = fl & 63, wave = fl >> 6;
   const int64_t f = (int64_t)pnl * so.tile_f + fl;
   const bool ok = f < vocab;
-  SplitLoads ld[kLogNodes];
+  SplitLoads<CM> ld[kLogNodes];
 #pragma unroll
   for (int k = 0; k < kLogNodes; ++k) split_issue(so, pnl, fl, min(n0 + k, n - 1), ld[k]);
 #pragma unroll
@@ -199,8 +215,8 @@ __global__ __launch_bounds__(256) void logits_finish_kernel(SplitOut so, uint16_
 hipError_t launch_logits_finish(const SplitOut& so, uint16_t* logits, int64_t vocab, f32x4* cand, int n,
                                 hipStream_t s) {
   if (so.tile_f > 256 || so.tile_f % 64) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(logits_finish_kernel, dim3(so.panels, (n + kLogNodes - 1) / kLogNodes), dim3(so.tile_f), 0, s,
-                     so, logits, vocab, cand, n);
+  LUCEV_SPLIT_LAUNCH(logits_finish_kernel, dim3(so.panels, (n + kLogNodes - 1) / kLogNodes), dim3(so.tile_f), so,
+                     logits, vocab, cand, n);
   return hipGetLastError();
 }
 
