@@ -76,6 +76,7 @@ ATTN_CASES = [
     ("ragged_prefix", 8, 2, 128, 1000, None, 16),
     ("27b_group", 48, 8, 128, 4100, (3, 8), 22),
     ("wide_tree", 48, 8, 128, 2051, (4, 10), 40),
+    ("five_tiles", 48, 8, 128, 1500, (3, 8), 13),  # 78 rows: the fifth tile split by key quarter
     ("empty_prefix", 8, 2, 128, 0, None, 5),
     ("single_node", 48, 8, 128, 777, None, 1),
     ("max_nodes", 8, 2, 64, 300, None, 64),

@@ -43,8 +43,17 @@ constexpr int attn_max_waves(int qpw) { return qpw == 1 ? 12 : 8; }
 // 16-lane group reads at once then fall in 16 different bank groups.  The
 // ragged last tile of the prefix goes through registers so tokens past it
 // are zero.
-template <int D, int QPW, bool QLO>
+//
+// SPLIT (one query tile per wave, RT = 4k + 1 tiles, RT + 3 <= 12): the four
+// SIMDs of a CU would carry k + 1, k, k, k tiles, so the last (ragged) tile
+// is instead shared by four waves, one per SIMD, each taking a fixed 16-key
+// quarter of every 64-key tile with its own (max, sum, O); the four states
+// are merged through LDS at the end.  The quarter's PV product is a
+// 16x16x16 MFMA, whose B operand (4 keys per lane) is exactly the layout the
+// 16-key score tile comes out in.
+template <int D, int QPW, bool QLO, bool SPLIT>
 __global__ __launch_bounds__(attn_max_waves(QPW) * 64) void attn_partial_kernel(AttnParams p) {
+  static_assert(!SPLIT || QPW == 1, "split tiles use one query tile per wave");
   constexpr int WAVES = attn_max_waves(QPW);
   constexpr int KCPR = D / 8;                   // 16-byte chunks per K row
   constexpr int KROWS = 64 / KCPR;              // K rows per 1 KB load
@@ -53,15 +62,20 @@ __global__ __launch_bounds__(attn_max_waves(QPW) * 64) void attn_partial_kernel(
   constexpr int NLD = (KBYTES + VBYTES) / 1024; // 1 KB loads per tile
   constexpr int LPW = (NLD + WAVES - 1) / WAVES;  // loads per wave per tile
   constexpr int BUF = KBYTES + VBYTES;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[3 * BUF + 1024];
+  constexpr int MERGE = SPLIT ? 4 * 16 * D * 4 + 2 * 64 * 4 : 0;  // quarter states
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[3 * BUF + 1024 + MERGE];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  // the wave index as a scalar: every branch on it is then a scalar branch
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lq = lane >> 4;
   const int chunk = blockIdx.x;
   const int g = blockIdx.y;
   const int G = p.n_q_heads / p.n_kv_heads;
   const int RT = (p.rows + 15) / 16;
+  const int FT = SPLIT ? RT - 1 : RT;           // tiles a wave owns whole
+  const bool quarter = SPLIT && wave >= FT && wave < FT + 4;
+  const int qq = wave - FT;                     // quarter: keys (qq >> 1) * 32 + (qq & 1) * 4 + ..
   const int k_begin = chunk * p.chunk;
   const int k_end = min(p.prefix_len, k_begin + p.chunk);
   const int n_tiles = (k_end - k_begin + KT - 1) / KT;
@@ -71,17 +85,18 @@ __global__ __launch_bounds__(attn_max_waves(QPW) * 64) void attn_partial_kernel(
 
   // Load j of a tile (j < NLD): K rows for j < KBYTES / 1024, else V^T rows.
   // This lane's global element offset at token 0 and its LDS byte offset.
-  auto load_slot = [&](int j, int64_t& goff, int& loff, int& tok, bool& is_v) {
+  // (offsets within a tile's K rows or V^T rows: below D * cap < 2^31)
+  auto load_slot = [&](int j, int& goff, int& loff, int& tok, bool& is_v) {
     if (j < KBYTES / 1024) {
       const int key = j * KROWS + lane / KCPR, pc = lane % KCPR;
       const int sw = ((key & 3) | (((key >> 3) & 3) << 2)) & (KCPR - 1);
-      goff = (int64_t)key * D + (pc ^ sw) * 8;
+      goff = key * D + (pc ^ sw) * 8;
       loff = j * 1024;
       tok = key;
       is_v = false;
     } else {
       const int dim = (j - KBYTES / 1024) * 8 + lane / 8, pc = lane % 8;
-      goff = (int64_t)dim * p.cap + (pc ^ ((dim >> 1) & 7)) * 8;
+      goff = dim * p.cap + (pc ^ ((dim >> 1) & 7)) * 8;
       loff = j * 1024;
       tok = (pc ^ ((dim >> 1) & 7)) * 8;
       is_v = true;
@@ -95,7 +110,7 @@ __global__ __launch_bounds__(attn_max_waves(QPW) * 64) void attn_partial_kernel(
     for (int r = 0; r < LPW; ++r) {
       const int j = wave + r * WAVES;
       uint8_t* dst = lds + (j < NLD ? b * BUF + j * 1024 : 3 * BUF);  // past NLD: scratch area
-      int64_t goff = 0;
+      int goff = 0;
       int loff = 0, tok = 0;
       bool is_v = false;
       if (j < NLD) load_slot(j, goff, loff, tok, is_v);
@@ -126,7 +141,7 @@ __global__ __launch_bounds__(attn_max_waves(QPW) * 64) void attn_partial_kernel(
   float m[QPW], l[QPW];
 #pragma unroll
   for (int i = 0; i < QPW; ++i) {
-    const int qt = wave * QPW + i;
+    const int qt = SPLIT ? min(wave, FT) : wave * QPW + i;
     const int row = qt * 16 + lr;
     const bool ok = qt < RT && row < p.rows;
     int node = 0, head = 0;
@@ -172,6 +187,23 @@ __global__ __launch_bounds__(attn_max_waves(QPW) * 64) void attn_partial_kernel(
     m[i] = -INFINITY;
     l[i] = 0.f;
   }
+  // One 16-key score tile of query tile i: A row r is key
+  // ks*32 + (r >> 2)*8 + h*4 + (r & 3), so this lane gets keys
+  // ks*32 + lq*8 + h*4 + ii of query lr (the order the PV operand wants).
+  auto score16 = [&](const uint16_t* K, int i, int ks, int h, float init) -> f32x4 {
+    f32x4 a4 = f32x4{init, init, init, init};
+    // this lane's key row; its swizzle is lr, so d chunk kk*4 + lq sits at
+    // (kk*4 + lq) ^ lr
+    const int key = ks * 32 + (lr >> 2) * 8 + h * 4 + (lr & 3);
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+      const bf16x8 a =
+          *reinterpret_cast<const bf16x8*>(K + key * D + (((kk * 4 + lq) ^ lr) & (KCPR - 1)) * 8);
+      a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[i][kk], a4, 0, 0, 0);
+      if constexpr (QLO) a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[i][kk], a4, 0, 0, 0);
+    }
+    return a4;
+  };
   // Scores of one 32-key half (keys ks*32 ..) for query tile i, as two 16-key
   // MFMA tiles.  With the hi/lo q (already scaled to log2 units) the
   // accumulators start at -bias, so they come out relative to the running
@@ -180,23 +212,58 @@ __global__ __launch_bounds__(attn_max_waves(QPW) * 64) void attn_partial_kernel(
     bias = m[i] == -INFINITY ? 0.f : m[i];
     const float init = QLO ? -bias : 0.f;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      f32x4 a4 = f32x4{init, init, init, init};
-      // this lane's key row (order permuted for the PV operand); its swizzle is
-      // lr, so d chunk kk*4 + lq sits at (kk*4 + lq) ^ lr
-      const int key = ks * 32 + (lr >> 2) * 8 + h * 4 + (lr & 3);
-#pragma unroll
-      for (int kk = 0; kk < D / 32; ++kk) {
-        const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(K + key * D + (((kk * 4 + lq) ^ lr) & (KCPR - 1)) * 8);
-        a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[i][kk], a4, 0, 0, 0);
-        if constexpr (QLO) a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[i][kk], a4, 0, 0, 0);
-      }
-      sc[h] = a4;
-    }
+    for (int h = 0; h < 2; ++h) sc[h] = score16(K, i, ks, h, init);
     if constexpr (!QLO) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) sc[h] = sc[h] * p.scale_log2 - bias;
+    }
+  };
+
+  // A split tile's quarter: keys ks*32 + lq*8 + h*4 + ii (ks = qq >> 1,
+  // h = qq & 1) of every 64-key tile, with the same lazy online softmax as a
+  // whole tile; PV as 16x16x16 MFMAs on 4 keys per lane.
+  auto quarter_tile = [&](const uint16_t* K, const uint16_t* V, int k0, auto masked) {
+    const int ks = qq >> 1, h = qq & 1;
+    const float bias = m[0] == -INFINITY ? 0.f : m[0];
+    f32x4 sc = score16(K, 0, ks, h, QLO ? -bias : 0.f);
+    if constexpr (!QLO) sc = sc * p.scale_log2 - bias;
+    if constexpr (decltype(masked)::value) {
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii)
+        if (k0 + ks * 32 + lq * 8 + h * 4 + ii >= k_end) sc[ii] = -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    mx = fmaxf(mx, shfl_xor(mx, 16));
+    mx = fmaxf(mx, shfl_xor(mx, 32));
+    if (__builtin_amdgcn_ballot_w64(bias + mx > m[0] + 8.f) != 0) {
+      const float m_new = fmaxf(m[0], bias + mx);
+      const float alpha = __builtin_amdgcn_exp2f(m[0] - m_new);
+      sc -= m_new - bias;
+      l[0] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) O[0][dt] *= alpha;
+      m[0] = m_new;
+    }
+    float psum = 0.f;
+    bf16x4 pb, pl;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const float pv = __builtin_amdgcn_exp2f(sc[ii]);
+      psum += pv;
+      const __bf16 hb = (__bf16)pv;
+      pb[ii] = hb;
+      pl[ii] = (__bf16)(pv - (float)hb);
+    }
+    l[0] += psum;
+    const s16x4 pbs = __builtin_bit_cast(s16x4, pb), pls = __builtin_bit_cast(s16x4, pl);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      // V^T row dt*16 + lr, keys ks*32 + lq*8 + h*4 .. + 3: 8 bytes of chunk
+      // ks*4 + lq, which the row's swizzle moved to (ks*4 + lq) ^ ((lr >> 1) & 7)
+      const s16x4 a = *reinterpret_cast<const s16x4*>(
+          V + (dt * 16 + lr) * KT + (((ks * 4 + lq) ^ ((lr >> 1) & 7)) * 8) + h * 4);
+      O[0][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pbs, O[0][dt], 0, 0, 0);
+      O[0][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pls, O[0][dt], 0, 0, 0);
     }
   };
 
@@ -268,6 +335,13 @@ __global__ __launch_bounds__(attn_max_waves(QPW) * 64) void attn_partial_kernel(
   auto compute = [&](int buf, int k0, auto masked) {
     const uint16_t* K = reinterpret_cast<const uint16_t*>(lds + buf * BUF);
     const uint16_t* V = reinterpret_cast<const uint16_t*>(lds + buf * BUF + KBYTES);
+    if constexpr (SPLIT) {
+      if (quarter) {
+        quarter_tile(K, V, k0, masked);
+        return;
+      }
+      if (wave >= FT) return;
+    }
 #pragma unroll
     for (int i = 0; i < QPW; ++i) {
       const int qt = wave * QPW + i;
@@ -303,7 +377,7 @@ __global__ __launch_bounds__(attn_max_waves(QPW) * 64) void attn_partial_kernel(
 #pragma unroll
   for (int i = 0; i < QPW; ++i) {
     const int qt = wave * QPW + i;
-    if (qt >= RT) continue;
+    if (qt >= FT) continue;
     float lt = l[i] + shfl_xor(l[i], 16);
     lt += shfl_xor(lt, 32);
     const int row = qt * 16 + lr;
@@ -318,6 +392,56 @@ __global__ __launch_bounds__(attn_max_waves(QPW) * 64) void attn_partial_kernel(
       if (lq == 0) {
         p.ml_part[prow * 2] = m[i];
         p.ml_part[prow * 2 + 1] = lt;
+      }
+    }
+  }
+
+  if constexpr (SPLIT) {
+    // merge the four quarter states of tile FT: O = sum_q 2^(m_q - M) O_q / L
+    float* sO = reinterpret_cast<float*>(lds + 3 * BUF + 1024);  // [4][16][D]
+    float* sm = sO + 4 * 16 * D;                                 // [4][16]
+    float* sl = sm + 64;
+    __syncthreads();  // (also: every wave is done with the tile ring)
+    if (quarter) {
+      float lt = l[0] + shfl_xor(l[0], 16);
+      lt += shfl_xor(lt, 32);
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt)
+        *reinterpret_cast<f32x4*>(sO + (qq * 16 + lr) * D + dt * 16 + lq * 4) = O[0][dt];
+      if (lq == 0) {
+        sm[qq * 16 + lr] = m[0];
+        sl[qq * 16 + lr] = lt;
+      }
+    }
+    __syncthreads();
+    const int row = FT * 16 + lr;
+    if (wave == FT && row < p.rows) {
+      float mq[4], M = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        mq[q] = sm[q * 16 + lr];
+        M = fmaxf(M, mq[q]);
+      }
+      float w[4], L = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        w[q] = __builtin_amdgcn_exp2f(mq[q] - M);
+        L += w[q] * sl[q * 16 + lr];
+      }
+      const float inv = 1.0f / L;
+      const int64_t prow = ((int64_t)chunk * p.n_kv_heads + g) * p.rows + row;
+      float* dst = p.o_part + prow * D + lq * 4;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) {
+        f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          o += w[q] * *reinterpret_cast<const f32x4*>(sO + (q * 16 + lr) * D + dt * 16 + lq * 4);
+        *reinterpret_cast<f32x4*>(dst + dt * 16) = o * inv;
+      }
+      if (lq == 0) {
+        p.ml_part[prow * 2] = M;
+        p.ml_part[prow * 2 + 1] = L;
       }
     }
   }
@@ -494,6 +618,9 @@ AttnPlan plan_attention(int n_nodes, int n_q_heads, int n_kv_heads, int head_dim
   const int rt = (a.rows + 15) / 16;
   a.qpw = rt <= attn_max_waves(1) ? 1 : (rt + attn_max_waves(2) - 1) / attn_max_waves(2);
   a.waves = attn_max_waves(a.qpw);
+  // a ragged last tile that would leave one SIMD a tile more than the others
+  // is shared by four waves, one per SIMD
+  a.split = a.qpw == 1 && rt % 4 == 1 && rt + 3 <= a.waves;
   // one block per CU over (chunk, KV head): chunks a multiple of the LDS tile
   int chunk = (int)(((int64_t)prefix_len * n_kv_heads + 255) / 256);
   chunk = ((chunk + KT - 1) / KT) * KT;
@@ -503,14 +630,25 @@ AttnPlan plan_attention(int n_nodes, int n_q_heads, int n_kv_heads, int head_dim
   return a;
 }
 
-template <int D, int QPW>
-static void launch_partial(const AttnPlan& plan, const AttnParams& p, hipStream_t s) {
+template <int D, int QPW, bool SPLIT>
+static void launch_partial3(const AttnPlan& plan, const AttnParams& p, hipStream_t s) {
   if (p.q32)
-    hipLaunchKernelGGL((attn_partial_kernel<D, QPW, true>), dim3(plan.n_chunks, p.n_kv_heads),
+    hipLaunchKernelGGL((attn_partial_kernel<D, QPW, true, SPLIT>), dim3(plan.n_chunks, p.n_kv_heads),
                        dim3(64 * attn_max_waves(QPW)), 0, s, p);
   else
-    hipLaunchKernelGGL((attn_partial_kernel<D, QPW, false>), dim3(plan.n_chunks, p.n_kv_heads),
+    hipLaunchKernelGGL((attn_partial_kernel<D, QPW, false, SPLIT>), dim3(plan.n_chunks, p.n_kv_heads),
                        dim3(64 * attn_max_waves(QPW)), 0, s, p);
+}
+
+template <int D, int QPW>
+static void launch_partial(const AttnPlan& plan, const AttnParams& p, hipStream_t s) {
+  if constexpr (QPW == 1) {
+    if (plan.split) {
+      launch_partial3<D, 1, true>(plan, p, s);
+      return;
+    }
+  }
+  launch_partial3<D, QPW, false>(plan, p, s);
 }
 
 hipError_t launch_attention(const AttnPlan& plan, int head_dim, const AttnParams& p,

@@ -105,6 +105,7 @@ struct AttnPlan {
   int rows;      // n * (Hq / Hkv) query rows per KV head
   int qpw;       // query tiles (16 rows) per wave
   int waves;     // waves per block
+  bool split;    // the ragged last query tile is shared by four waves (by key quarter)
 };
 
 struct AttnParams {
