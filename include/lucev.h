@@ -201,6 +201,39 @@ int lucev_accept_path(const lucev_shape* shape, const lucev_head_w* w, const luc
                       float* gap_out, int32_t* path_out, int32_t* path_len_out,
                       int32_t* committed_out, void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------ after the step */
+
+#define LUCEV_MAX_COMMIT_LAYERS 64
+
+/* Commit the accepted path into the KV caches, so the next step's prefix is
+ * this step's prefix plus the accepted tokens.  The target keeps its KV cache
+ * and drops what the tree rejected ("Lucebox Hub", section "Speculative
+ * decoding 계층 (DFlash / DDTree / DSpark)": the target adapter's KV
+ * snapshot / restore duty); here that is an append of the kept nodes only.
+ * Path node path[j] (root first) sits at depth j, so its key was rotated at
+ * position prefix_len + j; its key and value rows are written at cache token
+ * prefix_len + j of every listed layer.  The caller then advances prefix_len
+ * by *path_len.  The bonus token (the greedy token at the path's end) is not
+ * in the tree: it is the next step's root.
+ *   k_cache, v_cache : HOST arrays of n_layers DEVICE pointers, one layer's
+ *                      bf16 cache each (lucev_kv layout, written)
+ *   k_tree, v_tree   : HOST arrays of n_layers DEVICE pointers, one layer's
+ *                      bf16 [n_nodes][Hkv][d] tree K (after RoPE) / V as
+ *                      written by lucev_verify_layer (read)
+ *   path, path_len   : DEVICE outputs of lucev_accept_path (int32 [n_nodes],
+ *                      int32 [1]), read on the device, so no host round trip
+ *                      sits between acceptance and commit
+ * Requires 1 <= n_layers <= LUCEV_MAX_COMMIT_LAYERS, 1 <= n_nodes <=
+ * LUCEV_MAX_NODES and prefix_len + n_nodes <= capacity (room for the longest
+ * path); path entries outside [0, n_nodes) are skipped.  Returns LUCEV_OK,
+ * LUCEV_ERR_NULL_ARG, LUCEV_ERR_BAD_SHAPE, LUCEV_ERR_BAD_TREE (n_nodes),
+ * LUCEV_ERR_BAD_KV (capacity) or LUCEV_ERR_HIP. */
+int lucev_commit_path(const lucev_shape* shape, int32_t n_layers, uint16_t* const* k_cache,
+                      uint16_t* const* v_cache, const uint16_t* const* k_tree,
+                      const uint16_t* const* v_tree, int32_t prefix_len, int32_t capacity,
+                      int32_t n_nodes, const int32_t* path, const int32_t* path_len,
+                      void* stream);
+
 #ifdef __cplusplus
 }
 #endif

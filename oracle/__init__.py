@@ -31,5 +31,5 @@ assignments); none is "parity unpinned".
 from .reference import (  # noqa: F401
     bf16_to_f64, f16_to_f64, tree_depths, tree_ancestors, dequant_q4, rmsnorm,
     silu, rope, tree_attention, layer_forward, head_logits, argmax_gap,
-    accept_path, verify_forward, LayerWeights, HeadWeights, Shape,
+    accept_path, verify_forward, round_bf16, commit_path, LayerWeights, HeadWeights, Shape,
 )

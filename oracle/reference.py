@@ -243,6 +243,39 @@ def accept_path(parent: Sequence[int], token: Sequence[int], am: Sequence[int]):
     return path, committed
 
 
+def round_bf16(x) -> np.ndarray:
+    """fp64 -> the nearest bf16 value (ties to even), as fp64.
+
+    The KV cache holds bf16, so a committed key or value is stored rounded.
+    bf16 keeps 8 significant bits; frexp gives x = m 2^e with 0.5 <= |m| < 1,
+    so m is rounded to a multiple of 2^-8 (numpy's round is half-to-even).
+    Normal range only (no bf16 subnormals or overflow at these magnitudes).
+    """
+    m, e = np.frexp(np.asarray(x, np.float64))
+    return np.ldexp(np.round(m * 256.0) / 256.0, e)
+
+
+def commit_path(k_prefix: np.ndarray, v_prefix: np.ndarray, k_tree: np.ndarray,
+                v_tree: np.ndarray, path: Sequence[int]):
+    """The cache after committing the accepted path of one layer.
+
+    The target keeps its KV cache and drops what the tree rejected ("Lucebox
+    Hub", section "Speculative decoding 계층 (DFlash / DDTree / DSpark)": the
+    target adapter's KV snapshot / restore duty).  Path node path[j] (root
+    first) sits at depth j, i.e. at position P + j, and its key was rotated
+    there; its key and value, rounded to the cache's bf16, become tokens
+    P .. P + len - 1 after the P prefix tokens.
+    k_prefix / v_prefix: bf16 bits or fp64 [Hkv, P, d]; k_tree / v_tree: fp64
+    [N, Hkv, d].  Returns fp64 (k, v), each [Hkv, P + len(path), d].
+    """
+    kp = k_prefix if np.asarray(k_prefix).dtype == np.float64 else bf16_to_f64(k_prefix)
+    vp = v_prefix if np.asarray(v_prefix).dtype == np.float64 else bf16_to_f64(v_prefix)
+    idx = np.asarray(path, dtype=np.int64)
+    kn = round_bf16(np.asarray(k_tree)[idx]).transpose(1, 0, 2)
+    vn = round_bf16(np.asarray(v_tree)[idx]).transpose(1, 0, 2)
+    return np.concatenate([kp, kn], axis=1), np.concatenate([vp, vn], axis=1)
+
+
 def verify_forward(x_in: np.ndarray, layers: Sequence[LayerWeights],
                    kv: Sequence[tuple], head: Optional[HeadWeights],
                    parent: Sequence[int], shape: Shape,
@@ -259,11 +292,15 @@ def verify_forward(x_in: np.ndarray, layers: Sequence[LayerWeights],
     x = x_in if np.asarray(x_in).dtype == np.float64 else bf16_to_f64(x_in)
     hidden = []
     kt = vt = None
+    k_all, v_all = [], []
     for w, (kp, vp) in zip(layers, kv):
         x, kt, vt = layer_forward(x, w, kp, vp, parent, shape)
         if keep_hidden:
             hidden.append(x.copy())
-    out = {"hidden": hidden, "x": x, "k_tree": kt, "v_tree": vt}
+            k_all.append(kt)
+            v_all.append(vt)
+    out = {"hidden": hidden, "x": x, "k_tree": kt, "v_tree": vt,
+           "k_tree_layers": k_all, "v_tree_layers": v_all}
     if head is not None:
         logits = head_logits(x, head, shape)
         am, gap = argmax_gap(logits)

@@ -182,3 +182,29 @@ def test_wrong_weight_shape_is_rejected():
     rc = tv.lib().lucev_verify_layer(ctypes.byref(s), ctypes.byref(w), ctypes.byref(tree),
                                      ctypes.byref(kv), fake, fake, fake, fake, 1 << 40, None)
     assert rc == -2 and "wo" in tv.lucev_last_error()
+
+
+def test_commit_path_validation_before_any_launch():
+    tv = _tv()
+    _no_gpu()
+    fake = 1 << 20
+
+    def status(shape=None, layers=2, prefix=8, cap=100, n=5, path=fake, plen=fake, kc=None):
+        kc = [fake] * layers if kc is None else kc
+        try:
+            tv.lucev_commit_path(shape or _shape(tv), kc, [fake] * len(kc), [fake] * len(kc),
+                                 [fake] * len(kc), prefix, cap, n, path, plen)
+        except tv.LucevError as e:
+            return e.status
+        return 0
+
+    assert status(layers=0) == -2                    # no layer
+    assert status(layers=65) == -2                   # more than one call can carry
+    assert status(n=0) == -3 and status(n=65) == -3  # tree size
+    assert status(path=None) == -1 and status(plen=None) == -1
+    assert status(kc=[fake, None]) == -1             # a NULL layer pointer
+    assert status(prefix=96, cap=100, n=5) == -8     # no room for the longest path
+    assert status(prefix=-1) == -8
+    assert status(shape=_shape(tv, hidden=200)) == -2
+    # valid arguments get past validation to the device check (no GPU here)
+    assert status(prefix=95, cap=100, n=5) in (-6, -7)

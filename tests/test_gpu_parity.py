@@ -242,3 +242,68 @@ def test_repeated_steps_bit_identical(nodes, rec):
     for rep in range(1, len(outs)):
         for a, b in zip(outs[0], outs[rep]):
             assert np.array_equal(a, b), "step %d differs from step 0" % rep
+
+
+# ------------------------------------------------------------------ commit and the next step
+
+def test_commit_then_next_step_parity():
+    # step 1 on the GPU, lucev_commit_path of its accepted path into every
+    # layer's cache, then step 2 (a new tree) against prefix + path: the cache
+    # rows must be the step's own tree K / V, bit for bit, and step 2 must
+    # match the oracle run on the oracle's committed cache
+    torch = need_gpu()
+    import tree_verify_amd as tv
+    from tree_verify_amd.runner import VerifyRunner
+    import synth.device as sd
+    cfg = MID.replace(name="commit22")
+    seed, seed2 = cfg.seed + 501, cfg.seed + 502
+    n, P, Hkv, d = cfg.nodes, cfg.prefix, cfg.n_kv_heads, cfg.head_dim
+    say("case commit then next step, seed", seed)
+    ref = workload.planted_case(cfg, seed)
+    wl = sd.Workload(cfg, seed, "cuda")
+    shape = tv.make_shape(cfg.hidden, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ffn,
+                          cfg.vocab, cfg.rms_eps, cfg.rope_base)
+    r = VerifyRunner(shape, wl.layers, wl.head, n, wl.capacity, "cuda")
+    r.step(tv.make_tree(ref["parent"], ref["tokens"]), wl.x_in_f32(), P)
+    r.commit(n, P)
+    torch.cuda.synchronize()
+    plen = int(r.path_len.item())
+    path = [int(i) for i in r.path[:plen].cpu().numpy()]
+    say("  path", path)
+    assert path[0] == 0 and 1 <= plen <= n
+    for l, lw in enumerate(wl.layers):
+        k = lw["k"].cpu().numpy().view(np.uint16)   # [Hkv][cap][d]
+        v = lw["v"].cpu().numpy().view(np.uint16)   # [Hkv][d][cap]
+        kt = r.k_tree[l].cpu().numpy().view(np.uint16)  # [n][Hkv][d]
+        vt = r.v_tree[l].cpu().numpy().view(np.uint16)
+        for j, node in enumerate(path):
+            assert np.array_equal(k[:, P + j, :], kt[node]), "layer %d K row %d" % (l, j)
+            assert np.array_equal(v[:, :, P + j], vt[node]), "layer %d V column %d" % (l, j)
+        assert not k[:, P + plen:, :].any() and not v[:, :, P + plen:].any(), "rows past the path"
+        # against the oracle's committed rows (bf16 of its own tree K / V)
+        kr, vr = oracle.commit_path(synth.kv_prefix(cfg, l, seed)[0], synth.kv_prefix(cfg, l, seed)[1],
+                                    ref["k_tree_layers"][l], ref["v_tree_layers"][l], path)
+        ek = row_rel_err(oracle.bf16_to_f64(k[:, P:P + plen, :]).reshape(-1, d), kr[:, P:].reshape(-1, d)).max()
+        ev = row_rel_err(oracle.bf16_to_f64(v[:, :, P:P + plen]).transpose(0, 2, 1).reshape(-1, d),
+                         vr[:, P:].reshape(-1, d)).max()
+        assert ek < TOL and ev < TOL, (l, ek, ev)
+    # step 2 against prefix + path, a new tree and new inputs
+    parent2 = synth.tree_parents(cfg, seed2)
+    x2 = synth.hidden_in(cfg, seed2)
+    caches = [oracle.commit_path(*synth.kv_prefix(cfg, l, seed), ref["k_tree_layers"][l],
+                                 ref["v_tree_layers"][l], path) for l in range(cfg.layers)]
+    ref2 = oracle.verify_forward(x2, (workload.layer_weights(cfg, l, seed) for l in range(cfg.layers)),
+                                 caches, workload.head_weights(cfg, seed), parent2, workload.shape(cfg))
+    tok2 = synth.plant_tokens(cfg, parent2, ref2["argmax"], seed2)
+    x2g = torch.from_numpy(oracle.bf16_to_f64(x2).astype(np.float32)).cuda()
+    hid = [torch.zeros(n, cfg.hidden, dtype=torch.float32, device="cuda") for _ in range(cfg.layers)]
+    r.step(tv.make_tree(parent2, tok2), x2g, P + plen, hidden_out=hid)
+    torch.cuda.synchronize()
+    for l in range(cfg.layers):
+        e = row_rel_err(hid[l].cpu().numpy(), ref2["hidden"][l]).max()
+        assert e < TOL, "step 2 hidden of layer %d: %.3e" % (l, e)
+    el = row_rel_err(bf16_bits_to_f64(r.logits[:n]), ref2["logits"]).max()
+    say("  step 2 at prefix %d: logits rel err %.2e" % (P + plen, el))
+    assert el < TOL
+    decisive_compare(parent2, tok2, ref2["argmax"], ref2["gap"], r.argmax[:n].cpu().numpy(),
+                     r.path[:n].cpu().numpy(), int(r.path_len.item()), r.committed[:n].cpu().numpy())

@@ -452,3 +452,94 @@ def test_prefix_cache_convention_against_decoding_from_position_zero():
                 x, k1, v1 = oracle.layer_forward(x, lws[l], kc, vc, [-1], shp, prefix_len=P + t)
                 cs[l] = (np.concatenate([kc, k1[0][:, None]], 1), np.concatenate([vc, v1[0][:, None]], 1))
         np.testing.assert_allclose(tree[i], x[0], rtol=1e-11, atol=1e-11)
+
+
+# ------------------------------------------------------------------ commit of the accepted path
+
+def _bf16_grid():
+    """Every finite bf16 value, sorted, with its bit pattern (brute force)."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    vals = oracle.bf16_to_f64(bits)
+    ok = np.isfinite(vals)
+    order = np.argsort(vals[ok], kind="stable")
+    return vals[ok][order], bits[ok][order]
+
+
+def test_round_bf16_is_nearest_with_ties_to_even():
+    # against a search over the whole bf16 grid: a dropped carry, a
+    # truncation instead of rounding or ties away from zero all fail here
+    grid, gbits = _bf16_grid()
+    rng = np.random.default_rng(5)
+    x = np.concatenate([rng.standard_normal(4000) * 10.0 ** rng.integers(-6, 6, 4000),
+                        # exact halfway points between neighbouring bf16 values
+                        (grid[1000:1200] + grid[1001:1201]) / 2.0,
+                        (grid[40000:40100] + grid[40001:40101]) / 2.0])
+    got = oracle.round_bf16(x)
+    for xi, gi in zip(x, got):
+        j = np.searchsorted(grid, xi)
+        cands = [c for c in (j - 1, j) if 0 <= c < len(grid)]
+        dist = [abs(grid[c] - xi) for c in cands]
+        best = [c for c, dd in zip(cands, dist) if dd == min(dist)]
+        if len(best) > 1:  # a tie: the even bit pattern wins (+0 / -0 aside)
+            best = [c for c in best if gbits[c] % 2 == 0] or best
+        assert gi == grid[best[0]] or (gi == 0 and grid[best[0]] == 0), (xi, gi, grid[best[0]])
+
+
+def test_commit_path_appends_path_rows_in_order():
+    # hand-built: prefix rows stay, path rows follow root first, rounded
+    Hkv, d, P, N = 2, 3, 2, 5
+    rng = np.random.default_rng(9)
+    kp, vp = rng.standard_normal((Hkv, P, d)), rng.standard_normal((Hkv, P, d))
+    kt, vt = rng.standard_normal((N, Hkv, d)), rng.standard_normal((N, Hkv, d))
+    path = [0, 2, 4]
+    k2, v2 = oracle.commit_path(kp, vp, kt, vt, path)
+    assert k2.shape == (Hkv, P + 3, d) and v2.shape == (Hkv, P + 3, d)
+    np.testing.assert_array_equal(k2[:, :P], kp)
+    np.testing.assert_array_equal(v2[:, :P], vp)
+    for j, node in enumerate(path):
+        for g in range(Hkv):
+            np.testing.assert_array_equal(k2[g, P + j], oracle.round_bf16(kt[node, g]))
+            np.testing.assert_array_equal(v2[g, P + j], oracle.round_bf16(vt[node, g]))
+    # bf16-exact rows are stored unchanged
+    kb = oracle.bf16_to_f64(bf16(kt))
+    np.testing.assert_array_equal(oracle.commit_path(kp, vp, kb, vt, [1])[0][:, P], kb[1])
+
+
+def test_commit_then_decode_equals_decoding_with_a_bf16_cache():
+    # Step 1: a tree forward; keep the path [0, 1, 3].  Commit it, then step
+    # 2 is a one-node forward at position P + 3.  That must equal plain
+    # one-token decoding of 0, 1, 3 (within a step the nodes see each other's
+    # K / V unrounded), then the three cache entries rounded to bf16 (the
+    # cache format, at commit), then decoding the new token.
+    cfg = MINI.replace(layers=2)
+    lws, kvs, shp = _mini_inputs(cfg)
+    parent = [-1, 0, 0, 1, 2]
+    path = [0, 1, 3]
+    xn = oracle.bf16_to_f64(synth.hidden_in(cfg, 903, nodes=5))
+    x_new = oracle.bf16_to_f64(synth.hidden_in(cfg, 904, nodes=1))
+    out = oracle.verify_forward(xn, lws, kvs, None, parent, shp)
+    caches = [oracle.commit_path(kp, vp, out["k_tree_layers"][l], out["v_tree_layers"][l], path)
+              for l, (kp, vp) in enumerate(kvs)]
+    P = kvs[0][0].shape[1]
+    step2 = oracle.verify_forward(x_new, lws, caches, None, [-1], shp)["hidden"][-1][0]
+    # the same by sequential decoding with a rounding cache
+    cs = [(oracle.bf16_to_f64(k), oracle.bf16_to_f64(v)) for k, v in kvs]
+    seq = [xn[i:i + 1] for i in path] + [x_new]
+    for t, x in enumerate(seq):
+        if t == len(path):  # the commit: the step's entries are stored as bf16
+            cs = [(np.concatenate([kc[:, :P], oracle.round_bf16(kc[:, P:])], 1),
+                   np.concatenate([vc[:, :P], oracle.round_bf16(vc[:, P:])], 1)) for kc, vc in cs]
+        for l, w in enumerate(lws):
+            kc, vc = cs[l]
+            x, k1, v1 = oracle.layer_forward(x, w, kc, vc, [-1], shp, prefix_len=P + t)
+            cs[l] = (np.concatenate([kc, k1[0][:, None]], 1), np.concatenate([vc, v1[0][:, None]], 1))
+    np.testing.assert_allclose(step2, x[0], rtol=1e-10, atol=1e-10)
+    # without the rounding at commit the two would differ (the pin sees it)
+    assert np.max(np.abs(step2 - oracle.verify_forward(
+        x_new, lws, [(np.concatenate([oracle.bf16_to_f64(kp), out["k_tree_layers"][l][path].transpose(1, 0, 2)], 1),
+                      np.concatenate([oracle.bf16_to_f64(vp), out["v_tree_layers"][l][path].transpose(1, 0, 2)], 1))
+                     for l, (kp, vp) in enumerate(kvs)], None, [-1], shp)["hidden"][-1][0])) > 1e-9
+    # and the committed rows differ from the unrounded K / V only by bf16 rounding
+    k_unr = out["k_tree_layers"][0][path].transpose(1, 0, 2)
+    rel = np.abs(caches[0][0][:, P:] - k_unr) / np.maximum(np.abs(k_unr), 1e-300)
+    assert rel.max() <= 2.0 ** -8

@@ -92,6 +92,9 @@ def lib() -> ctypes.CDLL:
         L.lucev_accept_path.restype = c_i32
         L.lucev_accept_path.argtypes = [P(lucev_shape), P(lucev_head_w), P(lucev_tree), c_vp,
                                         c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]
+        L.lucev_commit_path.restype = c_i32
+        L.lucev_commit_path.argtypes = [P(lucev_shape), c_i32, P(c_vp), P(c_vp), P(c_vp), P(c_vp),
+                                        c_i32, c_i32, c_i32, c_vp, c_vp, c_vp]
         _lib = L
     return _lib
 
@@ -99,7 +102,7 @@ def lib() -> ctypes.CDLL:
 EXPORTED = ["lucev_abi_version", "lucev_status_str", "lucev_last_error",
             "lucev_q4_packed_bytes", "lucev_q4_pack", "lucev_q4_pack_device",
             "lucev_workspace_bytes", "lucev_workspace_init", "lucev_verify_layer",
-            "lucev_tree_attention", "lucev_accept_path"]
+            "lucev_tree_attention", "lucev_accept_path", "lucev_commit_path"]
 
 
 def _ptr(x) -> Optional[int]:
@@ -201,3 +204,21 @@ def lucev_accept_path(shape, w, tree, resid, logits_out, argmax_out, gap_out, pa
                                    _ptr(resid), _ptr(logits_out), _ptr(argmax_out), _ptr(gap_out),
                                    _ptr(path_out), _ptr(path_len_out), _ptr(committed_out),
                                    _ptr(ws), ws_bytes, stream), "lucev_accept_path")
+
+
+MAX_COMMIT_LAYERS = 64
+
+
+def lucev_commit_path(shape, k_cache, v_cache, k_tree, v_tree, prefix_len, capacity, n_nodes,
+                      path, path_len, stream=None) -> None:
+    """k_cache / v_cache / k_tree / v_tree: sequences of one device buffer per
+    layer (at most MAX_COMMIT_LAYERS); marshalled into host pointer arrays."""
+    n = len(k_cache)
+    arrs = []
+    for seq in (k_cache, v_cache, k_tree, v_tree):
+        if len(seq) != n:
+            raise ValueError("commit_path: per-layer lists differ in length")
+        arrs.append((ctypes.c_void_p * max(n, 1))(*[_ptr(x) for x in seq]))
+    _check(lib().lucev_commit_path(ctypes.byref(shape), n, arrs[0], arrs[1], arrs[2], arrs[3],
+                                   prefix_len, capacity, n_nodes, _ptr(path), _ptr(path_len),
+                                   stream), "lucev_commit_path")

@@ -469,4 +469,45 @@ int lucev_accept_path(const lucev_shape* shape, const lucev_head_w* w, const luc
   return LUCEV_OK;
 }
 
+int lucev_commit_path(const lucev_shape* shape, int32_t n_layers, uint16_t* const* k_cache,
+                      uint16_t* const* v_cache, const uint16_t* const* k_tree,
+                      const uint16_t* const* v_tree, int32_t prefix_len, int32_t capacity,
+                      int32_t n_nodes, const int32_t* path, const int32_t* path_len,
+                      void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (n_layers < 1 || n_layers > LUCEV_MAX_COMMIT_LAYERS)
+    return fail(LUCEV_ERR_BAD_SHAPE, "commit_path: n_layers %d outside [1, %d]", n_layers,
+                LUCEV_MAX_COMMIT_LAYERS);
+  if (n_nodes < 1 || n_nodes > LUCEV_MAX_NODES)
+    return fail(LUCEV_ERR_BAD_TREE, "commit_path: n_nodes %d outside [1, %d]", n_nodes, LUCEV_MAX_NODES);
+  if (!k_cache || !v_cache || !k_tree || !v_tree || !path || !path_len)
+    return fail(LUCEV_ERR_NULL_ARG, "commit_path: NULL argument");
+  if (prefix_len < 0 || capacity < 0 || (int64_t)prefix_len + n_nodes > capacity)
+    return fail(LUCEV_ERR_BAD_KV, "commit_path: prefix_len %d + n_nodes %d exceeds capacity %d",
+                prefix_len, n_nodes, capacity);
+  CommitArgs a;
+  memset(&a, 0, sizeof(a));
+  for (int l = 0; l < n_layers; ++l) {
+    if (!k_cache[l] || !v_cache[l] || !k_tree[l] || !v_tree[l])
+      return fail(LUCEV_ERR_NULL_ARG, "commit_path: NULL pointer for layer %d", l);
+    a.kc[l] = k_cache[l];
+    a.vc[l] = v_cache[l];
+    a.kt[l] = k_tree[l];
+    a.vt[l] = v_tree[l];
+  }
+  a.path = path;
+  a.path_len = path_len;
+  a.n_layers = n_layers;
+  a.n = n_nodes;
+  a.prefix_len = prefix_len;
+  a.cap = capacity;
+  a.n_kv_heads = shape->n_kv_heads;
+  a.head_dim = shape->head_dim;
+  if ((rc = check_device())) return rc;
+  hipError_t e = launch_commit(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "commit launch");
+  return LUCEV_OK;
+}
+
 }  // extern "C"

@@ -167,4 +167,17 @@ hipError_t launch_finalize(const f32x4* cand, int n_cand, const TreeArgs& t, int
                            hipStream_t s);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 
+// accepted-path commit into the KV caches of up to kMaxCommitLayers layers
+constexpr int kMaxCommitLayers = 64;
+struct CommitArgs {
+  uint16_t* kc[kMaxCommitLayers];
+  uint16_t* vc[kMaxCommitLayers];
+  const uint16_t* kt[kMaxCommitLayers];
+  const uint16_t* vt[kMaxCommitLayers];
+  const int32_t* path;
+  const int32_t* path_len;
+  int n_layers, n, prefix_len, cap, n_kv_heads, head_dim;
+};
+hipError_t launch_commit(const CommitArgs& a, hipStream_t s);
+
 }  // namespace lucev

@@ -161,4 +161,25 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Commit of the accepted path: block (j, KV head, layer), one thread per dim.
+// Path position j holds node path[j] at depth j (RoPE position prefix_len +
+// j); its key row goes to K token prefix_len + j and its value to column
+// prefix_len + j of the dim-major V.  Positions past *path_len do nothing.
+__global__ __launch_bounds__(128) void commit_kernel(CommitArgs a) {
+  const int j = blockIdx.x, g = blockIdx.y, l = blockIdx.z, t = threadIdx.x;
+  if (j >= *a.path_len) return;
+  const int node = a.path[j];
+  if (node < 0 || node >= a.n) return;
+  const int64_t src = ((int64_t)node * a.n_kv_heads + g) * a.head_dim + t;
+  const int64_t tok = a.prefix_len + j;
+  a.kc[l][((int64_t)g * a.cap + tok) * a.head_dim + t] = a.kt[l][src];
+  a.vc[l][((int64_t)g * a.head_dim + t) * a.cap + tok] = a.vt[l][src];
+}
+
+hipError_t launch_commit(const CommitArgs& a, hipStream_t s) {
+  if (a.head_dim > 128 || a.n_layers < 1 || a.n_layers > kMaxCommitLayers) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(commit_kernel, dim3(a.n, a.n_kv_heads, a.n_layers), dim3(a.head_dim), 0, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace lucev

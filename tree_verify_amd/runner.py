@@ -78,3 +78,15 @@ class VerifyRunner:
             tv.lucev_accept_path(self.shape, self._hw, tree, self.resid,
                                  self.logits if with_logits else None, self.argmax, self.gap,
                                  self.path, self.path_len, self.committed, self.ws, self.ws_bytes, st)
+
+    def commit(self, n: int, prefix_len: int, stream=None) -> None:
+        """Append the accepted path of the last step (its device outputs path /
+        path_len) to every layer's KV cache at prefix_len ..; the caller then
+        advances prefix_len by path_len."""
+        st = torch.cuda.current_stream().cuda_stream if stream is None else stream
+        step = tv.MAX_COMMIT_LAYERS
+        for l0 in range(0, len(self.layers), step):
+            ls = self.layers[l0:l0 + step]
+            tv.lucev_commit_path(self.shape, [lw["k"] for lw in ls], [lw["v"] for lw in ls],
+                                 self.k_tree[l0:l0 + step], self.v_tree[l0:l0 + step], prefix_len,
+                                 self.capacity, n, self.path, self.path_len, st)
