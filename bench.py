@@ -134,6 +134,56 @@ def copy_calibration(nbytes):
     print(json.dumps({"copy_bytes": nbytes}), flush=True)
 
 
+def chained(r, cfg, tv, steps, dev):
+    """k successive verify steps, each committing its accepted path: step s
+    takes a new tree and new synthetic inputs at prefix P + (tokens committed
+    so far).  The drafts are planted from the target's own greedy tokens
+    (probability p, as in the single-step workload) by an untimed first pass;
+    the timed pass is verify + acceptance + commit, captured as one graph and
+    replayed once under HIP events.  Stops early when the cache has no room
+    for another tree."""
+    import numpy as np
+    import torch
+    import synth
+    prefix, tokens_total, ms_total, done, lens = cfg.prefix, 0, 0.0, 0, []
+    stream = torch.cuda.Stream()
+    for s in range(steps):
+        if prefix + cfg.nodes > r.capacity:
+            break
+        seed = cfg.seed + 7000 + s
+        parent = synth.tree_parents(cfg, seed)
+        x = torch.from_numpy(((synth.hidden_in(cfg, seed).astype(np.uint32) << 16)
+                              .view(np.float32))).to(dev)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            r.step(tv.make_tree(parent, [0] * cfg.nodes), x, prefix, with_logits=False)
+            stream.synchronize()
+            am = r.argmax[:cfg.nodes].cpu().numpy()
+            tree = tv.make_tree(parent, synth.plant_tokens(cfg, parent, am, seed))
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                r.step(tree, x, prefix, with_logits=False)
+                r.commit(cfg.nodes, prefix)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            stream.synchronize()
+        n_acc = int(r.path_len.item())
+        ms_total += e0.elapsed_time(e1)
+        tokens_total += n_acc
+        lens.append(n_acc)
+        prefix += n_acc
+        done += 1
+    return {"steps": done, "committed_tokens": tokens_total, "path_lengths": lens,
+            "tokens_per_step": round(tokens_total / max(done, 1), 3),
+            "ms_per_step": round(ms_total / max(done, 1), 4),
+            "tokens_per_s": round(tokens_total / (ms_total * 1e-3), 1) if ms_total else None,
+            "what": "verify + acceptance + commit per step (one graph each), new tree and synthetic "
+                    "inputs each step, drafts planted from the target's greedy tokens with p=%.1f; "
+                    "committed = accepted drafts + the bonus token" % cfg.p_accept}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -142,6 +192,8 @@ def main():
     ap.add_argument("--config", default="stack27b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--attn-reps", type=int, default=20)
+    ap.add_argument("--chain", type=int, default=8,
+                    help="verify+commit steps of the chained leg (0: skip)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run one device copy of this many bytes (counter calibration)")
     args = ap.parse_args()
@@ -243,8 +295,12 @@ def main():
                      "bytes_per_launch": ab, "avg_launch_us": round(attn_ms * 1e3, 3)},
         "step_roofline_frac": round(gbs / HBM_PEAK_GBS, 4),
     }
+    if args.chain > 0:
+        del graph
+        line["chained"] = chained(r, cfg, tv, args.chain, dev)
+        log("chained: %s" % json.dumps(line["chained"]))
     if not args.no_cpu_baseline:
-        del wl, r, graph
+        del wl, r
         torch.cuda.empty_cache()
         line["cpu_baseline"] = cpu_baseline(cfg)
     print(json.dumps(line), flush=True)
