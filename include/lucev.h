@@ -201,6 +201,27 @@ int lucev_accept_path(const lucev_shape* shape, const lucev_head_w* w, const luc
                       float* gap_out, int32_t* path_out, int32_t* path_len_out,
                       int32_t* committed_out, void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------ draft hooks */
+
+/* The target's lm_head over arbitrary hidden rows: final RMSNorm, lm_head,
+ * greedy token and top1-top2 gap per row (fp32 logits), with no tree.  The
+ * target adapter projects the drafter's hidden states through the target's
+ * lm_head ("Lucebox Hub", section "Speculative decoding 계층 (DFlash /
+ * DDTree / DSpark)": the adapter's lm_head projection duty).  The other
+ * adapter duty, capture of chosen layers' activations, needs no entry point:
+ * resid_io after lucev_verify_layer of layer l IS layer l's output, and a
+ * caller copies it on the same stream (or inside the same graph).
+ *   x          : fp32 [n_rows][H] hidden rows (DEVICE)
+ *   logits_out : bf16 [n_rows][V] or NULL
+ *   argmax_out : int32 [n_rows];  gap_out: fp32 [n_rows] or NULL
+ * 1 <= n_rows <= LUCEV_MAX_NODES; the workspace is sized by
+ * lucev_workspace_bytes(shape, n_rows, 0) or larger.  Returns LUCEV_OK,
+ * LUCEV_ERR_NULL_ARG, LUCEV_ERR_BAD_SHAPE, LUCEV_ERR_BAD_TREE (n_rows),
+ * LUCEV_ERR_ALIGN, LUCEV_ERR_WORKSPACE, LUCEV_ERR_DEVICE or LUCEV_ERR_HIP. */
+int lucev_project_logits(const lucev_shape* shape, const lucev_head_w* w, int32_t n_rows,
+                         const float* x, uint16_t* logits_out, int32_t* argmax_out,
+                         float* gap_out, void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------ after the step */
 
 #define LUCEV_MAX_COMMIT_LAYERS 64

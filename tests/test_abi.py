@@ -208,3 +208,26 @@ def test_commit_path_validation_before_any_launch():
     assert status(shape=_shape(tv, hidden=200)) == -2
     # valid arguments get past validation to the device check (no GPU here)
     assert status(prefix=95, cap=100, n=5) in (-6, -7)
+
+
+def test_project_logits_validation_before_any_launch():
+    tv = _tv()
+    _no_gpu()
+    s = _shape(tv)
+    w, kv, fake = _layer_args(tv, s)
+    hw = tv.lucev_head_w(fake, tv.q4(fake, 512, 256))
+
+    def status(n=4, x=fake, am=fake, logits=None, ws_bytes=1 << 40, shape=s, head=hw):
+        try:
+            tv.lucev_project_logits(shape, head, n, x, logits, am, None, fake, ws_bytes)
+        except tv.LucevError as e:
+            return e.status
+        return 0
+
+    assert status(n=0) == -3 and status(n=65) == -3
+    assert status(x=None) == -1 and status(am=None) == -1
+    assert status(x=fake + 4) == -5
+    assert status(ws_bytes=64) == -4
+    assert status(shape=_shape(tv, hidden=200)) == -2
+    assert status(head=tv.lucev_head_w(fake, tv.q4(fake, 256, 256))) == -2  # lm_head rows != vocab
+    assert status() in (-6, -7)  # valid: reaches the device check

@@ -307,3 +307,49 @@ def test_commit_then_next_step_parity():
     assert el < TOL
     decisive_compare(parent2, tok2, ref2["argmax"], ref2["gap"], r.argmax[:n].cpu().numpy(),
                      r.path[:n].cpu().numpy(), int(r.path_len.item()), r.committed[:n].cpu().numpy())
+
+
+# ------------------------------------------------------------------ draft hooks
+
+def test_draft_hooks_capture_and_project():
+    # the two adapter hooks a drafter uses: a chosen layer's activations
+    # captured during verify, and the target's lm_head over arbitrary hidden
+    # rows (random rows standing in for a drafter's, plus the captured ones)
+    torch = need_gpu()
+    import tree_verify_amd as tv
+    from tree_verify_amd.runner import VerifyRunner
+    import synth.device as sd
+    cfg = MID.replace(name="hooks22")
+    seed = cfg.seed + 601
+    n, H, V = cfg.nodes, cfg.hidden, cfg.vocab
+    say("case draft hooks, seed", seed)
+    ref = workload.planted_case(cfg, seed)
+    wl = sd.Workload(cfg, seed, "cuda")
+    shape = tv.make_shape(cfg.hidden, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ffn,
+                          cfg.vocab, cfg.rms_eps, cfg.rope_base)
+    r = VerifyRunner(shape, wl.layers, wl.head, n, wl.capacity, "cuda")
+    cap0 = torch.zeros(n, H, dtype=torch.float32, device="cuda")
+    r.step(tv.make_tree(ref["parent"], ref["tokens"]), wl.x_in_f32(), cfg.prefix, capture={0: cap0})
+    torch.cuda.synchronize()
+    got0 = cap0.cpu().numpy().astype(np.float64)
+    e0 = row_rel_err(got0, ref["hidden"][0]).max()
+    assert e0 < TOL, "captured layer 0: %.3e" % e0
+    hw = workload.head_weights(cfg, seed)
+    rng = np.random.default_rng(seed)
+    for rows, label in [(rng.standard_normal((16, H)).astype(np.float32) * 3.0, "random rows"),
+                        (got0.astype(np.float32), "captured layer-0 rows")]:
+        m = len(rows)
+        x = torch.from_numpy(rows).cuda()
+        logits = torch.zeros(m, V, dtype=torch.int16, device="cuda")
+        am = torch.zeros(m, dtype=torch.int32, device="cuda")
+        gap = torch.zeros(m, dtype=torch.float32, device="cuda")
+        r.project(x, m, logits, am, gap)
+        torch.cuda.synchronize()
+        ol = oracle.head_logits(rows.astype(np.float64), hw, workload.shape(cfg))
+        oam, ogap = oracle.argmax_gap(ol)
+        el = row_rel_err(bf16_bits_to_f64(logits), ol).max()
+        dec = ogap > 0.05
+        say("  %s: logits rel err %.2e, decisive %d/%d" % (label, el, dec.sum(), m))
+        assert el < TOL
+        assert np.array_equal(am.cpu().numpy()[dec], oam[dec])
+        assert np.allclose(gap.cpu().numpy()[dec], ogap[dec], rtol=0.05, atol=0.05)

@@ -92,6 +92,9 @@ def lib() -> ctypes.CDLL:
         L.lucev_accept_path.restype = c_i32
         L.lucev_accept_path.argtypes = [P(lucev_shape), P(lucev_head_w), P(lucev_tree), c_vp,
                                         c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]
+        L.lucev_project_logits.restype = c_i32
+        L.lucev_project_logits.argtypes = [P(lucev_shape), P(lucev_head_w), c_i32, c_vp, c_vp, c_vp,
+                                           c_vp, c_vp, c_sz, c_vp]
         L.lucev_commit_path.restype = c_i32
         L.lucev_commit_path.argtypes = [P(lucev_shape), c_i32, P(c_vp), P(c_vp), P(c_vp), P(c_vp),
                                         c_i32, c_i32, c_i32, c_vp, c_vp, c_vp]
@@ -102,7 +105,8 @@ def lib() -> ctypes.CDLL:
 EXPORTED = ["lucev_abi_version", "lucev_status_str", "lucev_last_error",
             "lucev_q4_packed_bytes", "lucev_q4_pack", "lucev_q4_pack_device",
             "lucev_workspace_bytes", "lucev_workspace_init", "lucev_verify_layer",
-            "lucev_tree_attention", "lucev_accept_path", "lucev_commit_path"]
+            "lucev_tree_attention", "lucev_accept_path", "lucev_project_logits",
+            "lucev_commit_path"]
 
 
 def _ptr(x) -> Optional[int]:
@@ -204,6 +208,13 @@ def lucev_accept_path(shape, w, tree, resid, logits_out, argmax_out, gap_out, pa
                                    _ptr(resid), _ptr(logits_out), _ptr(argmax_out), _ptr(gap_out),
                                    _ptr(path_out), _ptr(path_len_out), _ptr(committed_out),
                                    _ptr(ws), ws_bytes, stream), "lucev_accept_path")
+
+
+def lucev_project_logits(shape, w, n_rows, x, logits_out, argmax_out, gap_out, ws, ws_bytes,
+                         stream=None) -> None:
+    _check(lib().lucev_project_logits(ctypes.byref(shape), ctypes.byref(w), n_rows, _ptr(x),
+                                      _ptr(logits_out), _ptr(argmax_out), _ptr(gap_out), _ptr(ws),
+                                      ws_bytes, stream), "lucev_project_logits")
 
 
 MAX_COMMIT_LAYERS = 64

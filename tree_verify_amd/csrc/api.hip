@@ -254,6 +254,30 @@ int run_attention(const lucev_shape* s, const TreeArgs& t, const lucev_kv* kv, c
   return LUCEV_OK;
 }
 
+// Final RMSNorm, lm_head (split-K partial tiles + consumer with the fp32
+// top-2 per panel), then the per-row greedy token and gap; the acceptance
+// walk too when path outputs are given.
+int run_head(const lucev_shape* shape, const lucev_head_w* w, const TreeArgs& t, const float* x,
+             uint16_t* logits_out, int32_t* argmax_out, float* gap_out, int32_t* path_out,
+             int32_t* path_len_out, int32_t* committed_out, void* ws, const Ws& L, hipStream_t st) {
+  const int n = t.n;
+  const int H = shape->hidden;
+  hipError_t e;
+  uint16_t* xa = at<uint16_t>(ws, L.xa);
+  if ((e = launch_norm_hilo(x, n, H, w->final_norm, shape->rms_eps, xa, st)) != hipSuccess)
+    return hip_fail(e, "final norm launch");
+  SplitOut so;
+  GemmParams p = gemm_params_split(w->lm_head, xa, n, ws, L, &so);
+  f32x4* cand = at<f32x4>(ws, L.cand);
+  if ((e = launch_gemm(true, p, st)) != hipSuccess) return hip_fail(e, "lm_head gemm launch");
+  if ((e = launch_logits_finish(so, logits_out, shape->vocab, cand, n, st)) != hipSuccess)
+    return hip_fail(e, "lm_head finish launch");
+  if ((e = launch_finalize(cand, so.panels, t, argmax_out, gap_out, path_out, path_len_out,
+                           committed_out, st)) != hipSuccess)
+    return hip_fail(e, "finalize launch");
+  return LUCEV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -450,23 +474,30 @@ int lucev_accept_path(const lucev_shape* shape, const lucev_head_w* w, const luc
   if ((rc = check_ws(shape, t.n, 0, ws, ws_bytes, &L))) return rc;
   if ((rc = check_device())) return rc;
 
-  hipStream_t st = (hipStream_t)stream;
-  const int n = t.n;
-  const int H = shape->hidden;
-  hipError_t e;
-  uint16_t* xa = at<uint16_t>(ws, L.xa);
-  if ((e = launch_norm_hilo(resid, n, H, w->final_norm, shape->rms_eps, xa, st)) != hipSuccess)
-    return hip_fail(e, "final norm launch");
-  SplitOut so;
-  GemmParams p = gemm_params_split(w->lm_head, xa, n, ws, L, &so);
-  f32x4* cand = at<f32x4>(ws, L.cand);
-  if ((e = launch_gemm(true, p, st)) != hipSuccess) return hip_fail(e, "lm_head gemm launch");
-  if ((e = launch_logits_finish(so, logits_out, shape->vocab, cand, n, st)) != hipSuccess)
-    return hip_fail(e, "lm_head finish launch");
-  if ((e = launch_finalize(cand, so.panels, t, argmax_out, gap_out, path_out, path_len_out,
-                           committed_out, st)) != hipSuccess)
-    return hip_fail(e, "finalize launch");
-  return LUCEV_OK;
+  return run_head(shape, w, t, resid, logits_out, argmax_out, gap_out, path_out, path_len_out,
+                  committed_out, ws, L, (hipStream_t)stream);
+}
+
+int lucev_project_logits(const lucev_shape* shape, const lucev_head_w* w, int32_t n_rows,
+                         const float* x, uint16_t* logits_out, int32_t* argmax_out, float* gap_out,
+                         void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (!w || !w->final_norm || !x || !argmax_out)
+    return fail(LUCEV_ERR_NULL_ARG, "project_logits: NULL argument");
+  if (n_rows < 1 || n_rows > LUCEV_MAX_NODES)
+    return fail(LUCEV_ERR_BAD_TREE, "project_logits: n_rows %d outside [1, %d]", n_rows, LUCEV_MAX_NODES);
+  if ((rc = check_q4(w->lm_head, shape->vocab, shape->hidden, "lm_head"))) return rc;
+  if (!aligned16(x) || (logits_out && !aligned16(logits_out)))
+    return fail(LUCEV_ERR_ALIGN, "project_logits: tensors must be 16-byte aligned");
+  Ws L;
+  if ((rc = check_ws(shape, n_rows, 0, ws, ws_bytes, &L))) return rc;
+  if ((rc = check_device())) return rc;
+  TreeArgs t;
+  memset(&t, 0, sizeof(t));
+  t.n = n_rows;
+  return run_head(shape, w, t, x, logits_out, argmax_out, gap_out, nullptr, nullptr, nullptr, ws, L,
+                  (hipStream_t)stream);
 }
 
 int lucev_commit_path(const lucev_shape* shape, int32_t n_layers, uint16_t* const* k_cache,

@@ -108,6 +108,7 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const f32x4* __restrict_
     argmax[lane] = am;
     if (gap) gap[lane] = v1 - v2;
   }
+  if (!path) return;  // a plain projection: no tree to walk
   // acceptance walk
   const int par = lane < n ? t.parent[lane] : 0;
   const int tok = lane < n ? t.token[lane] : 0;

@@ -6,7 +6,7 @@ stream.  Orchestration only: all arithmetic runs in liblucev.so.
 """
 from __future__ import annotations
 
-from typing import List, Optional, Sequence
+from typing import Dict, List, Optional, Sequence
 
 import torch
 
@@ -61,10 +61,12 @@ class VerifyRunner:
 
     def step(self, tree: tv.lucev_tree, x_in_f32: torch.Tensor, prefix_len: int,
              hidden_out: Optional[List[torch.Tensor]] = None, with_logits: bool = True,
-             stream=None) -> None:
+             stream=None, capture: Optional[Dict[int, torch.Tensor]] = None) -> None:
         """One verify step: residual <- x_in, every layer, then acceptance.
 
-        ``hidden_out``, if given, receives a copy of the residual after each layer.
+        ``hidden_out``, if given, receives a copy of the residual after each
+        layer; ``capture`` maps chosen layers to buffers that receive theirs
+        (the drafter-conditioning activations), copied on the same stream.
         """
         n = tree.n
         st = torch.cuda.current_stream().cuda_stream if stream is None else stream
@@ -74,6 +76,8 @@ class VerifyRunner:
                                   self.k_tree[l], self.v_tree[l], self.ws, self.ws_bytes, st)
             if hidden_out is not None:
                 hidden_out[l].copy_(self.resid[:n])
+            if capture is not None and l in capture:
+                capture[l][:n].copy_(self.resid[:n])
         if self._hw is not None:
             tv.lucev_accept_path(self.shape, self._hw, tree, self.resid,
                                  self.logits if with_logits else None, self.argmax, self.gap,
@@ -90,3 +94,11 @@ class VerifyRunner:
             tv.lucev_commit_path(self.shape, [lw["k"] for lw in ls], [lw["v"] for lw in ls],
                                  self.k_tree[l0:l0 + step], self.v_tree[l0:l0 + step], prefix_len,
                                  self.capacity, n, self.path, self.path_len, st)
+
+    def project(self, x_f32: torch.Tensor, n: int, logits: Optional[torch.Tensor],
+                argmax: torch.Tensor, gap: Optional[torch.Tensor] = None, stream=None) -> None:
+        """The target's final norm + lm_head over n hidden rows (a drafter's),
+        greedy token and gap per row; no tree."""
+        st = torch.cuda.current_stream().cuda_stream if stream is None else stream
+        tv.lucev_project_logits(self.shape, self._hw, n, x_f32, logits, argmax, gap, self.ws,
+                                self.ws_bytes, st)
