@@ -111,6 +111,23 @@ typedef struct {
   int32_t capacity;
 } lucev_kv;
 
+/* A paged bf16 KV cache for one layer: the prefix sits in a pool of
+ * LUCEV_PAGE_TOKENS-token pages, and block_table maps prefix tokens to pages.
+ *   k_pages     : bf16 [n_pages][Hkv][16][d]  keys after RoPE
+ *   v_pages     : bf16 [n_pages][Hkv][d][16]  values, dim-major within a page
+ *   block_table : DEVICE int32 [ceil(prefix_len / 16)]: the page holding
+ *                 prefix tokens 16i .. 16i + 15 (entries are clamped to
+ *                 [0, n_pages), so a bad entry cannot address outside the pool)
+ * The prefix covered is tokens 0 .. prefix_len - 1, as in lucev_kv.          */
+#define LUCEV_PAGE_TOKENS 16
+typedef struct {
+  const uint16_t* k_pages;
+  const uint16_t* v_pages;
+  const int32_t* block_table;
+  int32_t n_pages;
+  int32_t prefix_len;
+} lucev_kv_paged;
+
 /* The draft tree, in HOST memory, passed by value.  Node 0 is the root (the
  * last accepted token, not yet in the cache); parent[i] < i.  The library
  * derives depths, RoPE positions (prefix_len + depth) and ancestor masks into
@@ -183,6 +200,20 @@ int lucev_verify_layer(const lucev_shape* shape, const lucev_layer_w* w, const l
 int lucev_tree_attention(const lucev_shape* shape, const lucev_tree* tree, const lucev_kv* kv,
                          const uint16_t* q, const uint16_t* k_tree, const uint16_t* v_tree,
                          uint16_t* out, void* ws, size_t ws_bytes, void* stream);
+
+/* The same attention over a paged prefix: a pool of 16-token physical blocks
+ * and a block table per sequence, which changes layout and allocation only,
+ * with no approximation ("Lucebox Hub", section "Paged attention +
+ * continuous batching").  Results are bit-identical to lucev_tree_attention
+ * on the same keys and values stored contiguously.
+ * Requires each prefix chunk a block reads (about prefix_len * Hkv / 256
+ * tokens) to span at most 1024 pages.  Returns the codes of
+ * lucev_tree_attention; LUCEV_ERR_BAD_KV also for prefix_len < 0, n_pages < 1
+ * with a non-empty prefix, or chunks of more than 1024 pages. */
+int lucev_tree_attention_paged(const lucev_shape* shape, const lucev_tree* tree,
+                               const lucev_kv_paged* kv, const uint16_t* q, const uint16_t* k_tree,
+                               const uint16_t* v_tree, uint16_t* out, void* ws, size_t ws_bytes,
+                               void* stream);
 
 /* Final RMSNorm, lm_head, greedy token and top1-top2 gap per node (taken on
  * the fp32 logits), then greedy acceptance over the tree: a node is accepted

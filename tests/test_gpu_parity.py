@@ -353,3 +353,63 @@ def test_draft_hooks_capture_and_project():
         assert el < TOL
         assert np.array_equal(am.cpu().numpy()[dec], oam[dec])
         assert np.allclose(gap.cpu().numpy()[dec], ogap[dec], rtol=0.05, atol=0.05)
+
+
+# ------------------------------------------------------------------ paged prefix
+
+@pytest.mark.parametrize("case", [c for c in ATTN_CASES if c[4] != 0] + [("empty_prefix", 8, 2, 128, 0, None, 5)],
+                         ids=[c[0] for c in ATTN_CASES if c[4] != 0] + ["empty_prefix"])
+def test_tree_attention_paged_equals_contiguous(case):
+    # the same prefix scattered over a shuffled pool of 16-token pages (and
+    # non-zero filler past the prefix in the last page): the paged attention
+    # must give the contiguous result bit for bit, and both match the oracle
+    torch = need_gpu()
+    import tree_verify_amd as tv
+    import synth.device as sd
+    name, Hq, Hkv, d, P, rec, n = case
+    cfg = synth.Config("paged_" + name, layers=1, hidden=128, n_q_heads=Hq, n_kv_heads=Hkv,
+                       head_dim=d, ffn=128, vocab=64, prefix=P, nodes=n,
+                       max_children=rec[0] if rec else None, max_depth=rec[1] if rec else None,
+                       p_accept=0.7, seed=5151 + n)
+    say("paged attention case", name)
+    parent = synth.tree_parents(cfg)
+    cap = ((P + 7) // 8) * 8 + 8
+    k, v = sd.kv_cache(cfg, 0, cfg.seed, cap, "cuda")
+    NL = (P + 15) // 16
+    NP = NL + 5
+    perm = torch.from_numpy(np.random.default_rng(cfg.seed).permutation(NP)[:NL].astype(np.int64)).cuda()
+    k_pool = torch.full((NP, Hkv, 16, d), 0x4000, dtype=torch.int16, device="cuda")  # 2.0 filler
+    v_pool = torch.full((NP, Hkv, d, 16), 0x4000, dtype=torch.int16, device="cuda")
+    if NL:
+        kl = k[:, :NL * 16, :].reshape(Hkv, NL, 16, d).permute(1, 0, 2, 3).clone()
+        vl = v[:, :, :NL * 16].reshape(Hkv, d, NL, 16).permute(2, 0, 1, 3).clone()
+        tail = NL * 16 - P  # tokens past the prefix in the last page keep the filler
+        if tail:
+            kl[NL - 1, :, 16 - tail:, :] = 0x4000
+            vl[NL - 1, :, :, 16 - tail:] = 0x4000
+        k_pool[perm] = kl
+        v_pool[perm] = vl
+    table = perm.to(torch.int32).contiguous() if NL else torch.zeros(1, dtype=torch.int32, device="cuda")
+    tab = "normal"
+    q = sd.flat_table(tab, synth.stream_key(cfg.seed, 90, 0), n * Hq * d, "cuda")
+    kt = sd.flat_table(tab, synth.stream_key(cfg.seed, 91, 0), n * Hkv * d, "cuda")
+    vt = sd.flat_table(tab, synth.stream_key(cfg.seed, 92, 0), n * Hkv * d, "cuda")
+    shape = tv.make_shape(cfg.hidden, Hq, Hkv, d, cfg.ffn, cfg.vocab)
+    ws_bytes = tv.lucev_workspace_bytes(shape, n, max(P, 1))
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
+    tree = tv.make_tree(parent, [0] * n)
+    st = torch.cuda.current_stream().cuda_stream
+    out_c = torch.zeros(n * Hq * d, dtype=torch.int16, device="cuda")
+    out_p = torch.zeros(n * Hq * d, dtype=torch.int16, device="cuda")
+    tv.lucev_tree_attention(shape, tree, tv.make_kv(k, v, P, cap), q, kt, vt, out_c, ws, ws_bytes, st)
+    tv.lucev_tree_attention_paged(shape, tree, tv.make_kv_paged(k_pool, v_pool, table, NP, P), q, kt, vt,
+                                  out_p, ws, ws_bytes, st)
+    torch.cuda.synchronize()
+    assert torch.equal(out_c, out_p), "paged result differs from the contiguous one"
+    kp, vp = synth.kv_prefix(cfg, 0)
+    ref = oracle.tree_attention(bf16_bits_to_f64(q).reshape(n, Hq, d), bf16_bits_to_f64(kt).reshape(n, Hkv, d),
+                                bf16_bits_to_f64(vt).reshape(n, Hkv, d), oracle.bf16_to_f64(kp),
+                                oracle.bf16_to_f64(vp), parent)
+    err = row_rel_err(bf16_bits_to_f64(out_p).reshape(n * Hq, d), ref.reshape(n * Hq, d))
+    say("  %d pages of %d, max row rel err %.3e" % (NL, NP, err.max()))
+    assert err.max() < TOL

@@ -47,6 +47,14 @@ class lucev_kv(ctypes.Structure):
     _fields_ = [("k", c_vp), ("v", c_vp), ("prefix_len", c_i32), ("capacity", c_i32)]
 
 
+class lucev_kv_paged(ctypes.Structure):
+    _fields_ = [("k_pages", c_vp), ("v_pages", c_vp), ("block_table", c_vp), ("n_pages", c_i32),
+                ("prefix_len", c_i32)]
+
+
+PAGE_TOKENS = 16
+
+
 class lucev_tree(ctypes.Structure):
     _fields_ = [("n", c_i32), ("parent", c_i32 * MAX_NODES), ("token", c_i32 * MAX_NODES)]
 
@@ -92,6 +100,9 @@ def lib() -> ctypes.CDLL:
         L.lucev_accept_path.restype = c_i32
         L.lucev_accept_path.argtypes = [P(lucev_shape), P(lucev_head_w), P(lucev_tree), c_vp,
                                         c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]
+        L.lucev_tree_attention_paged.restype = c_i32
+        L.lucev_tree_attention_paged.argtypes = [P(lucev_shape), P(lucev_tree), P(lucev_kv_paged), c_vp,
+                                                 c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]
         L.lucev_project_logits.restype = c_i32
         L.lucev_project_logits.argtypes = [P(lucev_shape), P(lucev_head_w), c_i32, c_vp, c_vp, c_vp,
                                            c_vp, c_vp, c_sz, c_vp]
@@ -105,7 +116,7 @@ def lib() -> ctypes.CDLL:
 EXPORTED = ["lucev_abi_version", "lucev_status_str", "lucev_last_error",
             "lucev_q4_packed_bytes", "lucev_q4_pack", "lucev_q4_pack_device",
             "lucev_workspace_bytes", "lucev_workspace_init", "lucev_verify_layer",
-            "lucev_tree_attention", "lucev_accept_path", "lucev_project_logits",
+            "lucev_tree_attention", "lucev_tree_attention_paged", "lucev_accept_path", "lucev_project_logits",
             "lucev_commit_path"]
 
 
@@ -200,6 +211,17 @@ def lucev_tree_attention(shape, tree, kv, q, k_tree, v_tree, out, ws, ws_bytes, 
     _check(lib().lucev_tree_attention(ctypes.byref(shape), ctypes.byref(tree), ctypes.byref(kv),
                                       _ptr(q), _ptr(k_tree), _ptr(v_tree), _ptr(out), _ptr(ws),
                                       ws_bytes, stream), "lucev_tree_attention")
+
+
+def make_kv_paged(k_pages, v_pages, block_table, n_pages: int, prefix_len: int) -> lucev_kv_paged:
+    return lucev_kv_paged(_ptr(k_pages), _ptr(v_pages), _ptr(block_table), n_pages, prefix_len)
+
+
+def lucev_tree_attention_paged(shape, tree, kv, q, k_tree, v_tree, out, ws, ws_bytes,
+                               stream=None) -> None:
+    _check(lib().lucev_tree_attention_paged(ctypes.byref(shape), ctypes.byref(tree), ctypes.byref(kv),
+                                            _ptr(q), _ptr(k_tree), _ptr(v_tree), _ptr(out), _ptr(ws),
+                                            ws_bytes, stream), "lucev_tree_attention_paged")
 
 
 def lucev_accept_path(shape, w, tree, resid, logits_out, argmax_out, gap_out, path_out,

@@ -214,8 +214,11 @@ EpiArgs epi_blank() {
 int run_attention(const lucev_shape* s, const TreeArgs& t, const lucev_kv* kv, const uint16_t* q,
                   const uint16_t* k_tree, const uint16_t* v_tree, const float* q32,
                   const float* k32, const float* v32, uint16_t* out, int out_hilo, void* ws,
-                  const Ws& L, hipStream_t st) {
+                  const Ws& L, hipStream_t st, const int32_t* table = nullptr, int n_phys = 0) {
   AttnPlan plan = plan_attention(t.n, s->n_q_heads, s->n_kv_heads, s->head_dim, kv->prefix_len);
+  if (table && plan.chunk / kPageTokens > kMaxChunkPagesHost)
+    return fail(LUCEV_ERR_BAD_KV, "paged attention: %d-token prefix chunks exceed %d pages", plan.chunk,
+                kMaxChunkPagesHost);
   AttnParams p;
   p.q = q;
   p.q32 = q32;
@@ -231,6 +234,8 @@ int run_attention(const lucev_shape* s, const TreeArgs& t, const lucev_kv* kv, c
   p.rows = plan.rows;
   p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)s->head_dim));
   p.o_part = at<float>(ws, L.opart);
+  p.table = table;
+  p.n_phys = n_phys;
   p.ml_part = at<float>(ws, L.ml);
   CombineParams c;
   c.q = q;
@@ -370,6 +375,37 @@ int lucev_tree_attention(const lucev_shape* shape, const lucev_tree* tree, const
   if ((rc = check_device())) return rc;
   return run_attention(shape, t, kv, q, k_tree, v_tree, nullptr, nullptr, nullptr, out, 0, ws, L,
                        (hipStream_t)stream);
+}
+
+int lucev_tree_attention_paged(const lucev_shape* shape, const lucev_tree* tree,
+                               const lucev_kv_paged* kv, const uint16_t* q, const uint16_t* k_tree,
+                               const uint16_t* v_tree, uint16_t* out, void* ws, size_t ws_bytes,
+                               void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (!kv || !q || !k_tree || !v_tree || !out)
+    return fail(LUCEV_ERR_NULL_ARG, "tree_attention_paged: NULL argument");
+  if (kv->prefix_len < 0 || kv->n_pages < 0 || (kv->prefix_len > 0 && kv->n_pages < 1))
+    return fail(LUCEV_ERR_BAD_KV, "tree_attention_paged: prefix_len %d, n_pages %d", kv->prefix_len,
+                kv->n_pages);
+  if (kv->prefix_len > 0 && (!kv->k_pages || !kv->v_pages || !kv->block_table))
+    return fail(LUCEV_ERR_NULL_ARG, "tree_attention_paged: NULL page pool or block table");
+  if (!aligned16(kv->k_pages) || !aligned16(kv->v_pages) || !aligned16(q) || !aligned16(k_tree) ||
+      !aligned16(v_tree) || !aligned16(out))
+    return fail(LUCEV_ERR_ALIGN, "tree_attention_paged: tensors must be 16-byte aligned");
+  TreeArgs t;
+  if ((rc = prep_tree(tree, shape->vocab, kv->prefix_len, &t))) return rc;
+  Ws L;
+  if ((rc = check_ws(shape, t.n, kv->prefix_len, ws, ws_bytes, &L))) return rc;
+  if ((rc = check_device())) return rc;
+  // the pool stands in for the contiguous cache; the table supplies every address
+  lucev_kv flat;
+  flat.k = kv->k_pages;
+  flat.v = kv->v_pages;
+  flat.prefix_len = kv->prefix_len;
+  flat.capacity = 0;
+  return run_attention(shape, t, &flat, q, k_tree, v_tree, nullptr, nullptr, nullptr, out, 0, ws, L,
+                       (hipStream_t)stream, kv->prefix_len > 0 ? kv->block_table : nullptr, kv->n_pages);
 }
 
 int lucev_verify_layer(const lucev_shape* shape, const lucev_layer_w* w, const lucev_tree* tree,

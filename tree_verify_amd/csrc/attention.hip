@@ -26,6 +26,7 @@
 namespace lucev {
 
 constexpr int KT = 64;  // tokens per LDS tile
+constexpr int kMaxChunkPages = 1024;  // 16-token pages of one block's prefix chunk (paged cache)
 
 // Waves per block for a query-tile count and tiles per wave.
 constexpr int attn_max_waves(int qpw) { return qpw == 1 ? 12 : 8; }
@@ -51,7 +52,14 @@ constexpr int attn_max_waves(int qpw) { return qpw == 1 ? 12 : 8; }
 // are merged through LDS at the end.  The quarter's PV product is a
 // 16x16x16 MFMA, whose B operand (4 keys per lane) is exactly the layout the
 // 16-key score tile comes out in.
-template <int D, int QPW, bool QLO, bool SPLIT>
+//
+// PAGED: the prefix lives in 16-token pages, K as [page][Hkv][16][d] and V as
+// [page][Hkv][d][16], and table[t / 16] names the page holding token t.  Only
+// the global addresses of the tile loads change (a 1 KB K load covers 4 keys
+// of one page; a 16-byte V chunk covers 8 tokens of one page), so the LDS
+// tiles, and hence the results, are those of the contiguous cache.  The
+// block's slice of the table is copied into LDS first, clamped to the pool.
+template <int D, int QPW, bool QLO, bool SPLIT, bool PAGED = false>
 __global__ __launch_bounds__(attn_max_waves(QPW) * 64) void attn_partial_kernel(AttnParams p) {
   static_assert(!SPLIT || QPW == 1, "split tiles use one query tile per wave");
   constexpr int WAVES = attn_max_waves(QPW);
@@ -64,6 +72,7 @@ __global__ __launch_bounds__(attn_max_waves(QPW) * 64) void attn_partial_kernel(
   constexpr int BUF = KBYTES + VBYTES;
   constexpr int MERGE = SPLIT ? 4 * 16 * D * 4 + 2 * 64 * 4 : 0;  // quarter states
   __shared__ __attribute__((aligned(1024))) uint8_t lds[3 * BUF + 1024 + MERGE];
+  __shared__ int s_tab[PAGED ? kMaxChunkPages : 1];
 
   const int tid = threadIdx.x;
   // the wave index as a scalar: every branch on it is then a scalar branch
@@ -86,7 +95,7 @@ __global__ __launch_bounds__(attn_max_waves(QPW) * 64) void attn_partial_kernel(
   // Load j of a tile (j < NLD): K rows for j < KBYTES / 1024, else V^T rows.
   // This lane's global element offset at token 0 and its LDS byte offset.
   // (offsets within a tile's K rows or V^T rows: below D * cap < 2^31)
-  auto load_slot = [&](int j, int& goff, int& loff, int& tok, bool& is_v) {
+  auto load_slot = [&](int j, int& goff, int& loff, int& tok, bool& is_v, int& row, int& cofs) {
     if (j < KBYTES / 1024) {
       const int key = j * KROWS + lane / KCPR, pc = lane % KCPR;
       const int sw = ((key & 3) | (((key >> 3) & 3) << 2)) & (KCPR - 1);
@@ -94,12 +103,16 @@ __global__ __launch_bounds__(attn_max_waves(QPW) * 64) void attn_partial_kernel(
       loff = j * 1024;
       tok = key;
       is_v = false;
+      row = key;
+      cofs = (pc ^ sw) * 8;
     } else {
       const int dim = (j - KBYTES / 1024) * 8 + lane / 8, pc = lane % 8;
       goff = dim * p.cap + (pc ^ ((dim >> 1) & 7)) * 8;
       loff = j * 1024;
       tok = (pc ^ ((dim >> 1) & 7)) * 8;
       is_v = true;
+      row = dim;
+      cofs = 0;
     }
   };
   // issue this wave's loads of tile t (clamped to the last tile) into buffer b
@@ -111,10 +124,20 @@ __global__ __launch_bounds__(attn_max_waves(QPW) * 64) void attn_partial_kernel(
       const int j = wave + r * WAVES;
       uint8_t* dst = lds + (j < NLD ? b * BUF + j * 1024 : 3 * BUF);  // past NLD: scratch area
       int goff = 0;
-      int loff = 0, tok = 0;
+      int loff = 0, tok = 0, row = 0, cofs = 0;
       bool is_v = false;
-      if (j < NLD) load_slot(j, goff, loff, tok, is_v);
-      const uint16_t* src = j < NLD ? (is_v ? vbase + goff + k0 : kbase + goff + (int64_t)k0 * D) : kbase;
+      if (j < NLD) load_slot(j, goff, loff, tok, is_v, row, cofs);
+      const uint16_t* src;
+      if constexpr (PAGED) {
+        // token of the chunk this lane's 16 bytes start at, and its page
+        const int tic = k0 - k_begin + tok;
+        const int64_t pg = s_tab[tic >> 4];
+        src = j >= NLD ? p.kc
+              : !is_v ? p.kc + ((pg * p.n_kv_heads + g) * 16 + (tic & 15)) * D + cofs
+                      : p.vc + ((pg * p.n_kv_heads + g) * D + row) * 16 + (tic & 15);
+      } else {
+        src = j < NLD ? (is_v ? vbase + goff + k0 : kbase + goff + (int64_t)k0 * D) : kbase;
+      }
       if (!ragged || j >= NLD) {
         __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
       } else {
@@ -363,6 +386,13 @@ __global__ __launch_bounds__(attn_max_waves(QPW) * 64) void attn_partial_kernel(
       compute(buf, k0, std::integral_constant<bool, true>());
   };
 
+  if constexpr (PAGED) {
+    // the pages of this chunk's tiles (entries past the prefix: page 0, never read)
+    const int pg0 = k_begin >> 4, npg = (k_end - k_begin + 15) >> 4;
+    for (int i = tid; i < n_tiles * (KT / 16); i += WAVES * 64)
+      s_tab[i] = i < npg ? min(max(p.table[pg0 + i], 0), p.n_phys - 1) : 0;
+    __syncthreads();
+  }
   if (n_tiles > 0) {
     issue(0, 0);
     issue(1, 1);
@@ -632,7 +662,10 @@ AttnPlan plan_attention(int n_nodes, int n_q_heads, int n_kv_heads, int head_dim
 
 template <int D, int QPW, bool SPLIT>
 static void launch_partial3(const AttnPlan& plan, const AttnParams& p, hipStream_t s) {
-  if (p.q32)
+  if (p.table)
+    hipLaunchKernelGGL((attn_partial_kernel<D, QPW, false, SPLIT, true>), dim3(plan.n_chunks, p.n_kv_heads),
+                       dim3(64 * attn_max_waves(QPW)), 0, s, p);
+  else if (p.q32)
     hipLaunchKernelGGL((attn_partial_kernel<D, QPW, true, SPLIT>), dim3(plan.n_chunks, p.n_kv_heads),
                        dim3(64 * attn_max_waves(QPW)), 0, s, p);
   else

@@ -118,7 +118,11 @@ struct AttnParams {
   float scale_log2;    // log2(e) / sqrt(d)
   float* o_part;       // fp32 [n_chunks][Hkv][rows][d], normalised per chunk
   float* ml_part;      // fp32 [n_chunks][Hkv][rows][2]: (max, sum) in log2 units
+  const int32_t* table;  // paged cache: page of each 16 prefix tokens, or NULL (contiguous)
+  int n_phys;            // pages in the pool (paged cache)
 };
+constexpr int kPageTokens = 16;
+constexpr int kMaxChunkPagesHost = 1024;  // pages of one block's prefix chunk
 
 struct CombineParams {
   const uint16_t* q;       // bf16 inputs, used when the fp32 ones are NULL
