@@ -184,6 +184,45 @@ def chained(r, cfg, tv, steps, dev):
                     "committed = accepted drafts + the bonus token" % cfg.p_accept}
 
 
+def paged_leg(r, cfg, tv, shape, tree, q, out, dev, reps, layers=4):
+    """The same one-layer tree attention over a paged prefix: the first
+    `layers` layers' caches re-laid into a shuffled pool of 16-token pages
+    (set-up, not timed), launches rotating over them so the last-level cache
+    does not serve repeats; HIP events on the launch stream."""
+    import numpy as np
+    import torch
+    Hkv, d, P = cfg.n_kv_heads, cfg.head_dim, cfg.prefix
+    NL = (P + 15) // 16
+    L = min(layers, cfg.layers)
+    pools = []
+    for l in range(L):
+        k, v = r.layers[l]["k"], r.layers[l]["v"]
+        perm = torch.from_numpy(np.random.default_rng(cfg.seed + l).permutation(NL).astype(np.int64)).to(dev)
+        kp = torch.empty(NL, Hkv, 16, d, dtype=torch.int16, device=dev)
+        vp = torch.empty(NL, Hkv, d, 16, dtype=torch.int16, device=dev)
+        kp[perm] = k[:, :NL * 16, :].reshape(Hkv, NL, 16, d).permute(1, 0, 2, 3)
+        vp[perm] = v[:, :, :NL * 16].reshape(Hkv, d, NL, 16).permute(2, 0, 1, 3)
+        pools.append((kp, vp, perm.to(torch.int32).contiguous()))
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        st = stream.cuda_stream
+        kvs = [tv.make_kv_paged(kp, vp, tab, NL, P) for kp, vp, tab in pools]
+        for i in range(3):
+            tv.lucev_tree_attention_paged(shape, tree, kvs[i % L], q, r.k_tree[0], r.v_tree[0], out, r.ws,
+                                          r.ws_bytes, st)
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        for i in range(reps):
+            tv.lucev_tree_attention_paged(shape, tree, kvs[i % L], q, r.k_tree[0], r.v_tree[0], out, r.ws,
+                                          r.ws_bytes, st)
+        a1.record(stream)
+    torch.cuda.synchronize()
+    us = a0.elapsed_time(a1) / reps * 1e3
+    del pools
+    return us
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -278,6 +317,9 @@ def main():
     ab = attention_bytes(cfg, n)
     attn_gbs = ab / (attn_ms * 1e-3) / 1e9
     log("tree attention (one layer): %.2f us, %.1f GB/s" % (attn_ms * 1e3, attn_gbs))
+    paged_us = paged_leg(r, cfg, tv, shape, tree, q, out, dev, args.attn_reps) if cfg.prefix > 0 else None
+    if paged_us:
+        log("paged tree attention (one layer): %.2f us, %.1f GB/s" % (paged_us, ab / (paged_us * 1e-6) / 1e9))
 
     line = {
         "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
@@ -295,6 +337,12 @@ def main():
                      "bytes_per_launch": ab, "avg_launch_us": round(attn_ms * 1e3, 3)},
         "step_roofline_frac": round(gbs / HBM_PEAK_GBS, 4),
     }
+    if paged_us:
+        line["paged_attention"] = {"avg_launch_us": round(paged_us, 3),
+                                   "gbs": round(ab / (paged_us * 1e-6) / 1e9, 2),
+                                   "vs_contiguous": round(attn_ms * 1e3 / paged_us, 4),
+                                   "what": "lucev_tree_attention_paged, the prefix in a shuffled pool of "
+                                           "16-token pages, rotating over 4 layers' pools"}
     if args.chain > 0:
         del graph
         line["chained"] = chained(r, cfg, tv, args.chain, dev)
