@@ -188,7 +188,8 @@ def paged_leg(r, cfg, tv, shape, tree, q, out, dev, reps, layers=4):
     """The same one-layer tree attention over a paged prefix: the first
     `layers` layers' caches re-laid into a shuffled pool of 16-token pages
     (set-up, not timed), launches rotating over them so the last-level cache
-    does not serve repeats; HIP events on the launch stream."""
+    does not serve repeats, replayed from a graph and timed with HIP events
+    on the launch stream."""
     import numpy as np
     import torch
     Hkv, d, P = cfg.n_kv_heads, cfg.head_dim, cfg.prefix
@@ -211,13 +212,18 @@ def paged_leg(r, cfg, tv, shape, tree, q, out, dev, reps, layers=4):
         for i in range(3):
             tv.lucev_tree_attention_paged(shape, tree, kvs[i % L], q, r.k_tree[0], r.v_tree[0], out, r.ws,
                                           r.ws_bytes, st)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(reps):
+                tv.lucev_tree_attention_paged(shape, tree, kvs[i % L], q, r.k_tree[0], r.v_tree[0], out,
+                                              r.ws, r.ws_bytes, stream.cuda_stream)
+        g.replay()
         a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a0.record(stream)
-        for i in range(reps):
-            tv.lucev_tree_attention_paged(shape, tree, kvs[i % L], q, r.k_tree[0], r.v_tree[0], out, r.ws,
-                                          r.ws_bytes, st)
+        g.replay()
         a1.record(stream)
     torch.cuda.synchronize()
+    del g
     us = a0.elapsed_time(a1) / reps * 1e3
     del pools
     return us
@@ -305,14 +311,21 @@ def main():
         for _ in range(3):
             tv.lucev_tree_attention(shape, tree, kv0, q, r.k_tree[0], r.v_tree[0], out, r.ws,
                                     r.ws_bytes, st)
+        # the timed launches are replayed from a graph, so host-side call
+        # overhead cannot open gaps between them
+        ag = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(ag, stream=astream):
+            for i in range(args.attn_reps):
+                kvi = r.kv(i % cfg.layers, cfg.prefix)
+                tv.lucev_tree_attention(shape, tree, kvi, q, r.k_tree[0], r.v_tree[0], out, r.ws,
+                                        r.ws_bytes, astream.cuda_stream)
+        ag.replay()
         a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a0.record(astream)
-        for i in range(args.attn_reps):
-            kvi = r.kv(i % cfg.layers, cfg.prefix)
-            tv.lucev_tree_attention(shape, tree, kvi, q, r.k_tree[0], r.v_tree[0], out, r.ws,
-                                    r.ws_bytes, st)
+        ag.replay()
         a1.record(astream)
     torch.cuda.synchronize()
+    del ag
     attn_ms = a0.elapsed_time(a1) / args.attn_reps
     ab = attention_bytes(cfg, n)
     attn_gbs = ab / (attn_ms * 1e-3) / 1e9

@@ -463,7 +463,9 @@ int gemm_ntx(int n_nodes) { return (2 * n_nodes + 15) / 16; }
 // registers hold two groups' weights beside the accumulators of ntx tiles
 // (one-group units measured slower inside the verify step, also for the
 // projections whose weights spread thinly over the blocks)
-int gemm_ug(int kgroups, int ntx) { return (kgroups % 2 == 0 && ntx <= 3) ? 2 : 1; }
+// (two groups per unit measured slower with one tile per wave; kept for
+// other tilings)
+int gemm_ug(int kgroups, int ntx) { return (kGemmFT > 1 && kgroups % 2 == 0 && ntx <= 3) ? 2 : 1; }
 
 GemmPlan plan_gemm(int64_t n_out, int64_t k_in, int n_nodes) {
   GemmPlan g;
