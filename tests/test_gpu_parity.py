@@ -413,3 +413,45 @@ def test_tree_attention_paged_equals_contiguous(case):
     err = row_rel_err(bf16_bits_to_f64(out_p).reshape(n * Hq, d), ref.reshape(n * Hq, d))
     say("  %d pages of %d, max row rel err %.3e" % (NL, NP, err.max()))
     assert err.max() < TOL
+
+
+# Graph replays of a 27B-class layer + head step, each checked bit for bit
+# against the first.  Direct-to-LDS loads from several waves writing the same
+# LDS bytes (surplus loads sent to one shared pad) made about one replay in
+# three differ; every wave now has its own pad.
+def test_graph_replays_bit_identical_27b_layer():
+    torch = need_gpu()
+    import tree_verify_amd as tv
+    from tree_verify_amd.runner import VerifyRunner
+    import synth.device as sd
+    cfg = synth.get("layer27b")
+    seed = cfg.seed
+    say("case layer27b graph replays, seed", seed)
+    wl = sd.Workload(cfg, seed, "cuda")
+    shape = tv.make_shape(cfg.hidden, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ffn,
+                          cfg.vocab, cfg.rms_eps, cfg.rope_base)
+    r = VerifyRunner(shape, wl.layers, wl.head, cfg.nodes, wl.capacity, "cuda")
+    parent = synth.tree_parents(cfg, seed)
+    tree = tv.make_tree(parent, [0] * cfg.nodes)
+    x = wl.x_in_f32().contiguous()
+    hid = [torch.zeros(cfg.nodes, cfg.hidden, dtype=torch.float32, device="cuda")]
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        r.step(tree, x, cfg.prefix, hidden_out=hid)
+        stream.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            r.step(tree, x, cfg.prefix, hidden_out=hid)
+    torch.cuda.synchronize()
+    first = None
+    for rep in range(12):
+        with torch.cuda.stream(stream):
+            g.replay()
+            stream.synchronize()
+        cur = (hid[0].cpu().numpy().copy(), r.k_tree[0].cpu().numpy().copy(), r.logits.cpu().numpy().copy())
+        if first is None:
+            first = cur
+        else:
+            for a, b in zip(first, cur):
+                assert np.array_equal(a, b), "replay %d differs from the first" % rep

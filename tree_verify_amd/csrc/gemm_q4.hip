@@ -161,12 +161,23 @@ __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rsrc, u
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
 }
 
+// the smallest multiple of 16 rows >= rows whose slice (rows x rb bytes) is a
+// multiple of `waves` 1 KB loads
+constexpr int stage_rows(int rows, int rb, int waves) {
+  int r = rows;
+  while ((r * rb) % (1024 * waves) != 0) r += 16;
+  return r;
+}
+
 template <int WAVES, int FT, int NTX, int UG, bool EXACT>
 __global__ __launch_bounds__(WAVES * 64, 2) void gemm_q4_kernel(GemmParams p) {
   constexpr int NTH = WAVES * 64;
   constexpr int PT = WAVES * FT;   // tiles per panel
   constexpr int TILE_F = PT * 16;
-  constexpr int XR = NTX * 16;     // staged hi/lo rows
+  // staged hi/lo rows: whole row tiles, rounded up (extra tiles re-read row
+  // 0 and are never used) so a slice is a whole number of 1 KB loads per
+  // wave: no wave issues a load past the slice's last
+  constexpr int XR = stage_rows(NTX * 16, UG * 256, WAVES);
   constexpr int RB = UG * 256;     // bytes of a staged row (UG * 128 fp16)
   constexpr int XBUF = XR * RB;    // bytes of one staged slice
   constexpr int XI = XBUF / 1024;  // 1 KB direct-to-LDS loads per slice
@@ -463,9 +474,7 @@ int gemm_ntx(int n_nodes) { return (2 * n_nodes + 15) / 16; }
 // registers hold two groups' weights beside the accumulators of ntx tiles
 // (one-group units measured slower inside the verify step, also for the
 // projections whose weights spread thinly over the blocks)
-// (two groups per unit measured slower with one tile per wave; kept for
-// other tilings)
-int gemm_ug(int kgroups, int ntx) { return (kGemmFT > 1 && kgroups % 2 == 0 && ntx <= 3) ? 2 : 1; }
+int gemm_ug(int kgroups, int ntx) { return (kgroups % 2 == 0 && ntx <= 3) ? 2 : 1; }
 
 GemmPlan plan_gemm(int64_t n_out, int64_t k_in, int n_nodes) {
   GemmPlan g;

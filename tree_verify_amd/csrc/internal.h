@@ -14,11 +14,8 @@ enum { W_PLAIN = 0, W_QKV = 1, W_GU = 2 };  // same values as LUCEV_W_*
 #ifndef LUCEV_GEMM_WAVES
 #define LUCEV_GEMM_WAVES 8
 #endif
-// One 16-row tile per wave (128-row panels) and one 128-column group per
-// unit: measured 3-5% faster per step than two tiles and two groups, whose
-// larger units left the last blocks of the small projections a unit behind.
 #ifndef LUCEV_GEMM_FT
-#define LUCEV_GEMM_FT 1
+#define LUCEV_GEMM_FT 2
 #endif
 #ifndef LUCEV_GEMM_BPC
 #define LUCEV_GEMM_BPC 1
