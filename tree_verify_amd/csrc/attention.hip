@@ -35,8 +35,9 @@ constexpr int attn_max_waves(int qpw) { return qpw == 1 ? 12 : 8; }
 // past the last query tile only load).  K and V^T tiles of 64 tokens go
 // straight from HBM into a ring of three LDS buffers with 16-byte
 // direct-to-LDS loads, two tiles ahead of the MFMAs; every wave issues the
-// same number of them per tile (padded with loads into a scratch area), so a
-// fixed vmcnt wait plus one barrier per tile publishes a tile.  A load
+// same number of them per tile (one less for the waves past the tile's last
+// load), so a fixed per-wave vmcnt wait plus one barrier per tile publishes a
+// tile.  A load
 // instruction fills 1 KB of LDS, 16 bytes per lane in lane order, so the bank
 // swizzles are applied on the global side: LDS chunk c of K row `key` holds
 // the row's 16-byte chunk c ^ ((key & 3) | ((key >> 3) & 3) << 2), and chunk
@@ -71,7 +72,7 @@ __global__ __launch_bounds__(attn_max_waves(QPW) * 64) void attn_partial_kernel(
   constexpr int LPW = (NLD + WAVES - 1) / WAVES;  // loads per wave per tile
   constexpr int BUF = KBYTES + VBYTES;
   constexpr int MERGE = SPLIT ? 4 * 16 * D * 4 + 2 * 64 * 4 : 0;  // quarter states
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[3 * BUF + 1024 + MERGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[3 * BUF + MERGE];
   __shared__ int s_tab[PAGED ? kMaxChunkPages : 1];
 
   const int tid = threadIdx.x;
@@ -122,7 +123,11 @@ __global__ __launch_bounds__(attn_max_waves(QPW) * 64) void attn_partial_kernel(
 #pragma unroll
     for (int r = 0; r < LPW; ++r) {
       const int j = wave + r * WAVES;
-      uint8_t* dst = lds + (j < NLD ? b * BUF + j * 1024 : 3 * BUF);  // past NLD: scratch area
+      // no load past the tile's last (surplus direct-to-LDS loads from
+      // several waves into one shared scratch area made GEMM replays differ;
+      // here such a wave simply waits for one load less, below)
+      if (j >= NLD) continue;
+      uint8_t* dst = lds + b * BUF + j * 1024;
       int goff = 0;
       int loff = 0, tok = 0, row = 0, cofs = 0;
       bool is_v = false;
@@ -397,7 +402,12 @@ __global__ __launch_bounds__(attn_max_waves(QPW) * 64) void attn_partial_kernel(
     issue(0, 0);
     issue(1, 1);
     for (int t = 0; t < n_tiles; ++t) {
-      wait_vmcnt<LPW>();  // this wave's part of tile t has landed
+      // this wave's part of tile t has landed (only tile t + 1's loads, LPW
+      // or LPW - 1 of them, may still be in flight)
+      if (wave < NLD - (LPW - 1) * WAVES)
+        wait_vmcnt<LPW>();
+      else
+        wait_vmcnt<LPW - 1>();
       lds_barrier();      // every part has; every wave is done with tile t - 1
       issue(t + 2, (t + 2) % 3);
       compute_tile(t % 3, t);
@@ -428,7 +438,7 @@ __global__ __launch_bounds__(attn_max_waves(QPW) * 64) void attn_partial_kernel(
 
   if constexpr (SPLIT) {
     // merge the four quarter states of tile FT: O = sum_q 2^(m_q - M) O_q / L
-    float* sO = reinterpret_cast<float*>(lds + 3 * BUF + 1024);  // [4][16][D]
+    float* sO = reinterpret_cast<float*>(lds + 3 * BUF);  // [4][16][D]
     float* sm = sO + 4 * 16 * D;                                 // [4][16]
     float* sl = sm + 64;
     __syncthreads();  // (also: every wave is done with the tile ring)
