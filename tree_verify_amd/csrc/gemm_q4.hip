@@ -152,17 +152,15 @@ struct WRegs {
   u32x2 s[UG][FT];  // the row's 4 block scales
 };
 
-// 16-byte buffer load straight into LDS: this lane's bytes land at
-// lds + 16 * lane.  (A function of its own: called from a lambda inside the
-// kernel template, the builtin keeps the host pass from emitting the
-// kernel's launch stub.)
-__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rsrc, uint8_t* lds, uint32_t voff,
-                                                  uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+// 16-byte buffer load into registers.  (A function of its own: called from a
+// lambda inside the kernel template, the builtin keeps the host pass from
+// emitting the kernel's launch stub.)
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, soff, 0));
 }
 
 // the smallest multiple of 16 rows >= rows whose slice (rows x rb bytes) is a
-// multiple of `waves` 1 KB loads
+// multiple of `waves` 1 KB pieces
 constexpr int stage_rows(int rows, int rb, int waves) {
   int r = rows;
   while ((r * rb) % (1024 * waves) != 0) r += 16;
@@ -175,24 +173,21 @@ __global__ __launch_bounds__(WAVES * 64, 2) void gemm_q4_kernel(GemmParams p) {
   constexpr int PT = WAVES * FT;   // tiles per panel
   constexpr int TILE_F = PT * 16;
   // staged hi/lo rows: whole row tiles, rounded up (extra tiles re-read row
-  // 0 and are never used) so a slice is a whole number of 1 KB loads per
-  // wave: no wave issues a load past the slice's last
+  // 0 and are never used) so a slice is the same whole number of 1 KB
+  // pieces for every wave
   constexpr int XR = stage_rows(NTX * 16, UG * 256, WAVES);
   constexpr int RB = UG * 256;     // bytes of a staged row (UG * 128 fp16)
   constexpr int XBUF = XR * RB;    // bytes of one staged slice
-  constexpr int XI = XBUF / 1024;  // 1 KB direct-to-LDS loads per slice
-  constexpr int XIW = (XI + WAVES - 1) / WAVES;  // of them per wave
+  constexpr int XI = XBUF / 1024;  // 1 KB pieces per slice (16 bytes a lane)
+  constexpr int XIW = XI / WAVES;  // of them per wave
   constexpr int TILE_N = NTX * 8;  // nodes
   constexpr int TILE = TILE_F * TILE_N;
-  static_assert(XBUF % 1024 == 0, "a staged slice is whole 1 KB loads");
-  // three slice buffers as separate arrays: the compiler can then tell a
-  // direct-to-LDS load into one from operand reads of another, and does not
-  // wait for it
+  static_assert(XI % WAVES == 0, "a staged slice is whole 1 KB pieces per wave");
+  // three slice buffers as separate arrays: the compiler can then tell the
+  // stores into one from the operand reads of another
   __shared__ __attribute__((aligned(1024))) uint8_t sx0[XBUF];
   __shared__ __attribute__((aligned(1024))) uint8_t sx1[XBUF];
   __shared__ __attribute__((aligned(1024))) uint8_t sx2[XBUF];
-  // target of a wave's loads past a slice's last (every wave issues XIW)
-  __shared__ __attribute__((aligned(1024))) uint8_t sx_pad[XI % WAVES ? 1024 : 16];
   __shared__ float tile[TILE_F][TILE_N + 1];
 
   const int tid = threadIdx.x;
@@ -243,19 +238,19 @@ __global__ __launch_bounds__(WAVES * 64, 2) void gemm_q4_kernel(GemmParams p) {
 #pragma unroll
       for (int ft = 0; ft < FT; ++ft) wload_one(k, r, g, ft);
   };
-  // Activation slice of a unit: XR rows x UG * 128 columns, loaded straight
-  // into LDS (16 bytes a lane, 1 KB a wave instruction, no registers).  A
-  // load fills RB-byte rows in lane order; the lane at 16-byte position p of
-  // row r fetches chunk p ^ (r % 16) of that row, so chunk c of row r sits at
+  // Activation slice of a unit: XR rows x UG * 128 columns, loaded into
+  // registers (16 bytes a lane, 1 KB a wave instruction) one step before it
+  // is stored to LDS, the step before the unit's own.  A 1 KB piece fills
+  // RB-byte rows in lane order; the lane at 16-byte position p of row r
+  // fetches chunk p ^ (r % 16) of that row, so chunk c of row r sits at
   // position c ^ (r % 16) and the MFMA operand reads (16 rows, one chunk)
   // fall in 16 different bank groups.  Rows past the 2n operand rows re-read
   // row 0: they only feed accumulator rows of padding nodes, which no
-  // epilogue or consumer reads.  A wave's loads past the slice's last go to a
-  // pad area nothing reads.
-  uint32_t x_off[XIW];  // bytes from the slice's first column, per load of this wave
+  // epilogue or consumer reads.
+  uint32_t x_off[XIW];  // bytes from the slice's first column, per piece of this wave
 #pragma unroll
   for (int q = 0; q < XIW; ++q) {
-    const int ins = min(wave + WAVES * q, XI - 1);
+    const int ins = wave + WAVES * q;
     const int row = ins * (1024 / RB) + lane / (RB / 16);
     const int pos = lane % (RB / 16);
     const int src_row = row < 2 * nn ? row : 0;
@@ -267,13 +262,18 @@ __global__ __launch_bounds__(WAVES * 64, 2) void gemm_q4_kernel(GemmParams p) {
   // range is the operand rows, so a stray offset reads zeros.
   const __amdgpu_buffer_rsrc_t x_rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)p.X, (short)0, (int)(2 * nn * K * 2), 0x00020000);
-  auto xload = [&](Cur k, uint8_t* dst) {
+  struct XRegs {
+    u32x4 v[XIW];
+  };
+  auto xload = [&](Cur k, XRegs& xr) {
     const uint32_t col_bytes = (uint32_t)(k.c * UG * 256);
 #pragma unroll
-    for (int q = 0; q < XIW; ++q) {
-      const int ins = wave_s + WAVES * q;
-      buffer_load_lds16(x_rsrc, ins < XI ? dst + ins * 1024 : sx_pad, x_off[q], col_bytes);
-    }
+    for (int q = 0; q < XIW; ++q) xr.v[q] = buffer_load16(x_rsrc, x_off[q], col_bytes);
+  };
+  auto xstore = [&](const XRegs& xr, uint8_t* dst) {
+#pragma unroll
+    for (int q = 0; q < XIW; ++q)
+      *reinterpret_cast<u32x4*>(dst + (wave_s + WAVES * q) * 1024 + lane * 16) = xr.v[q];
   };
 
   f32x4 acc[FT][NTX];
@@ -367,18 +367,19 @@ __global__ __launch_bounds__(WAVES * 64, 2) void gemm_q4_kernel(GemmParams p) {
     lds_barrier();  // the LDS tile is reused by the next panel
   };
 
-  // One unit u: load the activation slice of unit u + 2 into the LDS buffer
-  // unit u - 1 used (which every wave has finished), MFMA unit u while
-  // loading the weights of unit u + 2 into the register slot unit u - 1 used,
-  // wait for this wave's part of the slice of unit u + 1 (loaded one unit
-  // earlier; only the loads issued after it may still be in flight), and
-  // finish the panel when u ends a segment.  Unit u uses slice buffer and
-  // weight slot u % 3 (counted from the block's first unit).  Prefetches past
-  // the block's last unit re-read that unit, so every path issues the same
-  // loads.
+  // One unit u: load the activation slice of unit u + 2 into registers, MFMA
+  // unit u (its slice in LDS) while loading the weights of unit u + 2 into
+  // the register slot unit u - 1 used, store the slice of unit u + 1 (loaded
+  // one step earlier) into the LDS buffer unit u - 2 used, which every wave
+  // has finished, and finish the panel when u ends a segment.  Unit u uses
+  // slice buffer, slice registers and weight slot u % 3 (counted from the
+  // block's first unit).  The compiler waits for each register load where
+  // its value is used.  Prefetches past the block's last unit re-read that
+  // unit, so every path issues the same loads.
   const int64_t u_last = u_end - 1;
   if (u_begin < u_end) {
     WRegs<UG, FT> r0, r1, r2;
+    XRegs x0, x1, x2;
     Cur pf = cur_of(u_begin);  // next unit to prefetch
     int64_t pf_u = u_begin;
     // (selects, not branches: with a branch the compiler may reuse an earlier
@@ -391,30 +392,29 @@ __global__ __launch_bounds__(WAVES * 64, 2) void gemm_q4_kernel(GemmParams p) {
       k.pnl += c == GU ? 1 : 0;
       k.c = c == GU ? 0 : c;
     };
-    // loads issued after a slice's, until the wait for it
-    constexpr int kAfterSlice = 2 * (2 * UG * FT) + XIW;
     // The prologue asks for the first unit's weights alone: every block's
     // requests reach memory at once, and the first unit's arrive sooner
     // without the second's queued beside them; the second unit's weights
     // are requested at the start of the first step.
-    xload(pf, sx0);
+    xload(pf, x0);
     __builtin_amdgcn_sched_barrier(0);
     wload(pf, r0);
     next(pf, pf_u);
     __builtin_amdgcn_sched_barrier(0);
-    xload(pf, sx1);
+    xload(pf, x1);
     __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt<2 * UG * FT + XIW>();  // slice of the first unit has landed
-    dma_barrier();
+    xstore(x0, sx0);
+    lds_barrier();
     int64_t u = u_begin;
     Cur cu = cur_of(u_begin);
-    auto step = [&](const uint8_t* xs, uint8_t* xfill, WRegs<UG, FT>& r, WRegs<UG, FT>& rf) {
-      xload(pf, xfill);
+    auto step = [&](const uint8_t* xs, uint8_t* xw, const XRegs& xr_w, XRegs& xr_l, WRegs<UG, FT>& r,
+                    WRegs<UG, FT>& rf) {
+      xload(pf, xr_l);
       __builtin_amdgcn_sched_barrier(0);
       compute(xs, r, pf, rf);
       __builtin_amdgcn_sched_barrier(0);
-      wait_vmcnt<kAfterSlice>();  // this wave's part of the next unit's slice has landed
-      dma_barrier();
+      xstore(xr_w, xw);
+      lds_barrier();
       next(pf, pf_u);
       if (cu.c == GU - 1 || u == u_last) flush(cu.pnl);
       advance(cu);
@@ -424,18 +424,18 @@ __global__ __launch_bounds__(WAVES * 64, 2) void gemm_q4_kernel(GemmParams p) {
     wload(pf, r1);
     next(pf, pf_u);
     __builtin_amdgcn_sched_barrier(0);
-    step(sx0, sx2, r0, r2);
+    step(sx0, sx1, x1, x2, r0, r2);
     // a counted loop with the remainder after it: no exit from the middle of
     // the loop body, whose paths would make the load waits conservative
     const int64_t n_units = u_end - u_begin;
     int64_t k = 1;
     for (; k + 3 <= n_units; k += 3) {
-      step(sx1, sx0, r1, r0);
-      step(sx2, sx1, r2, r1);
-      step(sx0, sx2, r0, r2);
+      step(sx1, sx2, x2, x0, r1, r0);
+      step(sx2, sx0, x0, x1, r2, r1);
+      step(sx0, sx1, x1, x2, r0, r2);
     }
-    if (k < n_units) step(sx1, sx0, r1, r0);
-    if (k + 1 < n_units) step(sx2, sx1, r2, r1);
+    if (k < n_units) step(sx1, sx2, x2, x0, r1, r0);
+    if (k + 1 < n_units) step(sx2, sx0, x0, x1, r2, r1);
   }
 }
 
