@@ -417,16 +417,20 @@ def test_tree_attention_paged_equals_contiguous(case):
 
 # Graph replays of a 27B-class layer + head step, each checked bit for bit
 # against the first.  Direct-to-LDS loads from several waves writing the same
-# LDS bytes (surplus loads sent to one shared pad) made about one replay in
-# three differ; every wave now has its own pad.
-def test_graph_replays_bit_identical_27b_layer():
+# LDS bytes (surplus loads sent to one shared pad), and GEMM slices loaded
+# straight into LDS and awaited by a partial load count, each made replays
+# differ.  The ragged prefix ends mid-tile, so the attention's last tile
+# takes its register-load path beside the direct-to-LDS tiles.
+@pytest.mark.parametrize("trim", [0, 37])
+def test_graph_replays_bit_identical_27b_layer(trim):
     torch = need_gpu()
     import tree_verify_amd as tv
     from tree_verify_amd.runner import VerifyRunner
     import synth.device as sd
     cfg = synth.get("layer27b")
     seed = cfg.seed
-    say("case layer27b graph replays, seed", seed)
+    prefix = cfg.prefix - trim
+    say("case layer27b graph replays, seed", seed, "prefix", prefix)
     wl = sd.Workload(cfg, seed, "cuda")
     shape = tv.make_shape(cfg.hidden, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ffn,
                           cfg.vocab, cfg.rms_eps, cfg.rope_base)
@@ -438,11 +442,11 @@ def test_graph_replays_bit_identical_27b_layer():
     torch.cuda.synchronize()
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
-        r.step(tree, x, cfg.prefix, hidden_out=hid)
+        r.step(tree, x, prefix, hidden_out=hid)
         stream.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
-            r.step(tree, x, cfg.prefix, hidden_out=hid)
+            r.step(tree, x, prefix, hidden_out=hid)
     torch.cuda.synchronize()
     first = None
     for rep in range(12):
