@@ -191,6 +191,7 @@ GemmParams gemm_params(const lucev_q4& w, const uint16_t* X, int n, void* ws, co
   p.partials = at<float>(ws, L.split);
   p.c_max = pl.c_max;
   p.ug = pl.ug;
+  p.ft = pl.ft;
   return p;
 }
 

@@ -454,13 +454,22 @@ static hipError_t launch_t(const GemmParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// the plan's tiles per wave: gemm_ft_for(ntx), or one (kGemmNarrowUnits)
+template <int NTX, bool EXACT>
+static hipError_t launch_ft(const GemmParams& p, hipStream_t s) {
+  if constexpr (gemm_ft_for(NTX) > 1) {
+    if (p.ft == 1) return launch_t<1, NTX, EXACT>(p, s);
+  }
+  return launch_t<gemm_ft_for(NTX), NTX, EXACT>(p, s);
+}
+
 template <bool EXACT>
 static hipError_t launch_ntx(const GemmParams& p, hipStream_t s) {
   switch (gemm_ntx(p.n_nodes)) {
-    case 1: return launch_t<gemm_ft_for(1), 1, EXACT>(p, s);
-    case 2: return launch_t<gemm_ft_for(2), 2, EXACT>(p, s);
-    case 3: return launch_t<gemm_ft_for(3), 3, EXACT>(p, s);
-    case 4: return launch_t<gemm_ft_for(4), 4, EXACT>(p, s);
+    case 1: return launch_ft<1, EXACT>(p, s);
+    case 2: return launch_ft<2, EXACT>(p, s);
+    case 3: return launch_ft<3, EXACT>(p, s);
+    case 4: return launch_ft<4, EXACT>(p, s);
     case 5: return launch_t<gemm_ft_for(5), 5, EXACT>(p, s);
     case 6: return launch_t<gemm_ft_for(6), 6, EXACT>(p, s);
     case 7: return launch_t<gemm_ft_for(7), 7, EXACT>(p, s);
@@ -479,18 +488,22 @@ int gemm_ug(int kgroups, int ntx) { return (kgroups % 2 == 0 && ntx <= 3) ? 2 : 
 GemmPlan plan_gemm(int64_t n_out, int64_t k_in, int n_nodes) {
   GemmPlan g;
   g.ntx = gemm_ntx(n_nodes);
-  g.ft = gemm_ft_for(g.ntx);
   g.n_tiles = (int)(n_out / 16);
   g.kgroups = (int)(k_in / 128);
-  const int pt = kGemmWaves * g.ft;
-  g.panels = (g.n_tiles + pt - 1) / pt;
-  g.ug = gemm_ug(g.kgroups, g.ntx);
-  g.units = (int64_t)g.panels * (g.kgroups / g.ug);
+  auto shape = [&](int ft, int ug) {
+    g.ft = ft;
+    g.ug = ug;
+    const int pt = kGemmWaves * ft;
+    g.panels = (g.n_tiles + pt - 1) / pt;
+    g.units = (int64_t)g.panels * (g.kgroups / ug);
+  };
   // kGemmBlocksPerCU resident blocks on each of the 256 CUs, at least one
   // unit each
   const int64_t target = 256 * kGemmBlocksPerCU;
+  shape(gemm_ft_for(g.ntx), gemm_ug(g.kgroups, g.ntx));
+  if (g.ft > 1 && g.units < kGemmNarrowUnits * target) shape(1, 1);
   g.blocks = (int)(g.units < target ? g.units : target);
-  g.tile_floats = pt * 16 * g.ntx * 8;
+  g.tile_floats = kGemmWaves * g.ft * 16 * g.ntx * 8;
   const int gu = g.kgroups / g.ug;
   g.c_max = 1;
   for (int pnl = 0; pnl < g.panels; ++pnl) {

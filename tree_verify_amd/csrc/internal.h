@@ -68,6 +68,7 @@ struct GemmParams {
   float* partials;          // per-block partial tiles (see SplitOut)
   int c_max;                // partial-tile slots per panel
   int ug;                   // 128-column groups per unit (the plan's)
+  int ft;                   // 16-row tiles per wave (the plan's)
 };
 
 // Arguments of the QKV consumer (RoPE, q/k/v outputs).
@@ -87,6 +88,11 @@ int gemm_ntx(int n_nodes);  // 16-row MFMA tiles of the 2n hi/lo rows
 int gemm_ug(int kgroups, int ntx);  // 128-column groups per unit
 // tiles per wave: fewer when many node tiles already fill the registers
 constexpr int gemm_ft_for(int ntx) { return ntx <= 4 ? kGemmFT : (kGemmFT > 1 ? kGemmFT / 2 : 1); }
+// A matrix whose wide plan (gemm_ft_for tiles per wave, gemm_ug groups per
+// unit) gives fewer units than this many per block takes one tile per wave
+// and one column group per unit: four times the units, so the blocks' shares
+// even out.
+constexpr int kGemmNarrowUnits = 4;
 GemmPlan plan_gemm(int64_t n_out, int64_t k_in, int n_nodes);
 // Every block writes its share of each panel it touches as a partial tile;
 // a consumer kernel sums them.  exact: weights enter exactly (QKV, Wo,
