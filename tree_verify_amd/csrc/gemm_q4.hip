@@ -454,7 +454,8 @@ static hipError_t launch_t(const GemmParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-// the plan's tiles per wave: gemm_ft_for(ntx), or one (kGemmNarrowUnits)
+// the plan's tiles per wave: gemm_ft_for(ntx), or one (kGemmNarrowUnits,
+// kGemmMidUnits)
 template <int NTX, bool EXACT>
 static hipError_t launch_ft(const GemmParams& p, hipStream_t s) {
   if constexpr (gemm_ft_for(NTX) > 1) {
@@ -502,6 +503,7 @@ GemmPlan plan_gemm(int64_t n_out, int64_t k_in, int n_nodes) {
   const int64_t target = 256 * kGemmBlocksPerCU;
   shape(gemm_ft_for(g.ntx), gemm_ug(g.kgroups, g.ntx));
   if (g.ft > 1 && g.units < kGemmNarrowUnits * target) shape(1, 1);
+  else if (g.ft > 1 && g.units < kGemmMidUnits * target) shape(1, g.ug);
   g.blocks = (int)(g.units < target ? g.units : target);
   g.tile_floats = kGemmWaves * g.ft * 16 * g.ntx * 8;
   const int gu = g.kgroups / g.ug;

@@ -89,10 +89,12 @@ int gemm_ug(int kgroups, int ntx);  // 128-column groups per unit
 // tiles per wave: fewer when many node tiles already fill the registers
 constexpr int gemm_ft_for(int ntx) { return ntx <= 4 ? kGemmFT : (kGemmFT > 1 ? kGemmFT / 2 : 1); }
 // A matrix whose wide plan (gemm_ft_for tiles per wave, gemm_ug groups per
-// unit) gives fewer units than this many per block takes one tile per wave
-// and one column group per unit: four times the units, so the blocks' shares
-// even out.
+// unit) gives fewer units than kGemmNarrowUnits per block takes one tile per
+// wave and one column group per unit (four times the units, so the blocks'
+// shares even out); one with fewer than kGemmMidUnits takes one tile per wave
+// and keeps its column groups (twice the units).
 constexpr int kGemmNarrowUnits = 4;
+constexpr int kGemmMidUnits = 12;
 GemmPlan plan_gemm(int64_t n_out, int64_t k_in, int n_nodes);
 // Every block writes its share of each panel it touches as a partial tile;
 // a consumer kernel sums them.  exact: weights enter exactly (QKV, Wo,
