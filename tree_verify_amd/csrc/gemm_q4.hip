@@ -353,8 +353,9 @@ __global__ __launch_bounds__(WAVES * 64, 2) void gemm_q4_kernel(GemmParams p) {
 
     // this block's share of the panel, node-major; a later kernel sums the
     // contributors and applies the epilogue (plain stores: that kernel starts
-    // after this one has finished).  A fixed store count per thread keeps
-    // exact wait counts for the loads still in flight across the flush.
+    // after this one has finished).  A fixed store count per thread, with no
+    // branch, lets the compiler count the loads still in flight across the
+    // flush exactly rather than wait for all of them.
     const int bf = block_of_unit(pnl * GU, U, B);
     static_assert(TILE % NTH == 0, "partial tile must split evenly over the threads");
     float* dst = p.partials + ((int64_t)pnl * p.c_max + (b - bf)) * TILE;
