@@ -188,16 +188,26 @@ def test_tiny_decode_single_node():
 
 
 # mid-size shape: every GEMM's feature groups are cut across blocks (the
-# split-K reduction path), 1 to 4 node tiles, ragged prefix
+# split-K reduction path), 2 to 8 node tiles (16 nodes per tile of hi/lo
+# rows), ragged prefix
 MID = synth.Config("mid", layers=2, hidden=1024, n_q_heads=8, n_kv_heads=2, head_dim=128,
                    ffn=3584, vocab=32768, prefix=1000, nodes=22, max_children=3, max_depth=8,
                    p_accept=0.7, seed=3100)
 
 
-@pytest.mark.parametrize("nodes,rec", [(22, (3, 8)), (40, (4, 10)), (64, (None, None)), (16, (None, None))])
+@pytest.mark.parametrize("nodes,rec", [(22, (3, 8)), (40, (4, 10)), (64, (None, None)), (16, (None, None)),
+                                       (28, (3, 9)), (48, (4, 10)), (56, (None, None))])
 def test_midsize_parity(nodes, rec):
     cfg = MID.replace(nodes=nodes, max_children=rec[0], max_depth=rec[1], name="mid%d" % nodes)
     _check_case(cfg, cfg.seed + nodes)
+
+
+# A 27B-class layer + head with 28 nodes (four node tiles): gate/up and
+# lm_head take two row tiles per wave with one column group per unit; QKV, Wo
+# and down one tile per wave.
+def test_layer27b_four_node_tiles_parity():
+    cfg = synth.get("layer27b").replace(nodes=28, max_children=3, max_depth=9, name="layer27b_n28")
+    _check_case(cfg, cfg.seed + 28)
 
 
 @pytest.mark.parametrize("run", range(2))
