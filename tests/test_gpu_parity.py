@@ -223,9 +223,9 @@ def test_small_decode_config_parity(run):
 
 
 # Repeated steps on the same inputs must agree bit for bit: every reduction
-# has a fixed order, so any difference is a race.  40 nodes stage activation
-# slices whose direct-to-LDS loads do not divide evenly over the GEMM's waves
-# (the surplus loads land in a pad area); 22 nodes divide evenly.
+# has a fixed order, so any difference is a race.  The two node counts give
+# three and five node tiles, so different staged slice shapes in the GEMM
+# (48 and 80 operand rows, staged as 64 and 96).
 @pytest.mark.parametrize("nodes,rec", [(40, (4, 10)), (22, (3, 8))])
 def test_repeated_steps_bit_identical(nodes, rec):
     torch = need_gpu()
