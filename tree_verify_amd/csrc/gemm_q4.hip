@@ -257,9 +257,9 @@ __global__ __launch_bounds__(WAVES * 64, 2) void gemm_q4_kernel(GemmParams p) {
     x_off[q] = (uint32_t)((src_row * K + (pos ^ (row & 15)) * 8) * 2);
   }
   // Buffer loads: the per-lane offset is a register fixed for the whole
-  // kernel (a per-unit address register would have to outlive the load, which
-  // reads it late) and the unit's column offset a scalar; the descriptor's
-  // range is the operand rows, so a stray offset reads zeros.
+  // kernel and the unit's column offset a scalar, so a load costs no vector
+  // address arithmetic; the descriptor's range is the operand rows, so a
+  // stray offset reads zeros.
   const __amdgpu_buffer_rsrc_t x_rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)p.X, (short)0, (int)(2 * nn * K * 2), 0x00020000);
   struct XRegs {
