@@ -33,11 +33,11 @@ constexpr int attn_max_waves(int qpw) { return qpw == 1 ? 12 : 8; }
 
 // One block per (prefix chunk, KV head), one wave per QPW query tiles (waves
 // past the last query tile only load).  K and V^T tiles of 64 tokens go
-// straight from HBM into a ring of three LDS buffers with 16-byte
-// direct-to-LDS loads, two tiles ahead of the MFMAs; every wave issues the
-// same number of them per tile (one less for the waves past the tile's last
-// load), so a fixed per-wave vmcnt wait plus one barrier per tile publishes a
-// tile.  A load
+// straight from HBM into two LDS buffers with 16-byte direct-to-LDS loads:
+// the next tile's loads are issued right after the barrier that publishes
+// the current one, so they fly while the current tile is in the MFMAs, and
+// each wave waits for all of its loads (vmcnt 0) before the next barrier.
+// A load
 // instruction fills 1 KB of LDS, 16 bytes per lane in lane order, so the bank
 // swizzles are applied on the global side: LDS chunk c of K row `key` holds
 // the row's 16-byte chunk c ^ ((key & 3) | ((key >> 3) & 3) << 2), and chunk
@@ -72,7 +72,7 @@ __global__ __launch_bounds__(attn_max_waves(QPW) * 64) void attn_partial_kernel(
   constexpr int LPW = (NLD + WAVES - 1) / WAVES;  // loads per wave per tile
   constexpr int BUF = KBYTES + VBYTES;
   constexpr int MERGE = SPLIT ? 4 * 16 * D * 4 + 2 * 64 * 4 : 0;  // quarter states
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[3 * BUF + MERGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * BUF + MERGE];
   __shared__ int s_tab[PAGED ? kMaxChunkPages : 1];
 
   const int tid = threadIdx.x;
@@ -116,16 +116,15 @@ __global__ __launch_bounds__(attn_max_waves(QPW) * 64) void attn_partial_kernel(
       cofs = 0;
     }
   };
-  // issue this wave's loads of tile t (clamped to the last tile) into buffer b
+  // issue this wave's loads of tile t (< n_tiles) into buffer b
   auto issue = [&](int t, int b) {
-    const int k0 = k_begin + min(t, n_tiles - 1) * KT;
+    const int k0 = k_begin + t * KT;
     const bool ragged = k0 + KT > k_end;
 #pragma unroll
     for (int r = 0; r < LPW; ++r) {
       const int j = wave + r * WAVES;
       // no load past the tile's last (surplus direct-to-LDS loads from
-      // several waves into one shared scratch area made GEMM replays differ;
-      // here such a wave simply waits for one load less, below)
+      // several waves into one shared scratch area made GEMM replays differ)
       if (j >= NLD) continue;
       uint8_t* dst = lds + b * BUF + j * 1024;
       int goff = 0;
@@ -400,17 +399,11 @@ __global__ __launch_bounds__(attn_max_waves(QPW) * 64) void attn_partial_kernel(
   }
   if (n_tiles > 0) {
     issue(0, 0);
-    issue(1, 1);
     for (int t = 0; t < n_tiles; ++t) {
-      // this wave's part of tile t has landed (only tile t + 1's loads, LPW
-      // or LPW - 1 of them, may still be in flight)
-      if (wave < NLD - (LPW - 1) * WAVES)
-        wait_vmcnt<LPW>();
-      else
-        wait_vmcnt<LPW - 1>();
-      lds_barrier();      // every part has; every wave is done with tile t - 1
-      issue(t + 2, (t + 2) % 3);
-      compute_tile(t % 3, t);
+      wait_vmcnt<0>();  // this wave's part of tile t has landed
+      lds_barrier();    // every part has; every wave is done with tile t - 1
+      if (t + 1 < n_tiles) issue(t + 1, (t + 1) & 1);  // into tile t - 1's buffer
+      compute_tile(t & 1, t);
     }
   }
 
@@ -438,7 +431,7 @@ __global__ __launch_bounds__(attn_max_waves(QPW) * 64) void attn_partial_kernel(
 
   if constexpr (SPLIT) {
     // merge the four quarter states of tile FT: O = sum_q 2^(m_q - M) O_q / L
-    float* sO = reinterpret_cast<float*>(lds + 3 * BUF);  // [4][16][D]
+    float* sO = reinterpret_cast<float*>(lds + 2 * BUF);  // [4][16][D]
     float* sm = sO + 4 * 16 * D;                                 // [4][16]
     float* sl = sm + 64;
     __syncthreads();  // (also: every wave is done with the tile ring)
