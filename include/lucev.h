@@ -35,7 +35,14 @@
  *   - bf16 / fp16 tensors are passed as uint16_t bit patterns.
  *   - Shapes: hidden, ffn and n_q_heads*head_dim multiples of 128; hidden <= 8192;
  *     head_dim in {64, 128}; n_q_heads a multiple of n_kv_heads;
- *     vocab a multiple of 16; 1 <= tree nodes <= LUCEV_MAX_NODES.
+ *     vocab a multiple of 16; 1 <= tree nodes <= LUCEV_MAX_NODES.  Entry
+ *     points that run the tree attention also need n * n_q_heads /
+ *     n_kv_heads <= LUCEV_MAX_ATTN_ROWS (every query row of a KV head is held
+ *     by one workgroup); larger trees return LUCEV_ERR_BAD_SHAPE.
+ *   - KV cache descriptors (lucev_kv): 0 <= prefix_len <= capacity and
+ *     capacity a multiple of 8 (each V^T row is read in 16-byte pieces), else
+ *     LUCEV_ERR_BAD_KV; k and v non-NULL when prefix_len > 0
+ *     (LUCEV_ERR_NULL_ARG) and 16-byte aligned (LUCEV_ERR_ALIGN).
  */
 #ifndef LUCEV_H
 #define LUCEV_H
@@ -49,6 +56,7 @@ extern "C" {
 
 #define LUCEV_ABI_VERSION 1
 #define LUCEV_MAX_NODES 64
+#define LUCEV_MAX_ATTN_ROWS 512  /* n * n_q_heads / n_kv_heads */
 
 /* status codes */
 #define LUCEV_OK 0
@@ -60,7 +68,9 @@ extern "C" {
 #define LUCEV_ERR_ALIGN -5      /* a pointer is not 16-byte aligned */
 #define LUCEV_ERR_HIP -6        /* a HIP call failed; see lucev_last_error() */
 #define LUCEV_ERR_DEVICE -7     /* current device is not gfx950 */
-#define LUCEV_ERR_BAD_KV -8     /* prefix_len < 0 or > capacity */
+#define LUCEV_ERR_BAD_KV -8     /* prefix_len < 0 or > capacity, capacity < 0 or not a
+                                   multiple of 8; paged: see lucev_tree_attention_paged;
+                                   commit: prefix_len + n_nodes > capacity */
 
 /* Model shape shared by every layer. */
 typedef struct {
@@ -182,21 +192,34 @@ int lucev_workspace_init(void* ws, size_t ws_bytes, void* stream);
 /* One decoder layer over all tree nodes (RMSNorm, fused QKV projection, RoPE
  * at prefix_len + depth, tree-masked GQA attention over the prefix and each
  * node's ancestors, output projection + residual, RMSNorm, SwiGLU FFN +
- * residual).
+ * residual).  The target verifies the whole drafted tree in one forward
+ * ("Lucebox Hub", section "Speculative decoding 계층 (DFlash / DDTree /
+ * DSpark)"), and that forward reads every weight once for all nodes (same
+ * page, section "배경: 어떤 문제를 푸는가", item 1).
  *   resid_io   : fp32 [n][H] residual stream, updated in place
  *   k_tree_out : bf16 [n][Hkv][d] this layer's tree keys after RoPE
  *   v_tree_out : bf16 [n][Hkv][d] this layer's tree values
- * Attention inside uses the workspace; outputs must not alias inputs. */
+ * Attention inside uses the workspace; outputs must not alias inputs.
+ * Returns LUCEV_OK, LUCEV_ERR_NULL_ARG, LUCEV_ERR_BAD_SHAPE (dims, weight
+ * shapes, attention rows), LUCEV_ERR_BAD_TREE, LUCEV_ERR_BAD_KV,
+ * LUCEV_ERR_ALIGN, LUCEV_ERR_WORKSPACE, LUCEV_ERR_DEVICE or LUCEV_ERR_HIP. */
 int lucev_verify_layer(const lucev_shape* shape, const lucev_layer_w* w, const lucev_tree* tree,
                        const lucev_kv* kv, float* resid_io, uint16_t* k_tree_out,
                        uint16_t* v_tree_out, void* ws, size_t ws_bytes, void* stream);
 
 /* Tree-masked GQA attention alone.  Node i, query head h attends with scale
  * 1/sqrt(d) to all prefix keys of KV head h/(Hq/Hkv) and to the tree keys of
- * i's ancestors and itself.
+ * i's ancestors and itself: one forward over the tree gives each node what
+ * decoding its own root path would ("Lucebox Hub", section "Speculative
+ * decoding 계층 (DFlash / DDTree / DSpark)"), and a long context makes the
+ * KV prefix the bulk of the bytes (same page, section "KVFlash").
  *   q      : bf16 [n][Hq][d] after RoPE
  *   k_tree : bf16 [n][Hkv][d] after RoPE;  v_tree : bf16 [n][Hkv][d]
- *   out    : bf16 [n][Hq][d] */
+ *   out    : bf16 [n][Hq][d]
+ * Returns LUCEV_OK, LUCEV_ERR_NULL_ARG, LUCEV_ERR_BAD_SHAPE (dims, or more
+ * than LUCEV_MAX_ATTN_ROWS query rows per KV head), LUCEV_ERR_BAD_TREE,
+ * LUCEV_ERR_BAD_KV, LUCEV_ERR_ALIGN, LUCEV_ERR_WORKSPACE, LUCEV_ERR_DEVICE or
+ * LUCEV_ERR_HIP. */
 int lucev_tree_attention(const lucev_shape* shape, const lucev_tree* tree, const lucev_kv* kv,
                          const uint16_t* q, const uint16_t* k_tree, const uint16_t* v_tree,
                          uint16_t* out, void* ws, size_t ws_bytes, void* stream);
@@ -219,14 +242,20 @@ int lucev_tree_attention_paged(const lucev_shape* shape, const lucev_tree* tree,
  * the fp32 logits), then greedy acceptance over the tree: a node is accepted
  * when its parent is accepted and its drafted token equals the parent's
  * greedy token; the path ends at the deepest accepted node (lowest index on
- * ties).  All outputs are DEVICE buffers:
+ * ties).  Decoding is greedy at temperature 0 and the tree keeps the longest
+ * accepted path ("Lucebox: 추측 디코딩과 전용 커널로 ...", section "Lucebox
+ * 설치 및 실행"); the target adapter projects through its lm_head ("Lucebox
+ * Hub", section "Speculative decoding 계층 (DFlash / DDTree / DSpark)").
+ * All outputs are DEVICE buffers:
  *   resid         : fp32 [n][H] final residual stream (input)
  *   logits_out    : bf16 [n][V] or NULL
  *   argmax_out    : int32 [n]
  *   gap_out       : fp32 [n] or NULL
  *   path_out      : int32 [n]; path_len_out: int32 [1]
  *   committed_out : int32 [n]: accepted drafted tokens along the path, then
- *                   the greedy token at its end (path_len entries) */
+ *                   the greedy token at its end (path_len entries)
+ * Returns LUCEV_OK, LUCEV_ERR_NULL_ARG, LUCEV_ERR_BAD_SHAPE, LUCEV_ERR_BAD_TREE,
+ * LUCEV_ERR_ALIGN, LUCEV_ERR_WORKSPACE, LUCEV_ERR_DEVICE or LUCEV_ERR_HIP. */
 int lucev_accept_path(const lucev_shape* shape, const lucev_head_w* w, const lucev_tree* tree,
                       const float* resid, uint16_t* logits_out, int32_t* argmax_out,
                       float* gap_out, int32_t* path_out, int32_t* path_len_out,

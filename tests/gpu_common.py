@@ -36,10 +36,16 @@ def decisive_compare(parent, tokens, oracle_am, oracle_gap, gpu_am, gpu_path, gp
                      gpu_committed, thr=0.05):
     """Greedy tokens must match wherever the oracle's top1-top2 gap exceeds thr;
     the path must match exactly when every oracle-accepted node is decisive.
-    Returns (n_decisive_tokens, path_decided)."""
+    On every run, decided or not, the GPU's walk must be exactly the oracle's
+    walk over the GPU's own greedy tokens (bit-exact path, length and
+    committed tokens).  Returns (n_decisive_tokens, path_decided)."""
     dec = oracle_gap > thr
     bad = [i for i in range(len(oracle_am)) if dec[i] and gpu_am[i] != oracle_am[i]]
     assert not bad, "greedy token mismatch at decisive nodes %s" % bad
+    wpath, wcommitted = oracle.accept_path(parent, tokens, [int(a) for a in gpu_am])
+    assert int(gpu_len) == len(wpath), "walk length %d, oracle walk over the GPU tokens %d" % (gpu_len, len(wpath))
+    assert list(gpu_path[:gpu_len]) == list(wpath), "walk differs from the oracle walk over the GPU tokens"
+    assert list(gpu_committed[:gpu_len]) == list(wcommitted), "committed tokens differ"
     path, committed = oracle.accept_path(parent, tokens, oracle_am)
     # nodes whose greedy token the acceptance actually consulted
     acc_nodes = _accepted_nodes(parent, tokens, oracle_am)

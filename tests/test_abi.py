@@ -231,3 +231,23 @@ def test_project_logits_validation_before_any_launch():
     assert status(shape=_shape(tv, hidden=200)) == -2
     assert status(head=tv.lucev_head_w(fake, tv.q4(fake, 256, 256))) == -2  # lm_head rows != vocab
     assert status() in (-6, -7)  # valid: reaches the device check
+
+
+def test_attention_row_limit_is_a_shape_error():
+    # n * Hq / Hkv query rows of one KV head must fit one workgroup
+    # (LUCEV_MAX_ATTN_ROWS); one row more is rejected before any launch
+    tv = _tv()
+    _no_gpu()
+    s = _shape(tv, n_q_heads=32, n_kv_heads=2)  # 16 query heads per KV head
+    parent32 = [-1] + list(range(31))
+    assert _status(tv, shape=s, tree=tv.make_tree(parent32 + [31])) == -2   # 33 x 16 = 528 rows
+    assert "512" in tv.lucev_last_error()
+    assert _status(tv, shape=s, tree=tv.make_tree(parent32)) in (-6, -7)    # 512: reaches the device check
+    fake = 1 << 20
+    kv = tv.lucev_kv(fake, fake, 128, 256)
+    try:
+        tv.lucev_tree_attention(s, tv.make_tree(parent32 + [31]), kv, fake, fake, fake, fake, fake, 1 << 40)
+        rc = 0
+    except tv.LucevError as e:
+        rc = e.status
+    assert rc == -2

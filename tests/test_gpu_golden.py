@@ -6,8 +6,12 @@ the same inputs with the device twin of the generator, runs one verify step
 exactly as bench.py does (captured graph replay), and is compared on:
 greedy tokens where the oracle's top1-top2 gap exceeds 0.05, the accepted
 path and committed tokens whenever every accepted node is that decisive, and
-sampled logits / final hidden states (per-row max error over the sampled
-columns divided by the row's max |value|, bound 2e-2).
+sampled logits / final hidden states / hidden states after layers 0, 1, L/2
+and L-1 (per-row max error over the sampled columns divided by the row's max
+|value|, bound 2e-2), the logits at each node's eight largest oracle logits,
+and, at every node, that the GPU's greedy token is one of the oracle's top
+eight within the 0.05 near-tie band of the top.  On every run the GPU's walk
+must equal the oracle's walk over the GPU's own greedy tokens.
 """
 import json
 import os
@@ -59,14 +63,17 @@ def test_full_size_against_oracle_fixture(name, seed):
     r = VerifyRunner(shape, wl.layers, wl.head, cfg.nodes, wl.capacity, "cuda")
     tree = tv.make_tree(g["parent"], g["tokens"])
     x32 = wl.x_in_f32().contiguous()
+    layer_samples = g.get("layer_hidden", [])
+    cap = {ls["layer"]: torch.zeros(cfg.nodes, cfg.hidden, dtype=torch.float32, device="cuda")
+           for ls in layer_samples}
     torch.cuda.synchronize()  # x32 was made on the default stream
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
-        r.step(tree, x32, cfg.prefix)
+        r.step(tree, x32, cfg.prefix, capture=cap)
         stream.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=stream):
-            r.step(tree, x32, cfg.prefix)
+            r.step(tree, x32, cfg.prefix, capture=cap)
     torch.cuda.synchronize()
     outs = []
     for rep in range(2):  # replays must agree bit for bit with each other
@@ -74,10 +81,13 @@ def test_full_size_against_oracle_fixture(name, seed):
         torch.cuda.synchronize()
         outs.append((r.argmax.cpu().numpy().copy(), r.logits.cpu().numpy().copy(),
                      r.resid.cpu().numpy().copy(), r.path.cpu().numpy().copy(),
-                     int(r.path_len.item()), r.committed.cpu().numpy().copy(), r.gap.cpu().numpy().copy()))
-    for a, b in zip(outs[0], outs[1]):
+                     int(r.path_len.item()), r.committed.cpu().numpy().copy(), r.gap.cpu().numpy().copy(),
+                     [cap[l].cpu().numpy().copy() for l in sorted(cap)]))
+    for a, b in zip(outs[0][:7], outs[1][:7]):
         assert np.array_equal(np.asarray(a), np.asarray(b)), "graph replays differ"
-    am, logits_bits, resid, path, plen, committed, gap = outs[0]
+    for a, b in zip(outs[0][7], outs[1][7]):
+        assert np.array_equal(a, b), "graph replays differ (captured layer)"
+    am, logits_bits, resid, path, plen, committed, gap, layers_got = outs[0]
     n = cfg.nodes
     oam = np.array(g["argmax"])
     ogap = np.array(g["gap"])
@@ -88,10 +98,29 @@ def test_full_size_against_oracle_fixture(name, seed):
     err_l = np.max(np.abs(logits[:, cols] - np.array(g["logits"])), axis=1) / np.array(g["logit_rowmax"])
     hcols = np.array(g["hidden_cols"])
     err_h = np.max(np.abs(resid[:n, hcols] - np.array(g["hidden"])), axis=1) / np.array(g["hidden_rowmax"])
-    # top-8 ids per node: the GPU's fp32 ranking of the oracle's top entries
-    print("  decisive %d/%d, path decided %s, logits err %.2e, final hidden err %.2e" %
-          (ndec, n, decided, err_l.max(), err_h.max()), flush=True)
+    # the logits at each node's eight largest oracle logits
+    tidx = np.array(g["logit_top_idx"])
+    tval = np.array(g["logit_top_val"])
+    err_t = np.max(np.abs(np.take_along_axis(logits, tidx, axis=1) - tval), axis=1) / np.array(g["logit_rowmax"])
+    # at every node (decisive or not) the GPU's greedy token is one the oracle
+    # ranks within 0.05 of its top: among its top eight, no further below
+    for i in range(n):
+        hit = np.nonzero(tidx[i] == am[i])[0]
+        assert len(hit) == 1, "node %d: GPU token %d not among the oracle's top eight" % (i, am[i])
+        assert tval[i, hit[0]] >= tval[i, 0] - 0.05, "node %d: GPU token %.4f below the top" % (i, tval[i, hit[0]])
+    # hidden states after the sampled layers
+    lcols = np.array(g.get("layer_cols", []), np.int64)
+    err_layers = []
+    for ls, got_l in zip(sorted(layer_samples, key=lambda v: v["layer"]), layers_got):
+        e = np.max(np.abs(got_l[:n, lcols] - np.array(ls["values"])), axis=1) / np.array(ls["rowmax"])
+        err_layers.append((ls["layer"], float(e.max())))
+    print("  decisive %d/%d, path decided %s, logits err %.2e (top-8 %.2e), final hidden err %.2e, "
+          "layers %s" % (ndec, n, decided, err_l.max(), err_t.max(), err_h.max(),
+                         ", ".join("%d: %.2e" % le for le in err_layers)), flush=True)
     dec = ogap > 0.05
     assert np.allclose(gap[:n][dec], ogap[dec], rtol=0.05, atol=0.05)
     assert err_l.max() < TOL, err_l
+    assert err_t.max() < TOL, err_t
     assert err_h.max() < TOL, err_h
+    for l, e in err_layers:
+        assert e < TOL, "hidden state after layer %d: rel err %.3e" % (l, e)

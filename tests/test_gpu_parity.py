@@ -80,6 +80,9 @@ ATTN_CASES = [
     ("empty_prefix", 8, 2, 128, 0, None, 5),
     ("single_node", 48, 8, 128, 777, None, 1),
     ("max_nodes", 8, 2, 64, 300, None, 64),
+    ("three_tiles_per_wave", 48, 8, 128, 700, None, 64),   # 384 rows: 24 tiles, 3 per wave
+    ("four_tiles_per_wave", 32, 4, 128, 515, None, 64),    # 512 rows (the limit): 32 tiles, 4 per wave
+    ("four_tiles_d64", 16, 1, 64, 260, (4, 10), 32),       # 512 rows of head_dim 64
 ]
 
 
@@ -431,16 +434,21 @@ def test_tree_attention_paged_equals_contiguous(case):
 # straight into LDS and awaited by a partial load count, each made replays
 # differ.  The ragged prefix ends mid-tile, so the attention's last tile
 # takes its register-load path beside the direct-to-LDS tiles.
-@pytest.mark.parametrize("trim", [0, 37])
-def test_graph_replays_bit_identical_27b_layer(trim):
+#
+# The 40-node tree is the wide plan (C5's budget): two query tiles per wave in
+# the attention (15 tiles of 16 rows per KV head) and five node tiles in the
+# GEMMs.
+@pytest.mark.parametrize("nodes,rec,trim", [(22, (3, 8), 0), (22, (3, 8), 37), (40, (4, 10), 37)],
+                         ids=["n22", "n22_ragged", "n40_ragged"])
+def test_graph_replays_bit_identical_27b_layer(nodes, rec, trim):
     torch = need_gpu()
     import tree_verify_amd as tv
     from tree_verify_amd.runner import VerifyRunner
     import synth.device as sd
-    cfg = synth.get("layer27b")
-    seed = cfg.seed
+    cfg = synth.get("layer27b").replace(nodes=nodes, max_children=rec[0], max_depth=rec[1])
+    seed = cfg.seed + (0 if nodes == 22 else nodes)
     prefix = cfg.prefix - trim
-    say("case layer27b graph replays, seed", seed, "prefix", prefix)
+    say("case layer27b graph replays, nodes", nodes, "seed", seed, "prefix", prefix)
     wl = sd.Workload(cfg, seed, "cuda")
     shape = tv.make_shape(cfg.hidden, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ffn,
                           cfg.vocab, cfg.rms_eps, cfg.rope_base)

@@ -48,6 +48,16 @@ int check_shape(const lucev_shape* s) {
   return LUCEV_OK;
 }
 
+// The tree attention holds all n * Hq / Hkv query rows of a KV head in one
+// block (kMaxAttnRows at most).
+int check_attn_rows(const lucev_shape* s, int n) {
+  const int rows = n * (s->n_q_heads / s->n_kv_heads);
+  if (rows > kMaxAttnRows)
+    return fail(LUCEV_ERR_BAD_SHAPE, "tree attention: n * n_q_heads / n_kv_heads = %d query rows per KV head exceeds %d",
+                rows, kMaxAttnRows);
+  return LUCEV_OK;
+}
+
 // Depths, RoPE positions and ancestor masks of the draft tree.
 int prep_tree(const lucev_tree* t, int vocab, int prefix_len, TreeArgs* out) {
   if (!t) return fail(LUCEV_ERR_NULL_ARG, "tree is NULL");
@@ -369,6 +379,7 @@ int lucev_tree_attention(const lucev_shape* shape, const lucev_tree* tree, const
   if ((rc = check_kv(kv))) return rc;
   TreeArgs t;
   if ((rc = prep_tree(tree, shape->vocab, kv->prefix_len, &t))) return rc;
+  if ((rc = check_attn_rows(shape, t.n))) return rc;
   if (!aligned16(q) || !aligned16(k_tree) || !aligned16(v_tree) || !aligned16(out))
     return fail(LUCEV_ERR_ALIGN, "tree_attention: tensors must be 16-byte aligned");
   Ws L;
@@ -396,6 +407,7 @@ int lucev_tree_attention_paged(const lucev_shape* shape, const lucev_tree* tree,
     return fail(LUCEV_ERR_ALIGN, "tree_attention_paged: tensors must be 16-byte aligned");
   TreeArgs t;
   if ((rc = prep_tree(tree, shape->vocab, kv->prefix_len, &t))) return rc;
+  if ((rc = check_attn_rows(shape, t.n))) return rc;
   Ws L;
   if ((rc = check_ws(shape, t.n, kv->prefix_len, ws, ws_bytes, &L))) return rc;
   if ((rc = check_device())) return rc;
@@ -419,6 +431,7 @@ int lucev_verify_layer(const lucev_shape* shape, const lucev_layer_w* w, const l
   if ((rc = check_kv(kv))) return rc;
   TreeArgs t;
   if ((rc = prep_tree(tree, shape->vocab, kv->prefix_len, &t))) return rc;
+  if ((rc = check_attn_rows(shape, t.n))) return rc;
   const int64_t H = shape->hidden, F = shape->ffn, Hq = shape->n_q_heads, Hkv = shape->n_kv_heads,
                 d = shape->head_dim;
   if ((rc = check_q4(w->wqkv, (Hq + 2 * Hkv) * d, H, "wqkv"))) return rc;

@@ -642,6 +642,8 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(CombineParams c, Tree
   }
 }
 
+static_assert(kMaxAttnRows == attn_max_waves(4) * 4 * 16, "the widest plan covers every allowed row");
+
 int attention_max_chunks(int n_kv_heads) { return (256 + n_kv_heads - 1) / n_kv_heads; }
 
 AttnPlan plan_attention(int n_nodes, int n_q_heads, int n_kv_heads, int head_dim, int prefix_len) {

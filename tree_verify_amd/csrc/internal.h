@@ -147,6 +147,9 @@ struct CombineParams {
   int out_hilo;
 };
 
+// Every query row of a KV head lives in one block of the partial kernel: at
+// most 8 waves x 4 tiles x 16 rows.
+constexpr int kMaxAttnRows = 512;
 AttnPlan plan_attention(int n_nodes, int n_q_heads, int n_kv_heads, int head_dim, int prefix_len);
 int attention_max_chunks(int n_kv_heads);
 hipError_t launch_attention(const AttnPlan& plan, int head_dim, const AttnParams& p,
