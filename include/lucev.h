@@ -224,6 +224,24 @@ int lucev_tree_attention(const lucev_shape* shape, const lucev_tree* tree, const
                          const uint16_t* q, const uint16_t* k_tree, const uint16_t* v_tree,
                          uint16_t* out, void* ws, size_t ws_bytes, void* stream);
 
+/* lucev_tree_attention without a workspace, for callers that cannot allocate
+ * device memory or hand the library a buffer (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  Same arguments,
+ * kernels and results as lucev_tree_attention (bit-identical).  Its chunk
+ * partials live in one scratch array of LUCEV_NOALLOC_SCRATCH_BYTES inside the
+ * library, one per GPU, held until the process ends; a call needs
+ * about 256 * n * (n_q_heads / n_kv_heads) * (4 * head_dim + 8) bytes of it
+ * (a 22-node tree of 48/8 heads, d = 128: 17.6 MB; 40 nodes: 31.9 MB) and
+ * returns LUCEV_ERR_WORKSPACE when that exceeds the array.  Every call on one
+ * GPU shares the array: calls that overlap on one GPU (other streams, other
+ * host threads) race and must be serialised by the caller.  Nothing in the
+ * array needs clearing between calls.  Otherwise returns the codes of
+ * lucev_tree_attention. */
+#define LUCEV_NOALLOC_SCRATCH_BYTES (32u << 20)
+int lucev_tree_attention_noalloc(const lucev_shape* shape, const lucev_tree* tree, const lucev_kv* kv,
+                                 const uint16_t* q, const uint16_t* k_tree, const uint16_t* v_tree,
+                                 uint16_t* out, void* stream);
+
 /* The same attention over a paged prefix: a pool of 16-token physical blocks
  * and a block table per sequence, which changes layout and allocation only,
  * with no approximation ("Lucebox Hub", section "Paged attention +

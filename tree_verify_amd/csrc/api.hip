@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/lucev.h"
 #include "internal.h"
 
@@ -117,6 +119,37 @@ int check_device() {
   return LUCEV_OK;
 }
 
+// Scratch of lucev_tree_attention_noalloc (the chunk partials of the tree
+// attention), for callers that cannot allocate.  Each GPU the library runs on
+// holds its own copy of this array until the process ends.  In host code the
+// name `scratch` is only a stand-in: the device address comes from
+// hipGetSymbolAddress, looked up once per device (scratch_on_device).
+constexpr size_t kNoAllocScratchBytes = (size_t)LUCEV_NOALLOC_SCRATCH_BYTES;
+static __device__ __attribute__((aligned(256))) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 128;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // the array's device address on each device (NULL: not looked up yet)
+
+// The device address of `scratch` on the current device, looked up on the
+// first call on that device (with it current).
+int scratch_on_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(LUCEV_ERR_DEVICE, "device id %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(LUCEV_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LUCEV_OK;
+}
+
 struct Ws {
   size_t xa, xm, q32, k32, v32, opart, ml, split, cand, total;
 };
@@ -224,8 +257,8 @@ EpiArgs epi_blank() {
 // out bf16 [n][Hq][d], or the Wo operand's fp16 hi/lo rows when out_hilo is set
 int run_attention(const lucev_shape* s, const TreeArgs& t, const lucev_kv* kv, const uint16_t* q,
                   const uint16_t* k_tree, const uint16_t* v_tree, const float* q32,
-                  const float* k32, const float* v32, uint16_t* out, int out_hilo, void* ws,
-                  const Ws& L, hipStream_t st, const int32_t* table = nullptr, int n_phys = 0) {
+                  const float* k32, const float* v32, uint16_t* out, int out_hilo, float* o_part,
+                  float* ml_part, hipStream_t st, const int32_t* table = nullptr, int n_phys = 0) {
   AttnPlan plan = plan_attention(t.n, s->n_q_heads, s->n_kv_heads, s->head_dim, kv->prefix_len);
   if (table && plan.chunk / kPageTokens > kMaxChunkPagesHost)
     return fail(LUCEV_ERR_BAD_KV, "paged attention: %d-token prefix chunks exceed %d pages", plan.chunk,
@@ -244,10 +277,10 @@ int run_attention(const lucev_shape* s, const TreeArgs& t, const lucev_kv* kv, c
   p.n_kv_heads = s->n_kv_heads;
   p.rows = plan.rows;
   p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)s->head_dim));
-  p.o_part = at<float>(ws, L.opart);
+  p.o_part = o_part;
   p.table = table;
   p.n_phys = n_phys;
-  p.ml_part = at<float>(ws, L.ml);
+  p.ml_part = ml_part;
   CombineParams c;
   c.q = q;
   c.k_tree = k_tree;
@@ -385,7 +418,38 @@ int lucev_tree_attention(const lucev_shape* shape, const lucev_tree* tree, const
   Ws L;
   if ((rc = check_ws(shape, t.n, kv->prefix_len, ws, ws_bytes, &L))) return rc;
   if ((rc = check_device())) return rc;
-  return run_attention(shape, t, kv, q, k_tree, v_tree, nullptr, nullptr, nullptr, out, 0, ws, L,
+  return run_attention(shape, t, kv, q, k_tree, v_tree, nullptr, nullptr, nullptr, out, 0,
+                       at<float>(ws, L.opart), at<float>(ws, L.ml), (hipStream_t)stream);
+}
+
+int lucev_tree_attention_noalloc(const lucev_shape* shape, const lucev_tree* tree, const lucev_kv* kv,
+                                 const uint16_t* q, const uint16_t* k_tree, const uint16_t* v_tree,
+                                 uint16_t* out, void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (!q || !k_tree || !v_tree || !out) return fail(LUCEV_ERR_NULL_ARG, "tree_attention_noalloc: NULL tensor");
+  if ((rc = check_kv(kv))) return rc;
+  TreeArgs t;
+  if ((rc = prep_tree(tree, shape->vocab, kv->prefix_len, &t))) return rc;
+  if ((rc = check_attn_rows(shape, t.n))) return rc;
+  if (!aligned16(q) || !aligned16(k_tree) || !aligned16(v_tree) || !aligned16(out))
+    return fail(LUCEV_ERR_ALIGN, "tree_attention_noalloc: tensors must be 16-byte aligned");
+  // the chunk partials of this call: O [chunks][Hkv][rows][d], then (max, sum)
+  // [chunks][Hkv][rows][2], all fp32
+  const AttnPlan plan = plan_attention(t.n, shape->n_q_heads, shape->n_kv_heads, shape->head_dim, kv->prefix_len);
+  const size_t o_bytes = align256((size_t)plan.n_chunks * shape->n_kv_heads * plan.rows * shape->head_dim * 4);
+  const size_t need = o_bytes + (size_t)plan.n_chunks * shape->n_kv_heads * plan.rows * 2 * 4;
+  if (need > kNoAllocScratchBytes)
+    return fail(LUCEV_ERR_WORKSPACE,
+                "tree_attention_noalloc: this call needs %zu bytes of scratch, more than the %zu the library holds "
+                "(fewer nodes or a shorter prefix, or lucev_tree_attention with a workspace)",
+                need, kNoAllocScratchBytes);
+  if ((rc = check_device())) return rc;
+  void* base = nullptr;
+  if ((rc = scratch_on_device(&base))) return rc;
+  float* o_part = static_cast<float*>(base);
+  float* ml_part = reinterpret_cast<float*>(static_cast<uint8_t*>(base) + o_bytes);
+  return run_attention(shape, t, kv, q, k_tree, v_tree, nullptr, nullptr, nullptr, out, 0, o_part, ml_part,
                        (hipStream_t)stream);
 }
 
@@ -417,8 +481,9 @@ int lucev_tree_attention_paged(const lucev_shape* shape, const lucev_tree* tree,
   flat.v = kv->v_pages;
   flat.prefix_len = kv->prefix_len;
   flat.capacity = 0;
-  return run_attention(shape, t, &flat, q, k_tree, v_tree, nullptr, nullptr, nullptr, out, 0, ws, L,
-                       (hipStream_t)stream, kv->prefix_len > 0 ? kv->block_table : nullptr, kv->n_pages);
+  return run_attention(shape, t, &flat, q, k_tree, v_tree, nullptr, nullptr, nullptr, out, 0,
+                       at<float>(ws, L.opart), at<float>(ws, L.ml), (hipStream_t)stream,
+                       kv->prefix_len > 0 ? kv->block_table : nullptr, kv->n_pages);
 }
 
 int lucev_verify_layer(const lucev_shape* shape, const lucev_layer_w* w, const lucev_tree* tree,
@@ -475,8 +540,8 @@ int lucev_verify_layer(const lucev_shape* shape, const lucev_layer_w* w, const l
     for (int j = 0; j < d / 2; ++j) ea.inv_freq[j] = pow((double)shape->rope_base, -2.0 * j / (double)d);
     if ((e = launch_qkv_finish(so, ea, n, st)) != hipSuccess) return hip_fail(e, "qkv finish launch");
   }
-  if ((rc = run_attention(shape, t, kv, nullptr, k_tree_out, v_tree_out, q32, k32, v32, xa, 1, ws, L,
-                          st)))
+  if ((rc = run_attention(shape, t, kv, nullptr, k_tree_out, v_tree_out, q32, k32, v32, xa, 1,
+                          at<float>(ws, L.opart), at<float>(ws, L.ml), st)))
     return rc;
   {
     GemmParams p = gemm_params_split(w->wo, xa, n, ws, L, &so);
