@@ -224,6 +224,17 @@ int lucev_tree_attention(const lucev_shape* shape, const lucev_tree* tree, const
                          const uint16_t* q, const uint16_t* k_tree, const uint16_t* v_tree,
                          uint16_t* out, void* ws, size_t ws_bytes, void* stream);
 
+/* The same attention on fp32 inputs and output, exactly as lucev_verify_layer
+ * runs it inside the step (queries carried at about 16 significant bits in
+ * the prefix pass, tree keys and values in fp32):
+ *   q      : fp32 [n][Hq][d] after RoPE
+ *   k_tree : fp32 [n][Hkv][d] after RoPE;  v_tree : fp32 [n][Hkv][d]
+ *   out    : fp32 [n][Hq][d]
+ * Returns the codes of lucev_tree_attention. */
+int lucev_tree_attention_f32(const lucev_shape* shape, const lucev_tree* tree, const lucev_kv* kv,
+                             const float* q, const float* k_tree, const float* v_tree, float* out, void* ws,
+                             size_t ws_bytes, void* stream);
+
 /* lucev_tree_attention without a workspace, for callers that cannot allocate
  * device memory or hand the library a buffer (code under HIP graph capture,
  * tight serving loops, harnesses that forbid allocation).  Same arguments,

@@ -123,6 +123,47 @@ def test_tree_attention_parity(case):
     assert err.max() < TOL
 
 
+F32_CASES = [c for c in ATTN_CASES if c[0] in ("27b_group", "wide_tree", "five_tiles", "empty_prefix",
+                                               "three_tiles_per_wave", "ragged_prefix")]
+
+
+# The fp32-input attention (lucev_tree_attention_f32) runs the step's own
+# kernels (queries split into bf16 hi + lo in the prefix pass, fp32 tree keys
+# and values in the combine); inputs are fp32 with all 24 bits populated.
+@pytest.mark.parametrize("case", F32_CASES, ids=[c[0] for c in F32_CASES])
+def test_tree_attention_f32_parity(case):
+    torch = need_gpu()
+    import tree_verify_amd as tv
+    import synth.device as sd
+    name, Hq, Hkv, d, P, rec, n = case
+    cfg = synth.Config("attn32_" + name, layers=1, hidden=128, n_q_heads=Hq, n_kv_heads=Hkv,
+                       head_dim=d, ffn=128, vocab=64, prefix=P, nodes=n,
+                       max_children=rec[0] if rec else None, max_depth=rec[1] if rec else None,
+                       p_accept=0.7, seed=6262 + n)
+    say("fp32 attention case", name)
+    parent = synth.tree_parents(cfg)
+    cap = ((P + 7) // 8) * 8 + 8
+    k, v = sd.kv_cache(cfg, 0, cfg.seed, cap, "cuda")
+    rng = np.random.default_rng(cfg.seed)
+    qh = rng.standard_normal((n, Hq, d)).astype(np.float32)
+    kth = rng.standard_normal((n, Hkv, d)).astype(np.float32)
+    vth = rng.standard_normal((n, Hkv, d)).astype(np.float32)
+    q, kt, vt = (torch.from_numpy(a).to("cuda") for a in (qh, kth, vth))
+    out = torch.zeros(n, Hq, d, dtype=torch.float32, device="cuda")
+    shape = tv.make_shape(cfg.hidden, Hq, Hkv, d, cfg.ffn, cfg.vocab)
+    ws_bytes = tv.lucev_workspace_bytes(shape, n, P)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
+    tv.lucev_tree_attention_f32(shape, tv.make_tree(parent, [0] * n), tv.make_kv(k, v, P, cap), q, kt, vt, out,
+                                ws, ws_bytes, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    kp, vp = synth.kv_prefix(cfg, 0)
+    ref = oracle.tree_attention(qh.astype(np.float64), kth.astype(np.float64), vth.astype(np.float64),
+                                oracle.bf16_to_f64(kp), oracle.bf16_to_f64(vp), parent)
+    err = row_rel_err(out.cpu().numpy().reshape(n * Hq, d), ref.reshape(n * Hq, d))
+    say("  max row rel err %.3e" % err.max())
+    assert err.max() < TOL
+
+
 # ------------------------------------------------------------------ whole steps
 
 def _run_gpu_step(cfg, seed, tokens, parent, layers=None, want_hidden=True):

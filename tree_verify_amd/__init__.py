@@ -101,6 +101,9 @@ def lib() -> ctypes.CDLL:
         L.lucev_accept_path.argtypes = [P(lucev_shape), P(lucev_head_w), P(lucev_tree), c_vp,
                                         c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]
         L.lucev_tree_attention_paged.restype = c_i32
+        L.lucev_tree_attention_f32.restype = c_i32
+        L.lucev_tree_attention_f32.argtypes = [P(lucev_shape), P(lucev_tree), P(lucev_kv), c_vp, c_vp, c_vp,
+                                               c_vp, c_vp, c_sz, c_vp]
         L.lucev_tree_attention_noalloc.restype = c_i32
         L.lucev_tree_attention_noalloc.argtypes = [P(lucev_shape), P(lucev_tree), P(lucev_kv), c_vp, c_vp,
                                                    c_vp, c_vp, c_vp]
@@ -119,7 +122,7 @@ def lib() -> ctypes.CDLL:
 EXPORTED = ["lucev_abi_version", "lucev_status_str", "lucev_last_error",
             "lucev_q4_packed_bytes", "lucev_q4_pack", "lucev_q4_pack_device",
             "lucev_workspace_bytes", "lucev_workspace_init", "lucev_verify_layer",
-            "lucev_tree_attention", "lucev_tree_attention_noalloc", "lucev_tree_attention_paged", "lucev_accept_path", "lucev_project_logits",
+            "lucev_tree_attention", "lucev_tree_attention_f32", "lucev_tree_attention_noalloc", "lucev_tree_attention_paged", "lucev_accept_path", "lucev_project_logits",
             "lucev_commit_path"]
 
 
@@ -214,6 +217,12 @@ def lucev_tree_attention(shape, tree, kv, q, k_tree, v_tree, out, ws, ws_bytes, 
     _check(lib().lucev_tree_attention(ctypes.byref(shape), ctypes.byref(tree), ctypes.byref(kv),
                                       _ptr(q), _ptr(k_tree), _ptr(v_tree), _ptr(out), _ptr(ws),
                                       ws_bytes, stream), "lucev_tree_attention")
+
+
+def lucev_tree_attention_f32(shape, tree, kv, q, k_tree, v_tree, out, ws, ws_bytes, stream=None) -> None:
+    _check(lib().lucev_tree_attention_f32(ctypes.byref(shape), ctypes.byref(tree), ctypes.byref(kv),
+                                          _ptr(q), _ptr(k_tree), _ptr(v_tree), _ptr(out), _ptr(ws),
+                                          ws_bytes, stream), "lucev_tree_attention_f32")
 
 
 NOALLOC_SCRATCH_BYTES = 32 << 20

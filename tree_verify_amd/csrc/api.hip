@@ -254,11 +254,13 @@ EpiArgs epi_blank() {
 }
 
 // q / k_tree / v_tree bf16 (always); q32 / k32 / v32 fp32 copies or NULL;
-// out bf16 [n][Hq][d], or the Wo operand's fp16 hi/lo rows when out_hilo is set
+// out bf16 [n][Hq][d], or the Wo operand's fp16 hi/lo rows when out_hilo is
+// set; out32 (fp32 [n][Hq][d]) instead of both when not NULL
 int run_attention(const lucev_shape* s, const TreeArgs& t, const lucev_kv* kv, const uint16_t* q,
                   const uint16_t* k_tree, const uint16_t* v_tree, const float* q32,
                   const float* k32, const float* v32, uint16_t* out, int out_hilo, float* o_part,
-                  float* ml_part, hipStream_t st, const int32_t* table = nullptr, int n_phys = 0) {
+                  float* ml_part, hipStream_t st, const int32_t* table = nullptr, int n_phys = 0,
+                  float* out32 = nullptr) {
   AttnPlan plan = plan_attention(t.n, s->n_q_heads, s->n_kv_heads, s->head_dim, kv->prefix_len);
   if (table && plan.chunk / kPageTokens > kMaxChunkPagesHost)
     return fail(LUCEV_ERR_BAD_KV, "paged attention: %d-token prefix chunks exceed %d pages", plan.chunk,
@@ -298,6 +300,7 @@ int run_attention(const lucev_shape* s, const TreeArgs& t, const lucev_kv* kv, c
   c.scale_log2 = p.scale_log2;
   c.out = out;
   c.out_hilo = out_hilo;
+  c.out32 = out32;
   hipError_t e = launch_attention(plan, s->head_dim, p, c, t, st);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return LUCEV_OK;
@@ -420,6 +423,26 @@ int lucev_tree_attention(const lucev_shape* shape, const lucev_tree* tree, const
   if ((rc = check_device())) return rc;
   return run_attention(shape, t, kv, q, k_tree, v_tree, nullptr, nullptr, nullptr, out, 0,
                        at<float>(ws, L.opart), at<float>(ws, L.ml), (hipStream_t)stream);
+}
+
+int lucev_tree_attention_f32(const lucev_shape* shape, const lucev_tree* tree, const lucev_kv* kv,
+                             const float* q, const float* k_tree, const float* v_tree, float* out, void* ws,
+                             size_t ws_bytes, void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (!q || !k_tree || !v_tree || !out) return fail(LUCEV_ERR_NULL_ARG, "tree_attention_f32: NULL tensor");
+  if ((rc = check_kv(kv))) return rc;
+  TreeArgs t;
+  if ((rc = prep_tree(tree, shape->vocab, kv->prefix_len, &t))) return rc;
+  if ((rc = check_attn_rows(shape, t.n))) return rc;
+  if (!aligned16(q) || !aligned16(k_tree) || !aligned16(v_tree) || !aligned16(out))
+    return fail(LUCEV_ERR_ALIGN, "tree_attention_f32: tensors must be 16-byte aligned");
+  Ws L;
+  if ((rc = check_ws(shape, t.n, kv->prefix_len, ws, ws_bytes, &L))) return rc;
+  if ((rc = check_device())) return rc;
+  // q, k_tree, v_tree as the fp32 inputs the verify step hands its attention
+  return run_attention(shape, t, kv, nullptr, nullptr, nullptr, q, k_tree, v_tree, nullptr, 0,
+                       at<float>(ws, L.opart), at<float>(ws, L.ml), (hipStream_t)stream, nullptr, 0, out);
 }
 
 int lucev_tree_attention_noalloc(const lucev_shape* shape, const lucev_tree* tree, const lucev_kv* kv,

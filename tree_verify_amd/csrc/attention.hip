@@ -28,31 +28,39 @@ namespace lucev {
 constexpr int KT = 64;  // tokens per LDS tile
 constexpr int kMaxChunkPages = 1024;  // 16-token pages of one block's prefix chunk (paged cache)
 
-// Waves per block for a query-tile count and tiles per wave.
-constexpr int attn_max_waves(int qpw) { return qpw == 1 ? 12 : 8; }
+// Waves of the partial kernel: ROWW row waves (one to three per SIMD), each
+// holding up to QPW whole 16-row query tiles in registers and reading each K
+// and V^T fragment of a tile from LDS once for all of them; with SPLIT the
+// last four waves (one per SIMD) also hold one key quarter each of the last
+// query tile.
+constexpr int attn_waves(int roww, bool split) { return (void)split, roww; }
 
-// One block per (prefix chunk, KV head), one wave per QPW query tiles (waves
-// past the last query tile only load).  K and V^T tiles of 64 tokens go
-// straight from HBM into two LDS buffers with 16-byte direct-to-LDS loads:
-// the next tile's loads are issued right after the barrier that publishes
-// the current one, so they fly while the current tile is in the MFMAs, and
-// each wave waits for all of its loads (vmcnt 0) before the next barrier.
-// A load
+// One block per (prefix chunk, KV head).  K and V^T tiles of 64 tokens go
+// straight from HBM into a ring of NBUF LDS buffers with 16-byte
+// direct-to-LDS loads, NBUF - 1 tiles ahead: after the barrier that
+// publishes tile t, every wave issues its share of tile t + NBUF - 1 into
+// the buffer tile t - 1 used, then computes tile t.  Before that barrier each
+// wave waits until only its loads of the tiles after t are in flight
+// (vmcnt); no other vector-memory load is issued inside the loop.  A load
 // instruction fills 1 KB of LDS, 16 bytes per lane in lane order, so the bank
 // swizzles are applied on the global side: LDS chunk c of K row `key` holds
 // the row's 16-byte chunk c ^ ((key & 3) | ((key >> 3) & 3) << 2), and chunk
-// c of V^T row `dim` holds chunk c ^ ((dim >> 1) & 7); the 16 rows one
-// 16-lane group reads at once then fall in 16 different bank groups.  The
-// ragged last tile of the prefix goes through registers so tokens past it
-// are zero.
+// c of V^T row `dim` holds chunk c ^ ((dim >> 1) & 7).  The ragged last tile
+// of the prefix goes through registers so tokens past it are zero.
 //
-// SPLIT (one query tile per wave, RT = 4k + 1 tiles, RT + 3 <= 12): the four
-// SIMDs of a CU would carry k + 1, k, k, k tiles, so the last (ragged) tile
-// is instead shared by four waves, one per SIMD, each taking a fixed 16-key
-// quarter of every 64-key tile with its own (max, sum, O); the four states
-// are merged through LDS at the end.  The quarter's PV product is a
-// 16x16x16 MFMA, whose B operand (4 keys per lane) is exactly the layout the
-// 16-key score tile comes out in.
+// A row wave takes one 32-key half of a tile at a time: all of the half's K
+// fragments and V^T fragments are read from LDS up front, the scores of all
+// its query tiles go to the MFMA pipe, and the softmax of one query tile (VALU)
+// then runs while the MFMAs of the next are still in flight.  Cross-lane
+// reductions use the gfx950 permlane swaps (no LDS traffic).
+//
+// SPLIT (RT = 4k + 1 query tiles): the four SIMDs would carry k + 1, k, k, k
+// tiles, so the last (ragged) tile is instead shared by the last four waves
+// (one per SIMD), wave ROWW - 4 + q taking the fixed 16-key quarter q of every
+// 64-key tile with its own (max, sum, O) beside any whole tiles it owns; the
+// four states are merged through LDS at the end.  The quarter's PV product is a 16x16x16
+// MFMA, whose B operand (4 keys per lane) is exactly the layout the 16-key
+// score tile comes out in.
 //
 // PAGED: the prefix lives in 16-token pages, K as [page][Hkv][16][d] and V as
 // [page][Hkv][d][16], and table[t / 16] names the page holding token t.  Only
@@ -60,19 +68,47 @@ constexpr int attn_max_waves(int qpw) { return qpw == 1 ? 12 : 8; }
 // of one page; a 16-byte V chunk covers 8 tokens of one page), so the LDS
 // tiles, and hence the results, are those of the contiguous cache.  The
 // block's slice of the table is copied into LDS first, clamped to the pool.
-template <int D, int QPW, bool QLO, bool SPLIT, bool PAGED = false>
-__global__ __launch_bounds__(attn_max_waves(QPW) * 64) void attn_partial_kernel(AttnParams p) {
-  static_assert(!SPLIT || QPW == 1, "split tiles use one query tile per wave");
-  constexpr int WAVES = attn_max_waves(QPW);
-  constexpr int KCPR = D / 8;                   // 16-byte chunks per K row
-  constexpr int KROWS = 64 / KCPR;              // K rows per 1 KB load
-  constexpr int KBYTES = KT * D * 2;            // one K tile
-  constexpr int VBYTES = D * KT * 2;            // one V^T tile (rows of 128 bytes)
-  constexpr int NLD = (KBYTES + VBYTES) / 1024; // 1 KB loads per tile
-  constexpr int LPW = (NLD + WAVES - 1) / WAVES;  // loads per wave per tile
+
+// max and sum over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48)
+__device__ __forceinline__ float rows_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Two fp32 values as bf16 hi (nearest) and lo (the nearest bf16 of the
+// remainder): about 16 significant bits.
+__device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)a, (__bf16)b});
+  const float ha = __uint_as_float(hi << 16), hb = __uint_as_float(hi & 0xFFFF0000u);
+  lo = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)(a - ha), (__bf16)(b - hb)});
+}
+
+// SPLITM: 0 no split tile; 1 the quarters go to the last four of the waves
+// that own whole tiles; 2 to four extra waves that own no whole tile.
+template <int D, int QPW, int ROWW, int NBUF, bool QLO, int SPLITM, bool PAGED>
+__global__ __launch_bounds__(ROWW * 64) void attn_partial_kernel(AttnParams p) {
+  constexpr bool SPLIT = SPLITM != 0;
+  constexpr int WAVES = ROWW;
+  constexpr int KCPR = D / 8;                    // 16-byte chunks per K row
+  constexpr int KROWS = 64 / KCPR;               // K rows per 1 KB load
+  constexpr int KBYTES = KT * D * 2;             // one K tile
+  constexpr int VBYTES = D * KT * 2;             // one V^T tile (rows of 128 bytes)
+  constexpr int NLD = (KBYTES + VBYTES) / 1024;  // 1 KB loads per tile
+  constexpr int LPW = (NLD + WAVES - 1) / WAVES; // loads per wave per tile (some waves one fewer)
   constexpr int BUF = KBYTES + VBYTES;
-  constexpr int MERGE = SPLIT ? 4 * 16 * D * 4 + 2 * 64 * 4 : 0;  // quarter states
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * BUF + MERGE];
+  constexpr int MERGE = SPLIT ? 4 * 16 * D * 4 + 2 * 64 * 4 : 0;  // quarter states, after the loop
+  constexpr int LDS_BYTES = NBUF * BUF > MERGE ? NBUF * BUF : MERGE;
+  static_assert(NBUF >= 2 && NBUF <= 4, "ring depth");
+  static_assert(!SPLIT || ROWW >= 4, "the split tile's four key quarters go to the last four waves");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
   __shared__ int s_tab[PAGED ? kMaxChunkPages : 1];
 
   const int tid = threadIdx.x;
@@ -83,9 +119,14 @@ __global__ __launch_bounds__(attn_max_waves(QPW) * 64) void attn_partial_kernel(
   const int g = blockIdx.y;
   const int G = p.n_q_heads / p.n_kv_heads;
   const int RT = (p.rows + 15) / 16;
-  const int FT = SPLIT ? RT - 1 : RT;           // tiles a wave owns whole
-  const bool quarter = SPLIT && wave >= FT && wave < FT + 4;
-  const int qq = wave - FT;                     // quarter: keys (qq >> 1) * 32 + (qq & 1) * 4 + ..
+  const int FT = SPLIT ? RT - 1 : RT;  // tiles the row waves own whole
+  const bool has_q = SPLIT && wave >= ROWW - 4;  // holds a key quarter of tile FT
+  const int qq = wave - (ROWW - 4);              // which quarter
+  const bool full_lpw = wave + (LPW - 1) * WAVES < NLD;  // issues LPW loads per tile (else LPW - 1)
+  // query tiles held; the quarter's slot is QS (after the whole tiles when the
+  // wave owns both, else the wave's first)
+  constexpr int NQ = QPW + (SPLITM == 1 ? 1 : 0);
+  constexpr int QS = SPLITM == 1 ? QPW : 0;
   const int k_begin = chunk * p.chunk;
   const int k_end = min(p.prefix_len, k_begin + p.chunk);
   const int n_tiles = (k_end - k_begin + KT - 1) / KT;
@@ -93,59 +134,49 @@ __global__ __launch_bounds__(attn_max_waves(QPW) * 64) void attn_partial_kernel(
   const uint16_t* kbase = p.kc + (int64_t)g * p.cap * D;
   const uint16_t* vbase = p.vc + (int64_t)g * D * p.cap;
 
-  // Load j of a tile (j < NLD): K rows for j < KBYTES / 1024, else V^T rows.
-  // This lane's global element offset at token 0 and its LDS byte offset.
-  // (offsets within a tile's K rows or V^T rows: below D * cap < 2^31)
-  auto load_slot = [&](int j, int& goff, int& loff, int& tok, bool& is_v, int& row, int& cofs) {
-    if (j < KBYTES / 1024) {
-      const int key = j * KROWS + lane / KCPR, pc = lane % KCPR;
-      const int sw = ((key & 3) | (((key >> 3) & 3) << 2)) & (KCPR - 1);
-      goff = key * D + (pc ^ sw) * 8;
-      loff = j * 1024;
-      tok = key;
-      is_v = false;
-      row = key;
-      cofs = (pc ^ sw) * 8;
-    } else {
-      const int dim = (j - KBYTES / 1024) * 8 + lane / 8, pc = lane % 8;
-      goff = dim * p.cap + (pc ^ ((dim >> 1) & 7)) * 8;
-      loff = j * 1024;
-      tok = (pc ^ ((dim >> 1) & 7)) * 8;
-      is_v = true;
-      row = dim;
-      cofs = 0;
-    }
-  };
-  // issue this wave's loads of tile t (< n_tiles) into buffer b
+  // issue this wave's loads of tile t (< n_tiles) into buffer b: load j =
+  // wave + r * WAVES; K rows for j < KBYTES / 1024, else V^T rows
   auto issue = [&](int t, int b) {
     const int k0 = k_begin + t * KT;
     const bool ragged = k0 + KT > k_end;
 #pragma unroll
     for (int r = 0; r < LPW; ++r) {
       const int j = wave + r * WAVES;
-      // no load past the tile's last (surplus direct-to-LDS loads from
-      // several waves into one shared scratch area made GEMM replays differ)
-      if (j >= NLD) continue;
+      if (j >= NLD) continue;  // (wave-uniform)
       uint8_t* dst = lds + b * BUF + j * 1024;
-      int goff = 0;
-      int loff = 0, tok = 0, row = 0, cofs = 0;
-      bool is_v = false;
-      if (j < NLD) load_slot(j, goff, loff, tok, is_v, row, cofs);
+      int tok, row, goff, cofs;
+      bool is_v;
+      if (j < KBYTES / 1024) {
+        const int key = j * KROWS + lane / KCPR, pc = lane % KCPR;
+        const int sw = ((key & 3) | (((key >> 3) & 3) << 2)) & (KCPR - 1);
+        goff = key * D + (pc ^ sw) * 8;
+        tok = key;
+        is_v = false;
+        row = key;
+        cofs = (pc ^ sw) * 8;
+      } else {
+        const int dim = (j - KBYTES / 1024) * 8 + lane / 8, pc = lane % 8;
+        goff = dim * p.cap + (pc ^ ((dim >> 1) & 7)) * 8;
+        tok = (pc ^ ((dim >> 1) & 7)) * 8;
+        is_v = true;
+        row = dim;
+        cofs = 0;
+      }
       const uint16_t* src;
       if constexpr (PAGED) {
         // token of the chunk this lane's 16 bytes start at, and its page
         const int tic = k0 - k_begin + tok;
         const int64_t pg = s_tab[tic >> 4];
-        src = j >= NLD ? p.kc
-              : !is_v ? p.kc + ((pg * p.n_kv_heads + g) * 16 + (tic & 15)) * D + cofs
-                      : p.vc + ((pg * p.n_kv_heads + g) * D + row) * 16 + (tic & 15);
+        src = !is_v ? p.kc + ((pg * p.n_kv_heads + g) * 16 + (tic & 15)) * D + cofs
+                    : p.vc + ((pg * p.n_kv_heads + g) * D + row) * 16 + (tic & 15);
       } else {
-        src = j < NLD ? (is_v ? vbase + goff + k0 : kbase + goff + (int64_t)k0 * D) : kbase;
+        src = is_v ? vbase + goff + k0 : kbase + goff + (int64_t)k0 * D;
       }
-      if (!ragged || j >= NLD) {
+      if (!ragged) {
         __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
       } else {
-        // tokens past the prefix are zero: through registers
+        // tokens past the prefix are zero: through registers (the compiler
+        // waits for these loads before the LDS store)
         const int gk = k0 + tok;
         u32x4 val = u32x4{0u, 0u, 0u, 0u};
         if (gk < k_end) val = ld16(src);
@@ -160,15 +191,17 @@ __global__ __launch_bounds__(attn_max_waves(QPW) * 64) void attn_partial_kernel(
     }
   };
 
-  // query tiles of this wave; Q^T fragments stay in registers as bf16 hi + lo
-  // (about 16 significant bits of q; the keys are exact bf16)
-  bf16x8 qf[QPW][D / 32];
-  bf16x8 ql[QPW][D / 32];
-  f32x4 O[QPW][D / 16];
-  float m[QPW], l[QPW];
+  // this wave's query tiles (row wave w: tiles w, w + ROWW, ..., then with
+  // SPLIT the shared tile FT); Q^T fragments stay in registers, as bf16 hi +
+  // lo when QLO
+  auto my_tile = [&](int i) { return (SPLIT && i == QS && (SPLITM == 1 || has_q)) ? FT : wave + ROWW * i; };
+  bf16x8 qf[NQ][D / 32];
+  bf16x8 ql[QLO ? NQ : 1][D / 32];
+  f32x4 O[NQ][D / 16];
+  float m[NQ], l[NQ];
 #pragma unroll
-  for (int i = 0; i < QPW; ++i) {
-    const int qt = SPLIT ? min(wave, FT) : wave * QPW + i;
+  for (int i = 0; i < NQ; ++i) {
+    const int qt = my_tile(i);
     const int row = qt * 16 + lr;
     const bool ok = qt < RT && row < p.rows;
     int node = 0, head = 0;
@@ -187,62 +220,122 @@ __global__ __launch_bounds__(attn_max_waves(QPW) * 64) void attn_partial_kernel(
       }
 #pragma unroll
       for (int kk = 0; kk < D / 32; ++kk) {
-        bf16x8 hv, lv;
+        uint32_t hv[4], lv[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < 4; ++e) {
           // scores come out in log2 units: q carries log2(e) / sqrt(d)
-          const float x = ok ? __uint_as_float(raw[kk][e >> 2][e & 3]) * p.scale_log2 : 0.f;
-          const __bf16 hb = (__bf16)x;
-          hv[e] = hb;
-          lv[e] = (__bf16)(x - (float)hb);
+          const float x0 = ok ? __uint_as_float(raw[kk][e >> 1][(e & 1) * 2]) * p.scale_log2 : 0.f;
+          const float x1 = ok ? __uint_as_float(raw[kk][e >> 1][(e & 1) * 2 + 1]) * p.scale_log2 : 0.f;
+          split_pair(x0, x1, hv[e], lv[e]);
         }
-        qf[i][kk] = hv;
-        ql[i][kk] = lv;
+        qf[i][kk] = __builtin_bit_cast(bf16x8, u32x4{hv[0], hv[1], hv[2], hv[3]});
+        ql[i][kk] = __builtin_bit_cast(bf16x8, u32x4{lv[0], lv[1], lv[2], lv[3]});
       }
     } else {
       u32x4 raw[D / 32];
 #pragma unroll
       for (int kk = 0; kk < D / 32; ++kk) raw[kk] = ld16(p.q + qoff + kk * 32);
 #pragma unroll
-      for (int kk = 0; kk < D / 32; ++kk) {
+      for (int kk = 0; kk < D / 32; ++kk)
         qf[i][kk] = __builtin_bit_cast(bf16x8, ok ? raw[kk] : u32x4{0u, 0u, 0u, 0u});
-        ql[i][kk] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-      }
     }
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) O[i][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     m[i] = -INFINITY;
     l[i] = 0.f;
   }
-  // One 16-key score tile of query tile i: A row r is key
-  // ks*32 + (r >> 2)*8 + h*4 + (r & 3), so this lane gets keys
-  // ks*32 + lq*8 + h*4 + ii of query lr (the order the PV operand wants).
-  auto score16 = [&](const uint16_t* K, int i, int ks, int h, float init) -> f32x4 {
-    f32x4 a4 = f32x4{init, init, init, init};
-    // this lane's key row; its swizzle is lr, so d chunk kk*4 + lq sits at
-    // (kk*4 + lq) ^ lr
-    const int key = ks * 32 + (lr >> 2) * 8 + h * 4 + (lr & 3);
+
+  // Lazy online softmax of one query tile over one block of scores, then its
+  // PV.  The reference max only moves when some row's scores exceed it by more
+  // than 8 (log2 units): the exponentials stay below 2^8, the final division by
+  // l is unchanged, and most blocks skip the O rescale.  `sc` holds the scores
+  // taken against `bias`.
+  auto rescale_if_needed = [&](int i, float mx_here, float bias, auto& sc) {
+    constexpr int cnt = sizeof(sc) / sizeof(sc[0]);
+    const float mx = rows_max(mx_here);
+    if (__builtin_amdgcn_ballot_w64(bias + mx > m[i] + 8.f) != 0) {
+      const float m_new = fmaxf(m[i], bias + mx);
+      const float alpha = __builtin_amdgcn_exp2f(m[i] - m_new);
+      const float moved = m_new - bias;
 #pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) {
-      const bf16x8 a =
-          *reinterpret_cast<const bf16x8*>(K + key * D + (((kk * 4 + lq) ^ lr) & (KCPR - 1)) * 8);
-      a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[i][kk], a4, 0, 0, 0);
-      if constexpr (QLO) a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[i][kk], a4, 0, 0, 0);
+      for (int e = 0; e < cnt; ++e) sc[e] -= moved;
+      l[i] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) O[i][dt] *= alpha;
+      m[i] = m_new;
     }
-    return a4;
   };
-  // Scores of one 32-key half (keys ks*32 ..) for query tile i, as two 16-key
-  // MFMA tiles.  With the hi/lo q (already scaled to log2 units) the
-  // accumulators start at -bias, so they come out relative to the running
-  // max; bias is the reference the scores were taken against.
-  auto scores = [&](const uint16_t* K, int i, int ks, f32x4 (&sc)[2], float& bias) {
-    bias = m[i] == -INFINITY ? 0.f : m[i];
-    const float init = QLO ? -bias : 0.f;
+
+  // One 32-key half (keys ks*32 ..) of a tile for every whole query tile of a
+  // row wave.  The score MFMA's row r is key ks*32 + (r >> 2)*8 + h*4 + (r & 3),
+  // so this lane gets keys ks*32 + lq*8 + h*4 + ii of query lr: the 8
+  // consecutive keys the PV MFMA's B operand wants.
+  auto row_half = [&](const uint16_t* K, const uint16_t* V, int ks, int k0, auto masked) {
+    bf16x8 kf[2][D / 32];
+    bf16x8 vf[D / 16];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) sc[h] = score16(K, i, ks, h, init);
-    if constexpr (!QLO) {
+    for (int h = 0; h < 2; ++h) {
+      const int key = ks * 32 + (lr >> 2) * 8 + h * 4 + (lr & 3);  // its swizzle is lr
 #pragma unroll
-      for (int h = 0; h < 2; ++h) sc[h] = sc[h] * p.scale_log2 - bias;
+      for (int kk = 0; kk < D / 32; ++kk)
+        kf[h][kk] = *reinterpret_cast<const bf16x8*>(K + key * D + (((kk * 4 + lq) ^ lr) & (KCPR - 1)) * 8);
+    }
+    f32x4 sc[QPW][2];
+    float bias[QPW];
+#pragma unroll
+    for (int i = 0; i < QPW; ++i) {
+      if (my_tile(i) >= FT) continue;
+      bias[i] = m[i] == -INFINITY ? 0.f : m[i];
+      const float init = QLO ? -bias[i] : 0.f;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        f32x4 a4 = f32x4{init, init, init, init};
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk) {
+          a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[h][kk], qf[i][kk], a4, 0, 0, 0);
+          if constexpr (QLO) a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[h][kk], ql[i][kk], a4, 0, 0, 0);
+        }
+        if constexpr (!QLO) a4 = a4 * p.scale_log2 - bias[i];
+        sc[i][h] = a4;
+      }
+    }
+    // the half's V^T fragments, read while the score MFMAs run (the K
+    // fragments are dead by now)
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+      // V^T row dt*16 + lr (swizzle (lr >> 1) & 7), keys ks*32 + lq*8 ..
+      vf[dt] = *reinterpret_cast<const bf16x8*>(V + (dt * 16 + lr) * KT + (((ks * 4 + lq) ^ ((lr >> 1) & 7)) * 8));
+#pragma unroll
+    for (int i = 0; i < QPW; ++i) {
+      if (my_tile(i) >= FT) continue;
+      float s[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s[e] = sc[i][e >> 2][e & 3];
+      if constexpr (decltype(masked)::value) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (k0 + ks * 32 + lq * 8 + (e >> 2) * 4 + (e & 3) >= k_end) s[e] = -INFINITY;
+      }
+      const float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+      rescale_if_needed(i, mx, bias[i], s);
+      float pv[8], psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pv[e] = __builtin_amdgcn_exp2f(s[e]);
+        psum += pv[e];
+      }
+      l[i] += psum;
+      // P as bf16 hi + lo (about 16 significant bits)
+      uint32_t ph[4], pl[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) split_pair(pv[2 * e], pv[2 * e + 1], ph[e], pl[e]);
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{ph[0], ph[1], ph[2], ph[3]});
+      const bf16x8 plo = __builtin_bit_cast(bf16x8, u32x4{pl[0], pl[1], pl[2], pl[3]});
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) {
+        O[i][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pb, O[i][dt], 0, 0, 0);
+        O[i][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], plo, O[i][dt], 0, 0, 0);
+      }
     }
   };
 
@@ -250,146 +343,72 @@ __global__ __launch_bounds__(attn_max_waves(QPW) * 64) void attn_partial_kernel(
   // h = qq & 1) of every 64-key tile, with the same lazy online softmax as a
   // whole tile; PV as 16x16x16 MFMAs on 4 keys per lane.
   auto quarter_tile = [&](const uint16_t* K, const uint16_t* V, int k0, auto masked) {
+    constexpr int Q = QS;  // the quarter's slot in the tile arrays
     const int ks = qq >> 1, h = qq & 1;
-    const float bias = m[0] == -INFINITY ? 0.f : m[0];
-    f32x4 sc = score16(K, 0, ks, h, QLO ? -bias : 0.f);
-    if constexpr (!QLO) sc = sc * p.scale_log2 - bias;
-    if constexpr (decltype(masked)::value) {
+    const int key = ks * 32 + (lr >> 2) * 8 + h * 4 + (lr & 3);
+    bf16x8 kf[D / 32];
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii)
-        if (k0 + ks * 32 + lq * 8 + h * 4 + ii >= k_end) sc[ii] = -INFINITY;
+    for (int kk = 0; kk < D / 32; ++kk)
+      kf[kk] = *reinterpret_cast<const bf16x8*>(K + key * D + (((kk * 4 + lq) ^ lr) & (KCPR - 1)) * 8);
+    const float bias = m[Q] == -INFINITY ? 0.f : m[Q];
+    const float init = QLO ? -bias : 0.f;
+    f32x4 a4 = f32x4{init, init, init, init};
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+      a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk], qf[Q][kk], a4, 0, 0, 0);
+      if constexpr (QLO) a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk], ql[Q][kk], a4, 0, 0, 0);
     }
-    float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    mx = fmaxf(mx, shfl_xor(mx, 16));
-    mx = fmaxf(mx, shfl_xor(mx, 32));
-    if (__builtin_amdgcn_ballot_w64(bias + mx > m[0] + 8.f) != 0) {
-      const float m_new = fmaxf(m[0], bias + mx);
-      const float alpha = __builtin_amdgcn_exp2f(m[0] - m_new);
-      sc -= m_new - bias;
-      l[0] *= alpha;
+    if constexpr (!QLO) a4 = a4 * p.scale_log2 - bias;
+    s16x4 vq[D / 16];
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) O[0][dt] *= alpha;
-      m[0] = m_new;
-    }
-    float psum = 0.f;
-    bf16x4 pb, pl;
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const float pv = __builtin_amdgcn_exp2f(sc[ii]);
-      psum += pv;
-      const __bf16 hb = (__bf16)pv;
-      pb[ii] = hb;
-      pl[ii] = (__bf16)(pv - (float)hb);
-    }
-    l[0] += psum;
-    const s16x4 pbs = __builtin_bit_cast(s16x4, pb), pls = __builtin_bit_cast(s16x4, pl);
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
+    for (int dt = 0; dt < D / 16; ++dt)
       // V^T row dt*16 + lr, keys ks*32 + lq*8 + h*4 .. + 3: 8 bytes of chunk
       // ks*4 + lq, which the row's swizzle moved to (ks*4 + lq) ^ ((lr >> 1) & 7)
-      const s16x4 a = *reinterpret_cast<const s16x4*>(
-          V + (dt * 16 + lr) * KT + (((ks * 4 + lq) ^ ((lr >> 1) & 7)) * 8) + h * 4);
-      O[0][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pbs, O[0][dt], 0, 0, 0);
-      O[0][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pls, O[0][dt], 0, 0, 0);
-    }
-  };
-
-  // Online softmax of one half and its PV product.  The reference max only
-  // moves when some row's scores exceed it by more than 8 (log2 units): the
-  // exponentials stay below 2^8, the final division by l is unchanged, and
-  // most halves skip the rescale.  Returns by how much the reference moved.
-  auto softmax_pv = [&](const uint16_t* V, int i, int ks, f32x4 (&sc)[2], float bias, int k0,
-                        auto masked) -> float {
+      vq[dt] = *reinterpret_cast<const s16x4*>(V + (dt * 16 + lr) * KT + (((ks * 4 + lq) ^ ((lr >> 1) & 7)) * 8) +
+                                               h * 4);
+    float s[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s[e] = a4[e];
     if constexpr (decltype(masked)::value) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii)
-          if (k0 + ks * 32 + lq * 8 + h * 4 + ii >= k_end) sc[h][ii] = -INFINITY;
+      for (int e = 0; e < 4; ++e)
+        if (k0 + ks * 32 + lq * 8 + h * 4 + e >= k_end) s[e] = -INFINITY;
     }
-    // this lane holds query lr, keys ks*32 + lq*8 + h*4 + ii
-    float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-    mx = fmaxf(mx, shfl_xor(mx, 16));
-    mx = fmaxf(mx, shfl_xor(mx, 32));
-    float moved = 0.f;
-    if (__builtin_amdgcn_ballot_w64(bias + mx > m[i] + 8.f) != 0) {
-      const float m_new = fmaxf(m[i], bias + mx);
-      const float alpha = __builtin_amdgcn_exp2f(m[i] - m_new);
-      moved = m_new - bias;
+    rescale_if_needed(Q, fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), bias, s);
+    float pv[4], psum = 0.f;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) sc[h] -= moved;
-      l[i] *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) O[i][dt] *= alpha;
-      m[i] = m_new;
+    for (int e = 0; e < 4; ++e) {
+      pv[e] = __builtin_amdgcn_exp2f(s[e]);
+      psum += pv[e];
     }
-    float psum = 0.f;
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const float pv = __builtin_amdgcn_exp2f(sc[h][ii]);
-        sc[h][ii] = pv;
-        psum += pv;
-      }
-    l[i] += psum;
-    // P as bf16 hi + lo (about 16 significant bits)
-    bf16x8 pb, pl;
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const __bf16 h0 = (__bf16)sc[0][ii];
-      const __bf16 h1 = (__bf16)sc[1][ii];
-      pb[ii] = h0;
-      pb[4 + ii] = h1;
-      pl[ii] = (__bf16)(sc[0][ii] - (float)h0);
-      pl[4 + ii] = (__bf16)(sc[1][ii] - (float)h1);
-    }
+    l[Q] += psum;
+    uint32_t ph[2], pl[2];
+    split_pair(pv[0], pv[1], ph[0], pl[0]);
+    split_pair(pv[2], pv[3], ph[1], pl[1]);
+    const s16x4 pbs = __builtin_bit_cast(s16x4, u32x2{ph[0], ph[1]});
+    const s16x4 pls = __builtin_bit_cast(s16x4, u32x2{pl[0], pl[1]});
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
-      // V^T row dt*16 + lr (swizzle (lr >> 1) & 7), keys ks*32 + lq*8 ..
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-          V + (dt * 16 + lr) * KT + (((ks * 4 + lq) ^ ((lr >> 1) & 7)) * 8));
-      O[i][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, O[i][dt], 0, 0, 0);
-      O[i][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl, O[i][dt], 0, 0, 0);
+      O[Q][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vq[dt], pbs, O[Q][dt], 0, 0, 0);
+      O[Q][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vq[dt], pls, O[Q][dt], 0, 0, 0);
     }
-    // relative to m after this half, scores taken against bias sit lower by:
-    return m[i] - bias;
   };
 
-  // one 64-key tile, half after half (the second half's scores are taken
-  // against the reference the first half left)
   auto compute = [&](int buf, int k0, auto masked) {
     const uint16_t* K = reinterpret_cast<const uint16_t*>(lds + buf * BUF);
     const uint16_t* V = reinterpret_cast<const uint16_t*>(lds + buf * BUF + KBYTES);
+    // (scheduling fences: no half's LDS reads are hoisted into the one
+    // before it, which would hold two halves' fragments in registers)
+    if (wave < FT) {  // a row wave with no query tile only loads
+      row_half(K, V, 0, k0, masked);
+      __builtin_amdgcn_sched_barrier(0);
+      row_half(K, V, 1, k0, masked);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if constexpr (SPLIT) {
-      if (quarter) {
-        quarter_tile(K, V, k0, masked);
-        return;
-      }
-      if (wave >= FT) return;
-    }
-#pragma unroll
-    for (int i = 0; i < QPW; ++i) {
-      const int qt = wave * QPW + i;
-      if (qt >= RT) continue;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        f32x4 sc[2];
-        float bias;
-        scores(K, i, ks, sc, bias);
-        softmax_pv(V, i, ks, sc, bias, k0, masked);
-      }
+      if (has_q) quarter_tile(K, V, k0, masked);
     }
   };
-  auto compute_tile = [&](int buf, int t) {
-    const int k0 = k_begin + t * KT;
-    if (k0 + KT <= k_end)
-      compute(buf, k0, std::integral_constant<bool, false>());
-    else
-      compute(buf, k0, std::integral_constant<bool, true>());
-  };
-
   if constexpr (PAGED) {
     // the pages of this chunk's tiles (entries past the prefix: page 0, never read)
     const int pg0 = k_begin >> 4, npg = (k_end - k_begin + 15) >> 4;
@@ -398,21 +417,45 @@ __global__ __launch_bounds__(attn_max_waves(QPW) * 64) void attn_partial_kernel(
     __syncthreads();
   }
   if (n_tiles > 0) {
-    issue(0, 0);
-    for (int t = 0; t < n_tiles; ++t) {
-      wait_vmcnt<0>();  // this wave's part of tile t has landed
-      lds_barrier();    // every part has; every wave is done with tile t - 1
-      if (t + 1 < n_tiles) issue(t + 1, (t + 1) & 1);  // into tile t - 1's buffer
-      compute_tile(t & 1, t);
+#pragma unroll
+    for (int t = 0; t < NBUF - 1; ++t)
+      if (t < n_tiles) issue(t, t);
+    // whole tiles in the loop; a ragged last tile (masked keys) after it, so
+    // the loop body has a single path
+    const int n_whole = (k_end - k_begin) / KT;
+    auto step = [&](int t) {
+      // this wave's part of tile t has landed once at most its direct-to-LDS
+      // loads of the whole tiles after t (issued later, at most NBUF - 2 of
+      // them) are in flight; a ragged tile's register loads are complete
+      // before issue() returns, so they never count
+      const int ahead = min(n_whole - 1 - t, NBUF - 2);
+      if (NBUF >= 4 && ahead >= 2) {
+        if (full_lpw) wait_vmcnt<2 * LPW>();
+        else wait_vmcnt<2 * (LPW - 1)>();
+      } else if (NBUF >= 3 && ahead >= 1) {
+        if (full_lpw) wait_vmcnt<LPW>();
+        else wait_vmcnt<LPW - 1>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      lds_barrier();  // every part has; every wave is done with tile t - 1
+      if (t + NBUF - 1 < n_tiles) issue(t + NBUF - 1, (t + NBUF - 1) % NBUF);  // into tile t - 1's buffer
+    };
+    for (int t = 0; t < n_whole; ++t) {
+      step(t);
+      compute(t % NBUF, k_begin + t * KT, std::integral_constant<bool, false>());
+    }
+    if (n_whole < n_tiles) {
+      step(n_whole);
+      compute(n_whole % NBUF, k_begin + n_whole * KT, std::integral_constant<bool, true>());
     }
   }
 
 #pragma unroll
   for (int i = 0; i < QPW; ++i) {
-    const int qt = wave * QPW + i;
+    const int qt = my_tile(i);
     if (qt >= FT) continue;
-    float lt = l[i] + shfl_xor(l[i], 16);
-    lt += shfl_xor(lt, 32);
+    const float lt = rows_sum(l[i]);
     const int row = qt * 16 + lr;
     if (row < p.rows) {
       const float inv = 1.0f / lt;
@@ -431,24 +474,24 @@ __global__ __launch_bounds__(attn_max_waves(QPW) * 64) void attn_partial_kernel(
 
   if constexpr (SPLIT) {
     // merge the four quarter states of tile FT: O = sum_q 2^(m_q - M) O_q / L
-    float* sO = reinterpret_cast<float*>(lds + 2 * BUF);  // [4][16][D]
-    float* sm = sO + 4 * 16 * D;                                 // [4][16]
+    // (the merge area reuses the tile ring)
+    float* sO = reinterpret_cast<float*>(lds);  // [4][16][D]
+    float* sm = sO + 4 * 16 * D;                // [4][16]
     float* sl = sm + 64;
-    __syncthreads();  // (also: every wave is done with the tile ring)
-    if (quarter) {
-      float lt = l[0] + shfl_xor(l[0], 16);
-      lt += shfl_xor(lt, 32);
+    __syncthreads();  // every wave is done with the tile ring
+    if (has_q) {
+      const float lt = rows_sum(l[QS]);
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt)
-        *reinterpret_cast<f32x4*>(sO + (qq * 16 + lr) * D + dt * 16 + lq * 4) = O[0][dt];
+        *reinterpret_cast<f32x4*>(sO + (qq * 16 + lr) * D + dt * 16 + lq * 4) = O[QS][dt];
       if (lq == 0) {
-        sm[qq * 16 + lr] = m[0];
+        sm[qq * 16 + lr] = m[QS];
         sl[qq * 16 + lr] = lt;
       }
     }
     __syncthreads();
     const int row = FT * 16 + lr;
-    if (wave == FT && row < p.rows) {
+    if (wave == 0 && row < p.rows) {
       float mq[4], M = -INFINITY;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -629,7 +672,9 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(CombineParams c, Tree
     else
       rounds([&](int64_t vo) { return bf16_bits_to_f32(c.v_tree[vo]); });
     o /= L;
-    if (c.out_hilo) {
+    if (c.out32) {
+      c.out32[((int64_t)node * c.n_q_heads + h) * D + j] = o;
+    } else if (c.out_hilo) {
       // the Wo projection's operand: fp16 rows 2 node (hi) and 2 node + 1 (lo)
       const int64_t width = (int64_t)c.n_q_heads * D;
       const int64_t oo = (int64_t)(2 * node) * width + h * D + j;
@@ -642,20 +687,60 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(CombineParams c, Tree
   }
 }
 
-static_assert(kMaxAttnRows == attn_max_waves(4) * 4 * 16, "the widest plan covers every allowed row");
+static_assert(kMaxAttnRows == 8 * 4 * 16, "the widest plan (8 row waves of 4 tiles) covers every allowed row");
+
+// Depth of the partial kernel's LDS tile ring.
+#ifndef LUCEV_ATTN_NBUF
+#define LUCEV_ATTN_NBUF 2
+#endif
+constexpr int kAttnBufs = LUCEV_ATTN_NBUF;
 
 int attention_max_chunks(int n_kv_heads) { return (256 + n_kv_heads - 1) / n_kv_heads; }
 
+// Wave layout knobs (fixed at build time): where the quarters of a split
+// tile go (0: four extra waves beside one-tile waves; 1: the last four of
+// the one-tile waves; 2: four waves of two whole tiles each), and whether 13
+// to 16 query tiles take four waves of four tiles (1) or eight of two (0).
+#ifndef LUCEV_ATTN_SPLIT_LAYOUT
+#define LUCEV_ATTN_SPLIT_LAYOUT 0
+#endif
+#ifndef LUCEV_ATTN_WIDE4
+#define LUCEV_ATTN_WIDE4 0
+#endif
+
+// Query tiles per SIMD as even as possible.  RT <= 4: one tile per wave, four
+// waves; RT = 5 or 9 (4k + 1): the last tile split by key quarter; other RT up
+// to 12: one tile per wave, 8 or 12 waves; 13 to 16: eight waves of two tiles;
+// above 16: eight waves of three or four.
 AttnPlan plan_attention(int n_nodes, int n_q_heads, int n_kv_heads, int head_dim, int prefix_len) {
   (void)head_dim;
   AttnPlan a;
   a.rows = n_nodes * (n_q_heads / n_kv_heads);
   const int rt = (a.rows + 15) / 16;
-  a.qpw = rt <= attn_max_waves(1) ? 1 : (rt + attn_max_waves(2) - 1) / attn_max_waves(2);
-  a.waves = attn_max_waves(a.qpw);
-  // a ragged last tile that would leave one SIMD a tile more than the others
-  // is shared by four waves, one per SIMD
-  a.split = a.qpw == 1 && rt % 4 == 1 && rt + 3 <= a.waves;
+  a.split = false;
+  if (rt <= 4) {
+    a.roww = 4;
+    a.qpw = 1;
+  } else if (rt % 4 == 1 && rt <= 9) {
+    a.split = true;
+    if (LUCEV_ATTN_SPLIT_LAYOUT == 2) {
+      a.roww = 4;
+      a.qpw = (rt - 1) / 4;
+    } else {
+      a.qpw = 1;
+      a.roww = LUCEV_ATTN_SPLIT_LAYOUT == 1 ? rt - 1 : rt + 3;
+    }
+  } else if (rt <= 12) {
+    a.roww = 4 * ((rt + 3) / 4);
+    a.qpw = 1;
+  } else if (rt <= 16) {
+    a.roww = LUCEV_ATTN_WIDE4 ? 4 : 8;
+    a.qpw = LUCEV_ATTN_WIDE4 ? 4 : 2;
+  } else {
+    a.roww = 8;
+    a.qpw = (rt + 7) / 8;
+  }
+  a.waves = a.roww;
   // one block per CU over (chunk, KV head): chunks a multiple of the LDS tile
   int chunk = (int)(((int64_t)prefix_len * n_kv_heads + 255) / 256);
   chunk = ((chunk + KT - 1) / KT) * KT;
@@ -665,48 +750,58 @@ AttnPlan plan_attention(int n_nodes, int n_q_heads, int n_kv_heads, int head_dim
   return a;
 }
 
-template <int D, int QPW, bool SPLIT>
-static void launch_partial3(const AttnPlan& plan, const AttnParams& p, hipStream_t s) {
+template <int D, int QPW, int ROWW, int SPLITM>
+static void launch_partial(const AttnPlan& plan, const AttnParams& p, hipStream_t s) {
+  const dim3 grid(plan.n_chunks, p.n_kv_heads), block(64 * ROWW);
   if (p.table)
-    hipLaunchKernelGGL((attn_partial_kernel<D, QPW, false, SPLIT, true>), dim3(plan.n_chunks, p.n_kv_heads),
-                       dim3(64 * attn_max_waves(QPW)), 0, s, p);
+    hipLaunchKernelGGL((attn_partial_kernel<D, QPW, ROWW, kAttnBufs, false, SPLITM, true>), grid, block, 0, s, p);
   else if (p.q32)
-    hipLaunchKernelGGL((attn_partial_kernel<D, QPW, true, SPLIT>), dim3(plan.n_chunks, p.n_kv_heads),
-                       dim3(64 * attn_max_waves(QPW)), 0, s, p);
+    hipLaunchKernelGGL((attn_partial_kernel<D, QPW, ROWW, kAttnBufs, true, SPLITM, false>), grid, block, 0, s, p);
   else
-    hipLaunchKernelGGL((attn_partial_kernel<D, QPW, false, SPLIT>), dim3(plan.n_chunks, p.n_kv_heads),
-                       dim3(64 * attn_max_waves(QPW)), 0, s, p);
+    hipLaunchKernelGGL((attn_partial_kernel<D, QPW, ROWW, kAttnBufs, false, SPLITM, false>), grid, block, 0, s, p);
 }
 
-template <int D, int QPW>
-static void launch_partial(const AttnPlan& plan, const AttnParams& p, hipStream_t s) {
-  if constexpr (QPW == 1) {
-    if (plan.split) {
-      launch_partial3<D, 1, true>(plan, p, s);
-      return;
-    }
+template <int D>
+static void launch_partial_d(const AttnPlan& plan, const AttnParams& p, hipStream_t s) {
+  if (plan.split) {
+#if LUCEV_ATTN_SPLIT_LAYOUT == 2
+    if (plan.qpw == 1) launch_partial<D, 1, 4, 1>(plan, p, s);
+    else launch_partial<D, 2, 4, 1>(plan, p, s);
+#elif LUCEV_ATTN_SPLIT_LAYOUT == 1
+    if (plan.roww == 4) launch_partial<D, 1, 4, 1>(plan, p, s);
+    else launch_partial<D, 1, 8, 1>(plan, p, s);
+#else
+    if (plan.roww == 8) launch_partial<D, 1, 8, 2>(plan, p, s);
+    else launch_partial<D, 1, 12, 2>(plan, p, s);
+#endif
+    return;
   }
-  launch_partial3<D, QPW, false>(plan, p, s);
+  if (plan.qpw == 1) {
+    if (plan.roww == 4) launch_partial<D, 1, 4, 0>(plan, p, s);
+    else if (plan.roww == 8) launch_partial<D, 1, 8, 0>(plan, p, s);
+    else launch_partial<D, 1, 12, 0>(plan, p, s);
+    return;
+  }
+#if LUCEV_ATTN_WIDE4
+  if (plan.roww == 4) {
+    launch_partial<D, 4, 4, 0>(plan, p, s);
+    return;
+  }
+#endif
+  switch (plan.qpw) {
+    case 2: launch_partial<D, 2, 8, 0>(plan, p, s); break;
+    case 3: launch_partial<D, 3, 8, 0>(plan, p, s); break;
+    default: launch_partial<D, 4, 8, 0>(plan, p, s); break;
+  }
 }
 
 hipError_t launch_attention(const AttnPlan& plan, int head_dim, const AttnParams& p,
                             const CombineParams& c, const TreeArgs& t, hipStream_t s) {
   if (plan.n_chunks > 0) {
-    if (head_dim == 128) {
-      switch (plan.qpw) {
-        case 1: launch_partial<128, 1>(plan, p, s); break;
-        case 2: launch_partial<128, 2>(plan, p, s); break;
-        case 3: launch_partial<128, 3>(plan, p, s); break;
-        default: launch_partial<128, 4>(plan, p, s); break;
-      }
-    } else {
-      switch (plan.qpw) {
-        case 1: launch_partial<64, 1>(plan, p, s); break;
-        case 2: launch_partial<64, 2>(plan, p, s); break;
-        case 3: launch_partial<64, 3>(plan, p, s); break;
-        default: launch_partial<64, 4>(plan, p, s); break;
-      }
-    }
+    if (head_dim == 128)
+      launch_partial_d<128>(plan, p, s);
+    else
+      launch_partial_d<64>(plan, p, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -158,6 +158,13 @@ struct WRegs {
 __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, soff, 0));
 }
+// the same, non-temporal (the weights are read once)
+__device__ __forceinline__ u32x4 buffer_load16_nt(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, soff, 2));
+}
+__device__ __forceinline__ u32x2 buffer_load8_nt(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rsrc, voff, soff, 2));
+}
 
 // the smallest multiple of 16 rows >= rows whose slice (rows x rb bytes) is a
 // multiple of `waves` 1 KB pieces
@@ -195,42 +202,51 @@ __global__ __launch_bounds__(WAVES * 64, 2) void gemm_q4_kernel(GemmParams p) {
   const int lr = lane & 15, lq = lane >> 4;
   const int b = blockIdx.x;
   const int B = p.blocks;
-  const int64_t U = p.units;
+  const int U = (int)p.units;  // unit counts and offsets below stay far below 2^31
   const int G = p.kgroups;   // 128-column groups
   const int GU = G / UG;     // units per panel
   const int nn = p.n_nodes;
-  const int64_t K = p.k_in;
-  const int64_t u_begin = range_start(b, U, B);
-  const int64_t u_end = range_start(b + 1, U, B);
+  const int K = (int)p.k_in;
+  const int u_begin = b * U / B;  // range_start, in 32 bits (b * U < 2^31)
+  const int u_end = (b + 1) * U / B;
 
 
-  // A unit as (panel, unit within the panel), advanced without divisions.
+  // A unit as (panel, unit within the panel) plus this wave's first tile in
+  // the panel, advanced without divisions; all scalar and 32-bit.
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   struct Cur {
-    int pnl, c;
+    int pnl, c, t0;  // t0 = pnl * PT + wave * FT
   };
-  auto cur_of = [&](int64_t u) { return Cur{(int)(u / GU), (int)(u % GU)}; };
+  auto cur_of = [&](int u) {
+    const int pnl = u / GU;
+    return Cur{pnl, u - pnl * GU, pnl * PT + wave_s * FT};
+  };
   auto advance = [&](Cur& k) {
     if (++k.c == GU) {
       k.c = 0;
       ++k.pnl;
+      k.t0 += PT;
     }
   };
   // Load addresses: a wave-uniform base (scalar registers, advanced per
   // unit with scalar arithmetic) plus a per-lane offset fixed for the whole
   // kernel, so the loads cost no vector address arithmetic.
-  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t w_off = (uint32_t)lane * 16u;  // bytes into a 1 KB tile-group
   const uint32_t s_off = (uint32_t)lr * 8u;     // bytes into its 128-byte scale group
   // the weights are read once: non-temporal loads keep them from evicting
   // the activation rows, which every block re-reads, from L2
+  // Buffer descriptors over the nibble and scale regions (each below 2 GB), so
+  // a tile-group's address is a 32-bit scalar offset: tg * 1024 and tg * 128.
+  const __amdgpu_buffer_rsrc_t wq_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.wq, (short)0, (int)(p.n_out * K / 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t ws_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.wsc, (short)0, (int)(p.n_out * K / 16), 0x00020000);
   auto wload_one = [&](Cur k, WRegs<UG, FT>& r, int g, int ft) {
     // ragged last panel: re-read a valid tile (a wave-uniform clamp)
-    const int t = min(k.pnl * PT + wave_s * FT + ft, p.n_tiles - 1);
-    const int64_t tg = (int64_t)t * G + k.c * UG + g;
-    const uint8_t* wb = p.wq + tg * 1024;
-    const uint8_t* sb = reinterpret_cast<const uint8_t*>(p.wsc) + tg * 128;
-    r.w[g][ft] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wb + w_off));
-    r.s[g][ft] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(sb + s_off));
+    const int t = min(k.t0 + ft, p.n_tiles - 1);
+    const uint32_t tg = (uint32_t)(t * G + k.c * UG + g);
+    r.w[g][ft] = buffer_load16_nt(wq_rsrc, w_off, tg * 1024u);
+    r.s[g][ft] = buffer_load8_nt(ws_rsrc, s_off, tg * 128u);
   };
   auto wload = [&](Cur k, WRegs<UG, FT>& r) {
 #pragma unroll
@@ -336,7 +352,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void gemm_q4_kernel(GemmParams p) {
 
   // finish panel pnl: hi/lo rows merged into the LDS tile [feature][node],
   // split panels reduced across blocks, then the epilogue
-  auto flush = [&](int64_t pnl) {
+  auto flush = [&](int pnl) {
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft)
 #pragma unroll
@@ -356,7 +372,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void gemm_q4_kernel(GemmParams p) {
     // after this one has finished).  A fixed store count per thread, with no
     // branch, lets the compiler count the loads still in flight across the
     // flush exactly rather than wait for all of them.
-    const int bf = block_of_unit(pnl * GU, U, B);
+    const int bf = ((pnl * GU + 1) * B - 1) / U;  // block_of_unit, in 32 bits
     static_assert(TILE % NTH == 0, "partial tile must split evenly over the threads");
     float* dst = p.partials + ((int64_t)pnl * p.c_max + (b - bf)) * TILE;
 #pragma unroll
@@ -377,21 +393,23 @@ __global__ __launch_bounds__(WAVES * 64, 2) void gemm_q4_kernel(GemmParams p) {
   // block's first unit).  The compiler waits for each register load where
   // its value is used.  Prefetches past the block's last unit re-read that
   // unit, so every path issues the same loads.
-  const int64_t u_last = u_end - 1;
+  const int u_last = u_end - 1;
   if (u_begin < u_end) {
     WRegs<UG, FT> r0, r1, r2;
     XRegs x0, x1, x2;
     Cur pf = cur_of(u_begin);  // next unit to prefetch
-    int64_t pf_u = u_begin;
+    int pf_u = u_begin;
     // (selects, not branches: with a branch the compiler may reuse an earlier
     // load's registers on the path that does not advance, which makes every
     // later wait drain the queue)
-    auto next = [&](Cur& k, int64_t& ku) {
+    auto next = [&](Cur& k, int& ku) {
       const int adv = ku < u_last ? 1 : 0;
       ku += adv;
       const int c = k.c + adv;
-      k.pnl += c == GU ? 1 : 0;
-      k.c = c == GU ? 0 : c;
+      const int wrap = c == GU ? 1 : 0;
+      k.pnl += wrap;
+      k.t0 += wrap * PT;
+      k.c = wrap ? 0 : c;
     };
     // The prologue asks for the first unit's weights alone: every block's
     // requests reach memory at once, and the first unit's arrive sooner
@@ -406,7 +424,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void gemm_q4_kernel(GemmParams p) {
     __builtin_amdgcn_sched_barrier(0);
     xstore(x0, sx0);
     lds_barrier();
-    int64_t u = u_begin;
+    int u = u_begin;
     Cur cu = cur_of(u_begin);
     auto step = [&](const uint8_t* xs, uint8_t* xw, const XRegs& xr_w, XRegs& xr_l, WRegs<UG, FT>& r,
                     WRegs<UG, FT>& rf) {
@@ -428,8 +446,8 @@ __global__ __launch_bounds__(WAVES * 64, 2) void gemm_q4_kernel(GemmParams p) {
     step(sx0, sx1, x1, x2, r0, r2);
     // a counted loop with the remainder after it: no exit from the middle of
     // the loop body, whose paths would make the load waits conservative
-    const int64_t n_units = u_end - u_begin;
-    int64_t k = 1;
+    const int n_units = u_end - u_begin;
+    int k = 1;
     for (; k + 3 <= n_units; k += 3) {
       step(sx1, sx2, x2, x0, r1, r0);
       step(sx2, sx0, x0, x1, r2, r1);

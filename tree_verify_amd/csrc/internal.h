@@ -111,8 +111,9 @@ struct AttnPlan {
   int chunk;     // prefix tokens per block (multiple of 64)
   int n_chunks;  // ceil(prefix_len / chunk); 0 when the prefix is empty
   int rows;      // n * (Hq / Hkv) query rows per KV head
-  int qpw;       // query tiles (16 rows) per wave
-  int waves;     // waves per block
+  int roww;      // row waves per block (4 or 8)
+  int qpw;       // query tiles (16 rows) per row wave
+  int waves;     // waves per block (row waves + 4 quarter waves when split)
   bool split;    // the ragged last query tile is shared by four waves (by key quarter)
 };
 
@@ -145,10 +146,11 @@ struct CombineParams {
   float scale_log2;
   uint16_t* out;      // bf16 [n][Hq][d], or fp16 hi/lo rows [2n][Hq * d] when out_hilo
   int out_hilo;
+  float* out32;       // fp32 [n][Hq][d] instead of `out`, when not NULL
 };
 
 // Every query row of a KV head lives in one block of the partial kernel: at
-// most 8 waves x 4 tiles x 16 rows.
+// most 8 row waves x 4 tiles x 16 rows.
 constexpr int kMaxAttnRows = 512;
 AttnPlan plan_attention(int n_nodes, int n_q_heads, int n_kv_heads, int head_dim, int prefix_len);
 int attention_max_chunks(int n_kv_heads);
