@@ -156,11 +156,16 @@ struct Ws {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Which projections take their weights exactly (codes through the MFMA,
+// block scale in fp32) with hi + lo operand rows: QKV, Wo and lm_head; gate/up
+// and down round the weights once to fp16 and read the hi rows alone.
+constexpr bool kGemmExact[5] = {true, true, false, false, true};
+
 // every GEMM of a layer and the head, for a tree of n nodes
 void layer_gemms(const lucev_shape* s, int n, GemmPlan out[5]) {
   const int64_t H = s->hidden, F = s->ffn, Hq = s->n_q_heads, Hkv = s->n_kv_heads, d = s->head_dim;
   const int64_t dims[5][2] = {{(Hq + 2 * Hkv) * d, H}, {H, Hq * d}, {2 * F, H}, {H, F}, {s->vocab, H}};
-  for (int i = 0; i < 5; ++i) out[i] = plan_gemm(dims[i][0], dims[i][1], n);
+  for (int i = 0; i < 5; ++i) out[i] = plan_gemm(dims[i][0], dims[i][1], n, kGemmExact[i]);
 }
 
 bool ws_layout(const lucev_shape* s, int nmax, int pmax, Ws* w) {
@@ -215,9 +220,10 @@ T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
 }
 
-// X: the fp16 hi/lo operand rows [2n][k_in]
-GemmParams gemm_params(const lucev_q4& w, const uint16_t* X, int n, void* ws, const Ws& L) {
-  GemmPlan pl = plan_gemm(w.n_out, w.k_in, n);
+// X: the fp16 hi/lo operand rows [2n][k_in]; exact: weights enter exactly and
+// both operand rows are used (else weights rounded once to fp16, hi rows only)
+GemmParams gemm_params(const lucev_q4& w, const uint16_t* X, int n, bool exact, void* ws, const Ws& L) {
+  GemmPlan pl = plan_gemm(w.n_out, w.k_in, n, exact);
   GemmParams p;
   memset(&p, 0, sizeof(p));
   p.X = X;
@@ -239,11 +245,11 @@ GemmParams gemm_params(const lucev_q4& w, const uint16_t* X, int n, void* ws, co
 }
 
 // the same GEMM writing its per-block partial tiles into the split area
-GemmParams gemm_params_split(const lucev_q4& w, const uint16_t* X, int n, void* ws, const Ws& L,
-                             SplitOut* so) {
-  GemmParams p = gemm_params(w, X, n, ws, L);
+GemmParams gemm_params_split(const lucev_q4& w, const uint16_t* X, int n, bool exact, void* ws,
+                             const Ws& L, SplitOut* so) {
+  GemmParams p = gemm_params(w, X, n, exact, ws, L);
   p.partials = at<float>(ws, L.split);
-  *so = split_out(plan_gemm(w.n_out, w.k_in, n), p.partials);
+  *so = split_out(plan_gemm(w.n_out, w.k_in, n, exact), p.partials);
   return p;
 }
 
@@ -319,7 +325,7 @@ int run_head(const lucev_shape* shape, const lucev_head_w* w, const TreeArgs& t,
   if ((e = launch_norm_hilo(x, n, H, w->final_norm, shape->rms_eps, xa, st)) != hipSuccess)
     return hip_fail(e, "final norm launch");
   SplitOut so;
-  GemmParams p = gemm_params_split(w->lm_head, xa, n, ws, L, &so);
+  GemmParams p = gemm_params_split(w->lm_head, xa, n, true, ws, L, &so);
   f32x4* cand = at<f32x4>(ws, L.cand);
   if ((e = launch_gemm(true, p, st)) != hipSuccess) return hip_fail(e, "lm_head gemm launch");
   if ((e = launch_logits_finish(so, logits_out, shape->vocab, cand, n, st)) != hipSuccess)
@@ -547,7 +553,7 @@ int lucev_verify_layer(const lucev_shape* shape, const lucev_layer_w* w, const l
     return hip_fail(e, "attention norm launch");
   SplitOut so;
   {
-    GemmParams p = gemm_params_split(w->wqkv, xa, n, ws, L, &so);
+    GemmParams p = gemm_params_split(w->wqkv, xa, n, true, ws, L, &so);
     if ((e = launch_gemm(true, p, st)) != hipSuccess)
       return hip_fail(e, "qkv gemm launch");
     EpiArgs ea = epi_blank();
@@ -567,7 +573,7 @@ int lucev_verify_layer(const lucev_shape* shape, const lucev_layer_w* w, const l
                           at<float>(ws, L.opart), at<float>(ws, L.ml), st)))
     return rc;
   {
-    GemmParams p = gemm_params_split(w->wo, xa, n, ws, L, &so);
+    GemmParams p = gemm_params_split(w->wo, xa, n, true, ws, L, &so);
     if ((e = launch_gemm(true, p, st)) != hipSuccess)
       return hip_fail(e, "wo gemm launch");
     // residual += attention output projection, then the FFN RMSNorm (two
@@ -580,13 +586,13 @@ int lucev_verify_layer(const lucev_shape* shape, const lucev_layer_w* w, const l
   }
   // FFN half: gate/up (split) -> SwiGLU -> down (split) -> residual
   {
-    GemmParams p = gemm_params_split(w->wgu, xa, n, ws, L, &so);
+    GemmParams p = gemm_params_split(w->wgu, xa, n, false, ws, L, &so);
     if ((e = launch_gemm(false, p, st)) != hipSuccess)
       return hip_fail(e, "gate/up gemm launch");
     if ((e = launch_swiglu_finish(so, xm, (int)F, n, st)) != hipSuccess) return hip_fail(e, "swiglu launch");
   }
   {
-    GemmParams p = gemm_params_split(w->wd, xm, n, ws, L, &so);
+    GemmParams p = gemm_params_split(w->wd, xm, n, false, ws, L, &so);
     if ((e = launch_gemm(false, p, st)) != hipSuccess)
       return hip_fail(e, "down gemm launch");
     if ((e = launch_resid_finish(so, resid_io, (int)H, n, st)) != hipSuccess)

@@ -187,7 +187,10 @@ __global__ __launch_bounds__(WAVES * 64, 2) void gemm_q4_kernel(GemmParams p) {
   constexpr int XBUF = XR * RB;    // bytes of one staged slice
   constexpr int XI = XBUF / 1024;  // 1 KB pieces per slice (16 bytes a lane)
   constexpr int XIW = XI / WAVES;  // of them per wave
-  constexpr int TILE_N = NTX * 8;  // nodes
+  // operand rows per node: hi and lo (exact projections), or hi alone (gate/up
+  // and down, whose weights are themselves rounded once to fp16)
+  constexpr int RPN = EXACT ? 2 : 1;
+  constexpr int TILE_N = NTX * 16 / RPN;  // nodes
   constexpr int TILE = TILE_F * TILE_N;
   static_assert(XI % WAVES == 0, "a staged slice is whole 1 KB pieces per wave");
   // three slice buffers as separate arrays: the compiler can then tell the
@@ -269,7 +272,8 @@ __global__ __launch_bounds__(WAVES * 64, 2) void gemm_q4_kernel(GemmParams p) {
     const int ins = wave + WAVES * q;
     const int row = ins * (1024 / RB) + lane / (RB / 16);
     const int pos = lane % (RB / 16);
-    const int src_row = row < 2 * nn ? row : 0;
+    // (hi-only: staged row r is node r's hi row, 2r)
+    const int src_row = EXACT ? (row < 2 * nn ? row : 0) : (row < nn ? 2 * row : 0);
     x_off[q] = (uint32_t)((src_row * K + (pos ^ (row & 15)) * 8) * 2);
   }
   // Buffer loads: the per-lane offset is a register fixed for the whole
@@ -360,9 +364,15 @@ __global__ __launch_bounds__(WAVES * 64, 2) void gemm_q4_kernel(GemmParams p) {
         // D layout: column (feature) = lane % 16, rows 4 * (lane / 16) + i =
         // hi/lo rows of nodes nt * 8 + 2 * (lane / 16) + {0, 1}
         const int fl = (wave * FT + ft) * 16 + lr;
-        const int n0 = nt * 8 + 2 * lq;
-        tile[fl][n0] = acc[ft][nt][0] + acc[ft][nt][1];
-        tile[fl][n0 + 1] = acc[ft][nt][2] + acc[ft][nt][3];
+        if constexpr (EXACT) {
+          const int n0 = nt * 8 + 2 * lq;
+          tile[fl][n0] = acc[ft][nt][0] + acc[ft][nt][1];
+          tile[fl][n0 + 1] = acc[ft][nt][2] + acc[ft][nt][3];
+        } else {
+          // rows 4 * (lane / 16) + i are nodes nt * 16 + 4 * (lane / 16) + i
+#pragma unroll
+          for (int i = 0; i < 4; ++i) tile[fl][nt * 16 + 4 * lq + i] = acc[ft][nt][i];
+        }
         acc[ft][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
     lds_barrier();
@@ -485,19 +495,27 @@ static hipError_t launch_ft(const GemmParams& p, hipStream_t s) {
 
 template <bool EXACT>
 static hipError_t launch_ntx(const GemmParams& p, hipStream_t s) {
-  switch (gemm_ntx(p.n_nodes)) {
+  switch (gemm_ntx(p.n_nodes, EXACT)) {
     case 1: return launch_ft<1, EXACT>(p, s);
     case 2: return launch_ft<2, EXACT>(p, s);
     case 3: return launch_ft<3, EXACT>(p, s);
     case 4: return launch_ft<4, EXACT>(p, s);
-    case 5: return launch_t<gemm_ft_for(5), 5, EXACT>(p, s);
-    case 6: return launch_t<gemm_ft_for(6), 6, EXACT>(p, s);
-    case 7: return launch_t<gemm_ft_for(7), 7, EXACT>(p, s);
-    default: return launch_t<gemm_ft_for(8), 8, EXACT>(p, s);
+    default: break;
   }
+  // more than four operand tiles: the hi/lo rows of more than 32 nodes (the
+  // hi-only kernel has at most four tiles for 64 nodes)
+  if constexpr (EXACT) {
+    switch (gemm_ntx(p.n_nodes, EXACT)) {
+      case 5: return launch_t<gemm_ft_for(5), 5, EXACT>(p, s);
+      case 6: return launch_t<gemm_ft_for(6), 6, EXACT>(p, s);
+      case 7: return launch_t<gemm_ft_for(7), 7, EXACT>(p, s);
+      default: return launch_t<gemm_ft_for(8), 8, EXACT>(p, s);
+    }
+  }
+  return hipErrorInvalidValue;
 }
 
-int gemm_ntx(int n_nodes) { return (2 * n_nodes + 15) / 16; }
+int gemm_ntx(int n_nodes, bool exact) { return exact ? (2 * n_nodes + 15) / 16 : (n_nodes + 15) / 16; }
 
 // column groups per unit: two (256 inputs) when k_in allows it and the
 // registers hold two groups' weights beside the accumulators of ntx tiles
@@ -505,9 +523,10 @@ int gemm_ntx(int n_nodes) { return (2 * n_nodes + 15) / 16; }
 // projections whose weights spread thinly over the blocks)
 int gemm_ug(int kgroups, int ntx) { return (kgroups % 2 == 0 && ntx <= 3) ? 2 : 1; }
 
-GemmPlan plan_gemm(int64_t n_out, int64_t k_in, int n_nodes) {
+GemmPlan plan_gemm(int64_t n_out, int64_t k_in, int n_nodes, bool exact) {
   GemmPlan g;
-  g.ntx = gemm_ntx(n_nodes);
+  g.ntx = gemm_ntx(n_nodes, exact);
+  g.tile_n = exact ? g.ntx * 8 : g.ntx * 16;
   g.n_tiles = (int)(n_out / 16);
   g.kgroups = (int)(k_in / 128);
   auto shape = [&](int ft, int ug) {
@@ -524,7 +543,7 @@ GemmPlan plan_gemm(int64_t n_out, int64_t k_in, int n_nodes) {
   if (g.ft > 1 && g.units < kGemmNarrowUnits * target) shape(1, 1);
   else if (g.ft > 1 && g.units < kGemmMidUnits * target) shape(1, g.ug);
   g.blocks = (int)(g.units < target ? g.units : target);
-  g.tile_floats = kGemmWaves * g.ft * 16 * g.ntx * 8;
+  g.tile_floats = kGemmWaves * g.ft * 16 * g.tile_n;
   const int gu = g.kgroups / g.ug;
   g.c_max = 1;
   for (int pnl = 0; pnl < g.panels; ++pnl) {
@@ -543,7 +562,7 @@ SplitOut split_out(const GemmPlan& g, const float* part) {
   so.gu = g.kgroups / g.ug;
   so.c_max = g.c_max;
   so.tile_f = kGemmWaves * g.ft * 16;
-  so.tile_n = g.ntx * 8;
+  so.tile_n = g.tile_n;
   so.panels = g.panels;
   return so;
 }

@@ -32,6 +32,7 @@ constexpr int kGemmSchedMask = LUCEV_GEMM_SCHED_MASK;
 
 struct GemmPlan {
   int ft, ntx, ug, n_tiles, kgroups, panels, blocks, tile_floats;
+  int tile_n;  // nodes per partial tile
   int64_t units;
   int c_max;  // most blocks sharing one panel (partial-tile slots per panel)
 };
@@ -59,6 +60,7 @@ struct SplitOut {
 
 struct GemmParams {
   const uint16_t* X;        // fp16 [2 * n_nodes][k_in]: row 2i = hi(x_i), row 2i+1 = lo(x_i)
+                            // (the non-exact kernel reads the hi rows only)
   int n_nodes;
   const uint8_t* wq;        // nibble region of the packed matrix
   const uint16_t* wsc;      // scale region (fp16 bits)
@@ -84,7 +86,9 @@ struct EpiArgs {
   double inv_freq[kMaxNodes];  // base^(-2j/d), j < d/2
 };
 
-int gemm_ntx(int n_nodes);  // 16-row MFMA tiles of the 2n hi/lo rows
+// 16-row MFMA tiles of the operand: the 2n hi/lo rows (exact projections) or
+// the n hi rows (gate/up, down)
+int gemm_ntx(int n_nodes, bool exact);
 int gemm_ug(int kgroups, int ntx);  // 128-column groups per unit
 // tiles per wave: fewer when many node tiles already fill the registers
 constexpr int gemm_ft_for(int ntx) { return ntx <= 4 ? kGemmFT : (kGemmFT > 1 ? kGemmFT / 2 : 1); }
@@ -95,7 +99,7 @@ constexpr int gemm_ft_for(int ntx) { return ntx <= 4 ? kGemmFT : (kGemmFT > 1 ? 
 // and keeps its column groups (twice the units).
 constexpr int kGemmNarrowUnits = 4;
 constexpr int kGemmMidUnits = 12;
-GemmPlan plan_gemm(int64_t n_out, int64_t k_in, int n_nodes);
+GemmPlan plan_gemm(int64_t n_out, int64_t k_in, int n_nodes, bool exact);
 // Every block writes its share of each panel it touches as a partial tile;
 // a consumer kernel sums them.  exact: weights enter exactly (QKV, Wo,
 // lm_head), else rounded once to fp16.
