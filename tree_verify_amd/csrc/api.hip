@@ -322,7 +322,7 @@ int run_head(const lucev_shape* shape, const lucev_head_w* w, const TreeArgs& t,
   const int H = shape->hidden;
   hipError_t e;
   uint16_t* xa = at<uint16_t>(ws, L.xa);
-  if ((e = launch_norm_hilo(x, n, H, w->final_norm, shape->rms_eps, xa, st)) != hipSuccess)
+  if ((e = launch_norm_hilo(x, n, H, w->final_norm, shape->rms_eps, xa, true, st)) != hipSuccess)
     return hip_fail(e, "final norm launch");
   SplitOut so;
   GemmParams p = gemm_params_split(w->lm_head, xa, n, true, ws, L, &so);
@@ -549,7 +549,7 @@ int lucev_verify_layer(const lucev_shape* shape, const lucev_layer_w* w, const l
   hipError_t e;
 
   // attention half: RMSNorm -> QKV (split) -> RoPE -> tree attention -> Wo (split)
-  if ((e = launch_norm_hilo(resid_io, n, (int)H, w->attn_norm, eps, xa, st)) != hipSuccess)
+  if ((e = launch_norm_hilo(resid_io, n, (int)H, w->attn_norm, eps, xa, kGemmExact[0], st)) != hipSuccess)
     return hip_fail(e, "attention norm launch");
   SplitOut so;
   {
@@ -581,7 +581,7 @@ int lucev_verify_layer(const lucev_shape* shape, const lucev_layer_w* w, const l
     // handoff of the row's sum of squares, measured slower)
     if ((e = launch_resid_finish(so, resid_io, (int)H, n, st)) != hipSuccess)
       return hip_fail(e, "wo finish launch");
-    if ((e = launch_norm_hilo(resid_io, n, (int)H, w->ffn_norm, eps, xa, st)) != hipSuccess)
+    if ((e = launch_norm_hilo(resid_io, n, (int)H, w->ffn_norm, eps, xa, kGemmExact[2], st)) != hipSuccess)
       return hip_fail(e, "ffn norm launch");
   }
   // FFN half: gate/up (split) -> SwiGLU -> down (split) -> residual

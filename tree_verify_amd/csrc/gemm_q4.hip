@@ -380,8 +380,9 @@ __global__ __launch_bounds__(WAVES * 64, 2) void gemm_q4_kernel(GemmParams p) {
     // this block's share of the panel, node-major; a later kernel sums the
     // contributors and applies the epilogue (plain stores: that kernel starts
     // after this one has finished).  A fixed store count per thread, with no
-    // branch, lets the compiler count the loads still in flight across the
-    // flush exactly rather than wait for all of them.
+    // branch (padding nodes past the last are masked off, not skipped), lets
+    // the compiler count the loads still in flight across the flush exactly
+    // rather than wait for all of them.
     const int bf = ((pnl * GU + 1) * B - 1) / U;  // block_of_unit, in 32 bits
     static_assert(TILE % NTH == 0, "partial tile must split evenly over the threads");
     float* dst = p.partials + ((int64_t)pnl * p.c_max + (b - bf)) * TILE;
@@ -389,7 +390,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void gemm_q4_kernel(GemmParams p) {
     for (int k = 0; k < TILE / NTH; ++k) {
       const int i = tid + k * NTH;
       const int n = i / TILE_F, fl = i - n * TILE_F;
-      dst[i] = tile[fl][n];
+      if (n < nn) dst[i] = tile[fl][n];
     }
     lds_barrier();  // the LDS tile is reused by the next panel
   };

@@ -170,7 +170,8 @@ SplitOut split_out(const GemmPlan& g, const float* part);
 // QKV: RoPE (rotate-half pairs sit 8 rows apart in one tile) -> fp32 q/k/v
 // and bf16 tree K/V
 hipError_t launch_qkv_finish(const SplitOut& so, const EpiArgs& e, int n, hipStream_t s);
-// gate/up: silu(gate) * up -> fp16 hi/lo rows [2n][ffn]
+// gate/up: silu(gate) * up -> fp16 rows 2i of [2n][ffn] (hi rows; the down
+// projection reads no lo rows)
 hipError_t launch_swiglu_finish(const SplitOut& so, uint16_t* m, int ffn, int n, hipStream_t s);
 // residual: resid[n][hidden] += y
 hipError_t launch_resid_finish(const SplitOut& so, float* resid, int hidden, int n, hipStream_t s);
@@ -182,7 +183,7 @@ hipError_t launch_logits_finish(const SplitOut& so, uint16_t* logits, int64_t vo
 // RMSNorm of each row into the GEMM operand: u = x / sqrt(mean(x^2) + eps) * g
 // as fp16 hi/lo rows [2n][hidden]
 hipError_t launch_norm_hilo(const float* x, int n, int hidden, const uint16_t* g, float eps,
-                            uint16_t* out, hipStream_t s);
+                            uint16_t* out, bool write_lo, hipStream_t s);
 hipError_t launch_finalize(const f32x4* cand, int n_cand, const TreeArgs& t, int32_t* argmax,
                            float* gap, int32_t* path, int32_t* path_len, int32_t* committed,
                            hipStream_t s);

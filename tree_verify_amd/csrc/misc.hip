@@ -4,7 +4,8 @@
 namespace lucev {
 
 // RMSNorm of one row per block into the GEMM operand: u = x * g / sqrt(mean(x^2)
-// + eps), written as fp16 rows 2i (hi) and 2i+1 (lo = u - hi).  The row is
+// + eps), written as fp16 rows 2i (hi) and, when the GEMM reads it, 2i+1
+// (lo = u - hi).  The row is
 // read once into registers (all loads in flight together); the sum of
 // squares is reduced in a fixed order.
 constexpr int kNormThreads = 512;
@@ -12,7 +13,7 @@ constexpr int kNormMaxPer = 4;  // float4 per thread: rows up to 512 * 16 = 8192
 
 __global__ __launch_bounds__(kNormThreads) void norm_hilo_kernel(const float* __restrict__ x, int hidden,
                                                                  const uint16_t* __restrict__ g, float eps,
-                                                                 uint16_t* __restrict__ out) {
+                                                                 uint16_t* __restrict__ out, int write_lo) {
   __shared__ float red[kNormThreads / 64];
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
@@ -54,13 +55,15 @@ __global__ __launch_bounds__(kNormThreads) void norm_hilo_kernel(const float* __
       l[e] = f32_to_f16_bits(u[e] - (float)hh);
     }
     *reinterpret_cast<uint2*>(hi + i) = make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
-    *reinterpret_cast<uint2*>(lo + i) = make_uint2(l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16));
+    if (write_lo)
+      *reinterpret_cast<uint2*>(lo + i) = make_uint2(l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16));
   }
 }
 
 hipError_t launch_norm_hilo(const float* x, int n, int hidden, const uint16_t* g, float eps,
-                            uint16_t* out, hipStream_t s) {
-  hipLaunchKernelGGL(norm_hilo_kernel, dim3(n), dim3(kNormThreads), 0, s, x, hidden, g, eps, out);
+                            uint16_t* out, bool write_lo, hipStream_t s) {
+  hipLaunchKernelGGL(norm_hilo_kernel, dim3(n), dim3(kNormThreads), 0, s, x, hidden, g, eps, out,
+                     write_lo ? 1 : 0);
   return hipGetLastError();
 }
 

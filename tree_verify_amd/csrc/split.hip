@@ -135,9 +135,9 @@ __global__ __launch_bounds__(256) void swiglu_finish_kernel(SplitOut so, uint16_
     const float gt = s_y[k][(2 * a) * 16 + r];
     const float up = s_y[k][(2 * a + 1) * 16 + r];
     const float mv = gt / (1.0f + expf(-gt)) * up;
-    const f16 hi = (f16)mv;
-    m[(int64_t)(2 * node) * ffn + row] = __builtin_bit_cast(uint16_t, hi);
-    m[(int64_t)(2 * node + 1) * ffn + row] = f32_to_f16_bits(mv - (float)hi);
+    // the down projection reads the hi rows only (its weights are rounded
+    // once to fp16): no lo row is written
+    m[(int64_t)(2 * node) * ffn + row] = f32_to_f16_bits(mv);
   }
 }
 
