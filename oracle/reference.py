@@ -309,3 +309,52 @@ def verify_forward(x_in: np.ndarray, layers: Sequence[LayerWeights],
             path, committed = accept_path(parent, token, am)
             out.update(path=path, committed=committed)
     return out
+
+
+# ---------------------------------------------------------------- int8 KV prefix
+
+
+def quantize_q8_blocks(x) -> tuple:
+    """Symmetric int8 block-32 quantisation along the last axis.
+
+    The pages run the KV cache in int8 (q8_0) besides F16 and Q4_0 ("Lucebox
+    Hub", sections "Paged attention + continuous batching" and "설치·사용법")
+    without defining the format; the reading here is the block-32 form with one
+    fp16 scale per 32 values and no zero point.  Per block: amax = max |x|;
+    d = fp16(amax / 127) with the division in fp32; code = rint(x / d) in fp32
+    (ties to even), clamped to [-127, 127]; an all-zero block has d = 0 and
+    codes 0.  The decisions are taken in fp32, as the device quantiser takes
+    them.  ``x`` holds values exact in fp32 (e.g. bf16 ones) with a last axis
+    that is a multiple of 32.  Returns (codes int8, scales fp16 bits [..., L/32]).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    assert x.shape[-1] % 32 == 0
+    xb = x.astype(np.float32).reshape(x.shape[:-1] + (x.shape[-1] // 32, 32))
+    amax = np.max(np.abs(xb), axis=-1)
+    d16 = (amax / np.float32(127.0)).astype(np.float32).astype(np.float16)
+    dw = d16.astype(np.float32)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(dw > 0, np.rint(xb / np.where(dw > 0, dw, np.float32(1.0))), np.float32(0.0))
+    q = np.clip(q, -127, 127).astype(np.int8).reshape(x.shape)
+    return q, d16.view(np.uint16)
+
+
+def dequantize_q8_blocks(codes, scales) -> np.ndarray:
+    """code * d per block of 32 along the last axis, exactly in fp64."""
+    codes = np.asarray(codes, dtype=np.int8)
+    d = f16_to_f64(scales)
+    cb = codes.astype(np.float64).reshape(codes.shape[:-1] + (codes.shape[-1] // 32, 32))
+    return (cb * d[..., None]).reshape(codes.shape)
+
+
+def kv_prefix_from_q8(k_codes, k_scales, v_codes, v_scales, prefix_len: int):
+    """The fp64 prefix K / V [Hkv, P, d] an int8 cache stands for.
+
+    Keys are blocked along the head dim of each token: k_codes [Hkv, cap, d],
+    k_scales [Hkv, cap, d/32].  Values are blocked along the tokens of each
+    dim (the cache keeps V dim-major): v_codes [Hkv, d, cap], v_scales
+    [Hkv, d, cap/32].  Tokens past prefix_len are not part of the prefix.
+    """
+    k = dequantize_q8_blocks(k_codes, k_scales)[:, :prefix_len, :]
+    v = dequantize_q8_blocks(v_codes, v_scales)[:, :, :prefix_len].transpose(0, 2, 1)
+    return k, v
