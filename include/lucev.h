@@ -267,6 +267,49 @@ int lucev_tree_attention_paged(const lucev_shape* shape, const lucev_tree* tree,
                                const uint16_t* v_tree, uint16_t* out, void* ws, size_t ws_bytes,
                                void* stream);
 
+/* ------------------------------------------------------------ int8 KV prefix */
+
+/* One layer's KV cache held as int8 codes with one fp16 scale per block of 32
+ * values: the q8_0 cache type the pages run beside F16 and Q4_0 ("Lucebox
+ * Hub", sections "Paged attention + continuous batching" and "설치·사용법"),
+ * read here as value = d * code, code in [-127, 127], d = fp16(amax / 127).
+ * Keys are blocked along the head dim of each token, values along the tokens
+ * of each dim (the cache keeps V dim-major):
+ *   k_codes  : int8 [Hkv][capacity][d]        (16-byte aligned)
+ *   k_scales : fp16 [Hkv][capacity][d / 32]   (8-byte aligned)
+ *   v_codes  : int8 [Hkv][d][capacity]        (16-byte aligned)
+ *   v_scales : fp16 [Hkv][d][capacity / 32]   (4-byte aligned)
+ * capacity is a multiple of 32; tokens 0 .. prefix_len - 1 are the prefix. */
+typedef struct {
+  const int8_t* k_codes;
+  const uint16_t* k_scales;
+  const int8_t* v_codes;
+  const uint16_t* v_scales;
+  int32_t prefix_len;
+  int32_t capacity;
+} lucev_kv_q8;
+
+/* Quantise every token (0 .. capacity - 1) of a bf16 cache (lucev_kv layout)
+ * into the int8 layout above: per block, amax, d = fp16(amax / 127) from an
+ * fp32 division, code = rint(x / d) from an fp32 division (ties to even)
+ * clamped to [-127, 127]; a block of zeros gets d = 0.  All pointers DEVICE.
+ * Requires src->capacity % 32 == 0.  Returns LUCEV_OK, LUCEV_ERR_NULL_ARG,
+ * LUCEV_ERR_BAD_SHAPE, LUCEV_ERR_BAD_KV, LUCEV_ERR_ALIGN, LUCEV_ERR_DEVICE or
+ * LUCEV_ERR_HIP. */
+int lucev_kv_quantize_q8(const lucev_shape* shape, const lucev_kv* src, int8_t* k_codes, uint16_t* k_scales,
+                         int8_t* v_codes, uint16_t* v_scales, void* stream);
+
+/* lucev_tree_attention over an int8 prefix: every prefix key and value enters
+ * as d * code exactly (the codes go through fp16 MFMAs one 32-wide block at a
+ * time and each block's fp32 sum is multiplied by its scale); queries and P
+ * are carried at about 22 significant bits.  q, k_tree, v_tree and out as in
+ * lucev_tree_attention.  Returns its codes; LUCEV_ERR_BAD_KV also for a
+ * capacity that is not a multiple of 32, LUCEV_ERR_ALIGN for the alignments
+ * above. */
+int lucev_tree_attention_q8(const lucev_shape* shape, const lucev_tree* tree, const lucev_kv_q8* kv,
+                            const uint16_t* q, const uint16_t* k_tree, const uint16_t* v_tree, uint16_t* out,
+                            void* ws, size_t ws_bytes, void* stream);
+
 /* Final RMSNorm, lm_head, greedy token and top1-top2 gap per node (taken on
  * the fp32 logits), then greedy acceptance over the tree: a node is accepted
  * when its parent is accepted and its drafted token equals the parent's

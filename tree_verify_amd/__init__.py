@@ -47,6 +47,11 @@ class lucev_kv(ctypes.Structure):
     _fields_ = [("k", c_vp), ("v", c_vp), ("prefix_len", c_i32), ("capacity", c_i32)]
 
 
+class lucev_kv_q8(ctypes.Structure):
+    _fields_ = [("k_codes", c_vp), ("k_scales", c_vp), ("v_codes", c_vp), ("v_scales", c_vp),
+                ("prefix_len", c_i32), ("capacity", c_i32)]
+
+
 class lucev_kv_paged(ctypes.Structure):
     _fields_ = [("k_pages", c_vp), ("v_pages", c_vp), ("block_table", c_vp), ("n_pages", c_i32),
                 ("prefix_len", c_i32)]
@@ -104,6 +109,11 @@ def lib() -> ctypes.CDLL:
         L.lucev_tree_attention_f32.restype = c_i32
         L.lucev_tree_attention_f32.argtypes = [P(lucev_shape), P(lucev_tree), P(lucev_kv), c_vp, c_vp, c_vp,
                                                c_vp, c_vp, c_sz, c_vp]
+        L.lucev_tree_attention_q8.restype = c_i32
+        L.lucev_tree_attention_q8.argtypes = [P(lucev_shape), P(lucev_tree), P(lucev_kv_q8), c_vp, c_vp, c_vp,
+                                              c_vp, c_vp, c_sz, c_vp]
+        L.lucev_kv_quantize_q8.restype = c_i32
+        L.lucev_kv_quantize_q8.argtypes = [P(lucev_shape), P(lucev_kv), c_vp, c_vp, c_vp, c_vp, c_vp]
         L.lucev_tree_attention_noalloc.restype = c_i32
         L.lucev_tree_attention_noalloc.argtypes = [P(lucev_shape), P(lucev_tree), P(lucev_kv), c_vp, c_vp,
                                                    c_vp, c_vp, c_vp]
@@ -122,7 +132,8 @@ def lib() -> ctypes.CDLL:
 EXPORTED = ["lucev_abi_version", "lucev_status_str", "lucev_last_error",
             "lucev_q4_packed_bytes", "lucev_q4_pack", "lucev_q4_pack_device",
             "lucev_workspace_bytes", "lucev_workspace_init", "lucev_verify_layer",
-            "lucev_tree_attention", "lucev_tree_attention_f32", "lucev_tree_attention_noalloc", "lucev_tree_attention_paged", "lucev_accept_path", "lucev_project_logits",
+            "lucev_tree_attention", "lucev_tree_attention_f32", "lucev_tree_attention_noalloc",
+            "lucev_tree_attention_q8", "lucev_kv_quantize_q8", "lucev_tree_attention_paged", "lucev_accept_path", "lucev_project_logits",
             "lucev_commit_path"]
 
 
@@ -223,6 +234,21 @@ def lucev_tree_attention_f32(shape, tree, kv, q, k_tree, v_tree, out, ws, ws_byt
     _check(lib().lucev_tree_attention_f32(ctypes.byref(shape), ctypes.byref(tree), ctypes.byref(kv),
                                           _ptr(q), _ptr(k_tree), _ptr(v_tree), _ptr(out), _ptr(ws),
                                           ws_bytes, stream), "lucev_tree_attention_f32")
+
+
+def make_kv_q8(k_codes, k_scales, v_codes, v_scales, prefix_len: int, capacity: int) -> lucev_kv_q8:
+    return lucev_kv_q8(_ptr(k_codes), _ptr(k_scales), _ptr(v_codes), _ptr(v_scales), prefix_len, capacity)
+
+
+def lucev_kv_quantize_q8(shape, src, k_codes, k_scales, v_codes, v_scales, stream=None) -> None:
+    _check(lib().lucev_kv_quantize_q8(ctypes.byref(shape), ctypes.byref(src), _ptr(k_codes), _ptr(k_scales),
+                                      _ptr(v_codes), _ptr(v_scales), stream), "lucev_kv_quantize_q8")
+
+
+def lucev_tree_attention_q8(shape, tree, kv, q, k_tree, v_tree, out, ws, ws_bytes, stream=None) -> None:
+    _check(lib().lucev_tree_attention_q8(ctypes.byref(shape), ctypes.byref(tree), ctypes.byref(kv), _ptr(q),
+                                         _ptr(k_tree), _ptr(v_tree), _ptr(out), _ptr(ws), ws_bytes, stream),
+           "lucev_tree_attention_q8")
 
 
 NOALLOC_SCRATCH_BYTES = 32 << 20

@@ -266,7 +266,7 @@ int run_attention(const lucev_shape* s, const TreeArgs& t, const lucev_kv* kv, c
                   const uint16_t* k_tree, const uint16_t* v_tree, const float* q32,
                   const float* k32, const float* v32, uint16_t* out, int out_hilo, float* o_part,
                   float* ml_part, hipStream_t st, const int32_t* table = nullptr, int n_phys = 0,
-                  float* out32 = nullptr) {
+                  float* out32 = nullptr, const lucev_kv_q8* q8 = nullptr) {
   AttnPlan plan = plan_attention(t.n, s->n_q_heads, s->n_kv_heads, s->head_dim, kv->prefix_len);
   if (table && plan.chunk / kPageTokens > kMaxChunkPagesHost)
     return fail(LUCEV_ERR_BAD_KV, "paged attention: %d-token prefix chunks exceed %d pages", plan.chunk,
@@ -289,6 +289,10 @@ int run_attention(const lucev_shape* s, const TreeArgs& t, const lucev_kv* kv, c
   p.table = table;
   p.n_phys = n_phys;
   p.ml_part = ml_part;
+  p.kc8 = q8 ? q8->k_codes : nullptr;
+  p.ks16 = q8 ? q8->k_scales : nullptr;
+  p.vc8 = q8 ? q8->v_codes : nullptr;
+  p.vs16 = q8 ? q8->v_scales : nullptr;
   CombineParams c;
   c.q = q;
   c.k_tree = k_tree;
@@ -307,7 +311,8 @@ int run_attention(const lucev_shape* s, const TreeArgs& t, const lucev_kv* kv, c
   c.out = out;
   c.out_hilo = out_hilo;
   c.out32 = out32;
-  hipError_t e = launch_attention(plan, s->head_dim, p, c, t, st);
+  hipError_t e = q8 ? launch_attention_q8(plan, s->head_dim, p, c, t, st)
+                    : launch_attention(plan, s->head_dim, p, c, t, st);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return LUCEV_OK;
 }
@@ -449,6 +454,62 @@ int lucev_tree_attention_f32(const lucev_shape* shape, const lucev_tree* tree, c
   // q, k_tree, v_tree as the fp32 inputs the verify step hands its attention
   return run_attention(shape, t, kv, nullptr, nullptr, nullptr, q, k_tree, v_tree, nullptr, 0,
                        at<float>(ws, L.opart), at<float>(ws, L.ml), (hipStream_t)stream, nullptr, 0, out);
+}
+
+static int check_kv_q8(const lucev_shape* shape, const lucev_kv_q8* kv) {
+  if (!kv) return fail(LUCEV_ERR_NULL_ARG, "kv is NULL");
+  if (kv->prefix_len < 0 || kv->capacity < 0 || kv->prefix_len > kv->capacity)
+    return fail(LUCEV_ERR_BAD_KV, "prefix_len %d / capacity %d invalid", kv->prefix_len, kv->capacity);
+  if (kv->capacity % 32) return fail(LUCEV_ERR_BAD_KV, "an int8 cache's capacity must be a multiple of 32");
+  if (kv->prefix_len > 0 && (!kv->k_codes || !kv->k_scales || !kv->v_codes || !kv->v_scales))
+    return fail(LUCEV_ERR_NULL_ARG, "int8 cache: NULL codes or scales");
+  if (!aligned16(kv->k_codes) || !aligned16(kv->v_codes) || (reinterpret_cast<uintptr_t>(kv->k_scales) & 7u) ||
+      (reinterpret_cast<uintptr_t>(kv->v_scales) & 3u))
+    return fail(LUCEV_ERR_ALIGN, "int8 cache: codes must be 16-byte, K scales 8-byte, V scales 4-byte aligned");
+  (void)shape;
+  return LUCEV_OK;
+}
+
+int lucev_tree_attention_q8(const lucev_shape* shape, const lucev_tree* tree, const lucev_kv_q8* kv,
+                            const uint16_t* q, const uint16_t* k_tree, const uint16_t* v_tree, uint16_t* out,
+                            void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (!q || !k_tree || !v_tree || !out) return fail(LUCEV_ERR_NULL_ARG, "tree_attention_q8: NULL tensor");
+  if ((rc = check_kv_q8(shape, kv))) return rc;
+  TreeArgs t;
+  if ((rc = prep_tree(tree, shape->vocab, kv->prefix_len, &t))) return rc;
+  if ((rc = check_attn_rows(shape, t.n))) return rc;
+  if (!aligned16(q) || !aligned16(k_tree) || !aligned16(v_tree) || !aligned16(out))
+    return fail(LUCEV_ERR_ALIGN, "tree_attention_q8: tensors must be 16-byte aligned");
+  Ws L;
+  if ((rc = check_ws(shape, t.n, kv->prefix_len, ws, ws_bytes, &L))) return rc;
+  if ((rc = check_device())) return rc;
+  lucev_kv flat;  // geometry only; the int8 arrays come from kv
+  flat.k = nullptr;
+  flat.v = nullptr;
+  flat.prefix_len = kv->prefix_len;
+  flat.capacity = kv->capacity;
+  return run_attention(shape, t, &flat, q, k_tree, v_tree, nullptr, nullptr, nullptr, out, 0,
+                       at<float>(ws, L.opart), at<float>(ws, L.ml), (hipStream_t)stream, nullptr, 0, nullptr, kv);
+}
+
+int lucev_kv_quantize_q8(const lucev_shape* shape, const lucev_kv* src, int8_t* k_codes, uint16_t* k_scales,
+                         int8_t* v_codes, uint16_t* v_scales, void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if ((rc = check_kv(src))) return rc;
+  if (!src->k || !src->v || !k_codes || !k_scales || !v_codes || !v_scales)
+    return fail(LUCEV_ERR_NULL_ARG, "kv_quantize_q8: NULL pointer");
+  if (src->capacity % 32) return fail(LUCEV_ERR_BAD_KV, "kv_quantize_q8: capacity must be a multiple of 32");
+  if (!aligned16(k_codes) || !aligned16(v_codes) || (reinterpret_cast<uintptr_t>(k_scales) & 1u) ||
+      (reinterpret_cast<uintptr_t>(v_scales) & 1u))
+    return fail(LUCEV_ERR_ALIGN, "kv_quantize_q8: codes must be 16-byte aligned");
+  if ((rc = check_device())) return rc;
+  hipError_t e = launch_quantize_q8(src->k, src->v, shape->n_kv_heads, src->capacity, shape->head_dim, k_codes,
+                                    k_scales, v_codes, v_scales, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "quantize launch");
+  return LUCEV_OK;
 }
 
 int lucev_tree_attention_noalloc(const lucev_shape* shape, const lucev_tree* tree, const lucev_kv* kv,

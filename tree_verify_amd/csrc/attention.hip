@@ -21,11 +21,10 @@
 //             the (at most 64) ancestor keys with a log-sum-exp merge.
 #include <type_traits>
 
-#include "internal.h"
+#include "attn_common.h"
 
 namespace lucev {
 
-constexpr int KT = 64;  // tokens per LDS tile
 constexpr int kMaxChunkPages = 1024;  // 16-token pages of one block's prefix chunk (paged cache)
 
 // Waves of the partial kernel: ROWW row waves (one to three per SIMD), each
@@ -68,28 +67,6 @@ constexpr int attn_waves(int roww, bool split) { return (void)split, roww; }
 // of one page; a 16-byte V chunk covers 8 tokens of one page), so the LDS
 // tiles, and hence the results, are those of the contiguous cache.  The
 // block's slice of the table is copied into LDS first, clamped to the pool.
-
-// max and sum over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48)
-__device__ __forceinline__ float rows_max(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float rows_sum(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
-// Two fp32 values as bf16 hi (nearest) and lo (the nearest bf16 of the
-// remainder): about 16 significant bits.
-__device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint32_t& lo) {
-  hi = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)a, (__bf16)b});
-  const float ha = __uint_as_float(hi << 16), hb = __uint_as_float(hi & 0xFFFF0000u);
-  lo = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)(a - ha), (__bf16)(b - hb)});
-}
 
 // SPLITM: 0 no split tile; 1 the quarters go to the last four of the waves
 // that own whole tiles; 2 to four extra waves that own no whole tile.
@@ -805,6 +782,10 @@ hipError_t launch_attention(const AttnPlan& plan, int head_dim, const AttnParams
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  return launch_combine(head_dim, c, t, s);
+}
+
+hipError_t launch_combine(int head_dim, const CombineParams& c, const TreeArgs& t, hipStream_t s) {
   const int blocks = c.n * c.n_q_heads;
   if (head_dim == 128)
     hipLaunchKernelGGL((attn_combine_kernel<128>), dim3(blocks), dim3(256), 0, s, c, t);

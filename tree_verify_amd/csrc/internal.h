@@ -133,6 +133,14 @@ struct AttnParams {
   float* ml_part;      // fp32 [n_chunks][Hkv][rows][2]: (max, sum) in log2 units
   const int32_t* table;  // paged cache: page of each 16 prefix tokens, or NULL (contiguous)
   int n_phys;            // pages in the pool (paged cache)
+  // int8 cache (attention_q8.hip): codes and fp16 scales, K blocked along the
+  // head dim of a token, V along the tokens of a dim
+  const int8_t* kc8;     // [Hkv][cap][d]
+  const uint16_t* ks16;  // [Hkv][cap][d / 32]
+  const int8_t* vc8;     // [Hkv][d][cap]
+  const uint16_t* vs16;  // [Hkv][d][cap / 32]
+  int q8_groups;         // row groups per (chunk, KV head), set by the int8 launch
+  int q8_tiles;          // query tiles per row group
 };
 constexpr int kPageTokens = 16;
 constexpr int kMaxChunkPagesHost = 1024;  // pages of one block's prefix chunk
@@ -160,6 +168,13 @@ AttnPlan plan_attention(int n_nodes, int n_q_heads, int n_kv_heads, int head_dim
 int attention_max_chunks(int n_kv_heads);
 hipError_t launch_attention(const AttnPlan& plan, int head_dim, const AttnParams& p,
                             const CombineParams& c, const TreeArgs& t, hipStream_t s);
+// the same over an int8 prefix (p.kc8 ..), and the merge both end with
+hipError_t launch_attention_q8(const AttnPlan& plan, int head_dim, const AttnParams& p,
+                               const CombineParams& c, const TreeArgs& t, hipStream_t s);
+hipError_t launch_combine(int head_dim, const CombineParams& c, const TreeArgs& t, hipStream_t s);
+// int8 block-32 quantisation of a bf16 cache's first cap tokens
+hipError_t launch_quantize_q8(const uint16_t* kc, const uint16_t* vc, int hkv, int cap, int d, int8_t* k_codes,
+                              uint16_t* k_scales, int8_t* v_codes, uint16_t* v_scales, hipStream_t s);
 
 // ---------------------------------------------------------------- small kernels
 
