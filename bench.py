@@ -71,9 +71,12 @@ def cpu_baseline(cfg, budget_s=10.0):
     shp = workload.shape(cfg)
     x = oracle.bf16_to_f64(synth.hidden_in(cfg))
     dt, layers = 0.0, 0
-    while layers < cfg.layers and dt < budget_s:
-        lw = workload.layer_weights(cfg, layers)
-        kp, vp = synth.kv_prefix(cfg, layers)
+    # layer after layer until budget_s of oracle time; a stack that is done
+    # sooner starts over from its first layer until at least 2 s
+    while dt < budget_s and (layers < cfg.layers or dt < 2.0):
+        l = layers % cfg.layers
+        lw = workload.layer_weights(cfg, l)
+        kp, vp = synth.kv_prefix(cfg, l)
         t0 = time.perf_counter()
         x = oracle.layer_forward(x, lw, kp, vp, parent, shp)[0]  # (residual, tree K, tree V)
         dt += time.perf_counter() - t0
@@ -91,7 +94,7 @@ def cpu_baseline(cfg, budget_s=10.0):
         pass
     return {"value": round(layers * layer_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle", "seconds": round(dt, 3),
-            "sample": "the first %d of the %d layers of the %s step (%d-token prefix, %d-node tree), "
+            "sample": "%d layer passes over the %d layers of the %s step (%d-token prefix, %d-node tree), "
                       "run in sequence; GB/s over those layers' algorithmic bytes" % (
                           layers, cfg.layers, cfg.name, cfg.prefix, cfg.nodes)}
 
@@ -229,27 +232,189 @@ def paged_leg(r, cfg, tv, shape, tree, q, out, dev, reps, layers=4):
     return us
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="stack27b")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--attn-reps", type=int, default=20)
-    ap.add_argument("--chain", type=int, default=8,
-                    help="verify+commit steps of the chained leg (0: skip)")
-    ap.add_argument("--copy-bytes", type=int, default=0,
-                    help="only run one device copy of this many bytes (counter calibration)")
-    args = ap.parse_args()
-    if args.copy_bytes:
-        copy_calibration(args.copy_bytes)
-        return
-    if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(got --gpus %d)" % args.gpus, flush=True)
-        sys.exit(2)
+def percentiles(ms):
+    import numpy as np
+    a = np.asarray(ms, np.float64)
+    return {"p10": round(float(np.percentile(a, 10)), 5), "p50": round(float(np.percentile(a, 50)), 5),
+            "p90": round(float(np.percentile(a, 90)), 5)}
 
+
+def timed_replays(graph, steps, stream=None, flush=None):
+    """Replays of one graph, each between two HIP events on the stream it runs
+    on; with `flush`, a write of the whole flush buffer (outside the events)
+    before every replay, so no cache holds the step's bytes."""
+    import torch
+    st = stream or torch.cuda.current_stream()
+    ms = []
+    with torch.cuda.stream(st):
+        evs = []
+        for i in range(steps):
+            if flush is not None:
+                flush.fill_(i & 0x7F)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            graph.replay()
+            e1.record(st)
+            evs.append((e0, e1))
+        st.synchronize()
+        ms = [a.elapsed_time(b) for a, b in evs]
+    return ms
+
+
+def graph_of(stream, fn, reps):
+    """A graph of `reps` calls fn(i) captured on `stream` (after three eager
+    calls), replayed once untimed; returns the graph."""
+    import torch
+    with torch.cuda.stream(stream):
+        for i in range(3):
+            fn(i)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(reps):
+                fn(i)
+        g.replay()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(stream, g, reps):
+    """Per-call time of a graph of reps calls: HIP events around one replay on
+    the stream the calls were launched on."""
+    import torch
+    with torch.cuda.stream(stream):
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        g.replay()
+        a1.record(stream)
+    torch.cuda.synchronize()
+    return a0.elapsed_time(a1) / reps * 1e3  # us
+
+
+def q8_leg(r, cfg, tv, shape, tree, q, out, dev, reps, bf16_us, layers=4):
+    """The one-layer tree attention over an int8 block-32 prefix: the first
+    `layers` layers' caches quantised on the device (set-up, not timed), then
+    lucev_tree_attention_q8 from a graph rotating over them, beside the same
+    call over the bf16 caches (lucev_tree_attention)."""
+    import torch
+    Hkv, d, P, cap = cfg.n_kv_heads, cfg.head_dim, cfg.prefix, r.capacity
+    if cap % 32:
+        return None
+    L = min(layers, cfg.layers)
+    caches = []
+    st = torch.cuda.current_stream().cuda_stream
+    for l in range(L):
+        kc = torch.empty(Hkv, cap, d, dtype=torch.int8, device=dev)
+        ks = torch.empty(Hkv, cap, d // 32, dtype=torch.int16, device=dev)
+        vc = torch.empty(Hkv, d, cap, dtype=torch.int8, device=dev)
+        vs = torch.empty(Hkv, d, cap // 32, dtype=torch.int16, device=dev)
+        tv.lucev_kv_quantize_q8(shape, r.kv(l, P), kc, ks, vc, vs, st)
+        caches.append((kc, ks, vc, vs))
+    torch.cuda.synchronize()
+    kvs = [tv.make_kv_q8(kc, ks, vc, vs, P, cap) for kc, ks, vc, vs in caches]
+    stream = torch.cuda.Stream()
+    g = graph_of(stream, lambda i: tv.lucev_tree_attention_q8(shape, tree, kvs[i % L], q, r.k_tree[0], r.v_tree[0],
+                                                            out, r.ws, r.ws_bytes, stream.cuda_stream), reps)
+    us = time_graph(stream, g, reps)
+    del g, caches
+    n, Hq = cfg.nodes, cfg.n_q_heads
+    kv_bytes = P * Hkv * d * 2 * (1 + 2 / 32)
+    tot = kv_bytes + 2 * n * Hq * d * 2 + 2 * n * Hkv * d * 2
+    return {"avg_launch_us": round(us, 3), "gbs": round(tot / (us * 1e-6) / 1e9, 2),
+            "prefix_bytes": int(kv_bytes), "prefix_bytes_bf16": P * Hkv * d * 4,
+            "vs_bf16_time": round(bf16_us / us, 4), "kernel": tv.lucev_describe_attention(shape, n, P, tv.ATTN_Q8),
+            "what": "lucev_tree_attention_q8 (bf16 q, int8 block-32 prefix with fp16 scales), rotating over %d "
+                    "layers' quantised caches; vs_bf16_time = lucev_tree_attention time / this" % L}
+
+
+def stream_ceiling(cfg, tv, dev, reps=10):
+    """A bare non-temporal read (lucev_stream_read) of each kernel's
+    algorithmic bytes, from a graph rotating over disjoint regions of a 4 GiB
+    buffer: the rate a kernel moving that many bytes can reach here."""
+    import torch
+    H, F, Hq, Hkv, d, V = cfg.hidden, cfg.ffn, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.vocab
+    wb = lambda n_out, k_in: n_out * k_in * 18 // 32
+    sizes = {"attention": attention_bytes(cfg, cfg.nodes), "qkv": wb((Hq + 2 * Hkv) * d, H),
+             "wo": wb(H, Hq * d), "gate_up": wb(2 * F, H), "down": wb(H, F), "lm_head": wb(V, H)}
+    region = 1 << 30
+    buf = torch.empty(4 * region, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    out = {}
+    stream = torch.cuda.Stream()
+    for k, nb in sizes.items():
+        nb = min(nb, region) // 16 * 16
+        g = graph_of(stream, lambda i: tv.lucev_stream_read(buf.data_ptr() + (i % 4) * region, nb, sink,
+                                                            stream.cuda_stream), reps)
+        us = time_graph(stream, g, reps)
+        del g
+        out[k] = {"bytes": nb, "us": round(us, 3), "gbs": round(nb / (us * 1e-6) / 1e9, 1)}
+    per_layer = sum(out[k]["us"] for k in ("attention", "qkv", "wo", "gate_up", "down"))
+    out["step_ms_if_bare_reads"] = round((cfg.layers * per_layer + out["lm_head"]["us"]) / 1e3, 4)
+    del buf
+    return out
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def crossover(args):
+    """MFMA against the VALU dot-product GEMM path at small trees: an 8-layer
+    27B-shape stack (4096-token prefix) plus head at n = 1, 2, 4, 8 nodes, with
+    lucev_set_gemv_max_rows 0 (MFMA only) and 8 (dot products up to 8 operand
+    rows), each step replayed from a graph and timed with HIP events."""
+    import torch
+    import synth
+    import synth.device as sd
+    import tree_verify_amd as tv
+    from tree_verify_amd.runner import VerifyRunner
+    dev = torch.device("cuda:0")
+    base = synth.get("stack27b").replace(layers=8, prefix=4096, name="stack27b_8l_p4096")
+    out = {}
+    for n in (1, 2, 4, 8):
+        cfg = base.replace(nodes=n, max_children=None, max_depth=None)
+        wl = sd.Workload(cfg, device=dev)
+        shape = tv.make_shape(cfg.hidden, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ffn, cfg.vocab)
+        tree = tv.make_tree(synth.tree_parents(cfg), [0] * n)
+        x = wl.x_in_f32().contiguous()
+        for rows in (0, 8):
+            tv.lucev_set_gemv_max_rows(rows)
+            r = VerifyRunner(shape, wl.layers, wl.head, n, wl.capacity, dev, keep_logits=False)
+            st = torch.cuda.Stream()
+            with torch.cuda.stream(st):
+                r.step(tree, x, cfg.prefix, with_logits=False)
+                st.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=st):
+                    r.step(tree, x, cfg.prefix, with_logits=False)
+            torch.cuda.synchronize()
+            for _ in range(3):
+                g.replay()
+            ms = percentiles(timed_replays(g, args.steps))
+            out.setdefault("n%d" % n, {})["mfma" if rows == 0 else "valu_up_to_8_rows"] = ms
+            log("crossover n %d gemv rows %d: p50 %.4f ms" % (n, rows, ms["p50"]))
+            del g, r
+        tv.lucev_set_gemv_max_rows(0)
+        del wl
+        torch.cuda.empty_cache()
+    return {"crossover": out, "workload": base.name,
+            "what": "step ms (p10/p50/p90 over %d replays) with the int4 GEMMs on MFMA vs on VALU dot products "
+                    "wherever the operand rows (2 per node for QKV/Wo/lm_head, 1 for gate/up and down) are <= 8"
+                    % args.steps}
+
+
+CONFIGS_ALL = ["tiny", "small_decode", "small_tree", "layer27b", "stack27b", "longctx27b"]
+
+
+def run_config(cfg, args):
     import numpy as np
     import torch
     import synth
@@ -257,7 +422,6 @@ def main():
     import tree_verify_amd as tv
     from tree_verify_amd.runner import VerifyRunner
 
-    cfg = synth.get(args.config)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t0 = time.time()
@@ -281,6 +445,8 @@ def main():
         with torch.cuda.graph(graph, stream=stream):
             r.step(tree, x32, cfg.prefix, with_logits=False)
     torch.cuda.synchronize()
+    # warm: back-to-back replays, the K timed ones between one pair of events
+    # (the contract's figure) and each also between its own pair
     for _ in range(args.warmup):
         graph.replay()
     torch.cuda.synchronize()
@@ -291,48 +457,57 @@ def main():
     ev1.record()
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / args.steps
+    warm = timed_replays(graph, args.steps)
+    # cold: a 1 GiB write before each replay evicts L2 and the 256 MB
+    # last-level cache, so every byte of the step comes from HBM
+    flush = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device=dev)
+    cold = timed_replays(graph, args.cold_steps, flush=flush)
+    del flush
     path = r.path.cpu().numpy()[: int(r.path_len.item())].tolist()
     wb, kvb, ob = algorithmic_bytes(cfg, cfg.nodes)
     total = wb + kvb + ob
     gbs = total / (ms * 1e-3) / 1e9
-    log("step %.4f ms, %.1f GB/s (weights %.3f GB, KV %.3f GB, other %.4f GB), path %s" %
-        (ms, gbs, wb / 1e9, kvb / 1e9, ob / 1e9, path))
+    cold_p = percentiles(cold)
+    log("%s: step %.4f ms (warm p50 %.4f, cold p50 %.4f), %.1f GB/s, path %s" %
+        (cfg.name, ms, percentiles(warm)["p50"], cold_p["p50"], gbs, path))
 
-    # dominant kernel by bytes: the tree attention of one layer (prefix split
-    # partial kernel + combine), timed alone on its own stream with HIP events
-    astream = torch.cuda.Stream()
+    # dominant kernel by bytes: the step's own tree attention (fp32 q split
+    # into bf16 hi + lo, partial + combine) of one layer, launched through
+    # lucev_tree_attention_f32 from a graph on its own stream, rotating over
+    # the layers' caches; HIP events on that stream
     Hq, Hkv, d, n = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.nodes
+    rng = np.random.default_rng(cfg.seed)
+    q32 = torch.from_numpy(rng.standard_normal((n, Hq, d)).astype(np.float32)).to(dev)
+    k32 = torch.from_numpy(rng.standard_normal((n, Hkv, d)).astype(np.float32)).to(dev)
+    v32 = torch.from_numpy(rng.standard_normal((n, Hkv, d)).astype(np.float32)).to(dev)
+    o32 = torch.zeros(n, Hq, d, dtype=torch.float32, device=dev)
     q = sd.flat_table("normal", synth.stream_key(cfg.seed, 90, 0), n * Hq * d, dev)
     out = torch.zeros(n * Hq * d, dtype=torch.int16, device=dev)
-    torch.cuda.synchronize()  # q / out were made on the default stream
-    kv0 = r.kv(0, cfg.prefix)
-    with torch.cuda.stream(astream):
-        st = astream.cuda_stream
-        for _ in range(3):
-            tv.lucev_tree_attention(shape, tree, kv0, q, r.k_tree[0], r.v_tree[0], out, r.ws,
-                                    r.ws_bytes, st)
-        # the timed launches are replayed from a graph, so host-side call
-        # overhead cannot open gaps between them
-        ag = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(ag, stream=astream):
-            for i in range(args.attn_reps):
-                kvi = r.kv(i % cfg.layers, cfg.prefix)
-                tv.lucev_tree_attention(shape, tree, kvi, q, r.k_tree[0], r.v_tree[0], out, r.ws,
-                                        r.ws_bytes, astream.cuda_stream)
-        ag.replay()
-        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a0.record(astream)
-        ag.replay()
-        a1.record(astream)
     torch.cuda.synchronize()
+    astream = torch.cuda.Stream()
+    ag = graph_of(astream, lambda i: tv.lucev_tree_attention_f32(shape, tree, r.kv(i % cfg.layers, cfg.prefix), q32,
+                                                                k32, v32, o32, r.ws, r.ws_bytes,
+                                                                astream.cuda_stream), args.attn_reps)
+    attn_us = time_graph(astream, ag, args.attn_reps)
     del ag
-    attn_ms = a0.elapsed_time(a1) / args.attn_reps
+    bg = graph_of(astream, lambda i: tv.lucev_tree_attention(shape, tree, r.kv(i % cfg.layers, cfg.prefix), q,
+                                                            r.k_tree[0], r.v_tree[0], out, r.ws, r.ws_bytes,
+                                                            astream.cuda_stream), args.attn_reps)
+    bf16_us = time_graph(astream, bg, args.attn_reps)
+    del bg
     ab = attention_bytes(cfg, n)
-    attn_gbs = ab / (attn_ms * 1e-3) / 1e9
-    log("tree attention (one layer): %.2f us, %.1f GB/s" % (attn_ms * 1e3, attn_gbs))
+    attn_gbs = ab / (attn_us * 1e-6) / 1e9
+    log("tree attention (one layer, step variant): %.2f us, %.1f GB/s; bf16-q API %.2f us" %
+        (attn_us, attn_gbs, bf16_us))
     paged_us = paged_leg(r, cfg, tv, shape, tree, q, out, dev, args.attn_reps) if cfg.prefix > 0 else None
     if paged_us:
-        log("paged tree attention (one layer): %.2f us, %.1f GB/s" % (paged_us, ab / (paged_us * 1e-6) / 1e9))
+        log("paged tree attention (one layer): %.2f us" % paged_us)
+    q8 = None
+    if cfg.prefix > 0 and not args.no_q8:
+        q8 = q8_leg(r, cfg, tv, shape, tree, q, out, dev, args.attn_reps, bf16_us)
+        if q8:
+            log("int8-prefix tree attention (one layer): %.2f us (%.3fx the bf16 prefix's speed)" %
+                (q8["avg_launch_us"], q8["vs_bf16_time"]))
 
     line = {
         "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
@@ -344,27 +519,78 @@ def main():
                    "heads": "%d/%d" % (cfg.n_q_heads, cfg.n_kv_heads), "head_dim": cfg.head_dim,
                    "ffn": cfg.ffn, "vocab": cfg.vocab, "prefix": cfg.prefix, "tree_nodes": cfg.nodes,
                    "algorithmic_bytes": total, "tokens": tok_src, "accepted_path": path},
-        "roofline": {"bound": "hbm", "kernel": "tree attention, one layer (partial + combine)",
+        "warm_ms": percentiles(warm),
+        "cold_ms": dict(cold_p, steps=args.cold_steps, gbs_p50=round(total / (cold_p["p50"] * 1e-3) / 1e9, 2),
+                        what="each replay after a %d MiB write outside its events" % args.flush_mib),
+        "roofline": {"bound": "hbm", "kernel": tv.lucev_describe_attention(shape, n, cfg.prefix, tv.ATTN_F32),
                      "achieved": round(attn_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                     "bytes_per_launch": ab, "avg_launch_us": round(attn_ms * 1e3, 3)},
+                     "bytes_per_launch": ab, "avg_launch_us": round(attn_us, 3),
+                     "timed": "lucev_tree_attention_f32 (the verify step's variant), a graph of %d launches "
+                              "rotating over the layers' caches, HIP events on the launch stream" % args.attn_reps},
         "step_roofline_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "attention_bf16q_us": round(bf16_us, 3),
     }
     if paged_us:
         line["paged_attention"] = {"avg_launch_us": round(paged_us, 3),
                                    "gbs": round(ab / (paged_us * 1e-6) / 1e9, 2),
-                                   "vs_contiguous": round(attn_ms * 1e3 / paged_us, 4),
-                                   "what": "lucev_tree_attention_paged, the prefix in a shuffled pool of "
-                                           "16-token pages, rotating over 4 layers' pools"}
+                                   "vs_contiguous": round(bf16_us / paged_us, 4),
+                                   "what": "lucev_tree_attention_paged (bf16 q), the prefix in a shuffled pool of "
+                                           "16-token pages, rotating over 4 layers' pools; vs_contiguous = "
+                                           "lucev_tree_attention time / this"}
+    if q8:
+        line["q8_attention"] = q8
     if args.chain > 0:
         del graph
         line["chained"] = chained(r, cfg, tv, args.chain, dev)
         log("chained: %s" % json.dumps(line["chained"]))
+    del wl, r
+    torch.cuda.empty_cache()
+    if not args.no_ceiling:
+        sc = stream_ceiling(cfg, tv, dev)
+        line["stream_ceiling"] = sc
+        line["step_vs_bare_reads"] = round(sc["step_ms_if_bare_reads"] / ms, 4)
     if not args.no_cpu_baseline:
-        del wl, r
         torch.cuda.empty_cache()
-        line["cpu_baseline"] = cpu_baseline(cfg)
-    print(json.dumps(line), flush=True)
+        cb = cpu_baseline(cfg)
+        cb["cpu_model"] = cpu_model()
+        line["cpu_baseline"] = cb
+    return line
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="stack27b", help="a config name, or 'all' (one JSON line each)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-q8", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true")
+    ap.add_argument("--attn-reps", type=int, default=20)
+    ap.add_argument("--cold-steps", type=int, default=10)
+    ap.add_argument("--flush-mib", type=int, default=1024)
+    ap.add_argument("--chain", type=int, default=8,
+                    help="verify+commit steps of the chained leg (0: skip)")
+    ap.add_argument("--crossover", action="store_true",
+                    help="only compare the MFMA and VALU GEMM paths at 1, 2, 4, 8 nodes")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run one device copy of this many bytes (counter calibration)")
+    args = ap.parse_args()
+    if args.copy_bytes:
+        copy_calibration(args.copy_bytes)
+        return
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(got --gpus %d)" % args.gpus, flush=True)
+        sys.exit(2)
+    if args.crossover:
+        print(json.dumps(crossover(args)), flush=True)
+        return
+    import synth
+    names = CONFIGS_ALL if args.config == "all" else [args.config]
+    for name in names:
+        print(json.dumps(run_config(synth.get(name), args)), flush=True)
 
 
 if __name__ == "__main__":

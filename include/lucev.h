@@ -387,6 +387,46 @@ int lucev_commit_path(const lucev_shape* shape, int32_t n_layers, uint16_t* cons
                       int32_t n_nodes, const int32_t* path, const int32_t* path_len,
                       void* stream);
 
+/*
+ * lucev_set_gemv_max_rows: GEMM operand rows (two per node for the QKV, Wo
+ * and lm_head projections, whose activations travel as fp16 hi + lo rows; one
+ * per node for gate/up and down) at or below which the int4 projections take
+ * dot products on the vector ALUs (v_dot2_f32_f16) instead of MFMA.  The
+ * spec asks for MFMA only where M makes a dense contraction; measured
+ * on MI355X, MFMA is no slower at any node count (the dot products come
+ * within 5 % at one or two operand rows and lose from four on), so the
+ * default is 0.  rows in [0, 8], else LUCEV_ERR_BAD_SHAPE.  Process-wide; applies to
+ * calls made (and workspaces sized) afterwards, not to captured graphs.
+ */
+int lucev_set_gemv_max_rows(int32_t rows);
+
+/*
+ * Measurement helpers (not part of the verify step).
+ *
+ * lucev_describe_attention: the kernels the tree attention launches for this
+ * shape, tree size and prefix length -- the same plan every attention entry
+ * point uses -- as text: each kernel's template, grid and block, and the
+ * prefix chunk per workgroup.  variant 0 = lucev_tree_attention (bf16 q),
+ * 1 = lucev_tree_attention_f32 and the verify step (fp32 q, split into bf16
+ * hi + lo), 2 = lucev_tree_attention_paged, 3 = lucev_tree_attention_q8.
+ * Writes at most buf_len bytes, NUL-terminated (truncated if longer).
+ * Errors as lucev_tree_attention for the shape and tree size
+ * (LUCEV_ERR_BAD_SHAPE, LUCEV_ERR_BAD_TREE); LUCEV_ERR_NULL_ARG for a NULL or
+ * empty buf.  Host only: enqueues nothing.
+ *
+ * lucev_stream_read: reads `bytes` of device memory at src once, with
+ * non-temporal 16-byte loads spread over every CU, and enqueues nothing else;
+ * sink (device, 4 bytes) is written only when the loads' XOR fold hits one
+ * fixed value.  Its duration at a given size is the read rate a kernel that
+ * streams that many bytes can reach on this device (launch, ramp-up and tail
+ * included), the practical ceiling beside the 8 TB/s peak.  src 16-byte
+ * aligned and bytes a multiple of 16 (LUCEV_ERR_ALIGN), src and sink non-NULL
+ * (LUCEV_ERR_NULL_ARG).
+ */
+int lucev_describe_attention(const lucev_shape* shape, int32_t n_nodes, int32_t prefix_len, int32_t variant,
+                             char* buf, size_t buf_len);
+int lucev_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -254,6 +254,22 @@ def test_layer27b_four_node_tiles_parity():
     _check_case(cfg, cfg.seed + 28)
 
 
+# Decode-sized trees at the 27B layer shape, on MFMA (the default) and on the
+# VALU dot-product path (gemv rows 8: every projection of 1 and 2 nodes, and
+# gate/up and down of 4 nodes, take dot products; 2, 4 or 8 operand rows).
+@pytest.mark.parametrize("nodes,gemv", [(1, 0), (2, 0), (4, 0), (1, 8), (2, 8), (4, 8)])
+def test_layer27b_small_tree_parity(nodes, gemv):
+    import tree_verify_amd as tv
+    need_gpu()
+    cfg = synth.get("layer27b").replace(nodes=nodes, max_children=None, max_depth=None,
+                                        name="layer27b_n%d" % nodes)
+    tv.lucev_set_gemv_max_rows(gemv)
+    try:
+        _check_case(cfg, cfg.seed + 100 + nodes)
+    finally:
+        tv.lucev_set_gemv_max_rows(0)
+
+
 @pytest.mark.parametrize("run", range(2))
 def test_small_tree_config_parity(run):
     cfg = synth.get("small_tree")

@@ -125,6 +125,12 @@ def lib() -> ctypes.CDLL:
         L.lucev_commit_path.restype = c_i32
         L.lucev_commit_path.argtypes = [P(lucev_shape), c_i32, P(c_vp), P(c_vp), P(c_vp), P(c_vp),
                                         c_i32, c_i32, c_i32, c_vp, c_vp, c_vp]
+        L.lucev_describe_attention.restype = c_i32
+        L.lucev_describe_attention.argtypes = [P(lucev_shape), c_i32, c_i32, c_i32, ctypes.c_char_p, c_sz]
+        L.lucev_set_gemv_max_rows.restype = c_i32
+        L.lucev_set_gemv_max_rows.argtypes = [c_i32]
+        L.lucev_stream_read.restype = c_i32
+        L.lucev_stream_read.argtypes = [c_vp, c_sz, c_vp, c_vp]
         _lib = L
     return _lib
 
@@ -134,7 +140,8 @@ EXPORTED = ["lucev_abi_version", "lucev_status_str", "lucev_last_error",
             "lucev_workspace_bytes", "lucev_workspace_init", "lucev_verify_layer",
             "lucev_tree_attention", "lucev_tree_attention_f32", "lucev_tree_attention_noalloc",
             "lucev_tree_attention_q8", "lucev_kv_quantize_q8", "lucev_tree_attention_paged", "lucev_accept_path", "lucev_project_logits",
-            "lucev_commit_path"]
+            "lucev_commit_path", "lucev_describe_attention", "lucev_stream_read",
+            "lucev_set_gemv_max_rows"]
 
 
 def _ptr(x) -> Optional[int]:
@@ -302,3 +309,21 @@ def lucev_commit_path(shape, k_cache, v_cache, k_tree, v_tree, prefix_len, capac
     _check(lib().lucev_commit_path(ctypes.byref(shape), n, arrs[0], arrs[1], arrs[2], arrs[3],
                                    prefix_len, capacity, n_nodes, _ptr(path), _ptr(path_len),
                                    stream), "lucev_commit_path")
+
+
+ATTN_BF16, ATTN_F32, ATTN_PAGED, ATTN_Q8 = 0, 1, 2, 3
+
+
+def lucev_describe_attention(shape, n_nodes: int, prefix_len: int, variant: int) -> str:
+    buf = ctypes.create_string_buffer(512)
+    _check(lib().lucev_describe_attention(ctypes.byref(shape), n_nodes, prefix_len, variant, buf, len(buf)),
+           "lucev_describe_attention")
+    return buf.value.decode()
+
+
+def lucev_stream_read(src, nbytes: int, sink, stream=None) -> None:
+    _check(lib().lucev_stream_read(_ptr(src), nbytes, _ptr(sink), stream), "lucev_stream_read")
+
+
+def lucev_set_gemv_max_rows(rows: int) -> None:
+    _check(lib().lucev_set_gemv_max_rows(rows), "lucev_set_gemv_max_rows")

@@ -241,6 +241,7 @@ GemmParams gemm_params(const lucev_q4& w, const uint16_t* X, int n, bool exact, 
   p.c_max = pl.c_max;
   p.ug = pl.ug;
   p.ft = pl.ft;
+  p.vr = pl.vr;
   return p;
 }
 
@@ -743,6 +744,41 @@ int lucev_commit_path(const lucev_shape* shape, int32_t n_layers, uint16_t* cons
   if ((rc = check_device())) return rc;
   hipError_t e = launch_commit(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "commit launch");
+  return LUCEV_OK;
+}
+
+int lucev_describe_attention(const lucev_shape* shape, int32_t n_nodes, int32_t prefix_len, int32_t variant,
+                             char* buf, size_t buf_len) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (!buf || buf_len == 0) return fail(LUCEV_ERR_NULL_ARG, "describe_attention: NULL buffer");
+  if (n_nodes < 1 || n_nodes > LUCEV_MAX_NODES || prefix_len < 0)
+    return fail(LUCEV_ERR_BAD_TREE, "describe_attention: n_nodes %d / prefix_len %d invalid", n_nodes, prefix_len);
+  if ((rc = check_attn_rows(shape, n_nodes))) return rc;
+  if (variant < 0 || variant > 3) return fail(LUCEV_ERR_BAD_SHAPE, "describe_attention: variant %d", variant);
+  const AttnPlan plan = plan_attention(n_nodes, shape->n_q_heads, shape->n_kv_heads, shape->head_dim, prefix_len);
+  const int cb = n_nodes * shape->n_q_heads;
+  if (variant == 3)
+    describe_attention_q8(plan, shape->head_dim, shape->n_kv_heads, cb, buf, buf_len);
+  else
+    describe_attention(plan, shape->head_dim, shape->n_kv_heads, cb, variant == 1, variant == 2, buf, buf_len);
+  return LUCEV_OK;
+}
+
+int lucev_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  if (!sink || (bytes > 0 && !src)) return fail(LUCEV_ERR_NULL_ARG, "stream_read: NULL pointer");
+  if (bytes % 16 || !aligned16(src) || (reinterpret_cast<uintptr_t>(sink) & 3u))
+    return fail(LUCEV_ERR_ALIGN, "stream_read: src must be 16-byte aligned, bytes a multiple of 16, sink 4-byte aligned");
+  int rc = check_device();
+  if (rc) return rc;
+  hipError_t e = launch_stream_read(src, bytes, sink, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "stream read launch");
+  return LUCEV_OK;
+}
+
+int lucev_set_gemv_max_rows(int32_t rows) {
+  if (rows < 0 || rows > 8) return fail(LUCEV_ERR_BAD_SHAPE, "set_gemv_max_rows: %d outside [0, 8]", rows);
+  g_gemv_max_rows = rows;
   return LUCEV_OK;
 }
 

@@ -19,6 +19,8 @@
 //             row): max and sum in log2 units and the chunk-normalised O.
 //   combine: one block per (node, query head): merges the chunk partials and
 //             the (at most 64) ancestor keys with a log-sum-exp merge.
+#include <stdio.h>
+
 #include <type_traits>
 
 #include "attn_common.h"
@@ -738,38 +740,67 @@ static void launch_partial(const AttnPlan& plan, const AttnParams& p, hipStream_
     hipLaunchKernelGGL((attn_partial_kernel<D, QPW, ROWW, kAttnBufs, false, SPLITM, false>), grid, block, 0, s, p);
 }
 
-template <int D>
-static void launch_partial_d(const AttnPlan& plan, const AttnParams& p, hipStream_t s) {
+// The partial kernel's wave layout for a plan: (tiles per row wave, row
+// waves, where a split tile goes), as launch_partial_d instantiates it.
+struct PartialLayout {
+  int qpw, roww, splitm;
+};
+static PartialLayout partial_layout(const AttnPlan& plan) {
   if (plan.split) {
 #if LUCEV_ATTN_SPLIT_LAYOUT == 2
-    if (plan.qpw == 1) launch_partial<D, 1, 4, 1>(plan, p, s);
-    else launch_partial<D, 2, 4, 1>(plan, p, s);
+    return {plan.qpw == 1 ? 1 : 2, 4, 1};
 #elif LUCEV_ATTN_SPLIT_LAYOUT == 1
-    if (plan.roww == 4) launch_partial<D, 1, 4, 1>(plan, p, s);
-    else launch_partial<D, 1, 8, 1>(plan, p, s);
+    return {1, plan.roww == 4 ? 4 : 8, 1};
 #else
-    if (plan.roww == 8) launch_partial<D, 1, 8, 2>(plan, p, s);
-    else launch_partial<D, 1, 12, 2>(plan, p, s);
+    return {1, plan.roww == 8 ? 8 : 12, 2};
 #endif
-    return;
   }
-  if (plan.qpw == 1) {
-    if (plan.roww == 4) launch_partial<D, 1, 4, 0>(plan, p, s);
-    else if (plan.roww == 8) launch_partial<D, 1, 8, 0>(plan, p, s);
-    else launch_partial<D, 1, 12, 0>(plan, p, s);
-    return;
-  }
+  if (plan.qpw == 1) return {1, plan.roww == 4 ? 4 : (plan.roww == 8 ? 8 : 12), 0};
 #if LUCEV_ATTN_WIDE4
-  if (plan.roww == 4) {
-    launch_partial<D, 4, 4, 0>(plan, p, s);
-    return;
-  }
+  if (plan.roww == 4) return {4, 4, 0};
 #endif
-  switch (plan.qpw) {
-    case 2: launch_partial<D, 2, 8, 0>(plan, p, s); break;
-    case 3: launch_partial<D, 3, 8, 0>(plan, p, s); break;
-    default: launch_partial<D, 4, 8, 0>(plan, p, s); break;
+  return {plan.qpw <= 2 ? 2 : (plan.qpw == 3 ? 3 : 4), 8, 0};
+}
+
+template <int D>
+static void launch_partial_d(const AttnPlan& plan, const AttnParams& p, hipStream_t s) {
+  const PartialLayout v = partial_layout(plan);
+#define LUCEV_PARTIAL(Q, R, S)                  \
+  if (v.qpw == Q && v.roww == R && v.splitm == S) { \
+    launch_partial<D, Q, R, S>(plan, p, s);     \
+    return;                                     \
   }
+#if LUCEV_ATTN_SPLIT_LAYOUT == 2
+  LUCEV_PARTIAL(1, 4, 1)
+  LUCEV_PARTIAL(2, 4, 1)
+#elif LUCEV_ATTN_SPLIT_LAYOUT == 1
+  LUCEV_PARTIAL(1, 4, 1)
+  LUCEV_PARTIAL(1, 8, 1)
+#else
+  LUCEV_PARTIAL(1, 8, 2)
+  LUCEV_PARTIAL(1, 12, 2)
+#endif
+#if LUCEV_ATTN_WIDE4
+  LUCEV_PARTIAL(4, 4, 0)
+#endif
+  LUCEV_PARTIAL(1, 4, 0)
+  LUCEV_PARTIAL(1, 8, 0)
+  LUCEV_PARTIAL(1, 12, 0)
+  LUCEV_PARTIAL(2, 8, 0)
+  LUCEV_PARTIAL(3, 8, 0)
+  LUCEV_PARTIAL(4, 8, 0)
+#undef LUCEV_PARTIAL
+}
+
+int describe_attention(const AttnPlan& plan, int head_dim, int n_kv_heads, int combine_blocks, bool fp32_q,
+                       bool paged, char* buf, size_t len) {
+  const PartialLayout v = partial_layout(plan);
+  return snprintf(buf, len,
+                  "attn_partial_kernel<%d, %d, %d, %d, %s, %d, %s> grid (%d, %d) block %d, %d-token chunks; "
+                  "attn_combine_kernel<%d> grid %d block 256",
+                  head_dim, v.qpw, v.roww, kAttnBufs, (fp32_q && !paged) ? "true" : "false", v.splitm,
+                  paged ? "true" : "false", plan.n_chunks, n_kv_heads, 64 * v.roww, plan.chunk, head_dim,
+                  combine_blocks);
 }
 
 hipError_t launch_attention(const AttnPlan& plan, int head_dim, const AttnParams& p,

@@ -20,11 +20,14 @@
 //     1152) and stored into LDS in the bf16 kernel's swizzled layout, with
 //     the tile's scales beside them; the next tile's loads fly while the
 //     current tile is computed;
-//   * the MFMAs are f16 (codes exact, queries and P as fp16 hi + lo), one
-//     32-deep block at a time, and each block's fp32 result is multiplied by
-//     its scale as it is accumulated, so d * code enters exactly;
+//   * the MFMAs are f16 (codes exact; queries and P as nearest fp16, each
+//     off by at most 2^-11 of itself), one 32-deep block at a time, and each
+//     block's fp32 result is multiplied by its scale as it is accumulated, so
+//     d * code enters exactly;
 //   * no split query tile.
 // The combine kernel is the bf16 path's.
+#include <stdio.h>
+
 #include "attn_common.h"
 
 namespace lucev {
@@ -46,24 +49,23 @@ __device__ __forceinline__ u32x2 codes4_f16(uint32_t w) {
   return u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
 }
 
-// Two fp32 values as fp16 hi (nearest) and lo (the nearest fp16 of the
-// remainder): about 22 significant bits.
-__device__ __forceinline__ void split_pair_f16(float a, float b, uint32_t& hi, uint32_t& lo) {
-  const f16 ha = (f16)a, hb = (f16)b;
-  hi = __builtin_bit_cast(uint32_t, f16x2{ha, hb});
-  lo = __builtin_bit_cast(uint32_t, f16x2{(f16)(a - (float)ha), (f16)(b - (float)hb)});
+// Two fp32 values as fp16 (nearest), packed
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, f16x2{(f16)a, (f16)b});
 }
 
 // LDS tile of the int8 path: K [64 keys][D] fp16 and V^T [D][64] fp16 in the
-// bf16 kernel's swizzled layouts, then the K scales [64 keys][D/32] and the V
-// scales [D][2] (the tile's two 32-token blocks), all fp16.
+// bf16 kernel's swizzled layouts, then the scales widened to fp32 once, as
+// they are stored: K scales [D/32 blocks][64 keys] and V scales [2 token
+// blocks][D], so the four a lane applies to one MFMA result are one 16-byte
+// read.
 template <int D>
 struct Q8Tile {
   static constexpr int KBYTES = KT * D * 2;
   static constexpr int VBYTES = D * KT * 2;
   static constexpr int KSC = KBYTES + VBYTES;             // K scales
-  static constexpr int VSC = KSC + KT * (D / 32) * 2;     // V scales
-  static constexpr int BYTES = VSC + D * 2 * 2;
+  static constexpr int VSC = KSC + KT * (D / 32) * 4;     // V scales
+  static constexpr int BYTES = VSC + D * 2 * 4;
   // global loads per tile, 16 bytes a lane: K codes (one lane: 16 codes of a
   // key), V codes (16 tokens of a dim), K scales (8 bytes a lane), V scales
   // (4 bytes a lane per dim, two loads)
@@ -173,20 +175,23 @@ __global__ __launch_bounds__(ROWW * 64) void attn_partial_q8_kernel(
       *reinterpret_cast<u32x4*>(row + (((2 * part) ^ swz) * 16)) = u32x4{a[0], a[1], bb[0], bb[1]};
       *reinterpret_cast<u32x4*>(row + (((2 * part + 1) ^ swz) * 16)) = u32x4{c[0], c[1], d[0], d[1]};
     } else if (j == T::NK + T::NV) {
-      if constexpr (NBLK == 4)
-        *reinterpret_cast<u32x2*>(base + T::KSC + lane * 8) = u32x2{v[0], v[1]};
-      else
-        *reinterpret_cast<uint32_t*>(base + T::KSC + lane * 4) = v[0];
+      float* ksc = reinterpret_cast<float*>(base + T::KSC);
+#pragma unroll
+      for (int b = 0; b < NBLK; ++b)
+        ksc[b * KT + lane] = (float)__builtin_bit_cast(f16, (uint16_t)(v[b >> 1] >> (16 * (b & 1))));
     } else {
       const int dim = (j - T::NK - T::NV - 1) * 64 + lane;
-      if (dim < D) *reinterpret_cast<uint32_t*>(base + T::VSC + dim * 4) = v[0];
+      float* vsc = reinterpret_cast<float*>(base + T::VSC);
+      if (dim < D) {
+        vsc[dim] = (float)__builtin_bit_cast(f16, (uint16_t)(v[0] & 0xFFFFu));
+        vsc[D + dim] = (float)__builtin_bit_cast(f16, (uint16_t)(v[0] >> 16));
+      }
     }
   };
 
-  // this wave's query tiles: w, w + ROWW, ...; Q^T as fp16 hi + lo, scaled to
-  // log2 units
+  // this wave's query tile; Q^T as fp16, scaled to log2 units
   typedef f16 f16x8_t __attribute__((ext_vector_type(8)));
-  f16x8_t qf[D / 32], ql[D / 32];
+  f16x8_t qf[D / 32];
   f32x4 O[D / 16];
   float m = -INFINITY, l = 0.f;
   {
@@ -203,15 +208,14 @@ __global__ __launch_bounds__(ROWW * 64) void attn_partial_q8_kernel(
     for (int kk = 0; kk < D / 32; ++kk) raw[kk] = ld16(p.q + qoff + kk * 32);
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) {
-      uint32_t hv[4], lv[4];
+      uint32_t hv[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float x0 = ok ? bf16_bits_to_f32(raw[kk][e] & 0xFFFFu) * p.scale_log2 : 0.f;
         const float x1 = ok ? bf16_bits_to_f32(raw[kk][e] >> 16) * p.scale_log2 : 0.f;
-        split_pair_f16(x0, x1, hv[e], lv[e]);
+        hv[e] = pack_f16(x0, x1);
       }
       qf[kk] = __builtin_bit_cast(f16x8_t, u32x4{hv[0], hv[1], hv[2], hv[3]});
-      ql[kk] = __builtin_bit_cast(f16x8_t, u32x4{lv[0], lv[1], lv[2], lv[3]});
     }
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -228,18 +232,17 @@ __global__ __launch_bounds__(ROWW * 64) void attn_partial_q8_kernel(
     for (int h = 0; h < 2; ++h) {
       const int key = ks * 32 + (lr >> 2) * 8 + h * 4 + (lr & 3);  // its swizzle is lr
       // scales of this lane's MFMA output rows: keys ks*32 + lq*8 + h*4 + ii
-      const uint16_t* sp = reinterpret_cast<const uint16_t*>(buf + T::KSC) + (ks * 32 + lq * 8 + h * 4) * NBLK;
+      const float* sp = reinterpret_cast<const float*>(buf + T::KSC) + ks * 32 + lq * 8 + h * 4;
       f32x4 a4 = f32x4{-bias, -bias, -bias, -bias};
 #pragma unroll
       for (int kk = 0; kk < D / 32; ++kk) {
         // one 32-dim block of the keys: its fp32 sum times the block scale
         const f16x8_t kf =
             *reinterpret_cast<const f16x8_t*>(K + key * D + (((kk * 4 + lq) ^ lr) & (KCPR - 1)) * 8);
-        f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[kk], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-        t = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, ql[kk], t, 0, 0, 0);
+        const f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[kk], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        const f32x4 sc = *reinterpret_cast<const f32x4*>(sp + kk * KT);
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii)
-          a4[ii] = __builtin_fmaf(t[ii], (float)__builtin_bit_cast(f16, sp[ii * NBLK + kk]), a4[ii]);
+        for (int ii = 0; ii < 4; ++ii) a4[ii] = __builtin_fmaf(t[ii], sc[ii], a4[ii]);
       }
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) s[h * 4 + ii] = a4[ii];
@@ -270,47 +273,49 @@ __global__ __launch_bounds__(ROWW * 64) void attn_partial_q8_kernel(
       psum += pv[e];
     }
     l += psum;
-    uint32_t ph[4], pl[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) split_pair_f16(pv[2 * e], pv[2 * e + 1], ph[e], pl[e]);
-    const f16x8_t pb = __builtin_bit_cast(f16x8_t, u32x4{ph[0], ph[1], ph[2], ph[3]});
-    const f16x8_t plo = __builtin_bit_cast(f16x8_t, u32x4{pl[0], pl[1], pl[2], pl[3]});
+    const f16x8_t pb = __builtin_bit_cast(
+        f16x8_t, u32x4{pack_f16(pv[0], pv[1]), pack_f16(pv[2], pv[3]), pack_f16(pv[4], pv[5]), pack_f16(pv[6], pv[7])});
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
       // V^T row dt*16 + lr; the scales of this lane's 4 output dims (the half
       // is one 32-token block of every dim)
       const f16x8_t vf =
           *reinterpret_cast<const f16x8_t*>(V + (dt * 16 + lr) * KT + (((ks * 4 + lq) ^ ((lr >> 1) & 7)) * 8));
-      const uint16_t* sp = reinterpret_cast<const uint16_t*>(buf + T::VSC) + (dt * 16 + 4 * lq) * 2 + ks;
-      f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pb, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-      t = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, plo, t, 0, 0, 0);
+      const f32x4 sc = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(buf + T::VSC) + ks * D + dt * 16 +
+                                                      4 * lq);
+      const f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pb, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii)
-        O[dt][ii] = __builtin_fmaf(t[ii], (float)__builtin_bit_cast(f16, sp[ii * 2]), O[dt][ii]);
+      for (int ii = 0; ii < 4; ++ii) O[dt][ii] = __builtin_fmaf(t[ii], sc[ii], O[dt][ii]);
     }
   };
 
+  // Tiles go through registers two ahead: at step t the loads of tile t + 2
+  // are issued into the register set tile t used, tile t is computed, and
+  // tile t + 1 (loaded during step t - 1) is converted into the LDS buffer
+  // tile t - 1 used, which every wave has finished (the barrier at the top of
+  // step t).
   if (n_tiles > 0) {
-    u32x4 regs[LPW];
-    auto load_tile = [&](int t) {
+    u32x4 regs[2][LPW];
+    auto load_tile = [&](int t, u32x4 (&r)[LPW]) {
 #pragma unroll
-      for (int r = 0; r < LPW; ++r) {
-        const int j = wave + r * WAVES;
-        if (j < T::SLOTS) regs[r] = load_slot(t, j);
+      for (int k = 0; k < LPW; ++k) {
+        const int j = wave + k * WAVES;
+        if (j < T::SLOTS) r[k] = load_slot(t, j);
       }
     };
-    auto store_tile = [&](int t, int b) {
+    auto store_tile = [&](int t, const u32x4 (&r)[LPW], int b) {
 #pragma unroll
-      for (int r = 0; r < LPW; ++r) {
-        const int j = wave + r * WAVES;
-        if (j < T::SLOTS) store_slot(t, j, regs[r], b);
+      for (int k = 0; k < LPW; ++k) {
+        const int j = wave + k * WAVES;
+        if (j < T::SLOTS) store_slot(t, j, r[k], b);
       }
     };
-    load_tile(0);
-    store_tile(0, 0);
-    for (int t = 0; t < n_tiles; ++t) {
+    load_tile(0, regs[0]);
+    if (n_tiles > 1) load_tile(1, regs[1]);
+    store_tile(0, regs[0], 0);
+    auto step = [&](int t, u32x4 (&mine)[LPW], u32x4 (&next)[LPW]) {
       lds_barrier();  // tile t is in buffer t & 1; every wave is done with tile t - 1
-      if (t + 1 < n_tiles) load_tile(t + 1);
+      if (t + 2 < n_tiles) load_tile(t + 2, mine);
       const int k0 = k_begin + t * KT;
       if (active) {
         const uint8_t* buf = lds + (t & 1) * T::BYTES;
@@ -318,8 +323,15 @@ __global__ __launch_bounds__(ROWW * 64) void attn_partial_q8_kernel(
         row_half(buf, 0, k0, masked);
         row_half(buf, 1, k0, masked);
       }
-      if (t + 1 < n_tiles) store_tile(t + 1, (t + 1) & 1);  // into tile t - 1's buffer
+      if (t + 1 < n_tiles) store_tile(t + 1, next, (t + 1) & 1);
+    };
+    // unrolled by two so each register set is a fixed array
+    int t = 0;
+    for (; t + 1 < n_tiles; t += 2) {
+      step(t, regs[0], regs[1]);
+      step(t + 1, regs[1], regs[0]);
     }
+    if (t < n_tiles) step(t, regs[0], regs[1]);
   }
 
   if (active) {
@@ -341,16 +353,32 @@ __global__ __launch_bounds__(ROWW * 64) void attn_partial_q8_kernel(
 
 // Row groups: up to 4 query tiles in one 4-wave block, else groups of at
 // most 8 tiles (as even as they come) on 8-wave blocks.
+static void q8_groups(const AttnPlan& plan, int& groups, int& tiles) {
+  const int rt = (plan.rows + 15) / 16;
+  groups = rt <= 4 ? 1 : (rt + 7) / 8;
+  tiles = (rt + groups - 1) / groups;
+}
+
 template <int D>
 static void launch_q8_d(const AttnPlan& plan, AttnParams p, hipStream_t s) {
-  const int rt = (plan.rows + 15) / 16;
-  p.q8_groups = rt <= 4 ? 1 : (rt + 7) / 8;
-  p.q8_tiles = (rt + p.q8_groups - 1) / p.q8_groups;
+  q8_groups(plan, p.q8_groups, p.q8_tiles);
   const dim3 grid(((plan.n_chunks + 7) / 8) * 8 * p.q8_groups, p.n_kv_heads);
   if (p.q8_tiles <= 4)
     hipLaunchKernelGGL((attn_partial_q8_kernel<D, 4>), grid, dim3(256), 0, s, p);
   else
     hipLaunchKernelGGL((attn_partial_q8_kernel<D, 8>), grid, dim3(512), 0, s, p);
+}
+
+int describe_attention_q8(const AttnPlan& plan, int head_dim, int n_kv_heads, int combine_blocks, char* buf,
+                          size_t len) {
+  int groups, tiles;
+  q8_groups(plan, groups, tiles);
+  const int roww = tiles <= 4 ? 4 : 8;
+  return snprintf(buf, len,
+                  "attn_partial_q8_kernel<%d, %d> grid (%d, %d) block %d, %d-token chunks, %d row group(s) of %d "
+                  "tiles; attn_combine_kernel<%d> grid %d block 256",
+                  head_dim, roww, ((plan.n_chunks + 7) / 8) * 8 * groups, n_kv_heads, 64 * roww, plan.chunk, groups,
+                  tiles, head_dim, combine_blocks);
 }
 
 hipError_t launch_attention_q8(const AttnPlan& plan, int head_dim, const AttnParams& p,

@@ -7,20 +7,6 @@ namespace lucev {
 
 constexpr int KT = 64;  // prefix tokens per LDS tile
 
-// max and sum over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48)
-__device__ __forceinline__ float rows_max(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float rows_sum(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
 // Two fp32 values as bf16 hi (nearest) and lo (the nearest bf16 of the
 // remainder): about 16 significant bits.
 __device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint32_t& lo) {

@@ -174,8 +174,23 @@ constexpr int stage_rows(int rows, int rb, int waves) {
   return r;
 }
 
-template <int WAVES, int FT, int NTX, int UG, bool EXACT>
+// sum of a lane's 8 products with an fp16 operand row, on top of c
+__device__ __forceinline__ float dot8(f16x8 a, f16x8 b, float c) {
+  c = __builtin_amdgcn_fdot2(f16x2{a[0], a[1]}, f16x2{b[0], b[1]}, c, false);
+  c = __builtin_amdgcn_fdot2(f16x2{a[2], a[3]}, f16x2{b[2], b[3]}, c, false);
+  c = __builtin_amdgcn_fdot2(f16x2{a[4], a[5]}, f16x2{b[4], b[5]}, c, false);
+  return __builtin_amdgcn_fdot2(f16x2{a[6], a[7]}, f16x2{b[6], b[7]}, c, false);
+}
+
+// VR = 0: the products go to MFMA (NTX 16-row operand tiles).  VR in
+// {1, 2, 4, 8}: at most VR operand rows, too few for a dense contraction, so
+// each lane takes fp16 dot products (v_dot2_f32_f16) of its row's dequantised
+// weights with each operand row (read once per 16 lanes from the staged
+// slice), and the four column lanes of a row are summed at the panel's end;
+// the sums then take the MFMA accumulator layout, so the flush is shared.
+template <int WAVES, int FT, int NTX, int UG, bool EXACT, int VR>
 __global__ __launch_bounds__(WAVES * 64, 2) void gemm_q4_kernel(GemmParams p) {
+  static_assert(VR == 0 || (NTX == 1 && VR <= 8), "the dot-product path covers one operand tile");
   constexpr int NTH = WAVES * 64;
   constexpr int PT = WAVES * FT;   // tiles per panel
   constexpr int TILE_F = PT * 16;
@@ -301,6 +316,11 @@ __global__ __launch_bounds__(WAVES * 64, 2) void gemm_q4_kernel(GemmParams p) {
   for (int ft = 0; ft < FT; ++ft)
 #pragma unroll
     for (int nt = 0; nt < NTX; ++nt) acc[ft][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float accv[FT][VR > 0 ? VR : 1];  // dot-product path: this lane's share, per operand row
+#pragma unroll
+  for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+    for (int r = 0; r < (VR > 0 ? VR : 1); ++r) accv[ft][r] = 0.f;
 
   // this lane's A-operand chunk (row lr, chunk 4j + lq of a 128-column
   // group) in a staged slice, per j
@@ -323,6 +343,30 @@ __global__ __launch_bounds__(WAVES * 64, 2) void gemm_q4_kernel(GemmParams p) {
       for (int j = 0; j < 4; ++j) {
         prefetch(g * 4 + j, pf, rf);
         __builtin_amdgcn_sched_barrier(kGemmSchedMask);
+        if constexpr (VR > 0) {
+          // columns 32j + 8lq .. + 7 of operand rows 0 .. VR - 1 (chunk 4j + lq
+          // of row r sits at position (4j + lq) ^ r)
+          f16x8 xv[VR];
+#pragma unroll
+          for (int rr = 0; rr < VR; ++rr)
+            xv[rr] = *reinterpret_cast<const f16x8*>(xs + rr * RB + g * 256 + (((j * 4 + lq) ^ rr) * 16));
+#pragma unroll
+          for (int ft = 0; ft < FT; ++ft) {
+            if constexpr (EXACT) {
+              // exact codes q - 8 times fp16 operands, summed in fp32 over the
+              // lane's 8 columns of block j, then times the block scale
+              const f16x8 cq = codes8(r.w[g][ft][j]);
+              const float dj = (float)scale_pair(r.s[g][ft], j)[0];
+#pragma unroll
+              for (int rr = 0; rr < VR; ++rr) accv[ft][rr] = __builtin_fmaf(dot8(cq, xv[rr], 0.f), dj, accv[ft][rr]);
+            } else {
+              const f16x8 wb = dequant8(r.w[g][ft][j], scale_pair(r.s[g][ft], j));
+#pragma unroll
+              for (int rr = 0; rr < VR; ++rr) accv[ft][rr] = dot8(wb, xv[rr], accv[ft][rr]);
+            }
+          }
+          continue;
+        }
         f16x8 xa[NTX];
 #pragma unroll
         for (int nt = 0; nt < NTX; ++nt)
@@ -357,6 +401,26 @@ __global__ __launch_bounds__(WAVES * 64, 2) void gemm_q4_kernel(GemmParams p) {
   // finish panel pnl: hi/lo rows merged into the LDS tile [feature][node],
   // split panels reduced across blocks, then the epilogue
   auto flush = [&](int pnl) {
+    if constexpr (VR > 0) {
+      // the four column lanes of a weight row summed; operand row 4 lq + i
+      // then goes where the MFMA would have left it
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft) {
+        float tot[VR];
+#pragma unroll
+        for (int r = 0; r < VR; ++r) {
+          tot[r] = rows_sum(accv[ft][r]);
+          accv[ft][r] = 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float v = 0.f;
+#pragma unroll
+          for (int r = 0; r < VR; ++r) v = (r == 4 * lq + i) ? tot[r] : v;
+          acc[ft][0][i] = v;
+        }
+      }
+    }
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft)
 #pragma unroll
@@ -469,19 +533,29 @@ __global__ __launch_bounds__(WAVES * 64, 2) void gemm_q4_kernel(GemmParams p) {
   }
 }
 
-template <int FT, int NTX, bool EXACT>
+template <int FT, int NTX, bool EXACT, int VR = 0>
 static hipError_t launch_t(const GemmParams& p, hipStream_t s) {
   bool two = false;
-  if constexpr (NTX <= 3) two = p.ug == 2;
-  if constexpr (NTX <= 3) {
+  if constexpr (NTX <= 3 && VR < 8) two = p.ug == 2;
+  if constexpr (NTX <= 3 && VR < 8) {
     if (two) {
-      hipLaunchKernelGGL((gemm_q4_kernel<kGemmWaves, FT, NTX, 2, EXACT>), dim3(p.blocks), dim3(kGemmWaves * 64), 0, s,
-                         p);
+      hipLaunchKernelGGL((gemm_q4_kernel<kGemmWaves, FT, NTX, 2, EXACT, VR>), dim3(p.blocks), dim3(kGemmWaves * 64),
+                         0, s, p);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((gemm_q4_kernel<kGemmWaves, FT, NTX, 1, EXACT>), dim3(p.blocks), dim3(kGemmWaves * 64), 0, s, p);
+  hipLaunchKernelGGL((gemm_q4_kernel<kGemmWaves, FT, NTX, 1, EXACT, VR>), dim3(p.blocks), dim3(kGemmWaves * 64), 0,
+                     s, p);
   return hipGetLastError();
+}
+
+// the dot-product path: one operand tile, the plan's tiles per wave
+template <bool EXACT, int VR>
+static hipError_t launch_vr(const GemmParams& p, hipStream_t s) {
+  if constexpr (gemm_ft_for(1) > 1) {
+    if (p.ft == 1) return launch_t<1, 1, EXACT, VR>(p, s);
+  }
+  return launch_t<gemm_ft_for(1), 1, EXACT, VR>(p, s);
 }
 
 // the plan's tiles per wave: gemm_ft_for(ntx), or one (kGemmNarrowUnits,
@@ -496,6 +570,13 @@ static hipError_t launch_ft(const GemmParams& p, hipStream_t s) {
 
 template <bool EXACT>
 static hipError_t launch_ntx(const GemmParams& p, hipStream_t s) {
+  switch (p.vr) {
+    case 1: return launch_vr<EXACT, 1>(p, s);
+    case 2: return launch_vr<EXACT, 2>(p, s);
+    case 4: return launch_vr<EXACT, 4>(p, s);
+    case 8: return launch_vr<EXACT, 8>(p, s);
+    default: break;
+  }
   switch (gemm_ntx(p.n_nodes, EXACT)) {
     case 1: return launch_ft<1, EXACT>(p, s);
     case 2: return launch_ft<2, EXACT>(p, s);
@@ -518,15 +599,27 @@ static hipError_t launch_ntx(const GemmParams& p, hipStream_t s) {
 
 int gemm_ntx(int n_nodes, bool exact) { return exact ? (2 * n_nodes + 15) / 16 : (n_nodes + 15) / 16; }
 
+int g_gemv_max_rows = 0;
+
+// operand rows at or below g_gemv_max_rows take the dot-product path (rounded
+// up to 1, 2, 4 or 8 rows), more go to MFMA
+int gemm_vr(int n_nodes, bool exact) {
+  const int rows = exact ? 2 * n_nodes : n_nodes;
+  if (rows > g_gemv_max_rows) return 0;
+  return rows <= 1 ? 1 : rows <= 2 ? 2 : rows <= 4 ? 4 : 8;
+}
+
 // column groups per unit: two (256 inputs) when k_in allows it and the
 // registers hold two groups' weights beside the accumulators of ntx tiles
 // (one-group units measured slower inside the verify step, also for the
 // projections whose weights spread thinly over the blocks)
-int gemm_ug(int kgroups, int ntx) { return (kgroups % 2 == 0 && ntx <= 3) ? 2 : 1; }
+// (the 8-row dot-product path takes one group: two would spill)
+int gemm_ug(int kgroups, int ntx, int vr) { return (kgroups % 2 == 0 && ntx <= 3 && vr < 8) ? 2 : 1; }
 
 GemmPlan plan_gemm(int64_t n_out, int64_t k_in, int n_nodes, bool exact) {
   GemmPlan g;
   g.ntx = gemm_ntx(n_nodes, exact);
+  g.vr = gemm_vr(n_nodes, exact);
   g.tile_n = exact ? g.ntx * 8 : g.ntx * 16;
   g.n_tiles = (int)(n_out / 16);
   g.kgroups = (int)(k_in / 128);
@@ -540,7 +633,7 @@ GemmPlan plan_gemm(int64_t n_out, int64_t k_in, int n_nodes, bool exact) {
   // kGemmBlocksPerCU resident blocks on each of the 256 CUs, at least one
   // unit each
   const int64_t target = 256 * kGemmBlocksPerCU;
-  shape(gemm_ft_for(g.ntx), gemm_ug(g.kgroups, g.ntx));
+  shape(gemm_ft_for(g.ntx), gemm_ug(g.kgroups, g.ntx, g.vr));
   if (g.ft > 1 && g.units < kGemmNarrowUnits * target) shape(1, 1);
   else if (g.ft > 1 && g.units < kGemmMidUnits * target) shape(1, g.ug);
   g.blocks = (int)(g.units < target ? g.units : target);

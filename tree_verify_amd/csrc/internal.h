@@ -32,6 +32,7 @@ constexpr int kGemmSchedMask = LUCEV_GEMM_SCHED_MASK;
 
 struct GemmPlan {
   int ft, ntx, ug, n_tiles, kgroups, panels, blocks, tile_floats;
+  int vr;      // dot-product path: operand rows it covers (0: MFMA)
   int tile_n;  // nodes per partial tile
   int64_t units;
   int c_max;  // most blocks sharing one panel (partial-tile slots per panel)
@@ -71,6 +72,7 @@ struct GemmParams {
   int c_max;                // partial-tile slots per panel
   int ug;                   // 128-column groups per unit (the plan's)
   int ft;                   // 16-row tiles per wave (the plan's)
+  int vr;                   // operand rows of the dot-product path, 0 for MFMA (the plan's)
 };
 
 // Arguments of the QKV consumer (RoPE, q/k/v outputs).
@@ -89,7 +91,7 @@ struct EpiArgs {
 // 16-row MFMA tiles of the operand: the 2n hi/lo rows (exact projections) or
 // the n hi rows (gate/up, down)
 int gemm_ntx(int n_nodes, bool exact);
-int gemm_ug(int kgroups, int ntx);  // 128-column groups per unit
+int gemm_ug(int kgroups, int ntx, int vr);  // 128-column groups per unit
 // tiles per wave: fewer when many node tiles already fill the registers
 constexpr int gemm_ft_for(int ntx) { return ntx <= 4 ? kGemmFT : (kGemmFT > 1 ? kGemmFT / 2 : 1); }
 // A matrix whose wide plan (gemm_ft_for tiles per wave, gemm_ug groups per
@@ -99,6 +101,11 @@ constexpr int gemm_ft_for(int ntx) { return ntx <= 4 ? kGemmFT : (kGemmFT > 1 ? 
 // and keeps its column groups (twice the units).
 constexpr int kGemmNarrowUnits = 4;
 constexpr int kGemmMidUnits = 12;
+// Most operand rows (hi and lo rows of the exact projections, hi rows of the
+// others) that take the VALU dot-product path instead of MFMA: 0 by default
+// (MFMA measured no slower at any node count), at most 8 (lucev_set_gemv_max_rows).
+extern int g_gemv_max_rows;
+int gemm_vr(int n_nodes, bool exact);
 GemmPlan plan_gemm(int64_t n_out, int64_t k_in, int n_nodes, bool exact);
 // Every block writes its share of each panel it touches as a partial tile;
 // a consumer kernel sums them.  exact: weights enter exactly (QKV, Wo,
@@ -172,6 +179,13 @@ hipError_t launch_attention(const AttnPlan& plan, int head_dim, const AttnParams
 hipError_t launch_attention_q8(const AttnPlan& plan, int head_dim, const AttnParams& p,
                                const CombineParams& c, const TreeArgs& t, hipStream_t s);
 hipError_t launch_combine(int head_dim, const CombineParams& c, const TreeArgs& t, hipStream_t s);
+// the kernels, grids and blocks the attention launches for a plan (snprintf semantics)
+int describe_attention(const AttnPlan& plan, int head_dim, int n_kv_heads, int combine_blocks, bool fp32_q,
+                       bool paged, char* buf, size_t len);
+int describe_attention_q8(const AttnPlan& plan, int head_dim, int n_kv_heads, int combine_blocks, char* buf,
+                          size_t len);
+// one non-temporal read of `bytes` (multiple of 16) over the whole device
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s);
 // int8 block-32 quantisation of a bf16 cache's first cap tokens
 hipError_t launch_quantize_q8(const uint16_t* kc, const uint16_t* vc, int hkv, int cap, int d, int8_t* k_codes,
                               uint16_t* k_scales, int8_t* v_codes, uint16_t* v_scales, hipStream_t s);

@@ -165,6 +165,36 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------ streaming read
+// One read of a buffer with non-temporal 16-byte loads, four per thread per
+// step and every CU busy: the rate a kernel that streams that many bytes can
+// reach.  The loads are folded into one word so they are not dropped; sink is
+// written only if the fold hits one fixed value.
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ src, int64_t n16,
+                                                          uint32_t* sink) {
+  uint32_t acc = 0;
+  const int64_t step = (int64_t)gridDim.x * 1024;
+  for (int64_t base = (int64_t)blockIdx.x * 1024; base < n16; base += step) {
+    u32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = base + u * 256 + threadIdx.x;
+      v[u] = i < n16 ? __builtin_nontemporal_load(src + i) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s) {
+  const int64_t n16 = (int64_t)(bytes / 16);
+  const int64_t want = (n16 + 1023) / 1024;
+  const int blocks = (int)(want < 1 ? 1 : (want > 2048 ? 2048 : want));
+  hipLaunchKernelGGL(stream_read_kernel, dim3(blocks), dim3(256), 0, s, static_cast<const u32x4*>(src), n16, sink);
+  return hipGetLastError();
+}
+
 // Commit of the accepted path: block (j, KV head, layer), one thread per dim.
 // Path position j holds node path[j] at depth j (RoPE position prefix_len +
 // j); its key row goes to K token prefix_len + j and its value to column
