@@ -19,6 +19,55 @@ def need_gpu():
     return torch
 
 
+GUARD_BYTES = 4096
+GUARD_BYTE = 0xA5
+
+
+class Guarded:
+    """A device output buffer inside a larger allocation whose GUARD_BYTES
+    before and after hold a sentinel byte: check() fails when a kernel wrote
+    outside the buffer it was given.  The buffer itself starts 4096 bytes in,
+    so it keeps the allocation's alignment."""
+
+    def __init__(self, torch, shape, dtype, device="cuda"):
+        n = 1
+        for k in shape:
+            n *= int(k)
+        nbytes = n * torch.empty((), dtype=dtype).element_size()
+        self.raw = torch.full((2 * GUARD_BYTES + nbytes,), GUARD_BYTE, dtype=torch.uint8, device=device)
+        self.t = self.raw[GUARD_BYTES:GUARD_BYTES + nbytes].view(dtype).view(*shape)
+        self.t.zero_()
+
+    def check(self, what="buffer"):
+        lo = self.raw[:GUARD_BYTES].cpu().numpy()
+        hi = self.raw[-GUARD_BYTES:].cpu().numpy()
+        bad_lo = int(np.count_nonzero(lo != GUARD_BYTE))
+        bad_hi = int(np.count_nonzero(hi != GUARD_BYTE))
+        assert bad_lo == 0 and bad_hi == 0, "%s: %d bytes before and %d after it were overwritten" % (
+            what, bad_lo, bad_hi)
+
+
+def guarded_runner_class():
+    """VerifyRunner whose every buffer (workspace, residual, tree K/V, logits,
+    argmax, gap, path, committed) sits inside guard bands; check_guards()
+    asserts none was touched."""
+    import torch
+    from tree_verify_amd.runner import VerifyRunner
+
+    class GuardedRunner(VerifyRunner):
+        def _zeros(self, shape, dtype):
+            g = Guarded(torch, shape, dtype, self.device)
+            self.__dict__.setdefault("_guards", []).append(g)
+            return g.t
+
+        def check_guards(self):
+            torch.cuda.synchronize()
+            for i, g in enumerate(self._guards):
+                g.check("runner buffer %d" % i)
+
+    return GuardedRunner
+
+
 def bf16_bits_to_f64(t):
     """Device/host int16 tensor of bf16 bits -> fp64 numpy."""
     a = t.detach().cpu().numpy().view(np.uint16)

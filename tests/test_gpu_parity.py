@@ -12,7 +12,8 @@ import pytest
 
 import oracle
 import synth
-from gpu_common import (bf16_bits_to_f64, decisive_compare, need_gpu, row_rel_err)
+from gpu_common import (Guarded, bf16_bits_to_f64, decisive_compare, guarded_runner_class, need_gpu,
+                        row_rel_err)
 import workload
 
 pytestmark = pytest.mark.gpu
@@ -104,14 +105,17 @@ def test_tree_attention_parity(case):
     q = sd.flat_table(tab, synth.stream_key(cfg.seed, 90, 0), n * Hq * d, "cuda")
     kt = sd.flat_table(tab, synth.stream_key(cfg.seed, 91, 0), n * Hkv * d, "cuda")
     vt = sd.flat_table(tab, synth.stream_key(cfg.seed, 92, 0), n * Hkv * d, "cuda")
-    out = torch.zeros(n * Hq * d, dtype=torch.int16, device="cuda")
+    gout = Guarded(torch, (n * Hq * d,), torch.int16)
+    out = gout.t
     shape = tv.make_shape(cfg.hidden, Hq, Hkv, d, cfg.ffn, cfg.vocab)
     ws_bytes = tv.lucev_workspace_bytes(shape, n, P)
-    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
+    gws = Guarded(torch, (ws_bytes,), torch.uint8)
     tree = tv.make_tree(parent, [0] * n)
-    tv.lucev_tree_attention(shape, tree, tv.make_kv(k, v, P, cap), q, kt, vt, out, ws, ws_bytes,
+    tv.lucev_tree_attention(shape, tree, tv.make_kv(k, v, P, cap), q, kt, vt, out, gws.t, ws_bytes,
                             torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
+    gout.check("attention output")
+    gws.check("workspace")
     kp, vp = synth.kv_prefix(cfg, 0)
     ref = oracle.tree_attention(bf16_bits_to_f64(q).reshape(n, Hq, d),
                                 bf16_bits_to_f64(kt).reshape(n, Hkv, d),
@@ -149,13 +153,16 @@ def test_tree_attention_f32_parity(case):
     kth = rng.standard_normal((n, Hkv, d)).astype(np.float32)
     vth = rng.standard_normal((n, Hkv, d)).astype(np.float32)
     q, kt, vt = (torch.from_numpy(a).to("cuda") for a in (qh, kth, vth))
-    out = torch.zeros(n, Hq, d, dtype=torch.float32, device="cuda")
+    gout = Guarded(torch, (n, Hq, d), torch.float32)
+    out = gout.t
     shape = tv.make_shape(cfg.hidden, Hq, Hkv, d, cfg.ffn, cfg.vocab)
     ws_bytes = tv.lucev_workspace_bytes(shape, n, P)
-    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
+    gws = Guarded(torch, (ws_bytes,), torch.uint8)
     tv.lucev_tree_attention_f32(shape, tv.make_tree(parent, [0] * n), tv.make_kv(k, v, P, cap), q, kt, vt, out,
-                                ws, ws_bytes, torch.cuda.current_stream().cuda_stream)
+                                gws.t, ws_bytes, torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
+    gout.check("attention output")
+    gws.check("workspace")
     kp, vp = synth.kv_prefix(cfg, 0)
     ref = oracle.tree_attention(qh.astype(np.float64), kth.astype(np.float64), vth.astype(np.float64),
                                 oracle.bf16_to_f64(kp), oracle.bf16_to_f64(vp), parent)
@@ -169,18 +176,19 @@ def test_tree_attention_f32_parity(case):
 def _run_gpu_step(cfg, seed, tokens, parent, layers=None, want_hidden=True):
     torch = need_gpu()
     import tree_verify_amd as tv
-    from tree_verify_amd.runner import VerifyRunner
     import synth.device as sd
     wl = sd.Workload(cfg, seed, "cuda", layers=layers)
     shape = tv.make_shape(cfg.hidden, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ffn,
                           cfg.vocab, cfg.rms_eps, cfg.rope_base)
-    r = VerifyRunner(shape, wl.layers, wl.head, cfg.nodes, wl.capacity, "cuda")
+    # every runner buffer sits inside guard bands, checked after the step
+    r = guarded_runner_class()(shape, wl.layers, wl.head, cfg.nodes, wl.capacity, "cuda")
     n = cfg.nodes
     hid = [torch.zeros(n, cfg.hidden, dtype=torch.float32, device="cuda")
            for _ in range(wl.n_layers)] if want_hidden else None
     tree = tv.make_tree(parent, tokens)
     r.step(tree, wl.x_in_f32(), cfg.prefix, hidden_out=hid)
     torch.cuda.synchronize()
+    r.check_guards()
     out = {
         "hidden": [h.cpu().numpy().astype(np.float64) for h in hid] if hid else None,
         "k_tree": bf16_bits_to_f64(r.k_tree[-1][:n]),

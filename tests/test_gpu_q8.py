@@ -18,7 +18,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_common import bf16_bits_to_f64, need_gpu, row_rel_err
+from gpu_common import Guarded, bf16_bits_to_f64, need_gpu, row_rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -97,14 +97,17 @@ def test_kv_quantize_bit_exact(case):
     _plant_specials(kh, vh)
     k = torch.from_numpy(kh.view(np.int16)).to("cuda")
     v = torch.from_numpy(vh.view(np.int16)).to("cuda")
-    kc = torch.full((Hkv, cap, d), 99, dtype=torch.int8, device="cuda")
-    ks = torch.full((Hkv, cap, d // 32), 7, dtype=torch.int16, device="cuda")
-    vc = torch.full((Hkv, d, cap), 99, dtype=torch.int8, device="cuda")
-    vs = torch.full((Hkv, d, cap // 32), 7, dtype=torch.int16, device="cuda")
+    gk = [Guarded(torch, (Hkv, cap, d), torch.int8), Guarded(torch, (Hkv, cap, d // 32), torch.int16),
+          Guarded(torch, (Hkv, d, cap), torch.int8), Guarded(torch, (Hkv, d, cap // 32), torch.int16)]
+    for g_ in gk:
+        g_.t.fill_(99)
+    kc, ks, vc, vs = (g_.t for g_ in gk)
     shape = tv.make_shape(128, Hkv * 2, Hkv, d, 128, 64)
     tv.lucev_kv_quantize_q8(shape, tv.make_kv(k, v, P, cap), kc, ks, vc, vs,
                             torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
+    for g_, nm in zip(gk, ("K codes", "K scales", "V codes", "V scales")):
+        g_.check(nm)
     kc0, ks0 = oracle.quantize_q8_blocks(oracle.bf16_to_f64(kh))
     vc0, vs0 = oracle.quantize_q8_blocks(oracle.bf16_to_f64(vh))
     assert np.array_equal(kc.cpu().numpy(), kc0)
@@ -141,14 +144,16 @@ def _q8_cache_from_oracle(k, v):
 def _run_q8_attention(torch, tv, shape, parent, kc, ks, vc, vs, P, cap, q, kt, vt, n, Hq, d):
     dev = [torch.from_numpy(np.ascontiguousarray(a)).to("cuda") for a in
            (kc, ks.view(np.int16), vc, vs.view(np.int16))]
-    out = torch.zeros(n * Hq * d, dtype=torch.int16, device="cuda")
+    gout = Guarded(torch, (n * Hq * d,), torch.int16)
     ws_bytes = tv.lucev_workspace_bytes(shape, n, P)
-    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
+    gws = Guarded(torch, (ws_bytes,), torch.uint8)
     kv = tv.make_kv_q8(dev[0], dev[1], dev[2], dev[3], P, cap)
-    tv.lucev_tree_attention_q8(shape, tv.make_tree(parent, [0] * n), kv, q, kt, vt, out, ws, ws_bytes,
+    tv.lucev_tree_attention_q8(shape, tv.make_tree(parent, [0] * n), kv, q, kt, vt, gout.t, gws.t, ws_bytes,
                                torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
-    return out
+    gout.check("int8 attention output")
+    gws.check("workspace")
+    return gout.t
 
 
 @pytest.mark.parametrize("case", ATTN_Q8_CASES, ids=[c[0] for c in ATTN_Q8_CASES])

@@ -48,5 +48,46 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def asan_runtime() -> str:
+    """The ASan runtime of the ROCm clang (it carries the UBSan handlers too)."""
+    import glob
+    hits = sorted(glob.glob("/opt/rocm/lib/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not hits:
+        raise RuntimeError("no libclang_rt.asan-x86_64.so under /opt/rocm/lib/llvm")
+    return hits[-1]
+
+
+def build_host_sanitized(out_dir: str) -> str:
+    """The library with AddressSanitizer and UndefinedBehaviorSanitizer on its
+    host code (argument validation, the host packer, planning, workspace
+    sizing), for CPU tests that launch no kernel: the device code is built
+    unoptimised, only so the objects link.  Load it with asan_runtime()
+    preloaded."""
+    import concurrent.futures
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    inc = ["-I", os.path.join(HERE, "..", "include")]
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+    def one(src):
+        obj = os.path.join(out_dir, src + ".o")
+        cmd = [hipcc, "--offload-arch=gfx950", "-O1", "-std=c++17", "-fPIC", "-Wno-unused-result",
+               "-Xarch_device", "-O0"] + san + inc + ["-c", os.path.join(CSRC, src), "-o", obj]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError("hipcc (sanitized) failed on %s:\n%s" % (src, res.stdout + res.stderr))
+        return obj
+
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
+        objs = list(ex.map(one, SOURCES))
+    out = os.path.join(out_dir, "liblucev_host_san.so")
+    res = subprocess.run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC"] + san + objs + ["-o", out],
+                         capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("linking the sanitized build failed")
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

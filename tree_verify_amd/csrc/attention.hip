@@ -674,7 +674,7 @@ static_assert(kMaxAttnRows == 8 * 4 * 16, "the widest plan (8 row waves of 4 til
 #endif
 constexpr int kAttnBufs = LUCEV_ATTN_NBUF;
 
-int attention_max_chunks(int n_kv_heads) { return (256 + n_kv_heads - 1) / n_kv_heads; }
+int attention_max_chunks(int n_kv_heads) { return (device_cu_count() + n_kv_heads - 1) / n_kv_heads; }
 
 // Wave layout knobs (fixed at build time): where the quarters of a split
 // tile go (0: four extra waves beside one-tile waves; 1: the last four of
@@ -721,7 +721,8 @@ AttnPlan plan_attention(int n_nodes, int n_q_heads, int n_kv_heads, int head_dim
   }
   a.waves = a.roww;
   // one block per CU over (chunk, KV head): chunks a multiple of the LDS tile
-  int chunk = (int)(((int64_t)prefix_len * n_kv_heads + 255) / 256);
+  const int cus = device_cu_count();
+  int chunk = (int)(((int64_t)prefix_len * n_kv_heads + cus - 1) / cus);
   chunk = ((chunk + KT - 1) / KT) * KT;
   if (chunk < KT) chunk = KT;
   a.chunk = chunk;

@@ -62,15 +62,6 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// Device-coherent (agent-scope) fp32 load / store, for data one block
-// writes and another block of the same launch reads.
-__device__ __forceinline__ float ld_coherent(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_coherent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // Top-2 merge: best value, its index (lowest on exact ties) and the runner-up
 // (a tie at the top makes the runner-up equal to the best).  Associative and
 // commutative, so any fixed merge tree gives the same result.

@@ -630,9 +630,8 @@ GemmPlan plan_gemm(int64_t n_out, int64_t k_in, int n_nodes, bool exact) {
     g.panels = (g.n_tiles + pt - 1) / pt;
     g.units = (int64_t)g.panels * (g.kgroups / ug);
   };
-  // kGemmBlocksPerCU resident blocks on each of the 256 CUs, at least one
-  // unit each
-  const int64_t target = 256 * kGemmBlocksPerCU;
+  // kGemmBlocksPerCU resident blocks on each CU, at least one unit each
+  const int64_t target = (int64_t)device_cu_count() * kGemmBlocksPerCU;
   shape(gemm_ft_for(g.ntx), gemm_ug(g.kgroups, g.ntx, g.vr));
   if (g.ft > 1 && g.units < kGemmNarrowUnits * target) shape(1, 1);
   else if (g.ft > 1 && g.units < kGemmMidUnits * target) shape(1, g.ug);

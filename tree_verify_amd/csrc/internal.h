@@ -171,6 +171,10 @@ struct CombineParams {
 // Every query row of a KV head lives in one block of the partial kernel: at
 // most 8 row waves x 4 tiles x 16 rows.
 constexpr int kMaxAttnRows = 512;
+// compute units of the current device (256 on MI355X; that figure when no
+// device can be queried), cached per device: grids and prefix chunks are
+// sized to it
+int device_cu_count();
 AttnPlan plan_attention(int n_nodes, int n_q_heads, int n_kv_heads, int head_dim, int prefix_len);
 int attention_max_chunks(int n_kv_heads);
 hipError_t launch_attention(const AttnPlan& plan, int head_dim, const AttnParams& p,

@@ -26,19 +26,17 @@ class VerifyRunner:
         self.ws_bytes = tv.lucev_workspace_bytes(shape, n_max, capacity)
         if self.ws_bytes == 0:
             raise ValueError("unsupported shape for the workspace")
-        self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=self.device)
-        self.resid = torch.zeros(n_max, H, dtype=torch.float32, device=self.device)
-        self.k_tree = [torch.zeros(n_max, Hkv, d, dtype=torch.int16, device=self.device)
-                       for _ in self.layers]
-        self.v_tree = [torch.zeros(n_max, Hkv, d, dtype=torch.int16, device=self.device)
-                       for _ in self.layers]
-        self.logits = torch.zeros(n_max, V, dtype=torch.int16, device=self.device) if keep_logits else None
-        i32 = dict(dtype=torch.int32, device=self.device)
-        self.argmax = torch.zeros(n_max, **i32)
-        self.gap = torch.zeros(n_max, dtype=torch.float32, device=self.device)
-        self.path = torch.zeros(n_max, **i32)
-        self.path_len = torch.zeros(1, **i32)
-        self.committed = torch.zeros(n_max, **i32)
+        z = self._zeros
+        self.ws = z((self.ws_bytes,), torch.uint8)
+        self.resid = z((n_max, H), torch.float32)
+        self.k_tree = [z((n_max, Hkv, d), torch.int16) for _ in self.layers]
+        self.v_tree = [z((n_max, Hkv, d), torch.int16) for _ in self.layers]
+        self.logits = z((n_max, V), torch.int16) if keep_logits else None
+        self.argmax = z((n_max,), torch.int32)
+        self.gap = z((n_max,), torch.float32)
+        self.path = z((n_max,), torch.int32)
+        self.path_len = z((1,), torch.int32)
+        self.committed = z((n_max,), torch.int32)
         self._lw = [self._layer_struct(lw) for lw in self.layers]
         self._hw = None
         if head is not None:
@@ -47,6 +45,11 @@ class VerifyRunner:
         # the buffers above were zero-filled on the current stream; the step
         # may be issued on another one
         torch.cuda.synchronize(self.device)
+
+    def _zeros(self, shape, dtype) -> torch.Tensor:
+        """A zeroed device buffer the runner owns (a subclass may place its
+        buffers inside guarded allocations)."""
+        return torch.zeros(shape, dtype=dtype, device=self.device)
 
     def _layer_struct(self, lw: dict) -> tv.lucev_layer_w:
         s = self.shape
