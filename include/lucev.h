@@ -300,9 +300,10 @@ int lucev_kv_quantize_q8(const lucev_shape* shape, const lucev_kv* src, int8_t* 
                          int8_t* v_codes, uint16_t* v_scales, void* stream);
 
 /* lucev_tree_attention over an int8 prefix: every prefix key and value enters
- * as d * code exactly (the codes go through fp16 MFMAs one 32-wide block at a
- * time and each block's fp32 sum is multiplied by its scale); queries and P
- * are carried at about 22 significant bits.  q, k_tree, v_tree and out as in
+ * as the nearest fp16 of d * code (one rounding, within 2^-11 of itself, 16
+ * times finer than the int8 step), queries and P as nearest fp16, all
+ * products and sums in fp32 (fp16 MFMAs).  Prefix values must lie within the
+ * fp16 range (|x| <= 65504).  q, k_tree, v_tree and out as in
  * lucev_tree_attention.  Returns its codes; LUCEV_ERR_BAD_KV also for a
  * capacity that is not a multiple of 32, LUCEV_ERR_ALIGN for the alignments
  * above. */
@@ -391,11 +392,10 @@ int lucev_commit_path(const lucev_shape* shape, int32_t n_layers, uint16_t* cons
  * lucev_set_gemv_max_rows: GEMM operand rows (two per node for the QKV, Wo
  * and lm_head projections, whose activations travel as fp16 hi + lo rows; one
  * per node for gate/up and down) at or below which the int4 projections take
- * dot products on the vector ALUs (v_dot2_f32_f16) instead of MFMA.  The
- * spec asks for MFMA only where M makes a dense contraction; measured
- * on MI355X, MFMA is no slower at any node count (the dot products come
- * within 5 % at one or two operand rows and lose from four on), so the
- * default is 0.  rows in [0, 8], else LUCEV_ERR_BAD_SHAPE.  Process-wide; applies to
+ * dot products on the vector ALUs (v_dot2_f32_f16) instead of MFMA, for
+ * trees too small to make a dense contraction.  Measured on MI355X, MFMA is
+ * no slower at any node count (the dot products come within 5 % at one or
+ * two operand rows and lose from four on), so the default is 0.  rows in [0, 8], else LUCEV_ERR_BAD_SHAPE.  Process-wide; applies to
  * calls made (and workspaces sized) afterwards, not to captured graphs.
  */
 int lucev_set_gemv_max_rows(int32_t rows);

@@ -7,9 +7,8 @@ attention over an int8 prefix, through the C ABI, against the oracle.
   input comes from the device quantiser) and is compared with
   ``oracle.tree_attention`` over the fp64 prefix those codes stand for
   (``oracle.kv_prefix_from_q8``), to the bf16 attention's tolerance: the
-  kernel takes d * code exactly (codes exact in fp16, one fp32 scale multiply
-  per 32-block), so the int8 path adds no error of its own beyond the bf16
-  path's fp32 accumulation and bf16 output.
+  kernel takes the nearest fp16 of d * code and of q and P (2^-11 relative
+  each), far below the bf16 output's rounding.
 """
 import sys
 
@@ -120,14 +119,14 @@ def test_kv_quantize_bit_exact(case):
 
 ATTN_Q8_CASES = [
     # (name, Hq, Hkv, d, P, parent-recipe, n)
-    ("tiny_shape", 4, 2, 64, 128, None, 8),            # 2 query tiles, one 4-wave block
+    ("tiny_shape", 4, 2, 64, 128, None, 8),            # 1 query tile, a 4-wave block
     ("ragged_prefix", 8, 2, 128, 1000, None, 16),      # ragged last tile
-    ("27b_group", 48, 8, 128, 4100, (3, 8), 22),       # 9 query tiles: two row groups
-    ("wide_tree", 48, 8, 128, 2051, (4, 10), 40),      # 15 tiles: groups of 8 and 7
+    ("27b_group", 48, 8, 128, 4100, (3, 8), 22),       # 9 query tiles on 12 one-tile waves
+    ("wide_tree", 48, 8, 128, 2051, (4, 10), 40),      # 15 tiles, two per wave on 8 waves
     ("single_node", 48, 8, 128, 777, None, 1),
     ("empty_prefix", 8, 2, 128, 0, None, 5),
     ("short_prefix", 8, 2, 128, 33, None, 7),           # one tile, a 1-token second half
-    ("max_rows", 32, 4, 128, 515, None, 64),            # 512 rows: four groups of 8 tiles
+    ("max_rows", 32, 4, 128, 515, None, 64),            # 512 rows: two row groups of 16 tiles
     ("max_rows_d64", 16, 1, 64, 260, (4, 10), 32),      # 512 rows of head_dim 64
 ]
 

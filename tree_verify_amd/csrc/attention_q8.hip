@@ -5,27 +5,28 @@
 // "Paged attention + continuous batching" and "설치·사용법"; KV size is the
 // VRAM limit of section "배경: 어떤 문제를 푸는가", item 3).  Keys are blocked
 // along the head dim of each token, values along the tokens of each dim (the
-// cache keeps V dim-major), so a 32-key half of a tile and a 32-dim slice of
-// a key each carry one scale.
+// cache keeps V dim-major), so 16 consecutive codes a lane loads share one
+// scale.
 //
 // The partial kernel follows the bf16 one (blocks over prefix chunk and KV
-// head, 64-token tiles in a two-buffer LDS ring), with four differences:
-//   * one query tile (16 rows) per wave, and the query tiles of a KV head
-//     spread over up to 8-tile row groups, one block per (chunk, group):
-//     a wave's scores, O and fp16 hi/lo queries leave no room for a second
-//     tile in 256 registers.  The groups of a chunk sit on one XCD (block
-//     ids 8 apart), so the second group's tile reads hit that XCD's L2;
-//   * tiles go through registers: 16 codes per lane are loaded, turned into
-//     16 exact fp16 values (1024 + u under the fp16 exponent, then minus
-//     1152) and stored into LDS in the bf16 kernel's swizzled layout, with
-//     the tile's scales beside them; the next tile's loads fly while the
-//     current tile is computed;
-//   * the MFMAs are f16 (codes exact; queries and P as nearest fp16, each
-//     off by at most 2^-11 of itself), one 32-deep block at a time, and each
-//     block's fp32 result is multiplied by its scale as it is accumulated, so
-//     d * code enters exactly;
-//   * no split query tile.
-// The combine kernel is the bf16 path's.
+// head, 64-token tiles in a two-buffer LDS ring, S^T = K Q^T with the softmax
+// axis inside each lane, lazy rescale, P fed to O^T = V^T P^T from
+// registers), with these differences:
+//   * tiles go through registers, two tiles ahead: a lane loads 16 codes and
+//     their scale, turns the codes into exact fp16 values (the byte XOR 0x80
+//     placed under the exponent of 1024 with v_perm_b32, minus 1152), scales
+//     them with one packed fp16 multiply -- d * code rounded once to fp16,
+//     within 2^-11 of itself and 16 times finer than the int8 step -- and
+//     stores them into the bf16 kernel's swizzled LDS layouts;
+//   * every MFMA is f16 and single: K' q (q as nearest fp16) and V' P (P as
+//     nearest fp16), accumulated directly; the int8 cache's own rounding
+//     dwarfs these, so no hi/lo halves are carried;
+//   * no split query tile: query tiles go one per wave up to 12, then two
+//     per wave on 8 waves, and past 16 tiles to row groups, one block per
+//     (chunk, group); the groups of a chunk sit on one XCD (block ids 8
+//     apart) so the later groups' tile reads hit that XCD's L2.
+// Values of magnitude above the fp16 range (65504) are outside what the
+// fp16 tiles hold.  The combine kernel is the bf16 path's.
 #include <stdio.h>
 
 #include "attn_common.h"
@@ -33,6 +34,7 @@
 namespace lucev {
 
 typedef f16 f16x4 __attribute__((ext_vector_type(4)));
+typedef f16 f16x8_t __attribute__((ext_vector_type(8)));
 
 // 4 int8 codes (one dword) -> 4 exact fp16 values, in order: byte b of
 // w ^ 0x80808080 is u = code + 128; placed under the exponent of 1024 it reads
@@ -49,35 +51,53 @@ __device__ __forceinline__ u32x2 codes4_f16(uint32_t w) {
   return u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
 }
 
+// 16 codes (four dwords) times their scale: 16 fp16 values d * code, each
+// rounded once, as two 16-byte chunks in order
+__device__ __forceinline__ void scaled16(const u32x4& w, uint32_t scale16, u32x4& out0, u32x4& out1) {
+  const f16 d = __builtin_bit_cast(f16, (uint16_t)scale16);
+  const f16x2 dd = {d, d};
+  uint32_t o[8];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const u32x2 c = codes4_f16(w[q]);
+    // An empty asm makes the two converted pairs opaque before the multiply:
+    // without it this compiler keeps only the first pair's v_perm_b32 and
+    // stores its product for both pairs (a miscompile seen in the ISA and in
+    // wrong attention outputs).  It emits no instruction.
+    uint32_t c0 = c[0], c1 = c[1];
+    asm("" : "+v"(c0), "+v"(c1));
+    o[2 * q] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, c0) * dd);
+    o[2 * q + 1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, c1) * dd);
+  }
+  out0 = u32x4{o[0], o[1], o[2], o[3]};
+  out1 = u32x4{o[4], o[5], o[6], o[7]};
+}
+
 // Two fp32 values as fp16 (nearest), packed
 __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
   return __builtin_bit_cast(uint32_t, f16x2{(f16)a, (f16)b});
 }
 
-// LDS tile of the int8 path: K [64 keys][D] fp16 and V^T [D][64] fp16 in the
-// bf16 kernel's swizzled layouts, then the scales widened to fp32 once, as
-// they are stored: K scales [D/32 blocks][64 keys] and V scales [2 token
-// blocks][D], so the four a lane applies to one MFMA result are one 16-byte
-// read.
+// LDS tile of the int8 path: K' [64 keys][D] and V'^T [D][64], fp16, in the
+// bf16 kernel's swizzled layouts.
 template <int D>
 struct Q8Tile {
   static constexpr int KBYTES = KT * D * 2;
-  static constexpr int VBYTES = D * KT * 2;
-  static constexpr int KSC = KBYTES + VBYTES;             // K scales
-  static constexpr int VSC = KSC + KT * (D / 32) * 4;     // V scales
-  static constexpr int BYTES = VSC + D * 2 * 4;
-  // global loads per tile, 16 bytes a lane: K codes (one lane: 16 codes of a
-  // key), V codes (16 tokens of a dim), K scales (8 bytes a lane), V scales
-  // (4 bytes a lane per dim, two loads)
-  static constexpr int NK = KT * D / 1024;  // 1 KB of codes per wave-load
+  static constexpr int BYTES = 2 * KBYTES;
+  // wave-loads per tile, 16 codes a lane: K (D / 16 lanes per key), V (4
+  // lanes per dim, 16 tokens each)
+  static constexpr int NK = KT * D / 1024;
   static constexpr int NV = D * KT / 1024;
-  static constexpr int NS = 1 + (D * 4 + 255) / 256;  // K scales, then V scales (64 dims a load)
-  static constexpr int SLOTS = NK + NV + NS;
+  static constexpr int SLOTS = NK + NV;
 };
 
-template <int D, int ROWW>
-__global__ __launch_bounds__(ROWW * 64) void attn_partial_q8_kernel(
-    AttnParams p) {
+struct Q8Slot {
+  u32x4 codes;
+  uint32_t scale;  // fp16 bits
+};
+
+template <int D, int QPW, int ROWW>
+__global__ __launch_bounds__(ROWW * 64) void attn_partial_q8_kernel(AttnParams p) {
   using T = Q8Tile<D>;
   constexpr int WAVES = ROWW;
   constexpr int KCPR = D / 8;  // 16-byte chunks per K row
@@ -98,71 +118,59 @@ __global__ __launch_bounds__(ROWW * 64) void attn_partial_q8_kernel(
   const int g = blockIdx.y;
   const int G = p.n_q_heads / p.n_kv_heads;
   const int RT = (p.rows + 15) / 16;
-  const int qt = grp * p.q8_tiles + wave;  // this wave's query tile
-  const bool active = wave < p.q8_tiles && qt < RT;
   const int k_begin = chunk * p.chunk;
   const int k_end = min(p.prefix_len, k_begin + p.chunk);
   const int n_tiles = (k_end - k_begin + KT - 1) / KT;
+  // this wave's query tiles: group tiles wave, wave + ROWW, ...
+  auto tile_of = [&](int i) __attribute__((always_inline)) { return grp * p.q8_tiles + wave + ROWW * i; };
+  auto has_tile = [&](int i) __attribute__((always_inline)) { return wave + ROWW * i < p.q8_tiles && tile_of(i) < RT; };
 
   const int8_t* kcode = p.kc8 + (int64_t)g * p.cap * D;
   const int8_t* vcode = p.vc8 + (int64_t)g * D * p.cap;
   const uint16_t* kscale = p.ks16 + (int64_t)g * p.cap * NBLK;
   const uint16_t* vscale = p.vs16 + (int64_t)g * D * (p.cap / 32);
 
-  // One wave-load slot j of tile t into registers (zeros past the prefix).
-  // Slot kinds: [0, NK) K codes, [NK, NK + NV) V codes, then the scales.
-  auto load_slot = [&](int t, int j) -> u32x4 {
+  // One wave-load slot j of tile t: 16 codes of this lane and their scale
+  // (zeros past the prefix).  Slots [0, NK) hold K, [NK, NK + NV) V.
+  auto load_slot = [&](int t, int j) __attribute__((always_inline)) -> Q8Slot {
     const int k0 = k_begin + t * KT;
-    u32x4 v = u32x4{0u, 0u, 0u, 0u};
+    Q8Slot r{u32x4{0u, 0u, 0u, 0u}, 0u};
     if (j < T::NK) {
-      const int key = j * (1024 / D) + lane / (D / 16);  // 16 codes a lane: D / 16 lanes per key
-      const int c16 = lane % (D / 16);
-      if (k0 + key < k_end) v = ld16(kcode + (int64_t)(k0 + key) * D + c16 * 16);
-    } else if (j < T::NK + T::NV) {
-      const int jj = j - T::NK;
-      const int dim = jj * 16 + lane / 4, part = lane % 4;  // 16 tokens a lane: 4 lanes per dim
-      if (k0 + part * 16 < k_end) v = ld16(vcode + (int64_t)dim * p.cap + k0 + part * 16);
-    } else if (j == T::NK + T::NV) {
-      // K scales: key `lane`, its NBLK scales (NBLK * 2 bytes)
-      if (k0 + lane < k_end) {
-        const uint16_t* src = kscale + (int64_t)(k0 + lane) * NBLK;
-        if constexpr (NBLK == 4) {
-          const u32x2 w = *reinterpret_cast<const u32x2*>(src);
-          v = u32x4{w[0], w[1], 0u, 0u};
-        } else {
-          v = u32x4{*reinterpret_cast<const uint32_t*>(src), 0u, 0u, 0u};
-        }
+      const int key = j * (1024 / D) + lane / (D / 16);
+      const int c16 = lane % (D / 16);  // codes 16 c16 .. + 15 of the key: scale block c16 / 2
+      if (k0 + key < k_end) {
+        r.codes = ld16(kcode + (int64_t)(k0 + key) * D + c16 * 16);
+        r.scale = kscale[(int64_t)(k0 + key) * NBLK + (c16 >> 1)];
       }
     } else {
-      // V scales: dim (j - NK - NV - 1) * 64 + lane, the tile's two 32-token blocks
-      const int dim = (j - T::NK - T::NV - 1) * 64 + lane;
-      if (dim < D) {
-        const uint16_t* src = vscale + (int64_t)dim * (p.cap / 32) + k0 / 32;
-        const uint32_t s0 = k0 < k_end ? src[0] : 0u;
-        const uint32_t s1 = k0 + 32 < k_end ? src[1] : 0u;
-        v = u32x4{s0 | (s1 << 16), 0u, 0u, 0u};
+      const int jj = j - T::NK;
+      const int dim = jj * 16 + lane / 4, part = lane % 4;  // tokens k0 + 16 part .. + 15
+      if (k0 + part * 16 < k_end) {
+        r.codes = ld16(vcode + (int64_t)dim * p.cap + k0 + part * 16);
+        r.scale = vscale[(int64_t)dim * (p.cap / 32) + ((k0 + part * 16) >> 5)];
       }
     }
-    return v;
+    return r;
   };
-  // Slot j's registers into LDS buffer b: codes converted to fp16 in the
-  // swizzled tile layouts (tokens past the prefix were loaded as zero codes).
-  auto store_slot = [&](int t, int j, const u32x4& v, int b) {
+  // Slot j's registers into LDS buffer b, scaled to fp16 in the swizzled
+  // layouts (tokens past the prefix read as zero).
+  auto store_slot = [&](int t, int j, const Q8Slot& v, int b) __attribute__((always_inline)) {
     uint8_t* base = lds + b * T::BYTES;
     const int k0 = k_begin + t * KT;
     if (j < T::NK) {
       const int key = j * (1024 / D) + lane / (D / 16);
       const int c16 = lane % (D / 16);
       const int sw = ((key & 3) | (((key >> 3) & 3) << 2)) & (KCPR - 1);
-      const u32x2 a = codes4_f16(v[0]), bb = codes4_f16(v[1]), c = codes4_f16(v[2]), d = codes4_f16(v[3]);
+      u32x4 c0, c1;
+      scaled16(v.codes, v.scale, c0, c1);
       uint8_t* row = base + key * D * 2;
-      *reinterpret_cast<u32x4*>(row + (((2 * c16) ^ sw) * 16)) = u32x4{a[0], a[1], bb[0], bb[1]};
-      *reinterpret_cast<u32x4*>(row + (((2 * c16 + 1) ^ sw) * 16)) = u32x4{c[0], c[1], d[0], d[1]};
-    } else if (j < T::NK + T::NV) {
+      *reinterpret_cast<u32x4*>(row + (((2 * c16) ^ sw) * 16)) = c0;
+      *reinterpret_cast<u32x4*>(row + (((2 * c16 + 1) ^ sw) * 16)) = c1;
+    } else {
       const int jj = j - T::NK;
       const int dim = jj * 16 + lane / 4, part = lane % 4;
       const int swz = (dim >> 1) & 7;
-      u32x4 w = v;
+      u32x4 w = v.codes;
       // tokens past the prefix inside this 16-token run read as code 0
       const int valid = k_end - (k0 + part * 16);
       if (valid < 16) {
@@ -170,33 +178,22 @@ __global__ __launch_bounds__(ROWW * 64) void attn_partial_q8_kernel(
         for (int e = 0; e < 16; ++e)
           if (e >= valid) w[e >> 2] &= ~(0xFFu << (8 * (e & 3)));
       }
-      const u32x2 a = codes4_f16(w[0]), bb = codes4_f16(w[1]), c = codes4_f16(w[2]), d = codes4_f16(w[3]);
+      u32x4 c0, c1;
+      scaled16(w, v.scale, c0, c1);
       uint8_t* row = base + T::KBYTES + dim * KT * 2;
-      *reinterpret_cast<u32x4*>(row + (((2 * part) ^ swz) * 16)) = u32x4{a[0], a[1], bb[0], bb[1]};
-      *reinterpret_cast<u32x4*>(row + (((2 * part + 1) ^ swz) * 16)) = u32x4{c[0], c[1], d[0], d[1]};
-    } else if (j == T::NK + T::NV) {
-      float* ksc = reinterpret_cast<float*>(base + T::KSC);
-#pragma unroll
-      for (int b = 0; b < NBLK; ++b)
-        ksc[b * KT + lane] = (float)__builtin_bit_cast(f16, (uint16_t)(v[b >> 1] >> (16 * (b & 1))));
-    } else {
-      const int dim = (j - T::NK - T::NV - 1) * 64 + lane;
-      float* vsc = reinterpret_cast<float*>(base + T::VSC);
-      if (dim < D) {
-        vsc[dim] = (float)__builtin_bit_cast(f16, (uint16_t)(v[0] & 0xFFFFu));
-        vsc[D + dim] = (float)__builtin_bit_cast(f16, (uint16_t)(v[0] >> 16));
-      }
+      *reinterpret_cast<u32x4*>(row + (((2 * part) ^ swz) * 16)) = c0;
+      *reinterpret_cast<u32x4*>(row + (((2 * part + 1) ^ swz) * 16)) = c1;
     }
   };
 
-  // this wave's query tile; Q^T as fp16, scaled to log2 units
-  typedef f16 f16x8_t __attribute__((ext_vector_type(8)));
-  f16x8_t qf[D / 32];
-  f32x4 O[D / 16];
-  float m = -INFINITY, l = 0.f;
-  {
-    const int row = qt * 16 + lr;
-    const bool ok = active && row < p.rows;
+  // this wave's query tiles; Q^T as fp16, scaled to log2 units
+  f16x8_t qf[QPW][D / 32];
+  f32x4 O[QPW][D / 16];
+  float m[QPW], l[QPW];
+#pragma unroll
+  for (int i = 0; i < QPW; ++i) {
+    const int row = tile_of(i) * 16 + lr;
+    const bool ok = has_tile(i) && row < p.rows;
     int node = 0, head = 0;
     if (ok) {
       node = row / G;
@@ -215,109 +212,119 @@ __global__ __launch_bounds__(ROWW * 64) void attn_partial_q8_kernel(
         const float x1 = ok ? bf16_bits_to_f32(raw[kk][e] >> 16) * p.scale_log2 : 0.f;
         hv[e] = pack_f16(x0, x1);
       }
-      qf[kk] = __builtin_bit_cast(f16x8_t, u32x4{hv[0], hv[1], hv[2], hv[3]});
+      qf[i][kk] = __builtin_bit_cast(f16x8_t, u32x4{hv[0], hv[1], hv[2], hv[3]});
     }
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < D / 16; ++dt) O[i][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m[i] = -INFINITY;
+    l[i] = 0.f;
   }
 
-  // One 32-key half of a tile: scores (the K fragments and scales of one
-  // 16-key group at a time), their softmax, then PV one 16-dim tile at a time.
-  auto row_half = [&](const uint8_t* buf, int ks, int k0, bool masked) {
-    const uint16_t* K = reinterpret_cast<const uint16_t*>(buf);
-    const uint16_t* V = reinterpret_cast<const uint16_t*>(buf + T::KBYTES);
-    const float bias = m == -INFINITY ? 0.f : m;
-    float s[8];
+  // One 32-key half of a tile for every query tile of this wave: the half's
+  // K' fragments (one 16-key group at a time) against each tile's q, the
+  // softmax of each tile, then V'^T P^T one 16-dim tile at a time.
+  auto row_half = [&](const uint8_t* buf, int ks, int k0, bool masked) __attribute__((always_inline)) {
+    const f16* K = reinterpret_cast<const f16*>(buf);
+    const f16* V = reinterpret_cast<const f16*>(buf + T::KBYTES);
+    f32x4 sc[QPW][2];
+    float bias[QPW];
+#pragma unroll
+    for (int i = 0; i < QPW; ++i) bias[i] = m[i] == -INFINITY ? 0.f : m[i];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int key = ks * 32 + (lr >> 2) * 8 + h * 4 + (lr & 3);  // its swizzle is lr
-      // scales of this lane's MFMA output rows: keys ks*32 + lq*8 + h*4 + ii
-      const float* sp = reinterpret_cast<const float*>(buf + T::KSC) + ks * 32 + lq * 8 + h * 4;
-      f32x4 a4 = f32x4{-bias, -bias, -bias, -bias};
+      f16x8_t kf[D / 32];
 #pragma unroll
-      for (int kk = 0; kk < D / 32; ++kk) {
-        // one 32-dim block of the keys: its fp32 sum times the block scale
-        const f16x8_t kf =
-            *reinterpret_cast<const f16x8_t*>(K + key * D + (((kk * 4 + lq) ^ lr) & (KCPR - 1)) * 8);
-        const f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[kk], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-        const f32x4 sc = *reinterpret_cast<const f32x4*>(sp + kk * KT);
+      for (int kk = 0; kk < D / 32; ++kk)
+        kf[kk] = *reinterpret_cast<const f16x8_t*>(K + key * D + (((kk * 4 + lq) ^ lr) & (KCPR - 1)) * 8);
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) a4[ii] = __builtin_fmaf(t[ii], sc[ii], a4[ii]);
+      for (int i = 0; i < QPW; ++i) {
+        if (!has_tile(i)) continue;
+        f32x4 a4 = f32x4{-bias[i], -bias[i], -bias[i], -bias[i]};
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk) a4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[kk], qf[i][kk], a4, 0, 0, 0);
+        sc[i][h] = a4;
       }
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) s[h * 4 + ii] = a4[ii];
     }
-    if (masked) {
+    f16x8_t pb[QPW];
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (k0 + ks * 32 + lq * 8 + e >= k_end) s[e] = -INFINITY;
+    for (int i = 0; i < QPW; ++i) {
+      if (!has_tile(i)) continue;
+      float s[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s[e] = sc[i][e >> 2][e & 3];
+      if (masked) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (k0 + ks * 32 + lq * 8 + e >= k_end) s[e] = -INFINITY;
+      }
+      float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+      mx = rows_max(mx);
+      // lazy rescale: only when the running max moves up by more than 2^8
+      if (__builtin_amdgcn_ballot_w64(bias[i] + mx > m[i] + 8.f) != 0) {
+        const float m_new = fmaxf(m[i], bias[i] + mx);
+        const float alpha = __builtin_amdgcn_exp2f(m[i] - m_new);
+        const float moved = m_new - bias[i];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[e] -= moved;
+        l[i] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) O[i][dt] *= alpha;
+        m[i] = m_new;
+      }
+      float pv[8], psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pv[e] = __builtin_amdgcn_exp2f(s[e]);
+        psum += pv[e];
+      }
+      l[i] += psum;
+      pb[i] = __builtin_bit_cast(
+          f16x8_t, u32x4{pack_f16(pv[0], pv[1]), pack_f16(pv[2], pv[3]), pack_f16(pv[4], pv[5]), pack_f16(pv[6], pv[7])});
     }
-    float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
-    mx = rows_max(mx);
-    // lazy rescale: only when the running max moves up by more than 2^8
-    if (__builtin_amdgcn_ballot_w64(bias + mx > m + 8.f) != 0) {
-      const float m_new = fmaxf(m, bias + mx);
-      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-      const float moved = m_new - bias;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s[e] -= moved;
-      l *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) O[dt] *= alpha;
-      m = m_new;
-    }
-    float pv[8], psum = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      pv[e] = __builtin_amdgcn_exp2f(s[e]);
-      psum += pv[e];
-    }
-    l += psum;
-    const f16x8_t pb = __builtin_bit_cast(
-        f16x8_t, u32x4{pack_f16(pv[0], pv[1]), pack_f16(pv[2], pv[3]), pack_f16(pv[4], pv[5]), pack_f16(pv[6], pv[7])});
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
-      // V^T row dt*16 + lr; the scales of this lane's 4 output dims (the half
-      // is one 32-token block of every dim)
+      // V'^T row dt*16 + lr, tokens ks*32 + lq*8 .. + 7
       const f16x8_t vf =
           *reinterpret_cast<const f16x8_t*>(V + (dt * 16 + lr) * KT + (((ks * 4 + lq) ^ ((lr >> 1) & 7)) * 8));
-      const f32x4 sc = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(buf + T::VSC) + ks * D + dt * 16 +
-                                                      4 * lq);
-      const f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pb, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) O[dt][ii] = __builtin_fmaf(t[ii], sc[ii], O[dt][ii]);
+      for (int i = 0; i < QPW; ++i) {
+        if (!has_tile(i)) continue;
+        O[i][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pb[i], O[i][dt], 0, 0, 0);
+      }
     }
   };
 
   // Tiles go through registers two ahead: at step t the loads of tile t + 2
   // are issued into the register set tile t used, tile t is computed, and
-  // tile t + 1 (loaded during step t - 1) is converted into the LDS buffer
-  // tile t - 1 used, which every wave has finished (the barrier at the top of
+  // tile t + 1 (loaded during step t - 1) is scaled into the LDS buffer tile
+  // t - 1 used, which every wave has finished (the barrier at the top of
   // step t).
   if (n_tiles > 0) {
-    u32x4 regs[2][LPW];
-    auto load_tile = [&](int t, u32x4 (&r)[LPW]) {
+    Q8Slot regs[2][LPW];
+    auto load_tile = [&](int t, Q8Slot (&r)[LPW]) {
 #pragma unroll
       for (int k = 0; k < LPW; ++k) {
         const int j = wave + k * WAVES;
         if (j < T::SLOTS) r[k] = load_slot(t, j);
       }
     };
-    auto store_tile = [&](int t, const u32x4 (&r)[LPW], int b) {
+    auto store_tile = [&](int t, const Q8Slot (&r)[LPW], int b) {
 #pragma unroll
       for (int k = 0; k < LPW; ++k) {
         const int j = wave + k * WAVES;
         if (j < T::SLOTS) store_slot(t, j, r[k], b);
       }
     };
+    const bool any = has_tile(0);
     load_tile(0, regs[0]);
     if (n_tiles > 1) load_tile(1, regs[1]);
     store_tile(0, regs[0], 0);
-    auto step = [&](int t, u32x4 (&mine)[LPW], u32x4 (&next)[LPW]) {
+    auto step = [&](int t, Q8Slot (&mine)[LPW], Q8Slot (&next)[LPW]) {
       lds_barrier();  // tile t is in buffer t & 1; every wave is done with tile t - 1
       if (t + 2 < n_tiles) load_tile(t + 2, mine);
       const int k0 = k_begin + t * KT;
-      if (active) {
+      if (any) {
         const uint8_t* buf = lds + (t & 1) * T::BYTES;
         const bool masked = k0 + KT > k_end;
         row_half(buf, 0, k0, masked);
@@ -334,55 +341,70 @@ __global__ __launch_bounds__(ROWW * 64) void attn_partial_q8_kernel(
     if (t < n_tiles) step(t, regs[0], regs[1]);
   }
 
-  if (active) {
-    const float lt = rows_sum(l);
-    const int row = qt * 16 + lr;
+#pragma unroll
+  for (int i = 0; i < QPW; ++i) {
+    if (!has_tile(i)) continue;
+    const float lt = rows_sum(l[i]);
+    const int row = tile_of(i) * 16 + lr;
     if (row < p.rows) {
       const float inv = 1.0f / lt;
       const int64_t prow = ((int64_t)chunk * p.n_kv_heads + g) * p.rows + row;
       float* dst = p.o_part + prow * D + lq * 4;
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<f32x4*>(dst + dt * 16) = O[dt] * inv;
+      for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<f32x4*>(dst + dt * 16) = O[i][dt] * inv;
       if (lq == 0) {
-        p.ml_part[prow * 2] = m;
+        p.ml_part[prow * 2] = m[i];
         p.ml_part[prow * 2 + 1] = lt;
       }
     }
   }
 }
 
-// Row groups: up to 4 query tiles in one 4-wave block, else groups of at
-// most 8 tiles (as even as they come) on 8-wave blocks.
-static void q8_groups(const AttnPlan& plan, int& groups, int& tiles) {
+// Layouts: one query tile per wave up to 12 tiles (4, 8 or 12 waves), then
+// two tiles per wave on 8 waves, past 16 tiles in row groups of 16.  Measured
+// per layer: 9 tiles (the 27B shape, 22 nodes) 57-59 us on 12 one-tile waves
+// against 67 us on 8 two-tile waves; 15 tiles (40 nodes) 229-232 us on 8
+// two-tile waves against 232-233 us on 16 one-tile waves.
+struct Q8Layout {
+  int qpw, roww, groups, tiles;
+};
+static Q8Layout q8_layout(const AttnPlan& plan) {
   const int rt = (plan.rows + 15) / 16;
-  groups = rt <= 4 ? 1 : (rt + 7) / 8;
-  tiles = (rt + groups - 1) / groups;
+  if (rt <= 4) return {1, 4, 1, rt};
+  if (rt <= 8) return {1, 8, 1, rt};
+  if (rt <= 12) return {1, 12, 1, rt};
+  const int groups = (rt + 15) / 16;
+  return {2, 8, groups, (rt + groups - 1) / groups};
 }
 
 template <int D>
 static void launch_q8_d(const AttnPlan& plan, AttnParams p, hipStream_t s) {
-  q8_groups(plan, p.q8_groups, p.q8_tiles);
-  const dim3 grid(((plan.n_chunks + 7) / 8) * 8 * p.q8_groups, p.n_kv_heads);
-  if (p.q8_tiles <= 4)
-    hipLaunchKernelGGL((attn_partial_q8_kernel<D, 4>), grid, dim3(256), 0, s, p);
+  const Q8Layout v = q8_layout(plan);
+  p.q8_groups = v.groups;
+  p.q8_tiles = v.tiles;
+  const dim3 grid(((plan.n_chunks + 7) / 8) * 8 * v.groups, p.n_kv_heads);
+  if (v.roww == 4)
+    hipLaunchKernelGGL((attn_partial_q8_kernel<D, 1, 4>), grid, dim3(256), 0, s, p);
+  else if (v.qpw == 2)
+    hipLaunchKernelGGL((attn_partial_q8_kernel<D, 2, 8>), grid, dim3(512), 0, s, p);
+  else if (v.roww == 8)
+    hipLaunchKernelGGL((attn_partial_q8_kernel<D, 1, 8>), grid, dim3(512), 0, s, p);
   else
-    hipLaunchKernelGGL((attn_partial_q8_kernel<D, 8>), grid, dim3(512), 0, s, p);
+    hipLaunchKernelGGL((attn_partial_q8_kernel<D, 1, 12>), grid, dim3(768), 0, s, p);
 }
 
 int describe_attention_q8(const AttnPlan& plan, int head_dim, int n_kv_heads, int combine_blocks, char* buf,
                           size_t len) {
-  int groups, tiles;
-  q8_groups(plan, groups, tiles);
-  const int roww = tiles <= 4 ? 4 : 8;
+  const Q8Layout v = q8_layout(plan);
   return snprintf(buf, len,
-                  "attn_partial_q8_kernel<%d, %d> grid (%d, %d) block %d, %d-token chunks, %d row group(s) of %d "
+                  "attn_partial_q8_kernel<%d, %d, %d> grid (%d, %d) block %d, %d-token chunks, %d row group(s) of %d "
                   "tiles; attn_combine_kernel<%d> grid %d block 256",
-                  head_dim, roww, ((plan.n_chunks + 7) / 8) * 8 * groups, n_kv_heads, 64 * roww, plan.chunk, groups,
-                  tiles, head_dim, combine_blocks);
+                  head_dim, v.qpw, v.roww, ((plan.n_chunks + 7) / 8) * 8 * v.groups, n_kv_heads, 64 * v.roww,
+                  plan.chunk, v.groups, v.tiles, head_dim, combine_blocks);
 }
 
-hipError_t launch_attention_q8(const AttnPlan& plan, int head_dim, const AttnParams& p,
-                               const CombineParams& c, const TreeArgs& t, hipStream_t s) {
+hipError_t launch_attention_q8(const AttnPlan& plan, int head_dim, const AttnParams& p, const CombineParams& c,
+                               const TreeArgs& t, hipStream_t s) {
   if (plan.n_chunks > 0) {
     if (head_dim == 128)
       launch_q8_d<128>(plan, p, s);
