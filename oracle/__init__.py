@@ -17,8 +17,9 @@ What it computes, and from which passages:
   "Lucebox 설치 및 실행": decoding at temperature 0 is greedy; the tree budget
   is 22 nodes on an RTX 3090 and 40 on an RTX 5090.
 * "Lucebox Hub", sections "Paged attention + continuous batching" and
-  "설치·사용법": the KV cache may be held as int8 (q8_0); the quantiser and
-  dequantiser here are the block-32 reading of that format.
+  "설치·사용법": the KV cache may be held as int8 (q8_0) or 4-bit (Q4_0); the
+  quantisers and dequantisers here are the block-32 readings of those
+  formats.
 
 Because one forward over the tree must give, at every node, exactly what plain
 one-token-at-a-time greedy decoding of that node's root path gives, the oracle
@@ -36,4 +37,5 @@ from .reference import (  # noqa: F401
     silu, rope, tree_attention, layer_forward, head_logits, argmax_gap,
     accept_path, verify_forward, round_bf16, commit_path, LayerWeights, HeadWeights, Shape,
     quantize_q8_blocks, dequantize_q8_blocks, kv_prefix_from_q8,
+    quantize_q4_blocks, dequantize_q4_blocks, kv_prefix_from_q4,
 )

@@ -358,3 +358,45 @@ def kv_prefix_from_q8(k_codes, k_scales, v_codes, v_scales, prefix_len: int):
     k = dequantize_q8_blocks(k_codes, k_scales)[:, :prefix_len, :]
     v = dequantize_q8_blocks(v_codes, v_scales)[:, :, :prefix_len].transpose(0, 2, 1)
     return k, v
+
+
+def quantize_q4_blocks(x) -> tuple:
+    """Symmetric 4-bit block-32 quantisation along the last axis.
+
+    The pages list a 4-bit KV cache type (Q4_0) beside q8_0 and F16 ("Lucebox
+    Hub", sections "Paged attention + continuous batching" and "설치·사용법")
+    without defining it.  The reading here follows the int8 one and the
+    weights' own 4-bit form (a value is d * (q - 8) with q an unsigned
+    nibble): per block of 32, amax = max |x|; d = fp16(amax / 7) with the
+    division in fp32; q = rint(x / d) in fp32 (ties to even) clamped to
+    [-7, 7], plus 8, so nibbles run 1..15; an all-zero block has d = 0 and
+    nibbles 8.  Returns (nibbles uint8 in 0..15, scales fp16 bits [..., L/32]).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    assert x.shape[-1] % 32 == 0
+    xb = x.astype(np.float32).reshape(x.shape[:-1] + (x.shape[-1] // 32, 32))
+    amax = np.max(np.abs(xb), axis=-1)
+    d16 = (amax / np.float32(7.0)).astype(np.float32).astype(np.float16)
+    dw = d16.astype(np.float32)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(dw > 0, np.rint(xb / np.where(dw > 0, dw, np.float32(1.0))), np.float32(0.0))
+    q = (np.clip(q, -7, 7) + 8).astype(np.uint8).reshape(x.shape)
+    return q, d16.view(np.uint16)
+
+
+def dequantize_q4_blocks(nibbles, scales) -> np.ndarray:
+    """d * (q - 8) per block of 32 along the last axis, exactly in fp64."""
+    q = np.asarray(nibbles, dtype=np.int64) - 8
+    d = f16_to_f64(scales)
+    qb = q.astype(np.float64).reshape(q.shape[:-1] + (q.shape[-1] // 32, 32))
+    return (qb * d[..., None]).reshape(q.shape)
+
+
+def kv_prefix_from_q4(k_nibbles, k_scales, v_nibbles, v_scales, prefix_len: int):
+    """The fp64 prefix K / V [Hkv, P, d] a 4-bit cache stands for, in the int8
+    cache's orientation: k_nibbles [Hkv, cap, d] with k_scales [Hkv, cap, d/32];
+    v_nibbles [Hkv, d, cap] with v_scales [Hkv, d, cap/32] (one nibble value
+    per entry here; the device packs two per byte)."""
+    k = dequantize_q4_blocks(k_nibbles, k_scales)[:, :prefix_len, :]
+    v = dequantize_q4_blocks(v_nibbles, v_scales)[:, :, :prefix_len].transpose(0, 2, 1)
+    return k, v
