@@ -290,40 +290,48 @@ def time_graph(stream, g, reps):
     return a0.elapsed_time(a1) / reps * 1e3  # us
 
 
-def q8_leg(r, cfg, tv, shape, tree, q, out, dev, reps, bf16_us, layers=4):
-    """The one-layer tree attention over an int8 block-32 prefix: the first
-    `layers` layers' caches quantised on the device (set-up, not timed), then
-    lucev_tree_attention_q8 from a graph rotating over them, beside the same
-    call over the bf16 caches (lucev_tree_attention)."""
+def kvq_leg(r, cfg, tv, shape, tree, q, out, dev, reps, bf16_us, bits, layers=4):
+    """The one-layer tree attention over a quantised block-32 prefix (int8
+    codes, or 4-bit nibbles two to a byte): the first `layers` layers'
+    caches quantised on the device (set-up, not timed), then
+    lucev_tree_attention_q8 / _q4 from a graph rotating over them, beside the
+    same call over the bf16 caches (lucev_tree_attention)."""
     import torch
     Hkv, d, P, cap = cfg.n_kv_heads, cfg.head_dim, cfg.prefix, r.capacity
     if cap % 32:
         return None
     L = min(layers, cfg.layers)
+    if bits == 8:
+        quant, make, attn, variant = tv.lucev_kv_quantize_q8, tv.make_kv_q8, tv.lucev_tree_attention_q8, tv.ATTN_Q8
+        kdt, per = torch.int8, 1
+    else:
+        quant, make, attn, variant = tv.lucev_kv_quantize_q4, tv.make_kv_q4, tv.lucev_tree_attention_q4, tv.ATTN_Q4
+        kdt, per = torch.uint8, 2
     caches = []
     st = torch.cuda.current_stream().cuda_stream
     for l in range(L):
-        kc = torch.empty(Hkv, cap, d, dtype=torch.int8, device=dev)
+        kc = torch.empty(Hkv, cap, d // per, dtype=kdt, device=dev)
         ks = torch.empty(Hkv, cap, d // 32, dtype=torch.int16, device=dev)
-        vc = torch.empty(Hkv, d, cap, dtype=torch.int8, device=dev)
+        vc = torch.empty(Hkv, d, cap // per, dtype=kdt, device=dev)
         vs = torch.empty(Hkv, d, cap // 32, dtype=torch.int16, device=dev)
-        tv.lucev_kv_quantize_q8(shape, r.kv(l, P), kc, ks, vc, vs, st)
+        quant(shape, r.kv(l, P), kc, ks, vc, vs, st)
         caches.append((kc, ks, vc, vs))
     torch.cuda.synchronize()
-    kvs = [tv.make_kv_q8(kc, ks, vc, vs, P, cap) for kc, ks, vc, vs in caches]
+    kvs = [make(kc, ks, vc, vs, P, cap) for kc, ks, vc, vs in caches]
     stream = torch.cuda.Stream()
-    g = graph_of(stream, lambda i: tv.lucev_tree_attention_q8(shape, tree, kvs[i % L], q, r.k_tree[0], r.v_tree[0],
-                                                            out, r.ws, r.ws_bytes, stream.cuda_stream), reps)
+    g = graph_of(stream, lambda i: attn(shape, tree, kvs[i % L], q, r.k_tree[0], r.v_tree[0],
+                                        out, r.ws, r.ws_bytes, stream.cuda_stream), reps)
     us = time_graph(stream, g, reps)
     del g, caches
     n, Hq = cfg.nodes, cfg.n_q_heads
-    kv_bytes = P * Hkv * d * 2 * (1 + 2 / 32)
+    kv_bytes = P * Hkv * d * 2 * (bits / 8 + 2 / 32)
     tot = kv_bytes + 2 * n * Hq * d * 2 + 2 * n * Hkv * d * 2
+    name = "int8" if bits == 8 else "4-bit"
     return {"avg_launch_us": round(us, 3), "gbs": round(tot / (us * 1e-6) / 1e9, 2),
             "prefix_bytes": int(kv_bytes), "prefix_bytes_bf16": P * Hkv * d * 4,
-            "vs_bf16_time": round(bf16_us / us, 4), "kernel": tv.lucev_describe_attention(shape, n, P, tv.ATTN_Q8),
-            "what": "lucev_tree_attention_q8 (bf16 q, int8 block-32 prefix with fp16 scales), rotating over %d "
-                    "layers' quantised caches; vs_bf16_time = lucev_tree_attention time / this" % L}
+            "vs_bf16_time": round(bf16_us / us, 4), "kernel": tv.lucev_describe_attention(shape, n, P, variant),
+            "what": "lucev_tree_attention_q%d (bf16 q, %s block-32 prefix with fp16 scales), rotating over %d "
+                    "layers' quantised caches; vs_bf16_time = lucev_tree_attention time / this" % (bits, name, L)}
 
 
 def stream_ceiling(cfg, tv, dev, reps=10):
@@ -502,12 +510,14 @@ def run_config(cfg, args):
     paged_us = paged_leg(r, cfg, tv, shape, tree, q, out, dev, args.attn_reps) if cfg.prefix > 0 else None
     if paged_us:
         log("paged tree attention (one layer): %.2f us" % paged_us)
-    q8 = None
+    q8 = q4 = None
     if cfg.prefix > 0 and not args.no_q8:
-        q8 = q8_leg(r, cfg, tv, shape, tree, q, out, dev, args.attn_reps, bf16_us)
-        if q8:
-            log("int8-prefix tree attention (one layer): %.2f us (%.3fx the bf16 prefix's speed)" %
-                (q8["avg_launch_us"], q8["vs_bf16_time"]))
+        q8 = kvq_leg(r, cfg, tv, shape, tree, q, out, dev, args.attn_reps, bf16_us, 8)
+        q4 = kvq_leg(r, cfg, tv, shape, tree, q, out, dev, args.attn_reps, bf16_us, 4)
+        for nm, x in (("int8", q8), ("4-bit", q4)):
+            if x:
+                log("%s-prefix tree attention (one layer): %.2f us (%.3fx the bf16 prefix's speed)" %
+                    (nm, x["avg_launch_us"], x["vs_bf16_time"]))
 
     line = {
         "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
@@ -540,6 +550,8 @@ def run_config(cfg, args):
                                            "lucev_tree_attention time / this"}
     if q8:
         line["q8_attention"] = q8
+    if q4:
+        line["q4_attention"] = q4
     if args.chain > 0:
         del graph
         line["chained"] = chained(r, cfg, tv, args.chain, dev)
@@ -565,7 +577,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="stack27b", help="a config name, or 'all' (one JSON line each)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-q8", action="store_true")
+    ap.add_argument("--no-q8", action="store_true", help="skip the quantised-prefix (int8 and 4-bit) legs")
     ap.add_argument("--no-ceiling", action="store_true")
     ap.add_argument("--attn-reps", type=int, default=20)
     ap.add_argument("--cold-steps", type=int, default=10)

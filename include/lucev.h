@@ -311,6 +311,49 @@ int lucev_tree_attention_q8(const lucev_shape* shape, const lucev_tree* tree, co
                             const uint16_t* q, const uint16_t* k_tree, const uint16_t* v_tree, uint16_t* out,
                             void* ws, size_t ws_bytes, void* stream);
 
+/* ----------------------------------------------------------- 4-bit KV prefix */
+
+/* One layer's KV cache held as 4-bit codes with one fp16 scale per block of
+ * 32 values: the Q4_0 cache type of the same passages ("Lucebox Hub",
+ * sections "Paged attention + continuous batching" and "설치·사용법"), read
+ * here as value = d * (q - 8), nibble q in [0, 15] (q = 0 never written),
+ * d = fp16(amax / 7).  Blocks as in lucev_kv_q8 (K along the head dim of each
+ * token, V along the tokens of each dim); each block's 32 nibbles fill 16
+ * bytes, as four little-endian dwords of 8 values each, value e (0..7) of a
+ * dword at bits 4 (e / 2) + 16 (e % 2) .. +3 (the order a bit-field insert
+ * under an fp16 exponent decodes two at a time):
+ *   k_nibbles : [Hkv][capacity][d / 2] bytes   (16-byte aligned)
+ *   k_scales  : fp16 [Hkv][capacity][d / 32]   (8-byte aligned)
+ *   v_nibbles : [Hkv][d][capacity / 2] bytes   (16-byte aligned)
+ *   v_scales  : fp16 [Hkv][d][capacity / 32]   (4-byte aligned)
+ * capacity is a multiple of 32; tokens 0 .. prefix_len - 1 are the prefix. */
+typedef struct {
+  const uint8_t* k_nibbles;
+  const uint16_t* k_scales;
+  const uint8_t* v_nibbles;
+  const uint16_t* v_scales;
+  int32_t prefix_len;
+  int32_t capacity;
+} lucev_kv_q4;
+
+/* Quantise every token (0 .. capacity - 1) of a bf16 cache (lucev_kv layout)
+ * into the 4-bit layout above: per block, amax, d = fp16(amax / 7) from an
+ * fp32 division, code = rint(x / d) from an fp32 division (ties to even)
+ * clamped to [-7, 7], nibble code + 8; a block of zeros gets d = 0 and
+ * nibbles 8.  All pointers DEVICE.  Requires src->capacity % 32 == 0.
+ * Returns the codes of lucev_kv_quantize_q8. */
+int lucev_kv_quantize_q4(const lucev_shape* shape, const lucev_kv* src, uint8_t* k_nibbles, uint16_t* k_scales,
+                         uint8_t* v_nibbles, uint16_t* v_scales, void* stream);
+
+/* lucev_tree_attention over a 4-bit prefix: every prefix key and value
+ * enters as the nearest fp16 of d * (q - 8), queries and P as nearest fp16,
+ * all products and sums in fp32 (fp16 MFMAs), exactly as
+ * lucev_tree_attention_q8 does with its codes.  Prefix values must lie within
+ * the fp16 range.  Returns the codes of lucev_tree_attention_q8. */
+int lucev_tree_attention_q4(const lucev_shape* shape, const lucev_tree* tree, const lucev_kv_q4* kv,
+                            const uint16_t* q, const uint16_t* k_tree, const uint16_t* v_tree, uint16_t* out,
+                            void* ws, size_t ws_bytes, void* stream);
+
 /* Final RMSNorm, lm_head, greedy token and top1-top2 gap per node (taken on
  * the fp32 logits), then greedy acceptance over the tree: a node is accepted
  * when its parent is accepted and its drafted token equals the parent's
@@ -408,7 +451,8 @@ int lucev_set_gemv_max_rows(int32_t rows);
  * point uses -- as text: each kernel's template, grid and block, and the
  * prefix chunk per workgroup.  variant 0 = lucev_tree_attention (bf16 q),
  * 1 = lucev_tree_attention_f32 and the verify step (fp32 q, split into bf16
- * hi + lo), 2 = lucev_tree_attention_paged, 3 = lucev_tree_attention_q8.
+ * hi + lo), 2 = lucev_tree_attention_paged, 3 = lucev_tree_attention_q8,
+ * 4 = lucev_tree_attention_q4.
  * Writes at most buf_len bytes, NUL-terminated (truncated if longer).
  * Errors as lucev_tree_attention for the shape and tree size
  * (LUCEV_ERR_BAD_SHAPE, LUCEV_ERR_BAD_TREE); LUCEV_ERR_NULL_ARG for a NULL or

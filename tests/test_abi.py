@@ -251,3 +251,42 @@ def test_attention_row_limit_is_a_shape_error():
     except tv.LucevError as e:
         rc = e.status
     assert rc == -2
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_quantised_kv_validation_before_any_launch(bits):
+    tv = _tv()
+    _no_gpu()
+    s = _shape(tv)
+    fake = 1 << 20
+    attn = tv.lucev_tree_attention_q8 if bits == 8 else tv.lucev_tree_attention_q4
+    quant = tv.lucev_kv_quantize_q8 if bits == 8 else tv.lucev_kv_quantize_q4
+    make = tv.make_kv_q8 if bits == 8 else tv.make_kv_q4
+
+    def a_status(kv, out=fake):
+        try:
+            attn(s, tv.make_tree([-1, 0, 0]), kv, fake, fake, fake, out, fake, 1 << 40)
+        except tv.LucevError as e:
+            return e.status
+        return 0
+
+    def q_status(src, kc=fake, ks=fake):
+        try:
+            quant(s, src, kc, ks, fake, fake)
+        except tv.LucevError as e:
+            return e.status
+        return 0
+
+    assert a_status(make(fake, fake, fake, fake, 64, 100)) == -8        # capacity not a multiple of 32
+    assert a_status(make(fake, fake, fake, fake, 130, 128)) == -8       # prefix beyond capacity
+    assert a_status(make(fake, None, fake, fake, 64, 128)) == -1        # NULL scales
+    assert a_status(make(fake + 8, fake, fake, fake, 64, 128)) == -5    # codes not 16-byte aligned
+    assert a_status(make(fake, fake + 2, fake, fake, 64, 128)) == -5    # K scales not 8-byte aligned
+    assert a_status(make(fake, fake, fake, fake, 64, 128), out=None) == -1
+    assert a_status(make(fake, fake, fake, fake, 64, 128)) in (-6, -7)  # valid: reaches the device check
+    assert a_status(make(None, None, None, None, 0, 0)) in (-6, -7)     # an empty prefix needs no arrays
+    assert q_status(tv.lucev_kv(fake, fake, 64, 100)) == -8
+    assert q_status(tv.lucev_kv(fake, fake, 64, 128), kc=None) == -1
+    assert q_status(tv.lucev_kv(fake, fake, 64, 128), kc=fake + 4) == -5
+    assert q_status(tv.lucev_kv(fake, fake, 64, 128), ks=fake + 1) == -5
+    assert q_status(tv.lucev_kv(fake, fake, 64, 128)) in (-6, -7)

@@ -52,6 +52,11 @@ class lucev_kv_q8(ctypes.Structure):
                 ("prefix_len", c_i32), ("capacity", c_i32)]
 
 
+class lucev_kv_q4(ctypes.Structure):
+    _fields_ = [("k_nibbles", c_vp), ("k_scales", c_vp), ("v_nibbles", c_vp), ("v_scales", c_vp),
+                ("prefix_len", c_i32), ("capacity", c_i32)]
+
+
 class lucev_kv_paged(ctypes.Structure):
     _fields_ = [("k_pages", c_vp), ("v_pages", c_vp), ("block_table", c_vp), ("n_pages", c_i32),
                 ("prefix_len", c_i32)]
@@ -114,6 +119,11 @@ def lib() -> ctypes.CDLL:
                                               c_vp, c_vp, c_sz, c_vp]
         L.lucev_kv_quantize_q8.restype = c_i32
         L.lucev_kv_quantize_q8.argtypes = [P(lucev_shape), P(lucev_kv), c_vp, c_vp, c_vp, c_vp, c_vp]
+        L.lucev_tree_attention_q4.restype = c_i32
+        L.lucev_tree_attention_q4.argtypes = [P(lucev_shape), P(lucev_tree), P(lucev_kv_q4), c_vp, c_vp, c_vp,
+                                              c_vp, c_vp, c_sz, c_vp]
+        L.lucev_kv_quantize_q4.restype = c_i32
+        L.lucev_kv_quantize_q4.argtypes = [P(lucev_shape), P(lucev_kv), c_vp, c_vp, c_vp, c_vp, c_vp]
         L.lucev_tree_attention_noalloc.restype = c_i32
         L.lucev_tree_attention_noalloc.argtypes = [P(lucev_shape), P(lucev_tree), P(lucev_kv), c_vp, c_vp,
                                                    c_vp, c_vp, c_vp]
@@ -139,7 +149,8 @@ EXPORTED = ["lucev_abi_version", "lucev_status_str", "lucev_last_error",
             "lucev_q4_packed_bytes", "lucev_q4_pack", "lucev_q4_pack_device",
             "lucev_workspace_bytes", "lucev_workspace_init", "lucev_verify_layer",
             "lucev_tree_attention", "lucev_tree_attention_f32", "lucev_tree_attention_noalloc",
-            "lucev_tree_attention_q8", "lucev_kv_quantize_q8", "lucev_tree_attention_paged", "lucev_accept_path", "lucev_project_logits",
+            "lucev_tree_attention_q8", "lucev_kv_quantize_q8", "lucev_tree_attention_q4", "lucev_kv_quantize_q4",
+            "lucev_tree_attention_paged", "lucev_accept_path", "lucev_project_logits",
             "lucev_commit_path", "lucev_describe_attention", "lucev_stream_read",
             "lucev_set_gemv_max_rows"]
 
@@ -258,6 +269,21 @@ def lucev_tree_attention_q8(shape, tree, kv, q, k_tree, v_tree, out, ws, ws_byte
            "lucev_tree_attention_q8")
 
 
+def make_kv_q4(k_nibbles, k_scales, v_nibbles, v_scales, prefix_len: int, capacity: int) -> lucev_kv_q4:
+    return lucev_kv_q4(_ptr(k_nibbles), _ptr(k_scales), _ptr(v_nibbles), _ptr(v_scales), prefix_len, capacity)
+
+
+def lucev_kv_quantize_q4(shape, src, k_nibbles, k_scales, v_nibbles, v_scales, stream=None) -> None:
+    _check(lib().lucev_kv_quantize_q4(ctypes.byref(shape), ctypes.byref(src), _ptr(k_nibbles), _ptr(k_scales),
+                                      _ptr(v_nibbles), _ptr(v_scales), stream), "lucev_kv_quantize_q4")
+
+
+def lucev_tree_attention_q4(shape, tree, kv, q, k_tree, v_tree, out, ws, ws_bytes, stream=None) -> None:
+    _check(lib().lucev_tree_attention_q4(ctypes.byref(shape), ctypes.byref(tree), ctypes.byref(kv), _ptr(q),
+                                         _ptr(k_tree), _ptr(v_tree), _ptr(out), _ptr(ws), ws_bytes, stream),
+           "lucev_tree_attention_q4")
+
+
 NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
@@ -311,7 +337,7 @@ def lucev_commit_path(shape, k_cache, v_cache, k_tree, v_tree, prefix_len, capac
                                    stream), "lucev_commit_path")
 
 
-ATTN_BF16, ATTN_F32, ATTN_PAGED, ATTN_Q8 = 0, 1, 2, 3
+ATTN_BF16, ATTN_F32, ATTN_PAGED, ATTN_Q8, ATTN_Q4 = 0, 1, 2, 3, 4
 
 
 def lucev_describe_attention(shape, n_nodes: int, prefix_len: int, variant: int) -> str:

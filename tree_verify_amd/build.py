@@ -6,7 +6,7 @@ import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["api.hip", "gemm_q4.hip", "attention.hip", "attention_q8.hip", "misc.hip", "split.hip"]
+SOURCES = ["api.hip", "gemm_q4.hip", "attention.hip", "attention_kvq.hip", "misc.hip", "split.hip"]
 LIB = os.path.join(HERE, "liblucev.so")
 
 # Packed-fp32 VALU forms are kept out of the generated code on purpose.
@@ -20,7 +20,7 @@ HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
 # int8 attention takes only finite inputs, and its divisions and roundings
 # stay IEEE-exact in either mode).
 _ATTN = ["-mllvm", "-amdgpu-mfma-vgpr-form=true", "-mno-amdgpu-ieee", "-fno-honor-nans"]
-EXTRA = {"attention.hip": _ATTN, "attention_q8.hip": _ATTN}
+EXTRA = {"attention.hip": _ATTN, "attention_kvq.hip": _ATTN}
 
 
 def build(verbose: bool = False) -> str:

@@ -260,14 +260,25 @@ EpiArgs epi_blank() {
   return e;
 }
 
+// A quantised prefix as the attention reads it: int8 codes or packed
+// nibbles (bits 8 or 4) with fp16 block-32 scales
+struct KvQuant {
+  const void* k_codes;
+  const uint16_t* k_scales;
+  const void* v_codes;
+  const uint16_t* v_scales;
+  int bits;
+};
+
 // q / k_tree / v_tree bf16 (always); q32 / k32 / v32 fp32 copies or NULL;
 // out bf16 [n][Hq][d], or the Wo operand's fp16 hi/lo rows when out_hilo is
-// set; out32 (fp32 [n][Hq][d]) instead of both when not NULL
+// set; out32 (fp32 [n][Hq][d]) instead of both when not NULL; kq a quantised
+// prefix in place of kv's bf16 arrays, when not NULL
 int run_attention(const lucev_shape* s, const TreeArgs& t, const lucev_kv* kv, const uint16_t* q,
                   const uint16_t* k_tree, const uint16_t* v_tree, const float* q32,
                   const float* k32, const float* v32, uint16_t* out, int out_hilo, float* o_part,
                   float* ml_part, hipStream_t st, const int32_t* table = nullptr, int n_phys = 0,
-                  float* out32 = nullptr, const lucev_kv_q8* q8 = nullptr) {
+                  float* out32 = nullptr, const KvQuant* kq = nullptr) {
   AttnPlan plan = plan_attention(t.n, s->n_q_heads, s->n_kv_heads, s->head_dim, kv->prefix_len);
   if (table && plan.chunk / kPageTokens > kMaxChunkPagesHost)
     return fail(LUCEV_ERR_BAD_KV, "paged attention: %d-token prefix chunks exceed %d pages", plan.chunk,
@@ -290,10 +301,10 @@ int run_attention(const lucev_shape* s, const TreeArgs& t, const lucev_kv* kv, c
   p.table = table;
   p.n_phys = n_phys;
   p.ml_part = ml_part;
-  p.kc8 = q8 ? q8->k_codes : nullptr;
-  p.ks16 = q8 ? q8->k_scales : nullptr;
-  p.vc8 = q8 ? q8->v_codes : nullptr;
-  p.vs16 = q8 ? q8->v_scales : nullptr;
+  p.kc8 = kq ? static_cast<const int8_t*>(kq->k_codes) : nullptr;
+  p.ks16 = kq ? kq->k_scales : nullptr;
+  p.vc8 = kq ? static_cast<const int8_t*>(kq->v_codes) : nullptr;
+  p.vs16 = kq ? kq->v_scales : nullptr;
   CombineParams c;
   c.q = q;
   c.k_tree = k_tree;
@@ -312,7 +323,7 @@ int run_attention(const lucev_shape* s, const TreeArgs& t, const lucev_kv* kv, c
   c.out = out;
   c.out_hilo = out_hilo;
   c.out32 = out32;
-  hipError_t e = q8 ? launch_attention_q8(plan, s->head_dim, p, c, t, st)
+  hipError_t e = kq ? launch_attention_q8(plan, s->head_dim, kq->bits, p, c, t, st)
                     : launch_attention(plan, s->head_dim, p, c, t, st);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return LUCEV_OK;
@@ -457,58 +468,93 @@ int lucev_tree_attention_f32(const lucev_shape* shape, const lucev_tree* tree, c
                        at<float>(ws, L.opart), at<float>(ws, L.ml), (hipStream_t)stream, nullptr, 0, out);
 }
 
-static int check_kv_q8(const lucev_shape* shape, const lucev_kv_q8* kv) {
-  if (!kv) return fail(LUCEV_ERR_NULL_ARG, "kv is NULL");
-  if (kv->prefix_len < 0 || kv->capacity < 0 || kv->prefix_len > kv->capacity)
-    return fail(LUCEV_ERR_BAD_KV, "prefix_len %d / capacity %d invalid", kv->prefix_len, kv->capacity);
-  if (kv->capacity % 32) return fail(LUCEV_ERR_BAD_KV, "an int8 cache's capacity must be a multiple of 32");
-  if (kv->prefix_len > 0 && (!kv->k_codes || !kv->k_scales || !kv->v_codes || !kv->v_scales))
-    return fail(LUCEV_ERR_NULL_ARG, "int8 cache: NULL codes or scales");
-  if (!aligned16(kv->k_codes) || !aligned16(kv->v_codes) || (reinterpret_cast<uintptr_t>(kv->k_scales) & 7u) ||
-      (reinterpret_cast<uintptr_t>(kv->v_scales) & 3u))
-    return fail(LUCEV_ERR_ALIGN, "int8 cache: codes must be 16-byte, K scales 8-byte, V scales 4-byte aligned");
-  (void)shape;
+// prefix_len / capacity / pointers / alignment of a quantised cache
+static int check_kv_quant(int prefix_len, int capacity, const KvQuant& q, const char* what) {
+  if (prefix_len < 0 || capacity < 0 || prefix_len > capacity)
+    return fail(LUCEV_ERR_BAD_KV, "prefix_len %d / capacity %d invalid", prefix_len, capacity);
+  if (capacity % 32) return fail(LUCEV_ERR_BAD_KV, "%s cache: capacity must be a multiple of 32", what);
+  if (prefix_len > 0 && (!q.k_codes || !q.k_scales || !q.v_codes || !q.v_scales))
+    return fail(LUCEV_ERR_NULL_ARG, "%s cache: NULL codes or scales", what);
+  if (!aligned16(q.k_codes) || !aligned16(q.v_codes) || (reinterpret_cast<uintptr_t>(q.k_scales) & 7u) ||
+      (reinterpret_cast<uintptr_t>(q.v_scales) & 3u))
+    return fail(LUCEV_ERR_ALIGN, "%s cache: codes must be 16-byte, K scales 8-byte, V scales 4-byte aligned", what);
   return LUCEV_OK;
+}
+
+static int tree_attention_quant(const lucev_shape* shape, const lucev_tree* tree, int prefix_len, int capacity,
+                                const KvQuant& kq, const uint16_t* q, const uint16_t* k_tree,
+                                const uint16_t* v_tree, uint16_t* out, void* ws, size_t ws_bytes, void* stream,
+                                const char* what) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (!q || !k_tree || !v_tree || !out) return fail(LUCEV_ERR_NULL_ARG, "tree_attention_%s: NULL tensor", what);
+  if ((rc = check_kv_quant(prefix_len, capacity, kq, what))) return rc;
+  TreeArgs t;
+  if ((rc = prep_tree(tree, shape->vocab, prefix_len, &t))) return rc;
+  if ((rc = check_attn_rows(shape, t.n))) return rc;
+  if (!aligned16(q) || !aligned16(k_tree) || !aligned16(v_tree) || !aligned16(out))
+    return fail(LUCEV_ERR_ALIGN, "tree_attention_%s: tensors must be 16-byte aligned", what);
+  Ws L;
+  if ((rc = check_ws(shape, t.n, prefix_len, ws, ws_bytes, &L))) return rc;
+  if ((rc = check_device())) return rc;
+  lucev_kv flat;  // geometry only; the codes and scales come from kq
+  flat.k = nullptr;
+  flat.v = nullptr;
+  flat.prefix_len = prefix_len;
+  flat.capacity = capacity;
+  return run_attention(shape, t, &flat, q, k_tree, v_tree, nullptr, nullptr, nullptr, out, 0,
+                       at<float>(ws, L.opart), at<float>(ws, L.ml), (hipStream_t)stream, nullptr, 0, nullptr, &kq);
 }
 
 int lucev_tree_attention_q8(const lucev_shape* shape, const lucev_tree* tree, const lucev_kv_q8* kv,
                             const uint16_t* q, const uint16_t* k_tree, const uint16_t* v_tree, uint16_t* out,
                             void* ws, size_t ws_bytes, void* stream) {
-  int rc = check_shape(shape);
-  if (rc) return rc;
-  if (!q || !k_tree || !v_tree || !out) return fail(LUCEV_ERR_NULL_ARG, "tree_attention_q8: NULL tensor");
-  if ((rc = check_kv_q8(shape, kv))) return rc;
-  TreeArgs t;
-  if ((rc = prep_tree(tree, shape->vocab, kv->prefix_len, &t))) return rc;
-  if ((rc = check_attn_rows(shape, t.n))) return rc;
-  if (!aligned16(q) || !aligned16(k_tree) || !aligned16(v_tree) || !aligned16(out))
-    return fail(LUCEV_ERR_ALIGN, "tree_attention_q8: tensors must be 16-byte aligned");
-  Ws L;
-  if ((rc = check_ws(shape, t.n, kv->prefix_len, ws, ws_bytes, &L))) return rc;
-  if ((rc = check_device())) return rc;
-  lucev_kv flat;  // geometry only; the int8 arrays come from kv
-  flat.k = nullptr;
-  flat.v = nullptr;
-  flat.prefix_len = kv->prefix_len;
-  flat.capacity = kv->capacity;
-  return run_attention(shape, t, &flat, q, k_tree, v_tree, nullptr, nullptr, nullptr, out, 0,
-                       at<float>(ws, L.opart), at<float>(ws, L.ml), (hipStream_t)stream, nullptr, 0, nullptr, kv);
+  if (!kv) return fail(LUCEV_ERR_NULL_ARG, "kv is NULL");
+  const KvQuant kq{kv->k_codes, kv->k_scales, kv->v_codes, kv->v_scales, 8};
+  return tree_attention_quant(shape, tree, kv->prefix_len, kv->capacity, kq, q, k_tree, v_tree, out, ws, ws_bytes,
+                              stream, "q8");
 }
 
-int lucev_kv_quantize_q8(const lucev_shape* shape, const lucev_kv* src, int8_t* k_codes, uint16_t* k_scales,
-                         int8_t* v_codes, uint16_t* v_scales, void* stream) {
+int lucev_tree_attention_q4(const lucev_shape* shape, const lucev_tree* tree, const lucev_kv_q4* kv,
+                            const uint16_t* q, const uint16_t* k_tree, const uint16_t* v_tree, uint16_t* out,
+                            void* ws, size_t ws_bytes, void* stream) {
+  if (!kv) return fail(LUCEV_ERR_NULL_ARG, "kv is NULL");
+  const KvQuant kq{kv->k_nibbles, kv->k_scales, kv->v_nibbles, kv->v_scales, 4};
+  return tree_attention_quant(shape, tree, kv->prefix_len, kv->capacity, kq, q, k_tree, v_tree, out, ws, ws_bytes,
+                              stream, "q4");
+}
+
+// shape, source cache and output pointers of a quantisation call
+static int check_quantize(const lucev_shape* shape, const lucev_kv* src, const void* k_codes,
+                          const uint16_t* k_scales, const void* v_codes, const uint16_t* v_scales, const char* what) {
   int rc = check_shape(shape);
   if (rc) return rc;
   if ((rc = check_kv(src))) return rc;
   if (!src->k || !src->v || !k_codes || !k_scales || !v_codes || !v_scales)
-    return fail(LUCEV_ERR_NULL_ARG, "kv_quantize_q8: NULL pointer");
-  if (src->capacity % 32) return fail(LUCEV_ERR_BAD_KV, "kv_quantize_q8: capacity must be a multiple of 32");
+    return fail(LUCEV_ERR_NULL_ARG, "kv_quantize_%s: NULL pointer", what);
+  if (src->capacity % 32) return fail(LUCEV_ERR_BAD_KV, "kv_quantize_%s: capacity must be a multiple of 32", what);
   if (!aligned16(k_codes) || !aligned16(v_codes) || (reinterpret_cast<uintptr_t>(k_scales) & 1u) ||
       (reinterpret_cast<uintptr_t>(v_scales) & 1u))
-    return fail(LUCEV_ERR_ALIGN, "kv_quantize_q8: codes must be 16-byte aligned");
-  if ((rc = check_device())) return rc;
+    return fail(LUCEV_ERR_ALIGN, "kv_quantize_%s: codes must be 16-byte aligned", what);
+  return check_device();
+}
+
+int lucev_kv_quantize_q8(const lucev_shape* shape, const lucev_kv* src, int8_t* k_codes, uint16_t* k_scales,
+                         int8_t* v_codes, uint16_t* v_scales, void* stream) {
+  int rc = check_quantize(shape, src, k_codes, k_scales, v_codes, v_scales, "q8");
+  if (rc) return rc;
   hipError_t e = launch_quantize_q8(src->k, src->v, shape->n_kv_heads, src->capacity, shape->head_dim, k_codes,
                                     k_scales, v_codes, v_scales, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "quantize launch");
+  return LUCEV_OK;
+}
+
+int lucev_kv_quantize_q4(const lucev_shape* shape, const lucev_kv* src, uint8_t* k_nibbles, uint16_t* k_scales,
+                         uint8_t* v_nibbles, uint16_t* v_scales, void* stream) {
+  int rc = check_quantize(shape, src, k_nibbles, k_scales, v_nibbles, v_scales, "q4");
+  if (rc) return rc;
+  hipError_t e = launch_quantize_q4(src->k, src->v, shape->n_kv_heads, src->capacity, shape->head_dim, k_nibbles,
+                                    k_scales, v_nibbles, v_scales, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "quantize launch");
   return LUCEV_OK;
 }
@@ -755,11 +801,11 @@ int lucev_describe_attention(const lucev_shape* shape, int32_t n_nodes, int32_t 
   if (n_nodes < 1 || n_nodes > LUCEV_MAX_NODES || prefix_len < 0)
     return fail(LUCEV_ERR_BAD_TREE, "describe_attention: n_nodes %d / prefix_len %d invalid", n_nodes, prefix_len);
   if ((rc = check_attn_rows(shape, n_nodes))) return rc;
-  if (variant < 0 || variant > 3) return fail(LUCEV_ERR_BAD_SHAPE, "describe_attention: variant %d", variant);
+  if (variant < 0 || variant > 4) return fail(LUCEV_ERR_BAD_SHAPE, "describe_attention: variant %d", variant);
   const AttnPlan plan = plan_attention(n_nodes, shape->n_q_heads, shape->n_kv_heads, shape->head_dim, prefix_len);
   const int cb = n_nodes * shape->n_q_heads;
-  if (variant == 3)
-    describe_attention_q8(plan, shape->head_dim, shape->n_kv_heads, cb, buf, buf_len);
+  if (variant >= 3)
+    describe_attention_q8(plan, shape->head_dim, shape->n_kv_heads, cb, variant == 3 ? 8 : 4, buf, buf_len);
   else
     describe_attention(plan, shape->head_dim, shape->n_kv_heads, cb, variant == 1, variant == 2, buf, buf_len);
   return LUCEV_OK;

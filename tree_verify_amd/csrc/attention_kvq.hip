@@ -1,23 +1,29 @@
-// Tree attention over an int8 KV prefix, and the quantiser that writes one.
+// Tree attention over a quantised KV prefix (int8 or 4-bit codes), and the
+// quantisers that write one.
 //
-// The KV cache is held as int8 codes with one fp16 scale per 32 values, the
-// q8_0 cache type the pages run beside F16 and Q4_0 ("Lucebox Hub", sections
-// "Paged attention + continuous batching" and "설치·사용법"; KV size is the
-// VRAM limit of section "배경: 어떤 문제를 푸는가", item 3).  Keys are blocked
-// along the head dim of each token, values along the tokens of each dim (the
-// cache keeps V dim-major), so 16 consecutive codes a lane loads share one
-// scale.
+// The KV cache is held as int8 codes or 4-bit nibbles with one fp16 scale per
+// 32 values, the q8_0 and Q4_0 cache types the pages run beside F16 ("Lucebox
+// Hub", sections "Paged attention + continuous batching" and "설치·사용법";
+// KV size is the VRAM limit of section "배경: 어떤 문제를 푸는가", item 3).
+// Keys are blocked along the head dim of each token, values along the tokens
+// of each dim (the cache keeps V dim-major), so 16 consecutive codes a lane
+// loads share one scale.  A value is d * code (int8, code in [-127, 127]) or
+// d * (q - 8) (4-bit, nibble q in [0, 15]).  Nibbles are packed 8 to a
+// dword, value e of the 8 at bit 4 (e / 2) + 16 (e % 2), so that placing
+// them under an fp16 exponent with one v_bfi_b32 per pair yields them in
+// order.
 //
 // The partial kernel follows the bf16 one (blocks over prefix chunk and KV
 // head, 64-token tiles in a two-buffer LDS ring, S^T = K Q^T with the softmax
 // axis inside each lane, lazy rescale, P fed to O^T = V^T P^T from
 // registers), with these differences:
 //   * tiles go through registers, two tiles ahead: a lane loads 16 codes and
-//     their scale, turns the codes into exact fp16 values (the byte XOR 0x80
-//     placed under the exponent of 1024 with v_perm_b32, minus 1152), scales
-//     them with one packed fp16 multiply -- d * code rounded once to fp16,
-//     within 2^-11 of itself and 16 times finer than the int8 step -- and
-//     stores them into the bf16 kernel's swizzled LDS layouts;
+//     their scale, turns the codes into exact fp16 values (an int8 byte XOR
+//     0x80 placed under the exponent of 1024 with v_perm_b32, minus 1152; a
+//     nibble under the exponent of 1024 or 64 with v_bfi_b32, minus 1032 or
+//     72), scales them with one packed fp16 multiply -- the value rounded
+//     once to fp16, within 2^-11 of itself, finer than either format's step
+//     -- and stores them into the bf16 kernel's swizzled LDS layouts;
 //   * every MFMA is f16 and single: K' q (q as nearest fp16) and V' P (P as
 //     nearest fp16), accumulated directly; the int8 cache's own rounding
 //     dwarfs these, so no hi/lo halves are carried;
@@ -73,6 +79,44 @@ __device__ __forceinline__ void scaled16(const u32x4& w, uint32_t scale16, u32x4
   out1 = u32x4{o[4], o[5], o[6], o[7]};
 }
 
+// v_bfi_b32: (a & mask) | (b & ~mask)
+__device__ __forceinline__ uint32_t bfi_kv(uint32_t mask, uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(mask), "v"(a), "v"(b));
+  return r;
+}
+
+// 8 nibbles of one dword (value e at bit 4 (e / 2) + 16 (e % 2)) times their
+// scale: fp16 d * (q - 8) in order, as four dwords.  A nibble in the low
+// mantissa bits of 1024 reads 1024 + q, one four bits higher under 64 reads
+// 64 + q; subtracting 1032 or 72 leaves q - 8 exactly.
+__device__ __forceinline__ void nibbles8_scaled(uint32_t w, f16x2 dd, uint32_t* o) {
+  const uint32_t w8 = w >> 8;
+  const f16x2 b1032 = {(f16)1032.0f, (f16)1032.0f};
+  const f16x2 b72 = {(f16)72.0f, (f16)72.0f};
+  o[0] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, bfi_kv(0x000F000Fu, w, 0x64006400u)) - b1032) * dd);
+  o[1] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, bfi_kv(0x00F000F0u, w, 0x54005400u)) - b72) * dd);
+  o[2] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, bfi_kv(0x000F000Fu, w8, 0x64006400u)) - b1032) * dd);
+  o[3] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, bfi_kv(0x00F000F0u, w8, 0x54005400u)) - b72) * dd);
+}
+
+// 16 codes of a lane (int8: four dwords; 4-bit: the first two) times their
+// scale, as two 16-byte chunks in order
+template <int BITS>
+__device__ __forceinline__ void scaled16_kv(const u32x4& w, uint32_t scale16, u32x4& out0, u32x4& out1) {
+  if constexpr (BITS == 8) {
+    scaled16(w, scale16, out0, out1);
+  } else {
+    const f16 d = __builtin_bit_cast(f16, (uint16_t)scale16);
+    const f16x2 dd = {d, d};
+    uint32_t a[4], b[4];
+    nibbles8_scaled(w[0], dd, a);
+    nibbles8_scaled(w[1], dd, b);
+    out0 = u32x4{a[0], a[1], a[2], a[3]};
+    out1 = u32x4{b[0], b[1], b[2], b[3]};
+  }
+}
+
 // Two fp32 values as fp16 (nearest), packed
 __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
   return __builtin_bit_cast(uint32_t, f16x2{(f16)a, (f16)b});
@@ -96,8 +140,9 @@ struct Q8Slot {
   uint32_t scale;  // fp16 bits
 };
 
-template <int D, int QPW, int ROWW>
+template <int D, int QPW, int ROWW, int BITS>
 __global__ __launch_bounds__(ROWW * 64) void attn_partial_q8_kernel(AttnParams p) {
+  static_assert(BITS == 8 || BITS == 4, "int8 or 4-bit codes");
   using T = Q8Tile<D>;
   constexpr int WAVES = ROWW;
   constexpr int KCPR = D / 8;  // 16-byte chunks per K row
@@ -125,8 +170,9 @@ __global__ __launch_bounds__(ROWW * 64) void attn_partial_q8_kernel(AttnParams p
   auto tile_of = [&](int i) __attribute__((always_inline)) { return grp * p.q8_tiles + wave + ROWW * i; };
   auto has_tile = [&](int i) __attribute__((always_inline)) { return wave + ROWW * i < p.q8_tiles && tile_of(i) < RT; };
 
-  const int8_t* kcode = p.kc8 + (int64_t)g * p.cap * D;
-  const int8_t* vcode = p.vc8 + (int64_t)g * D * p.cap;
+  // code bytes of this KV head (BITS / 8 bytes per code)
+  const uint8_t* kcode = reinterpret_cast<const uint8_t*>(p.kc8) + (int64_t)g * p.cap * D * BITS / 8;
+  const uint8_t* vcode = reinterpret_cast<const uint8_t*>(p.vc8) + (int64_t)g * D * p.cap * BITS / 8;
   const uint16_t* kscale = p.ks16 + (int64_t)g * p.cap * NBLK;
   const uint16_t* vscale = p.vs16 + (int64_t)g * D * (p.cap / 32);
 
@@ -139,14 +185,24 @@ __global__ __launch_bounds__(ROWW * 64) void attn_partial_q8_kernel(AttnParams p
       const int key = j * (1024 / D) + lane / (D / 16);
       const int c16 = lane % (D / 16);  // codes 16 c16 .. + 15 of the key: scale block c16 / 2
       if (k0 + key < k_end) {
-        r.codes = ld16(kcode + (int64_t)(k0 + key) * D + c16 * 16);
+        if constexpr (BITS == 8) {
+          r.codes = ld16(kcode + (int64_t)(k0 + key) * D + c16 * 16);
+        } else {
+          const u32x2 w = *reinterpret_cast<const u32x2*>(kcode + (int64_t)(k0 + key) * (D / 2) + c16 * 8);
+          r.codes = u32x4{w[0], w[1], 0u, 0u};
+        }
         r.scale = kscale[(int64_t)(k0 + key) * NBLK + (c16 >> 1)];
       }
     } else {
       const int jj = j - T::NK;
       const int dim = jj * 16 + lane / 4, part = lane % 4;  // tokens k0 + 16 part .. + 15
       if (k0 + part * 16 < k_end) {
-        r.codes = ld16(vcode + (int64_t)dim * p.cap + k0 + part * 16);
+        if constexpr (BITS == 8) {
+          r.codes = ld16(vcode + (int64_t)dim * p.cap + k0 + part * 16);
+        } else {
+          const u32x2 w = *reinterpret_cast<const u32x2*>(vcode + (int64_t)dim * (p.cap / 2) + (k0 + part * 16) / 2);
+          r.codes = u32x4{w[0], w[1], 0u, 0u};
+        }
         r.scale = vscale[(int64_t)dim * (p.cap / 32) + ((k0 + part * 16) >> 5)];
       }
     }
@@ -162,7 +218,7 @@ __global__ __launch_bounds__(ROWW * 64) void attn_partial_q8_kernel(AttnParams p
       const int c16 = lane % (D / 16);
       const int sw = ((key & 3) | (((key >> 3) & 3) << 2)) & (KCPR - 1);
       u32x4 c0, c1;
-      scaled16(v.codes, v.scale, c0, c1);
+      scaled16_kv<BITS>(v.codes, v.scale, c0, c1);
       uint8_t* row = base + key * D * 2;
       *reinterpret_cast<u32x4*>(row + (((2 * c16) ^ sw) * 16)) = c0;
       *reinterpret_cast<u32x4*>(row + (((2 * c16 + 1) ^ sw) * 16)) = c1;
@@ -171,15 +227,23 @@ __global__ __launch_bounds__(ROWW * 64) void attn_partial_q8_kernel(AttnParams p
       const int dim = jj * 16 + lane / 4, part = lane % 4;
       const int swz = (dim >> 1) & 7;
       u32x4 w = v.codes;
-      // tokens past the prefix inside this 16-token run read as code 0
+      // tokens past the prefix inside this 16-token run read as value 0
+      // (int8 code 0; nibble 8)
       const int valid = k_end - (k0 + part * 16);
       if (valid < 16) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (e >= valid) w[e >> 2] &= ~(0xFFu << (8 * (e & 3)));
+        for (int e = 0; e < 16; ++e) {
+          if (e < valid) continue;
+          if constexpr (BITS == 8) {
+            w[e >> 2] &= ~(0xFFu << (8 * (e & 3)));
+          } else {
+            const int b = 4 * ((e & 7) >> 1) + 16 * (e & 1);
+            w[e >> 3] = (w[e >> 3] & ~(0xFu << b)) | (8u << b);
+          }
+        }
       }
       u32x4 c0, c1;
-      scaled16(w, v.scale, c0, c1);
+      scaled16_kv<BITS>(w, v.scale, c0, c1);
       uint8_t* row = base + T::KBYTES + dim * KT * 2;
       *reinterpret_cast<u32x4*>(row + (((2 * part) ^ swz) * 16)) = c0;
       *reinterpret_cast<u32x4*>(row + (((2 * part + 1) ^ swz) * 16)) = c1;
@@ -377,39 +441,46 @@ static Q8Layout q8_layout(const AttnPlan& plan) {
   return {2, 8, groups, (rt + groups - 1) / groups};
 }
 
-template <int D>
+template <int D, int BITS>
 static void launch_q8_d(const AttnPlan& plan, AttnParams p, hipStream_t s) {
   const Q8Layout v = q8_layout(plan);
   p.q8_groups = v.groups;
   p.q8_tiles = v.tiles;
   const dim3 grid(((plan.n_chunks + 7) / 8) * 8 * v.groups, p.n_kv_heads);
   if (v.roww == 4)
-    hipLaunchKernelGGL((attn_partial_q8_kernel<D, 1, 4>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((attn_partial_q8_kernel<D, 1, 4, BITS>), grid, dim3(256), 0, s, p);
   else if (v.qpw == 2)
-    hipLaunchKernelGGL((attn_partial_q8_kernel<D, 2, 8>), grid, dim3(512), 0, s, p);
+    hipLaunchKernelGGL((attn_partial_q8_kernel<D, 2, 8, BITS>), grid, dim3(512), 0, s, p);
   else if (v.roww == 8)
-    hipLaunchKernelGGL((attn_partial_q8_kernel<D, 1, 8>), grid, dim3(512), 0, s, p);
+    hipLaunchKernelGGL((attn_partial_q8_kernel<D, 1, 8, BITS>), grid, dim3(512), 0, s, p);
   else
-    hipLaunchKernelGGL((attn_partial_q8_kernel<D, 1, 12>), grid, dim3(768), 0, s, p);
+    hipLaunchKernelGGL((attn_partial_q8_kernel<D, 1, 12, BITS>), grid, dim3(768), 0, s, p);
 }
 
-int describe_attention_q8(const AttnPlan& plan, int head_dim, int n_kv_heads, int combine_blocks, char* buf,
-                          size_t len) {
+int describe_attention_q8(const AttnPlan& plan, int head_dim, int n_kv_heads, int combine_blocks, int bits,
+                          char* buf, size_t len) {
   const Q8Layout v = q8_layout(plan);
   return snprintf(buf, len,
-                  "attn_partial_q8_kernel<%d, %d, %d> grid (%d, %d) block %d, %d-token chunks, %d row group(s) of %d "
-                  "tiles; attn_combine_kernel<%d> grid %d block 256",
-                  head_dim, v.qpw, v.roww, ((plan.n_chunks + 7) / 8) * 8 * v.groups, n_kv_heads, 64 * v.roww,
+                  "attn_partial_q8_kernel<%d, %d, %d, %d> grid (%d, %d) block %d, %d-token chunks, %d row group(s) of "
+                  "%d tiles; attn_combine_kernel<%d> grid %d block 256",
+                  head_dim, v.qpw, v.roww, bits, ((plan.n_chunks + 7) / 8) * 8 * v.groups, n_kv_heads, 64 * v.roww,
                   plan.chunk, v.groups, v.tiles, head_dim, combine_blocks);
 }
 
-hipError_t launch_attention_q8(const AttnPlan& plan, int head_dim, const AttnParams& p, const CombineParams& c,
-                               const TreeArgs& t, hipStream_t s) {
+hipError_t launch_attention_q8(const AttnPlan& plan, int head_dim, int bits, const AttnParams& p,
+                               const CombineParams& c, const TreeArgs& t, hipStream_t s) {
   if (plan.n_chunks > 0) {
-    if (head_dim == 128)
-      launch_q8_d<128>(plan, p, s);
-    else
-      launch_q8_d<64>(plan, p, s);
+    if (head_dim == 128) {
+      if (bits == 8)
+        launch_q8_d<128, 8>(plan, p, s);
+      else
+        launch_q8_d<128, 4>(plan, p, s);
+    } else {
+      if (bits == 8)
+        launch_q8_d<64, 8>(plan, p, s);
+      else
+        launch_q8_d<64, 4>(plan, p, s);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -465,6 +536,63 @@ __global__ __launch_bounds__(256) void quantize_q8_kernel(const uint16_t* kc, co
     const int64_t v = i - nk;
     quantize_block32(vc + v * 32, v_codes + v * 32, v_scales + v);
   }
+}
+
+// The 4-bit form: d = fp16(amax / 7) (fp32 division), codes rint(x / d)
+// clamped to [-7, 7] (fp32, ties to even), stored as nibbles code + 8 in the
+// order the attention decodes (value e of each 8 at bit 4 (e / 2) +
+// 16 (e % 2)); a block of zeros gets d = 0 and nibbles 8.
+__device__ __forceinline__ void quantize_block32_q4(const uint16_t* src, uint8_t* nib, uint16_t* scale) {
+  float x[32];
+  float amax = 0.f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const u32x4 w = ld16(src + c * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float v = bf16_bits_to_f32(e & 1 ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xFFFFu));
+      x[c * 8 + e] = v;
+      amax = fmaxf(amax, fabsf(v));
+    }
+  }
+  const f16 d16 = (f16)(amax / 7.0f);
+  const float dw = (float)d16;
+  uint32_t packed[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float cf = dw > 0.f ? rintf(x[q * 8 + e] / dw) : 0.f;
+      cf = fminf(fmaxf(cf, -7.f), 7.f);
+      w |= ((uint32_t)((int)cf + 8) & 0xFu) << (4 * (e >> 1) + 16 * (e & 1));
+    }
+    packed[q] = w;
+  }
+  st16(nib, u32x4{packed[0], packed[1], packed[2], packed[3]});
+  *scale = __builtin_bit_cast(uint16_t, d16);
+}
+
+__global__ __launch_bounds__(256) void quantize_q4_kernel(const uint16_t* kc, const uint16_t* vc, int hkv, int cap,
+                                                          int d, uint8_t* k_nib, uint16_t* k_scales, uint8_t* v_nib,
+                                                          uint16_t* v_scales) {
+  const int64_t nk = (int64_t)hkv * cap * (d / 32);  // K blocks: (g, t, b)
+  const int64_t nv = (int64_t)hkv * d * (cap / 32);  // V blocks: (g, j, tb)
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < nk) {
+    quantize_block32_q4(kc + i * 32, k_nib + i * 16, k_scales + i);
+  } else if (i < nk + nv) {
+    const int64_t v = i - nk;
+    quantize_block32_q4(vc + v * 32, v_nib + v * 16, v_scales + v);
+  }
+}
+
+hipError_t launch_quantize_q4(const uint16_t* kc, const uint16_t* vc, int hkv, int cap, int d, uint8_t* k_nib,
+                              uint16_t* k_scales, uint8_t* v_nib, uint16_t* v_scales, hipStream_t s) {
+  const int64_t n = (int64_t)hkv * cap * (d / 32) + (int64_t)hkv * d * (cap / 32);
+  hipLaunchKernelGGL(quantize_q4_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, kc, vc, hkv, cap, d,
+                     k_nib, k_scales, v_nib, v_scales);
+  return hipGetLastError();
 }
 
 hipError_t launch_quantize_q8(const uint16_t* kc, const uint16_t* vc, int hkv, int cap, int d, int8_t* k_codes,

@@ -140,7 +140,7 @@ struct AttnParams {
   float* ml_part;      // fp32 [n_chunks][Hkv][rows][2]: (max, sum) in log2 units
   const int32_t* table;  // paged cache: page of each 16 prefix tokens, or NULL (contiguous)
   int n_phys;            // pages in the pool (paged cache)
-  // int8 cache (attention_q8.hip): codes and fp16 scales, K blocked along the
+  // quantised cache (attention_kvq.hip): int8 codes or packed nibbles and fp16 scales, K blocked along the
   // head dim of a token, V along the tokens of a dim
   const int8_t* kc8;     // [Hkv][cap][d]
   const uint16_t* ks16;  // [Hkv][cap][d / 32]
@@ -180,19 +180,22 @@ int attention_max_chunks(int n_kv_heads);
 hipError_t launch_attention(const AttnPlan& plan, int head_dim, const AttnParams& p,
                             const CombineParams& c, const TreeArgs& t, hipStream_t s);
 // the same over an int8 prefix (p.kc8 ..), and the merge both end with
-hipError_t launch_attention_q8(const AttnPlan& plan, int head_dim, const AttnParams& p,
+hipError_t launch_attention_q8(const AttnPlan& plan, int head_dim, int bits, const AttnParams& p,
                                const CombineParams& c, const TreeArgs& t, hipStream_t s);
 hipError_t launch_combine(int head_dim, const CombineParams& c, const TreeArgs& t, hipStream_t s);
 // the kernels, grids and blocks the attention launches for a plan (snprintf semantics)
 int describe_attention(const AttnPlan& plan, int head_dim, int n_kv_heads, int combine_blocks, bool fp32_q,
                        bool paged, char* buf, size_t len);
-int describe_attention_q8(const AttnPlan& plan, int head_dim, int n_kv_heads, int combine_blocks, char* buf,
-                          size_t len);
+int describe_attention_q8(const AttnPlan& plan, int head_dim, int n_kv_heads, int combine_blocks, int bits,
+                          char* buf, size_t len);
 // one non-temporal read of `bytes` (multiple of 16) over the whole device
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s);
 // int8 block-32 quantisation of a bf16 cache's first cap tokens
 hipError_t launch_quantize_q8(const uint16_t* kc, const uint16_t* vc, int hkv, int cap, int d, int8_t* k_codes,
                               uint16_t* k_scales, int8_t* v_codes, uint16_t* v_scales, hipStream_t s);
+// 4-bit block-32 quantisation (nibbles packed two to a byte)
+hipError_t launch_quantize_q4(const uint16_t* kc, const uint16_t* vc, int hkv, int cap, int d, uint8_t* k_nib,
+                              uint16_t* k_scales, uint8_t* v_nib, uint16_t* v_scales, hipStream_t s);
 
 // ---------------------------------------------------------------- small kernels
 
