@@ -26,9 +26,9 @@ EXTRA = {"attention.hip": _ATTN, "attention_kvq.hip": _ATTN}
 def build(verbose: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     inc = ["-I", os.path.join(HERE, "..", "include")]
+    import concurrent.futures
     with tempfile.TemporaryDirectory() as tmpd:
-        objs = []
-        for src in SOURCES:
+        def one(src):
             obj = os.path.join(tmpd, src + ".o")
             cmd = [hipcc] + HIPCC_FLAGS + EXTRA.get(src, []) + inc + ["-c", os.path.join(CSRC, src), "-o", obj]
             if verbose:
@@ -37,7 +37,11 @@ def build(verbose: bool = False) -> str:
             if res.returncode != 0:
                 sys.stderr.write(res.stdout + res.stderr)
                 raise RuntimeError("hipcc failed on %s" % src)
-            objs.append(obj)
+            return obj
+
+        # the sources compile independently (one hipcc each, in parallel)
+        with concurrent.futures.ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
+            objs = list(ex.map(one, SOURCES))
         tmp = LIB + ".tmp"
         cmd = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp]
         res = subprocess.run(cmd, capture_output=True, text=True)
