@@ -100,14 +100,17 @@ def cpu_baseline(cfg, budget_s=10.0):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "tree_attention_stack27b_traffic.txt")
+TRAFFIC_WORKLOAD = "stack27b"  # the workload those counters were taken on
 ATTN_SOURCE = os.path.join(ROOT, "tree_verify_amd", "csrc", "attention.hip")
 
 
-def measured_traffic():
+def measured_traffic(workload):
     """HBM bytes per launch of the tree attention from the committed rocprofv3
-    FETCH_SIZE / WRITE_SIZE summary, or None when the kernel source changed
-    since those counters were taken."""
+    FETCH_SIZE / WRITE_SIZE summary, or None for another workload than the
+    one the counters were taken on, or when the kernel source changed since."""
     import hashlib
+    if workload != TRAFFIC_WORKLOAD:
+        return None
     if not os.path.exists(TRAFFIC_FILE):
         return None
     fields = {}
@@ -534,7 +537,7 @@ def run_config(cfg, args):
                         what="each replay after a %d MiB write outside its events" % args.flush_mib),
         "roofline": {"bound": "hbm", "kernel": tv.lucev_describe_attention(shape, n, cfg.prefix, tv.ATTN_F32),
                      "achieved": round(attn_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(cfg.name),
                      "bytes_per_launch": ab, "avg_launch_us": round(attn_us, 3),
                      "timed": "lucev_tree_attention_f32 (the verify step's variant), a graph of %d launches "
                               "rotating over the layers' caches, HIP events on the launch stream" % args.attn_reps},
