@@ -88,7 +88,7 @@ __global__ __launch_bounds__(ROWW * 64) void attn_partial_kernel(AttnParams p) {
   static_assert(NBUF >= 2 && NBUF <= 4, "ring depth");
   static_assert(!SPLIT || ROWW >= 4, "the split tile's four key quarters go to the last four waves");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
-  __shared__ int s_tab[PAGED ? kMaxChunkPages : 1];
+  __shared__ __attribute__((aligned(16))) int s_tab[PAGED ? kMaxChunkPages : 1];
 
   const int tid = threadIdx.x;
   // the wave index as a scalar: every branch on it is then a scalar branch
@@ -115,7 +115,17 @@ __global__ __launch_bounds__(ROWW * 64) void attn_partial_kernel(AttnParams p) {
 
   // issue this wave's loads of tile t (< n_tiles) into buffer b: load j =
   // wave + r * WAVES; K rows for j < KBYTES / 1024, else V^T rows
-  auto issue = [&](int t, int b) {
+  // the pages of tile t (paged cache): its KT / 16 = 4 table entries, one
+  // 16-byte LDS read, taken before the barrier that precedes the tile's
+  // loads so the table lookup is off their path
+  typedef int int4v __attribute__((ext_vector_type(4)));
+  static_assert(KT / 16 == 4, "four pages per tile");
+  auto pages_of = [&](int t) -> int4v {
+    if constexpr (PAGED) return *reinterpret_cast<const int4v*>(&s_tab[t * (KT / 16)]);
+    return int4v{0, 0, 0, 0};
+  };
+  auto issue = [&](int t, int b, int4v pg4) {
+    (void)pg4;
     const int k0 = k_begin + t * KT;
     const bool ragged = k0 + KT > k_end;
 #pragma unroll
@@ -144,8 +154,10 @@ __global__ __launch_bounds__(ROWW * 64) void attn_partial_kernel(AttnParams p) {
       const uint16_t* src;
       if constexpr (PAGED) {
         // token of the chunk this lane's 16 bytes start at, and its page
+        // (page tok / 16 of the tile)
         const int tic = k0 - k_begin + tok;
-        const int64_t pg = s_tab[tic >> 4];
+        const int c = tok >> 4;
+        const int64_t pg = c == 0 ? pg4[0] : c == 1 ? pg4[1] : c == 2 ? pg4[2] : pg4[3];
         src = !is_v ? p.kc + ((pg * p.n_kv_heads + g) * 16 + (tic & 15)) * D + cofs
                     : p.vc + ((pg * p.n_kv_heads + g) * D + row) * 16 + (tic & 15);
       } else {
@@ -398,7 +410,7 @@ __global__ __launch_bounds__(ROWW * 64) void attn_partial_kernel(AttnParams p) {
   if (n_tiles > 0) {
 #pragma unroll
     for (int t = 0; t < NBUF - 1; ++t)
-      if (t < n_tiles) issue(t, t);
+      if (t < n_tiles) issue(t, t, pages_of(t));
     // whole tiles in the loop; a ragged last tile (masked keys) after it, so
     // the loop body has a single path
     const int n_whole = (k_end - k_begin) / KT;
@@ -407,6 +419,7 @@ __global__ __launch_bounds__(ROWW * 64) void attn_partial_kernel(AttnParams p) {
       // loads of the whole tiles after t (issued later, at most NBUF - 2 of
       // them) are in flight; a ragged tile's register loads are complete
       // before issue() returns, so they never count
+      const int4v pg_next = t + NBUF - 1 < n_tiles ? pages_of(t + NBUF - 1) : int4v{0, 0, 0, 0};
       const int ahead = min(n_whole - 1 - t, NBUF - 2);
       if (NBUF >= 4 && ahead >= 2) {
         if (full_lpw) wait_vmcnt<2 * LPW>();
@@ -418,7 +431,7 @@ __global__ __launch_bounds__(ROWW * 64) void attn_partial_kernel(AttnParams p) {
         wait_vmcnt<0>();
       }
       lds_barrier();  // every part has; every wave is done with tile t - 1
-      if (t + NBUF - 1 < n_tiles) issue(t + NBUF - 1, (t + NBUF - 1) % NBUF);  // into tile t - 1's buffer
+      if (t + NBUF - 1 < n_tiles) issue(t + NBUF - 1, (t + NBUF - 1) % NBUF, pg_next);  // into tile t - 1's buffer
     };
     for (int t = 0; t < n_whole; ++t) {
       step(t);
