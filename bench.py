@@ -425,6 +425,41 @@ def crossover(args):
 CONFIGS_ALL = ["tiny", "small_decode", "small_tree", "layer27b", "stack27b", "longctx27b"]
 
 
+def quantised_step_leg(r, tree, x32, cfg, stream, steps, bits, wb, ob):
+    """The whole step over int8 (bits 8) or 4-bit (bits 4) block-32 KV caches
+    (lucev_verify_layer_q8 / _q4): every layer's cache quantised on the device
+    (set-up, not timed), the step captured as a graph and replayed like the
+    main one.  GB/s over the step's algorithmic bytes with the quantised
+    prefix (codes + one fp16 scale per 32 values)."""
+    import torch
+    r.quantise_kv(bits, cfg.prefix)
+    torch.cuda.synchronize()
+    try:
+        with torch.cuda.stream(stream):
+            r.step(tree, x32, cfg.prefix, with_logits=False)
+            stream.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                r.step(tree, x32, cfg.prefix, with_logits=False)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        ms = timed_replays(g, steps, stream)
+        del g
+    finally:
+        r.clear_quantised_kv()
+        torch.cuda.synchronize()
+    kvb = int(cfg.layers * cfg.prefix * cfg.n_kv_heads * cfg.head_dim * 2 * (bits / 8 + 2 / 32))
+    p = percentiles(ms)
+    mean = sum(ms) / len(ms)
+    return {"ms_per_step": round(mean, 5), "warm_ms": p, "algorithmic_bytes": wb + kvb + ob, "kv_bytes": kvb,
+            "gbs": round((wb + kvb + ob) / (mean * 1e-3) / 1e9, 2),
+            "what": "the step (lucev_verify_layer_q%d every layer + acceptance) over %s block-32 KV caches; "
+                    "mean and p10/p50/p90 of %d replays, each between its own HIP events"
+                    % (bits, "int8" if bits == 8 else "4-bit", steps)}
+
+
 def run_config(cfg, args):
     import numpy as np
     import torch
@@ -513,6 +548,13 @@ def run_config(cfg, args):
     paged_us = paged_leg(r, cfg, tv, shape, tree, q, out, dev, args.attn_reps) if cfg.prefix > 0 else None
     if paged_us:
         log("paged tree attention (one layer): %.2f us" % paged_us)
+    qstep = {}
+    if cfg.prefix > 0 and not args.no_q8 and r.capacity % 32 == 0:
+        for bits in (8, 4):
+            qstep[bits] = quantised_step_leg(r, tree, x32, cfg, stream, args.steps, bits, wb, ob)
+            log("step over %s KV: %.4f ms (p50 %.4f), %.1f GB/s" %
+                ("int8" if bits == 8 else "4-bit", qstep[bits]["ms_per_step"], qstep[bits]["warm_ms"]["p50"],
+                 qstep[bits]["gbs"]))
     q8 = q4 = None
     if cfg.prefix > 0 and not args.no_q8:
         q8 = kvq_leg(r, cfg, tv, shape, tree, q, out, dev, args.attn_reps, bf16_us, 8)
@@ -551,6 +593,9 @@ def run_config(cfg, args):
                                    "what": "lucev_tree_attention_paged (bf16 q), the prefix in a shuffled pool of "
                                            "16-token pages, rotating over 4 layers' pools; vs_contiguous = "
                                            "lucev_tree_attention time / this"}
+    if qstep:
+        line["step_q8_kv"] = qstep.get(8)
+        line["step_q4_kv"] = qstep.get(4)
     if q8:
         line["q8_attention"] = q8
     if q4:
@@ -580,7 +625,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="stack27b", help="a config name, or 'all' (one JSON line each)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-q8", action="store_true", help="skip the quantised-prefix (int8 and 4-bit) legs")
+    ap.add_argument("--no-q8", action="store_true",
+                    help="skip the quantised-prefix (int8 and 4-bit) legs: one-layer attention and whole step")
     ap.add_argument("--no-ceiling", action="store_true")
     ap.add_argument("--attn-reps", type=int, default=20)
     ap.add_argument("--cold-steps", type=int, default=10)

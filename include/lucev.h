@@ -354,6 +354,26 @@ int lucev_tree_attention_q4(const lucev_shape* shape, const lucev_tree* tree, co
                             const uint16_t* q, const uint16_t* k_tree, const uint16_t* v_tree, uint16_t* out,
                             void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------- the step over a quantised prefix */
+
+/* lucev_verify_layer with the layer's prefix held as int8 (lucev_kv_q8) or
+ * 4-bit (lucev_kv_q4) codes: the pages run the target with q8_0 or Q4_0 K/V
+ * ("Lucebox Hub", sections "Paged attention + continuous batching" and
+ * "설치·사용법").  Everything but the attention's prefix part is
+ * lucev_verify_layer's; that part is lucev_tree_attention_q8 / _q4's (prefix
+ * keys and values as the nearest fp16 of their dequantised values, q -- the
+ * layer's fp32 q -- and P as nearest fp16, fp32 sums), while the tree keys
+ * and the merge stay in fp32 as in lucev_verify_layer.  Other arguments,
+ * outputs and workspace as lucev_verify_layer; the cache layouts, alignments
+ * and capacity % 32 as lucev_tree_attention_q8 / _q4.  Returns the codes of
+ * lucev_verify_layer. */
+int lucev_verify_layer_q8(const lucev_shape* shape, const lucev_layer_w* w, const lucev_tree* tree,
+                          const lucev_kv_q8* kv, float* resid_io, uint16_t* k_tree_out, uint16_t* v_tree_out,
+                          void* ws, size_t ws_bytes, void* stream);
+int lucev_verify_layer_q4(const lucev_shape* shape, const lucev_layer_w* w, const lucev_tree* tree,
+                          const lucev_kv_q4* kv, float* resid_io, uint16_t* k_tree_out, uint16_t* v_tree_out,
+                          void* ws, size_t ws_bytes, void* stream);
+
 /* Final RMSNorm, lm_head, greedy token and top1-top2 gap per node (taken on
  * the fp32 logits), then greedy acceptance over the tree: a node is accepted
  * when its parent is accepted and its drafted token equals the parent's

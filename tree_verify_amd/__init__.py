@@ -122,6 +122,10 @@ def lib() -> ctypes.CDLL:
         L.lucev_tree_attention_q4.restype = c_i32
         L.lucev_tree_attention_q4.argtypes = [P(lucev_shape), P(lucev_tree), P(lucev_kv_q4), c_vp, c_vp, c_vp,
                                               c_vp, c_vp, c_sz, c_vp]
+        for nm, kvt in (("lucev_verify_layer_q8", lucev_kv_q8), ("lucev_verify_layer_q4", lucev_kv_q4)):
+            getattr(L, nm).restype = c_i32
+            getattr(L, nm).argtypes = [P(lucev_shape), P(lucev_layer_w), P(lucev_tree), P(kvt), c_vp, c_vp,
+                                       c_vp, c_vp, c_sz, c_vp]
         L.lucev_kv_quantize_q4.restype = c_i32
         L.lucev_kv_quantize_q4.argtypes = [P(lucev_shape), P(lucev_kv), c_vp, c_vp, c_vp, c_vp, c_vp]
         L.lucev_tree_attention_noalloc.restype = c_i32
@@ -150,6 +154,7 @@ EXPORTED = ["lucev_abi_version", "lucev_status_str", "lucev_last_error",
             "lucev_workspace_bytes", "lucev_workspace_init", "lucev_verify_layer",
             "lucev_tree_attention", "lucev_tree_attention_f32", "lucev_tree_attention_noalloc",
             "lucev_tree_attention_q8", "lucev_kv_quantize_q8", "lucev_tree_attention_q4", "lucev_kv_quantize_q4",
+            "lucev_verify_layer_q8", "lucev_verify_layer_q4",
             "lucev_tree_attention_paged", "lucev_accept_path", "lucev_project_logits",
             "lucev_commit_path", "lucev_describe_attention", "lucev_stream_read",
             "lucev_set_gemv_max_rows"]
@@ -240,6 +245,22 @@ def lucev_verify_layer(shape, w, tree, kv, resid_io, k_tree_out, v_tree_out, ws,
                                     ctypes.byref(kv), _ptr(resid_io), _ptr(k_tree_out),
                                     _ptr(v_tree_out), _ptr(ws), ws_bytes, stream),
            "lucev_verify_layer")
+
+
+def lucev_verify_layer_q8(shape, w, tree, kv, resid_io, k_tree_out, v_tree_out, ws, ws_bytes,
+                          stream=None) -> None:
+    _check(lib().lucev_verify_layer_q8(ctypes.byref(shape), ctypes.byref(w), ctypes.byref(tree),
+                                       ctypes.byref(kv), _ptr(resid_io), _ptr(k_tree_out),
+                                       _ptr(v_tree_out), _ptr(ws), ws_bytes, stream),
+           "lucev_verify_layer_q8")
+
+
+def lucev_verify_layer_q4(shape, w, tree, kv, resid_io, k_tree_out, v_tree_out, ws, ws_bytes,
+                          stream=None) -> None:
+    _check(lib().lucev_verify_layer_q4(ctypes.byref(shape), ctypes.byref(w), ctypes.byref(tree),
+                                       ctypes.byref(kv), _ptr(resid_io), _ptr(k_tree_out),
+                                       _ptr(v_tree_out), _ptr(ws), ws_bytes, stream),
+           "lucev_verify_layer_q4")
 
 
 def lucev_tree_attention(shape, tree, kv, q, k_tree, v_tree, out, ws, ws_bytes, stream=None) -> None:

@@ -623,14 +623,20 @@ int lucev_tree_attention_paged(const lucev_shape* shape, const lucev_tree* tree,
                        kv->prefix_len > 0 ? kv->block_table : nullptr, kv->n_pages);
 }
 
-int lucev_verify_layer(const lucev_shape* shape, const lucev_layer_w* w, const lucev_tree* tree,
-                       const lucev_kv* kv, float* resid_io, uint16_t* k_tree_out,
-                       uint16_t* v_tree_out, void* ws, size_t ws_bytes, void* stream) {
+// One layer over a bf16 prefix (kq NULL) or a quantised one (kq; kv then
+// carries only prefix_len and capacity)
+static int verify_layer_impl(const lucev_shape* shape, const lucev_layer_w* w, const lucev_tree* tree,
+                             const lucev_kv* kv, const KvQuant* kq, float* resid_io, uint16_t* k_tree_out,
+                             uint16_t* v_tree_out, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_shape(shape);
   if (rc) return rc;
   if (!w || !resid_io || !k_tree_out || !v_tree_out || !w->attn_norm || !w->ffn_norm)
     return fail(LUCEV_ERR_NULL_ARG, "verify_layer: NULL argument");
-  if ((rc = check_kv(kv))) return rc;
+  if (kq) {
+    if ((rc = check_kv_quant(kv->prefix_len, kv->capacity, *kq, kq->bits == 8 ? "q8" : "q4"))) return rc;
+  } else if ((rc = check_kv(kv))) {
+    return rc;
+  }
   TreeArgs t;
   if ((rc = prep_tree(tree, shape->vocab, kv->prefix_len, &t))) return rc;
   if ((rc = check_attn_rows(shape, t.n))) return rc;
@@ -678,7 +684,7 @@ int lucev_verify_layer(const lucev_shape* shape, const lucev_layer_w* w, const l
     if ((e = launch_qkv_finish(so, ea, n, st)) != hipSuccess) return hip_fail(e, "qkv finish launch");
   }
   if ((rc = run_attention(shape, t, kv, nullptr, k_tree_out, v_tree_out, q32, k32, v32, xa, 1,
-                          at<float>(ws, L.opart), at<float>(ws, L.ml), st)))
+                          at<float>(ws, L.opart), at<float>(ws, L.ml), st, nullptr, 0, nullptr, kq)))
     return rc;
   {
     GemmParams p = gemm_params_split(w->wo, xa, n, true, ws, L, &so);
@@ -707,6 +713,38 @@ int lucev_verify_layer(const lucev_shape* shape, const lucev_layer_w* w, const l
       return hip_fail(e, "down finish launch");
   }
   return LUCEV_OK;
+}
+
+int lucev_verify_layer(const lucev_shape* shape, const lucev_layer_w* w, const lucev_tree* tree,
+                       const lucev_kv* kv, float* resid_io, uint16_t* k_tree_out,
+                       uint16_t* v_tree_out, void* ws, size_t ws_bytes, void* stream) {
+  return verify_layer_impl(shape, w, tree, kv, nullptr, resid_io, k_tree_out, v_tree_out, ws, ws_bytes, stream);
+}
+
+int lucev_verify_layer_q8(const lucev_shape* shape, const lucev_layer_w* w, const lucev_tree* tree,
+                          const lucev_kv_q8* kv, float* resid_io, uint16_t* k_tree_out, uint16_t* v_tree_out,
+                          void* ws, size_t ws_bytes, void* stream) {
+  if (!kv) return fail(LUCEV_ERR_NULL_ARG, "kv is NULL");
+  const KvQuant kq{kv->k_codes, kv->k_scales, kv->v_codes, kv->v_scales, 8};
+  lucev_kv geo;  // geometry only; the codes and scales come from kq
+  geo.k = nullptr;
+  geo.v = nullptr;
+  geo.prefix_len = kv->prefix_len;
+  geo.capacity = kv->capacity;
+  return verify_layer_impl(shape, w, tree, &geo, &kq, resid_io, k_tree_out, v_tree_out, ws, ws_bytes, stream);
+}
+
+int lucev_verify_layer_q4(const lucev_shape* shape, const lucev_layer_w* w, const lucev_tree* tree,
+                          const lucev_kv_q4* kv, float* resid_io, uint16_t* k_tree_out, uint16_t* v_tree_out,
+                          void* ws, size_t ws_bytes, void* stream) {
+  if (!kv) return fail(LUCEV_ERR_NULL_ARG, "kv is NULL");
+  const KvQuant kq{kv->k_nibbles, kv->k_scales, kv->v_nibbles, kv->v_scales, 4};
+  lucev_kv geo;
+  geo.k = nullptr;
+  geo.v = nullptr;
+  geo.prefix_len = kv->prefix_len;
+  geo.capacity = kv->capacity;
+  return verify_layer_impl(shape, w, tree, &geo, &kq, resid_io, k_tree_out, v_tree_out, ws, ws_bytes, stream);
 }
 
 int lucev_accept_path(const lucev_shape* shape, const lucev_head_w* w, const lucev_tree* tree,

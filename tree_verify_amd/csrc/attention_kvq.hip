@@ -24,9 +24,10 @@
 //     72), scales them with one packed fp16 multiply -- the value rounded
 //     once to fp16, within 2^-11 of itself, finer than either format's step
 //     -- and stores them into the bf16 kernel's swizzled LDS layouts;
-//   * every MFMA is f16 and single: K' q (q as nearest fp16) and V' P (P as
-//     nearest fp16), accumulated directly; the int8 cache's own rounding
-//     dwarfs these, so no hi/lo halves are carried;
+//   * every MFMA is f16 and single: K' q (q -- bf16, or the verify step's
+//     fp32 -- as nearest fp16) and V' P (P as nearest fp16), accumulated
+//     directly; the quantised cache's own rounding dwarfs these, so no hi/lo
+//     halves are carried;
 //   * no split query tile: query tiles go one per wave up to 12, then two
 //     per wave on 8 waves, and past 16 tiles to row groups, one block per
 //     (chunk, group); the groups of a chunk sit on one XCD (block ids 8
@@ -264,16 +265,36 @@ __global__ __launch_bounds__(ROWW * 64) void attn_partial_q8_kernel(AttnParams p
       head = g * G + (row - node * G);
     }
     const int64_t qoff = ((int64_t)node * p.n_q_heads + head) * D + lq * 8;
-    u32x4 raw[D / 32];
+    // q as bf16 (p.q), or fp32 (p.q32: the verify step's), to the nearest fp16
+    float qv[D / 32][8];
+    if (p.q32) {
+      u32x4 raw[D / 32][2];
 #pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) raw[kk] = ld16(p.q + qoff + kk * 32);
+      for (int kk = 0; kk < D / 32; ++kk) {
+        raw[kk][0] = ld16(p.q32 + qoff + kk * 32);
+        raw[kk][1] = ld16(p.q32 + qoff + kk * 32 + 4);
+      }
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qv[kk][e] = __uint_as_float(raw[kk][e >> 2][e & 3]);
+    } else {
+      u32x4 raw[D / 32];
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk) raw[kk] = ld16(p.q + qoff + kk * 32);
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          qv[kk][e] = bf16_bits_to_f32(e & 1 ? (raw[kk][e >> 1] >> 16) : (raw[kk][e >> 1] & 0xFFFFu));
+    }
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) {
       uint32_t hv[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float x0 = ok ? bf16_bits_to_f32(raw[kk][e] & 0xFFFFu) * p.scale_log2 : 0.f;
-        const float x1 = ok ? bf16_bits_to_f32(raw[kk][e] >> 16) * p.scale_log2 : 0.f;
+        const float x0 = ok ? qv[kk][2 * e] * p.scale_log2 : 0.f;
+        const float x1 = ok ? qv[kk][2 * e + 1] * p.scale_log2 : 0.f;
         hv[e] = pack_f16(x0, x1);
       }
       qf[i][kk] = __builtin_bit_cast(f16x8_t, u32x4{hv[0], hv[1], hv[2], hv[3]});

@@ -62,6 +62,33 @@ class VerifyRunner:
         lw = self.layers[l]
         return tv.make_kv(lw["k"], lw["v"], prefix_len, self.capacity)
 
+    def quantise_kv(self, bits: int, prefix_len: int, stream=None) -> None:
+        """Quantise every layer's bf16 cache (its whole capacity) into int8
+        (bits 8) or 4-bit (bits 4) block-32 codes held by the runner; later
+        steps read those instead of the bf16 caches (until clear_quantised_kv)."""
+        if bits not in (8, 4):
+            raise ValueError("bits must be 8 or 4")
+        st = torch.cuda.current_stream().cuda_stream if stream is None else stream
+        s = self.shape
+        Hkv, d, cap = s.n_kv_heads, s.head_dim, self.capacity
+        per = 8 // bits  # codes per byte
+        dt = torch.int8 if bits == 8 else torch.uint8
+        quant = tv.lucev_kv_quantize_q8 if bits == 8 else tv.lucev_kv_quantize_q4
+        make = tv.make_kv_q8 if bits == 8 else tv.make_kv_q4
+        self._kvq = []
+        for l in range(len(self.layers)):
+            kc = self._zeros((Hkv, cap, d // per), dt)
+            ks = self._zeros((Hkv, cap, d // 32), torch.int16)
+            vc = self._zeros((Hkv, d, cap // per), dt)
+            vs = self._zeros((Hkv, d, cap // 32), torch.int16)
+            quant(s, self.kv(l, prefix_len), kc, ks, vc, vs, st)
+            self._kvq.append((kc, ks, vc, vs))
+        self._kvq_bits = bits
+        self._kvq_make = make
+
+    def clear_quantised_kv(self) -> None:
+        self._kvq = None
+
     def step(self, tree: tv.lucev_tree, x_in_f32: torch.Tensor, prefix_len: int,
              hidden_out: Optional[List[torch.Tensor]] = None, with_logits: bool = True,
              stream=None, capture: Optional[Dict[int, torch.Tensor]] = None) -> None:
@@ -74,9 +101,16 @@ class VerifyRunner:
         n = tree.n
         st = torch.cuda.current_stream().cuda_stream if stream is None else stream
         self.resid[:n].copy_(x_in_f32[:n])
+        kvq = getattr(self, "_kvq", None)
         for l, lw in enumerate(self._lw):
-            tv.lucev_verify_layer(self.shape, lw, tree, self.kv(l, prefix_len), self.resid,
-                                  self.k_tree[l], self.v_tree[l], self.ws, self.ws_bytes, st)
+            if kvq:
+                kq = self._kvq_make(*kvq[l], prefix_len, self.capacity)
+                layer = tv.lucev_verify_layer_q8 if self._kvq_bits == 8 else tv.lucev_verify_layer_q4
+                layer(self.shape, lw, tree, kq, self.resid, self.k_tree[l], self.v_tree[l], self.ws,
+                      self.ws_bytes, st)
+            else:
+                tv.lucev_verify_layer(self.shape, lw, tree, self.kv(l, prefix_len), self.resid,
+                                      self.k_tree[l], self.v_tree[l], self.ws, self.ws_bytes, st)
             if hidden_out is not None:
                 hidden_out[l].copy_(self.resid[:n])
             if capture is not None and l in capture:
