@@ -122,6 +122,7 @@ ATTN_Q8_CASES = [
     ("tiny_shape", 4, 2, 64, 128, None, 8),            # 1 query tile, a 4-wave block
     ("ragged_prefix", 8, 2, 128, 1000, None, 16),      # ragged last tile
     ("27b_group", 48, 8, 128, 4100, (3, 8), 22),       # 9 query tiles on 12 one-tile waves
+    ("five_tiles", 48, 8, 128, 1531, None, 12),        # 5 query tiles on 8 one-tile waves, ragged prefix
     ("wide_tree", 48, 8, 128, 2051, (4, 10), 40),      # 15 tiles, two per wave on 8 waves
     ("single_node", 48, 8, 128, 777, None, 1),
     ("empty_prefix", 8, 2, 128, 0, None, 5),
