@@ -452,9 +452,9 @@ int lucev_commit_path(const lucev_shape* shape, int32_t n_layers, uint16_t* cons
                       void* stream);
 
 /*
- * lucev_set_gemv_max_rows: GEMM operand rows (two per node for the QKV, Wo
- * and lm_head projections, whose activations travel as fp16 hi + lo rows; one
- * per node for gate/up and down) at or below which the int4 projections take
+ * lucev_set_gemv_max_rows: GEMM operand rows (two per node for the QKV and
+ * Wo projections, whose activations travel as fp16 hi + lo rows; one per node
+ * for gate/up, down and the lm_head) at or below which the int4 projections take
  * dot products on the vector ALUs (v_dot2_f32_f16) instead of MFMA, for
  * trees too small to make a dense contraction.  Measured on MI355X, MFMA is
  * no slower at any node count (the dot products come within 5 % at one or
