@@ -290,3 +290,30 @@ def test_quantised_kv_validation_before_any_launch(bits):
     assert q_status(tv.lucev_kv(fake, fake, 64, 128), kc=fake + 4) == -5
     assert q_status(tv.lucev_kv(fake, fake, 64, 128), ks=fake + 1) == -5
     assert q_status(tv.lucev_kv(fake, fake, 64, 128)) in (-6, -7)
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_quantised_verify_layer_validation_before_any_launch(bits):
+    tv = _tv()
+    _no_gpu()
+    s = _shape(tv)
+    w, _, fake = _layer_args(tv, s)
+    layer = tv.lucev_verify_layer_q8 if bits == 8 else tv.lucev_verify_layer_q4
+    make = tv.make_kv_q8 if bits == 8 else tv.make_kv_q4
+
+    def status(kv, resid=fake, ws_bytes=1 << 40, tree=None):
+        try:
+            layer(s, w, tree or tv.make_tree([-1, 0, 0, 1], [1, 2, 3, 4]), kv, resid, fake, fake, fake, ws_bytes)
+        except tv.LucevError as e:
+            return e.status
+        return 0
+
+    assert status(make(fake, fake, fake, fake, 128, 200)) == -8        # capacity not a multiple of 32
+    assert status(make(fake, fake, fake, fake, 300, 256)) == -8        # prefix beyond capacity
+    assert status(make(fake, None, fake, fake, 128, 256)) == -1        # NULL scales
+    assert status(make(fake + 8, fake, fake, fake, 128, 256)) == -5    # codes not 16-byte aligned
+    assert status(make(fake, fake, fake, fake, 128, 256), resid=None) == -1
+    assert status(make(fake, fake, fake, fake, 128, 256), resid=fake + 4) == -5
+    assert status(make(fake, fake, fake, fake, 128, 256), ws_bytes=64) == -4
+    assert status(make(fake, fake, fake, fake, 128, 256), tree=tv.make_tree([0, 0])) == -3
+    assert status(make(fake, fake, fake, fake, 128, 256)) in (-6, -7)  # valid: reaches the device check
