@@ -38,6 +38,7 @@ class VerifyRunner:
         self.path_len = z((1,), torch.int32)
         self.committed = z((n_max,), torch.int32)
         self._lw = [self._layer_struct(lw) for lw in self.layers]
+        self._kvq = None  # per-layer quantised caches (quantise_kv), or None
         self._hw = None
         if head is not None:
             self._hw = tv.lucev_head_w(head["final_norm"].data_ptr(),
@@ -65,7 +66,8 @@ class VerifyRunner:
     def quantise_kv(self, bits: int, prefix_len: int, stream=None) -> None:
         """Quantise every layer's bf16 cache (its whole capacity) into int8
         (bits 8) or 4-bit (bits 4) block-32 codes held by the runner; later
-        steps read those instead of the bf16 caches (until clear_quantised_kv)."""
+        steps read those instead of the bf16 caches (until clear_quantised_kv).
+        commit() appends to the bf16 caches only: quantise again after it."""
         if bits not in (8, 4):
             raise ValueError("bits must be 8 or 4")
         st = torch.cuda.current_stream().cuda_stream if stream is None else stream
@@ -101,7 +103,7 @@ class VerifyRunner:
         n = tree.n
         st = torch.cuda.current_stream().cuda_stream if stream is None else stream
         self.resid[:n].copy_(x_in_f32[:n])
-        kvq = getattr(self, "_kvq", None)
+        kvq = self._kvq
         for l, lw in enumerate(self._lw):
             if kvq:
                 kq = self._kvq_make(*kvq[l], prefix_len, self.capacity)
