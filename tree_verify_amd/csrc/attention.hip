@@ -120,11 +120,11 @@ __global__ __launch_bounds__(ROWW * 64) void attn_partial_kernel(AttnParams p) {
   // loads so the table lookup is off their path
   typedef int int4v __attribute__((ext_vector_type(4)));
   static_assert(KT / 16 == 4, "four pages per tile");
-  auto pages_of = [&](int t) -> int4v {
+  auto pages_of = [&](int t) __attribute__((always_inline)) -> int4v {
     if constexpr (PAGED) return *reinterpret_cast<const int4v*>(&s_tab[t * (KT / 16)]);
     return int4v{0, 0, 0, 0};
   };
-  auto issue = [&](int t, int b, int4v pg4) {
+  auto issue = [&](int t, int b, int4v pg4) __attribute__((always_inline)) {
     (void)pg4;
     const int k0 = k_begin + t * KT;
     const bool ragged = k0 + KT > k_end;
@@ -185,7 +185,7 @@ __global__ __launch_bounds__(ROWW * 64) void attn_partial_kernel(AttnParams p) {
   // this wave's query tiles (row wave w: tiles w, w + ROWW, ..., then with
   // SPLIT the shared tile FT); Q^T fragments stay in registers, as bf16 hi +
   // lo when QLO
-  auto my_tile = [&](int i) { return (SPLIT && i == QS && (SPLITM == 1 || has_q)) ? FT : wave + ROWW * i; };
+  auto my_tile = [&](int i) __attribute__((always_inline)) { return (SPLIT && i == QS && (SPLITM == 1 || has_q)) ? FT : wave + ROWW * i; };
   bf16x8 qf[NQ][D / 32];
   bf16x8 ql[QLO ? NQ : 1][D / 32];
   f32x4 O[NQ][D / 16];
@@ -241,7 +241,7 @@ __global__ __launch_bounds__(ROWW * 64) void attn_partial_kernel(AttnParams p) {
   // than 8 (log2 units): the exponentials stay below 2^8, the final division by
   // l is unchanged, and most blocks skip the O rescale.  `sc` holds the scores
   // taken against `bias`.
-  auto rescale_if_needed = [&](int i, float mx_here, float bias, auto& sc) {
+  auto rescale_if_needed = [&](int i, float mx_here, float bias, auto& sc) __attribute__((always_inline)) {
     constexpr int cnt = sizeof(sc) / sizeof(sc[0]);
     const float mx = rows_max(mx_here);
     if (__builtin_amdgcn_ballot_w64(bias + mx > m[i] + 8.f) != 0) {
@@ -261,7 +261,7 @@ __global__ __launch_bounds__(ROWW * 64) void attn_partial_kernel(AttnParams p) {
   // row wave.  The score MFMA's row r is key ks*32 + (r >> 2)*8 + h*4 + (r & 3),
   // so this lane gets keys ks*32 + lq*8 + h*4 + ii of query lr: the 8
   // consecutive keys the PV MFMA's B operand wants.
-  auto row_half = [&](const uint16_t* K, const uint16_t* V, int ks, int k0, auto masked) {
+  auto row_half = [&](const uint16_t* K, const uint16_t* V, int ks, int k0, auto masked) __attribute__((always_inline)) {
     bf16x8 kf[2][D / 32];
     bf16x8 vf[D / 16];
 #pragma unroll
@@ -333,7 +333,7 @@ __global__ __launch_bounds__(ROWW * 64) void attn_partial_kernel(AttnParams p) {
   // A split tile's quarter: keys ks*32 + lq*8 + h*4 + ii (ks = qq >> 1,
   // h = qq & 1) of every 64-key tile, with the same lazy online softmax as a
   // whole tile; PV as 16x16x16 MFMAs on 4 keys per lane.
-  auto quarter_tile = [&](const uint16_t* K, const uint16_t* V, int k0, auto masked) {
+  auto quarter_tile = [&](const uint16_t* K, const uint16_t* V, int k0, auto masked) __attribute__((always_inline)) {
     constexpr int Q = QS;  // the quarter's slot in the tile arrays
     const int ks = qq >> 1, h = qq & 1;
     const int key = ks * 32 + (lr >> 2) * 8 + h * 4 + (lr & 3);
@@ -385,7 +385,7 @@ __global__ __launch_bounds__(ROWW * 64) void attn_partial_kernel(AttnParams p) {
     }
   };
 
-  auto compute = [&](int buf, int k0, auto masked) {
+  auto compute = [&](int buf, int k0, auto masked) __attribute__((always_inline)) {
     const uint16_t* K = reinterpret_cast<const uint16_t*>(lds + buf * BUF);
     const uint16_t* V = reinterpret_cast<const uint16_t*>(lds + buf * BUF + KBYTES);
     // (scheduling fences: no half's LDS reads are hoisted into the one
@@ -414,7 +414,7 @@ __global__ __launch_bounds__(ROWW * 64) void attn_partial_kernel(AttnParams p) {
     // whole tiles in the loop; a ragged last tile (masked keys) after it, so
     // the loop body has a single path
     const int n_whole = (k_end - k_begin) / KT;
-    auto step = [&](int t) {
+    auto step = [&](int t) __attribute__((always_inline)) {
       // this wave's part of tile t has landed once at most its direct-to-LDS
       // loads of the whole tiles after t (issued later, at most NBUF - 2 of
       // them) are in flight; a ragged tile's register loads are complete
