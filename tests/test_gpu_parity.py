@@ -81,9 +81,10 @@ ATTN_CASES = [
     ("empty_prefix", 8, 2, 128, 0, None, 5),
     ("single_node", 48, 8, 128, 777, None, 1),
     ("max_nodes", 8, 2, 64, 300, None, 64),
-    ("three_tiles_per_wave", 48, 8, 128, 700, None, 64),   # 384 rows: 24 tiles, 3 per wave
-    ("four_tiles_per_wave", 32, 4, 128, 515, None, 64),    # 512 rows (the limit): 32 tiles, 4 per wave
-    ("four_tiles_d64", 16, 1, 64, 260, (4, 10), 32),       # 512 rows of head_dim 64
+    ("row_groups_384_rows", 48, 8, 128, 700, None, 64),    # 24 tiles: two row groups of 12
+    ("row_groups_512_rows", 32, 4, 128, 515, None, 64),    # 512 rows (the limit): two groups of 16
+    ("row_groups_d64", 16, 1, 64, 260, (4, 10), 32),       # 512 rows of head_dim 64
+    ("row_groups_17_tiles", 48, 8, 128, 1100, (4, 10), 45),  # 270 rows: groups of 9 and 8 tiles
 ]
 
 
@@ -128,7 +129,7 @@ def test_tree_attention_parity(case):
 
 
 F32_CASES = [c for c in ATTN_CASES if c[0] in ("27b_group", "wide_tree", "five_tiles", "empty_prefix",
-                                               "three_tiles_per_wave", "ragged_prefix")]
+                                               "row_groups_384_rows", "row_groups_17_tiles", "ragged_prefix")]
 
 
 # The fp32-input attention (lucev_tree_attention_f32) runs the step's own

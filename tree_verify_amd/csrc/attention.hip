@@ -70,6 +70,11 @@ constexpr int attn_waves(int roww, bool split) { return (void)split, roww; }
 // tiles, and hence the results, are those of the contiguous cache.  The
 // block's slice of the table is copied into LDS first, clamped to the pool.
 
+// ROW GROUPS (more than 16 query tiles): the tiles are cut into groups of at
+// most 16, one block per (chunk, group) holding two tiles per wave on 8 waves;
+// the groups of a chunk sit on one XCD (block ids 8 apart), so the later
+// groups' tile reads hit that XCD's L2.
+//
 // SPLITM: 0 no split tile; 1 the quarters go to the last four of the waves
 // that own whole tiles; 2 to four extra waves that own no whole tile.
 template <int D, int QPW, int ROWW, int NBUF, bool QLO, int SPLITM, bool PAGED>
@@ -94,11 +99,20 @@ __global__ __launch_bounds__(ROWW * 64) void attn_partial_kernel(AttnParams p) {
   // the wave index as a scalar: every branch on it is then a scalar branch
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lq = lane >> 4;
-  const int chunk = blockIdx.x;
+  // block x -> (chunk, row group): chunks c and c + 8 are 8 * groups ids apart,
+  // the groups of chunk c ids 8 apart (one XCD); padding blocks past the
+  // last chunk leave at once
+  const int x = blockIdx.x;
+  const int grp = (x >> 3) % p.row_groups;
+  const int chunk = (x / (8 * p.row_groups)) * 8 + (x & 7);
+  if (chunk >= p.n_chunks) return;
   const int g = blockIdx.y;
   const int G = p.n_q_heads / p.n_kv_heads;
   const int RT = (p.rows + 15) / 16;
   const int FT = SPLIT ? RT - 1 : RT;  // tiles the row waves own whole
+  // this block's whole tiles: T0 .. TE - 1 (one group; a split plan has one)
+  const int T0 = grp * p.group_tiles;
+  const int TE = min(FT, T0 + p.group_tiles);
   const bool has_q = SPLIT && wave >= ROWW - 4;  // holds a key quarter of tile FT
   const int qq = wave - (ROWW - 4);              // which quarter
   const bool full_lpw = wave + (LPW - 1) * WAVES < NLD;  // issues LPW loads per tile (else LPW - 1)
@@ -185,7 +199,8 @@ __global__ __launch_bounds__(ROWW * 64) void attn_partial_kernel(AttnParams p) {
   // this wave's query tiles (row wave w: tiles w, w + ROWW, ..., then with
   // SPLIT the shared tile FT); Q^T fragments stay in registers, as bf16 hi +
   // lo when QLO
-  auto my_tile = [&](int i) __attribute__((always_inline)) { return (SPLIT && i == QS && (SPLITM == 1 || has_q)) ? FT : wave + ROWW * i; };
+  auto is_quarter = [&](int i) __attribute__((always_inline)) { return SPLIT && i == QS && (SPLITM == 1 || has_q); };
+  auto my_tile = [&](int i) __attribute__((always_inline)) { return is_quarter(i) ? FT : T0 + wave + ROWW * i; };
   bf16x8 qf[NQ][D / 32];
   bf16x8 ql[QLO ? NQ : 1][D / 32];
   f32x4 O[NQ][D / 16];
@@ -194,7 +209,7 @@ __global__ __launch_bounds__(ROWW * 64) void attn_partial_kernel(AttnParams p) {
   for (int i = 0; i < NQ; ++i) {
     const int qt = my_tile(i);
     const int row = qt * 16 + lr;
-    const bool ok = qt < RT && row < p.rows;
+    const bool ok = (is_quarter(i) ? qt < RT : qt < TE) && row < p.rows;
     int node = 0, head = 0;
     if (ok) {
       node = row / G;
@@ -275,7 +290,7 @@ __global__ __launch_bounds__(ROWW * 64) void attn_partial_kernel(AttnParams p) {
     float bias[QPW];
 #pragma unroll
     for (int i = 0; i < QPW; ++i) {
-      if (my_tile(i) >= FT) continue;
+      if (my_tile(i) >= TE) continue;
       bias[i] = m[i] == -INFINITY ? 0.f : m[i];
       const float init = QLO ? -bias[i] : 0.f;
 #pragma unroll
@@ -298,7 +313,7 @@ __global__ __launch_bounds__(ROWW * 64) void attn_partial_kernel(AttnParams p) {
       vf[dt] = *reinterpret_cast<const bf16x8*>(V + (dt * 16 + lr) * KT + (((ks * 4 + lq) ^ ((lr >> 1) & 7)) * 8));
 #pragma unroll
     for (int i = 0; i < QPW; ++i) {
-      if (my_tile(i) >= FT) continue;
+      if (my_tile(i) >= TE) continue;
       float s[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) s[e] = sc[i][e >> 2][e & 3];
@@ -390,7 +405,7 @@ __global__ __launch_bounds__(ROWW * 64) void attn_partial_kernel(AttnParams p) {
     const uint16_t* V = reinterpret_cast<const uint16_t*>(lds + buf * BUF + KBYTES);
     // (scheduling fences: no half's LDS reads are hoisted into the one
     // before it, which would hold two halves' fragments in registers)
-    if (wave < FT) {  // a row wave with no query tile only loads
+    if (T0 + wave < TE) {  // a row wave with no query tile only loads
       row_half(K, V, 0, k0, masked);
       __builtin_amdgcn_sched_barrier(0);
       row_half(K, V, 1, k0, masked);
@@ -446,7 +461,7 @@ __global__ __launch_bounds__(ROWW * 64) void attn_partial_kernel(AttnParams p) {
 #pragma unroll
   for (int i = 0; i < QPW; ++i) {
     const int qt = my_tile(i);
-    if (qt >= FT) continue;
+    if (qt >= TE) continue;
     const float lt = rows_sum(l[i]);
     const int row = qt * 16 + lr;
     if (row < p.rows) {
@@ -679,7 +694,6 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(CombineParams c, Tree
   }
 }
 
-static_assert(kMaxAttnRows == 8 * 4 * 16, "the widest plan (8 row waves of 4 tiles) covers every allowed row");
 
 // Depth of the partial kernel's LDS tile ring.
 #ifndef LUCEV_ATTN_NBUF
@@ -729,8 +743,8 @@ AttnPlan plan_attention(int n_nodes, int n_q_heads, int n_kv_heads, int head_dim
     a.roww = LUCEV_ATTN_WIDE4 ? 4 : 8;
     a.qpw = LUCEV_ATTN_WIDE4 ? 4 : 2;
   } else {
-    a.roww = 8;
-    a.qpw = (rt + 7) / 8;
+    a.roww = 8;  // row groups of at most 16 tiles, two per wave (partial_layout)
+    a.qpw = 2;
   }
   a.waves = a.roww;
   // one block per CU over (chunk, KV head): chunks a multiple of the LDS tile
@@ -743,9 +757,13 @@ AttnPlan plan_attention(int n_nodes, int n_q_heads, int n_kv_heads, int head_dim
   return a;
 }
 
+// Blocks of a launch: chunks rounded up to 8 (the block -> chunk map keeps a
+// chunk's row groups on one XCD), times the row groups.
+static int partial_blocks(const AttnPlan& plan, int groups) { return ((plan.n_chunks + 7) / 8) * 8 * groups; }
+
 template <int D, int QPW, int ROWW, int SPLITM>
-static void launch_partial(const AttnPlan& plan, const AttnParams& p, hipStream_t s) {
-  const dim3 grid(plan.n_chunks, p.n_kv_heads), block(64 * ROWW);
+static void launch_partial(const AttnPlan& plan, const AttnParams& p, int groups, hipStream_t s) {
+  const dim3 grid(partial_blocks(plan, groups), p.n_kv_heads), block(64 * ROWW);
   if (p.table)
     hipLaunchKernelGGL((attn_partial_kernel<D, QPW, ROWW, kAttnBufs, false, SPLITM, true>), grid, block, 0, s, p);
   else if (p.q32)
@@ -755,34 +773,42 @@ static void launch_partial(const AttnPlan& plan, const AttnParams& p, hipStream_
 }
 
 // The partial kernel's wave layout for a plan: (tiles per row wave, row
-// waves, where a split tile goes), as launch_partial_d instantiates it.
+// waves, where a split tile goes, row groups, tiles per group), as
+// launch_partial_d instantiates it.  Past 16 query tiles, row groups of at
+// most 16 tiles at two per wave: three or four tiles per wave on 8 waves
+// spill (94 and 186 registers with q as hi + lo), and a 64-node tree at the
+// 27B shape took 202 us a layer that way.
 struct PartialLayout {
-  int qpw, roww, splitm;
+  int qpw, roww, splitm, groups, tiles;
 };
 static PartialLayout partial_layout(const AttnPlan& plan) {
+  const int rt = (plan.rows + 15) / 16;
   if (plan.split) {
 #if LUCEV_ATTN_SPLIT_LAYOUT == 2
-    return {plan.qpw == 1 ? 1 : 2, 4, 1};
+    return {plan.qpw == 1 ? 1 : 2, 4, 1, 1, rt};
 #elif LUCEV_ATTN_SPLIT_LAYOUT == 1
-    return {1, plan.roww == 4 ? 4 : 8, 1};
+    return {1, plan.roww == 4 ? 4 : 8, 1, 1, rt};
 #else
-    return {1, plan.roww == 8 ? 8 : 12, 2};
+    return {1, plan.roww == 8 ? 8 : 12, 2, 1, rt};
 #endif
   }
-  if (plan.qpw == 1) return {1, plan.roww == 4 ? 4 : (plan.roww == 8 ? 8 : 12), 0};
+  if (plan.qpw == 1) return {1, plan.roww == 4 ? 4 : (plan.roww == 8 ? 8 : 12), 0, 1, rt};
 #if LUCEV_ATTN_WIDE4
-  if (plan.roww == 4) return {4, 4, 0};
+  if (plan.roww == 4) return {4, 4, 0, 1, rt};
 #endif
-  return {plan.qpw <= 2 ? 2 : (plan.qpw == 3 ? 3 : 4), 8, 0};
+  const int groups = (rt + 15) / 16;
+  return {2, 8, 0, groups, (rt + groups - 1) / groups};
 }
 
 template <int D>
-static void launch_partial_d(const AttnPlan& plan, const AttnParams& p, hipStream_t s) {
+static void launch_partial_d(const AttnPlan& plan, AttnParams p, hipStream_t s) {
   const PartialLayout v = partial_layout(plan);
-#define LUCEV_PARTIAL(Q, R, S)                  \
-  if (v.qpw == Q && v.roww == R && v.splitm == S) { \
-    launch_partial<D, Q, R, S>(plan, p, s);     \
-    return;                                     \
+  p.row_groups = v.groups;
+  p.group_tiles = v.tiles;
+#define LUCEV_PARTIAL(Q, R, S)                            \
+  if (v.qpw == Q && v.roww == R && v.splitm == S) {       \
+    launch_partial<D, Q, R, S>(plan, p, v.groups, s);     \
+    return;                                               \
   }
 #if LUCEV_ATTN_SPLIT_LAYOUT == 2
   LUCEV_PARTIAL(1, 4, 1)
@@ -801,8 +827,6 @@ static void launch_partial_d(const AttnPlan& plan, const AttnParams& p, hipStrea
   LUCEV_PARTIAL(1, 8, 0)
   LUCEV_PARTIAL(1, 12, 0)
   LUCEV_PARTIAL(2, 8, 0)
-  LUCEV_PARTIAL(3, 8, 0)
-  LUCEV_PARTIAL(4, 8, 0)
 #undef LUCEV_PARTIAL
 }
 
@@ -810,11 +834,11 @@ int describe_attention(const AttnPlan& plan, int head_dim, int n_kv_heads, int c
                        bool paged, char* buf, size_t len) {
   const PartialLayout v = partial_layout(plan);
   return snprintf(buf, len,
-                  "attn_partial_kernel<%d, %d, %d, %d, %s, %d, %s> grid (%d, %d) block %d, %d-token chunks; "
-                  "attn_combine_kernel<%d> grid %d block 256",
+                  "attn_partial_kernel<%d, %d, %d, %d, %s, %d, %s> grid (%d, %d) block %d, %d-token chunks, "
+                  "%d row group(s) of %d tiles; attn_combine_kernel<%d> grid %d block 256",
                   head_dim, v.qpw, v.roww, kAttnBufs, (fp32_q && !paged) ? "true" : "false", v.splitm,
-                  paged ? "true" : "false", plan.n_chunks, n_kv_heads, 64 * v.roww, plan.chunk, head_dim,
-                  combine_blocks);
+                  paged ? "true" : "false", partial_blocks(plan, v.groups), n_kv_heads, 64 * v.roww, plan.chunk,
+                  v.groups, v.tiles, head_dim, combine_blocks);
 }
 
 hipError_t launch_attention(const AttnPlan& plan, int head_dim, const AttnParams& p,

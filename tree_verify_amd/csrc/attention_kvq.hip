@@ -158,8 +158,8 @@ __global__ __launch_bounds__(ROWW * 64) void attn_partial_q8_kernel(AttnParams p
   // the groups of chunk c ids 8 apart (one XCD); padding blocks past the
   // last chunk leave at once
   const int x = blockIdx.x;
-  const int grp = (x >> 3) % p.q8_groups;
-  const int chunk = (x / (8 * p.q8_groups)) * 8 + (x & 7);
+  const int grp = (x >> 3) % p.row_groups;
+  const int chunk = (x / (8 * p.row_groups)) * 8 + (x & 7);
   if (chunk >= p.n_chunks) return;
   const int g = blockIdx.y;
   const int G = p.n_q_heads / p.n_kv_heads;
@@ -168,8 +168,8 @@ __global__ __launch_bounds__(ROWW * 64) void attn_partial_q8_kernel(AttnParams p
   const int k_end = min(p.prefix_len, k_begin + p.chunk);
   const int n_tiles = (k_end - k_begin + KT - 1) / KT;
   // this wave's query tiles: group tiles wave, wave + ROWW, ...
-  auto tile_of = [&](int i) __attribute__((always_inline)) { return grp * p.q8_tiles + wave + ROWW * i; };
-  auto has_tile = [&](int i) __attribute__((always_inline)) { return wave + ROWW * i < p.q8_tiles && tile_of(i) < RT; };
+  auto tile_of = [&](int i) __attribute__((always_inline)) { return grp * p.group_tiles + wave + ROWW * i; };
+  auto has_tile = [&](int i) __attribute__((always_inline)) { return wave + ROWW * i < p.group_tiles && tile_of(i) < RT; };
 
   // code bytes of this KV head (BITS / 8 bytes per code)
   const uint8_t* kcode = reinterpret_cast<const uint8_t*>(p.kc8) + (int64_t)g * p.cap * D * BITS / 8;
@@ -465,8 +465,8 @@ static Q8Layout q8_layout(const AttnPlan& plan) {
 template <int D, int BITS>
 static void launch_q8_d(const AttnPlan& plan, AttnParams p, hipStream_t s) {
   const Q8Layout v = q8_layout(plan);
-  p.q8_groups = v.groups;
-  p.q8_tiles = v.tiles;
+  p.row_groups = v.groups;
+  p.group_tiles = v.tiles;
   const dim3 grid(((plan.n_chunks + 7) / 8) * 8 * v.groups, p.n_kv_heads);
   if (v.roww == 4)
     hipLaunchKernelGGL((attn_partial_q8_kernel<D, 1, 4, BITS>), grid, dim3(256), 0, s, p);

@@ -146,8 +146,8 @@ struct AttnParams {
   const uint16_t* ks16;  // [Hkv][cap][d / 32]
   const int8_t* vc8;     // [Hkv][d][cap]
   const uint16_t* vs16;  // [Hkv][d][cap / 32]
-  int q8_groups;         // row groups per (chunk, KV head), set by the int8 launch
-  int q8_tiles;          // query tiles per row group
+  int row_groups;        // row groups per (chunk, KV head), set by the partial kernels' launches
+  int group_tiles;       // query tiles per row group
 };
 constexpr int kPageTokens = 16;
 constexpr int kMaxChunkPagesHost = 1024;  // pages of one block's prefix chunk
