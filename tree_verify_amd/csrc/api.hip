@@ -50,8 +50,8 @@ int check_shape(const lucev_shape* s) {
   return LUCEV_OK;
 }
 
-// The tree attention holds all n * Hq / Hkv query rows of a KV head in one
-// block (kMaxAttnRows at most).
+// The tree attention holds at most kMaxAttnRows query rows (n * Hq / Hkv) per
+// KV head: the limit the workspace and scratch sizes are quoted for.
 int check_attn_rows(const lucev_shape* s, int n) {
   const int rows = n * (s->n_q_heads / s->n_kv_heads);
   if (rows > kMaxAttnRows)

@@ -8,9 +8,10 @@
 // read exactly once per layer and every query row of a KV head shares it.
 //
 // Two kernels:
-//   partial : grid (prefix chunk, KV head).  All n * Hq/Hkv query rows of the
-//             KV head live in the block (16-row MFMA tiles, one or more per
-//             wave); K and V tiles of 64 tokens are staged through LDS.
+//   partial : grid (prefix chunk, KV head).  The n * Hq/Hkv query rows of the
+//             KV head live in the block (16-row MFMA tiles, one or two per
+//             wave; past 16 tiles, in row groups of at most 16, one block
+//             each); K and V tiles of 64 tokens are staged through LDS.
 //             S^T = K Q^T puts the softmax axis (keys) inside each lane, so
 //             the running max needs only two cross-lane steps; P then feeds
 //             O^T = V^T P^T directly from registers (the key order inside a
@@ -717,7 +718,7 @@ int attention_max_chunks(int n_kv_heads) { return (device_cu_count() + n_kv_head
 // Query tiles per SIMD as even as possible.  RT <= 4: one tile per wave, four
 // waves; RT = 5 or 9 (4k + 1): the last tile split by key quarter; other RT up
 // to 12: one tile per wave, 8 or 12 waves; 13 to 16: eight waves of two tiles;
-// above 16: eight waves of three or four.
+// above 16: row groups of at most 16 tiles, eight waves of two (partial_layout).
 AttnPlan plan_attention(int n_nodes, int n_q_heads, int n_kv_heads, int head_dim, int prefix_len) {
   (void)head_dim;
   AttnPlan a;
