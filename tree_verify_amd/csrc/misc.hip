@@ -79,7 +79,9 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const f32x4* __restrict_
                                                         int32_t* path, int32_t* path_len,
                                                         int32_t* committed) {
   // the candidate list of every node split over 1024 / n parts, so all
-  // threads load (a few candidates each, all in flight) before merging
+  // threads load (a few candidates each, all in flight), then the parts of a
+  // node merged pairwise in log2(parts) rounds (the merge is associative and
+  // commutative, so the tree does not change the result)
   __shared__ float s1[1024], s2[1024];
   __shared__ int si[1024];
   const int tid = threadIdx.x;
@@ -98,6 +100,18 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const f32x4* __restrict_
     s2[part * n + node] = v2;
     si[part * n + node] = i1;
   }
+  int half = 1;
+  while (half < parts) half <<= 1;
+  for (half >>= 1; half >= 1; half >>= 1) {
+    __syncthreads();
+    if (part < half && part + half < parts) {
+      const int o = (part + half) * n + node;
+      merge_top2(v1, i1, v2, s1[o], si[o], s2[o]);
+      s1[part * n + node] = v1;
+      s2[part * n + node] = v2;
+      si[part * n + node] = i1;
+    }
+  }
   __syncthreads();
   if (tid >= 64) return;
   const int lane = tid;
@@ -106,7 +120,6 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const f32x4* __restrict_
     v1 = s1[lane];
     v2 = s2[lane];
     i1 = si[lane];
-    for (int q = 1; q < parts; ++q) merge_top2(v1, i1, v2, s1[q * n + lane], si[q * n + lane], s2[q * n + lane]);
     am = i1;
     argmax[lane] = am;
     if (gap) gap[lane] = v1 - v2;
