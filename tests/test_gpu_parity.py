@@ -503,9 +503,11 @@ def test_tree_attention_paged_equals_contiguous(case):
 #
 # The 40-node tree is the wide plan (C5's budget): two query tiles per wave in
 # the attention (15 tiles of 16 rows per KV head) and five node tiles in the
-# GEMMs.
-@pytest.mark.parametrize("nodes,rec,trim", [(22, (3, 8), 0), (22, (3, 8), 37), (40, (4, 10), 37)],
-                         ids=["n22", "n22_ragged", "n40_ragged"])
+# GEMMs.  The 64-node tree takes the attention's row groups (24 tiles: two
+# blocks per chunk and KV head) and eight node tiles in the exact GEMMs.
+@pytest.mark.parametrize("nodes,rec,trim", [(22, (3, 8), 0), (22, (3, 8), 37), (40, (4, 10), 37),
+                                            (64, (None, None), 37)],
+                         ids=["n22", "n22_ragged", "n40_ragged", "n64_ragged_row_groups"])
 def test_graph_replays_bit_identical_27b_layer(nodes, rec, trim):
     torch = need_gpu()
     import tree_verify_amd as tv
