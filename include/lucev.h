@@ -468,8 +468,10 @@ int lucev_set_gemv_max_rows(int32_t rows);
  *
  * lucev_describe_attention: the kernels the tree attention launches for this
  * shape, tree size and prefix length -- the same plan every attention entry
- * point uses -- as text: each kernel's template, grid and block, and the
- * prefix chunk per workgroup.  variant 0 = lucev_tree_attention (bf16 q),
+ * point uses -- as text: each kernel's template, grid and block, the
+ * prefix chunk per workgroup and the query row groups (past 16 query tiles
+ * per KV head, one workgroup per chunk and group).  variant 0 =
+ * lucev_tree_attention (bf16 q),
  * 1 = lucev_tree_attention_f32 and the verify step (fp32 q, split into bf16
  * hi + lo), 2 = lucev_tree_attention_paged, 3 = lucev_tree_attention_q8,
  * 4 = lucev_tree_attention_q4.
