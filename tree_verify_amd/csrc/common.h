@@ -50,17 +50,6 @@ __device__ __forceinline__ T shfl_xor(T v, int mask) {
   return __shfl_xor(v, mask, kWave);
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += shfl_xor(v, m);
-  return v;
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, shfl_xor(v, m));
-  return v;
-}
 
 // Top-2 merge: best value, its index (lowest on exact ties) and the runner-up
 // (a tie at the top makes the runner-up equal to the best).  Associative and
@@ -121,6 +110,37 @@ __device__ __forceinline__ float rows_sum(float x) {
   const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// The value of a partner lane within each row of 16 (DPP: quad_perm, half-row
+// and row mirrors), with no LDS traffic.
+template <int CTRL>
+__device__ __forceinline__ float dpp_partner(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7 - i within each 8
+constexpr int kDppMirror = 0x140;     // lane i <-> 15 - i within each 16
+
+// Sum / max over the 64 lanes, every lane getting the same bits (each step
+// combines a lane with a partner that combines the same two values): pairs,
+// quads, eights and rows of 16 by DPP, then the four rows by the permlane
+// swaps.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_partner<kDppXor1>(v);
+  v += dpp_partner<kDppXor2>(v);
+  v += dpp_partner<kDppHalfMirror>(v);
+  v += dpp_partner<kDppMirror>(v);
+  return rows_sum(v);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_partner<kDppXor1>(v));
+  v = fmaxf(v, dpp_partner<kDppXor2>(v));
+  v = fmaxf(v, dpp_partner<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_partner<kDppMirror>(v));
+  return rows_max(v);
 }
 
 }  // namespace lucev
