@@ -45,12 +45,6 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
   return (float)__builtin_bit_cast(f16, (uint16_t)b);
 }
 
-template <typename T>
-__device__ __forceinline__ T shfl_xor(T v, int mask) {
-  return __shfl_xor(v, mask, kWave);
-}
-
-
 // Top-2 merge: best value, its index (lowest on exact ties) and the runner-up
 // (a tie at the top makes the runner-up equal to the best).  Associative and
 // commutative, so any fixed merge tree gives the same result.
@@ -141,6 +135,38 @@ __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, dpp_partner<kDppHalfMirror>(v));
   v = fmaxf(v, dpp_partner<kDppMirror>(v));
   return rows_max(v);
+}
+
+// Top-2 over the 64 lanes (merge_top2 at every step, so the result is the
+// same whatever the pairing): DPP partners within rows of 16, then the
+// permlane swaps across rows, which hand each lane its own and its partner's
+// triple (in either order; the merge does not care).
+template <int CTRL>
+__device__ __forceinline__ void top2_dpp_step(float& v1, int& i1, float& v2) {
+  merge_top2(v1, i1, v2, dpp_partner<CTRL>(v1),
+             __builtin_amdgcn_update_dpp(0, i1, CTRL, 0xF, 0xF, false), dpp_partner<CTRL>(v2));
+}
+template <bool ROW32>
+__device__ __forceinline__ void top2_swap_step(float& v1, int& i1, float& v2) {
+  auto sw = [](uint32_t x) {
+    if constexpr (ROW32) return __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    else return __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  };
+  const auto a = sw(__float_as_uint(v1)), b = sw((uint32_t)i1), c = sw(__float_as_uint(v2));
+  float w1 = __uint_as_float(a[0]), w2 = __uint_as_float(c[0]);
+  int j1 = (int)b[0];
+  merge_top2(w1, j1, w2, __uint_as_float(a[1]), (int)b[1], __uint_as_float(c[1]));
+  v1 = w1;
+  i1 = j1;
+  v2 = w2;
+}
+__device__ __forceinline__ void wave_top2(float& v1, int& i1, float& v2) {
+  top2_dpp_step<kDppXor1>(v1, i1, v2);
+  top2_dpp_step<kDppXor2>(v1, i1, v2);
+  top2_dpp_step<kDppHalfMirror>(v1, i1, v2);
+  top2_dpp_step<kDppMirror>(v1, i1, v2);
+  top2_swap_step<false>(v1, i1, v2);
+  top2_swap_step<true>(v1, i1, v2);
 }
 
 }  // namespace lucev

@@ -194,9 +194,7 @@ __global__ __launch_bounds__(256) void logits_finish_kernel(SplitOut so, uint16_
     if (logits && ok && node < n) logits[(int64_t)node * vocab + f] = f32_to_bf16_bits(y);
     float v1 = ok ? y : -INFINITY, v2 = -INFINITY;
     int i1 = ok ? (int)f : 0x7fffffff;
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1)
-      merge_top2(v1, i1, v2, shfl_xor(v1, m), __shfl_xor(i1, m, 64), shfl_xor(v2, m));
+    wave_top2(v1, i1, v2);
     if (lane == 0) {
       s_v1[k][wave] = v1;
       s_v2[k][wave] = v2;
