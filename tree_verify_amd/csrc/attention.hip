@@ -545,8 +545,9 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(CombineParams c, Tree
   constexpr int kAncRound = 4;    // ancestors per wave per round of key loads
   __shared__ float s_w[kMaxChunks];
   __shared__ float s_anc[kMaxNodes];
+  __shared__ float s_wa[kMaxNodes];
   __shared__ int s_alist[kMaxNodes];
-  __shared__ float s_red[4];
+  __shared__ float s_red[4], s_red2[4];
   __shared__ float s_acc[PARTS][D];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -573,15 +574,10 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(CombineParams c, Tree
     ov[r] = ch < c.n_chunks ? c.o_part[prow(ch) * D + j] : 0.f;
   }
 
-  // the node's ancestors (itself included), in increasing order
+  // the node's ancestors (itself included), in increasing order: node j
+  // (lane j of the first wave) is the k-th, k = its set bits below j
   const int na = __popcll(anc);
-  if (tid == 0) {
-    uint64_t m = anc;
-    for (int k = 0; k < na; ++k) {
-      s_alist[k] = __builtin_ctzll(m);
-      m &= m - 1;
-    }
-  }
+  if (tid < kMaxNodes && ((anc >> tid) & 1ull)) s_alist[__popcll(anc & ((1ull << tid) - 1ull))] = tid;
   __syncthreads();
   // ancestor scores: wave w takes ancestors w, w + 4, ..., kAncRound of them
   // per round with every key load of the round in flight at once
@@ -625,8 +621,9 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(CombineParams c, Tree
   if (lane == 0) s_red[wave] = mx;
   __syncthreads();
   float M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-  for (int k = 0; k < na; ++k) M = fmaxf(M, s_anc[k]);
-  __syncthreads();
+  // ancestor k's score on lane k (at most 64 ancestors), reduced in the wave
+  const float sa = lane < na ? s_anc[lane] : -INFINITY;
+  M = fmaxf(M, wave_max(sa));
   float lsum = 0.f;
   if (tid < c.n_chunks) {
     const float w = __builtin_amdgcn_exp2f(cm - M) * cl;
@@ -639,10 +636,13 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(CombineParams c, Tree
     lsum += w;
   }
   lsum = wave_sum(lsum);
-  if (lane == 0) s_red[wave] = lsum;
+  if (lane == 0) s_red2[wave] = lsum;
   __syncthreads();
-  float L = (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
-  for (int k = 0; k < na; ++k) L += __builtin_amdgcn_exp2f(s_anc[k] - M);
+  float L = (s_red2[0] + s_red2[1]) + (s_red2[2] + s_red2[3]);
+  // the ancestors' weights: lane k's, kept for the values' sum below
+  const float wa = lane < na ? __builtin_amdgcn_exp2f(sa - M) : 0.f;
+  if (tid < kMaxNodes) s_wa[tid] = wa;
+  L += wave_sum(wa);
 
   // weighted sum of the chunk outputs: PARTS threads per dim, fixed order
   float acc = 0.f;
@@ -670,7 +670,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(CombineParams c, Tree
         // moved down behind a branch
 #pragma unroll
         for (int r = 0; r < 4 * kAncRound; ++r) {
-          const float w = k0 + r < na ? __builtin_amdgcn_exp2f(s_anc[min(k0 + r, na - 1)] - M) : 0.f;
+          const float w = k0 + r < na ? s_wa[min(k0 + r, na - 1)] : 0.f;
           o += w * vv[r];
         }
       }
