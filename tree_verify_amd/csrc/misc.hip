@@ -134,9 +134,7 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const f32x4* __restrict_
   const uint64_t anc = lane < n ? t.anc[lane] : 0ull;
   const bool acc = lane < n && ((anc & ~mm) == 0ull);
   const int depth = __popcll(anc) - 1;
-  int key = acc ? (depth << 8) | (255 - lane) : -1;
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) key = max(key, __shfl_xor(key, m, 64));
+  const int key = (int)wave_max((float)(acc ? (depth << 8) | (255 - lane) : -1));
   const int end = 255 - (key & 255);
   const uint64_t anc_end = __shfl(anc, end, 64);
   const int am_end = __shfl(am, end, 64);
