@@ -255,6 +255,16 @@ def test_midsize_parity(nodes, rec):
     _check_case(cfg, cfg.seed + nodes)
 
 
+# A tree verified against an empty cache (the first step after an empty
+# prompt): the attention's prefix pass launches nothing and the combine merges
+# each node's ancestors alone; RoPE positions are the depths.  Also a single
+# node (decode) on an empty cache.
+@pytest.mark.parametrize("nodes,rec", [(22, (3, 8)), (1, (None, None))], ids=["tree22", "decode"])
+def test_step_empty_prefix(nodes, rec):
+    cfg = MID.replace(prefix=0, nodes=nodes, max_children=rec[0], max_depth=rec[1], name="mid_noprefix%d" % nodes)
+    _check_case(cfg, cfg.seed + 500 + nodes)
+
+
 # A 27B-class layer + head with 28 nodes (four node tiles): gate/up and
 # lm_head take two row tiles per wave with one column group per unit; QKV, Wo
 # and down one tile per wave.
