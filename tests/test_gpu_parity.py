@@ -265,6 +265,14 @@ def test_step_empty_prefix(nodes, rec):
     _check_case(cfg, cfg.seed + 500 + nodes)
 
 
+# A chain of 64 drafts (the deepest tree allowed), every draft the target's
+# own greedy token: the last node has 64 ancestors, so the combine takes every
+# ancestor round, and the whole chain is accepted (the walk's longest path).
+def test_step_chain_of_64():
+    cfg = MID.replace(nodes=64, max_children=1, max_depth=None, p_accept=1.0, name="chain64")
+    _check_case(cfg, cfg.seed + 700)
+
+
 # A 27B-class layer + head with 28 nodes (four node tiles): gate/up and
 # lm_head take two row tiles per wave with one column group per unit; QKV, Wo
 # and down one tile per wave.
