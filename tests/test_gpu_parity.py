@@ -79,6 +79,7 @@ ATTN_CASES = [
     ("wide_tree", 48, 8, 128, 2051, (4, 10), 40),
     ("five_tiles", 48, 8, 128, 1500, (3, 8), 13),  # 78 rows: the fifth tile split by key quarter
     ("empty_prefix", 8, 2, 128, 0, None, 5),
+    ("short_prefix", 8, 2, 128, 33, None, 7),              # one ragged tile, a one-token second half
     ("single_node", 48, 8, 128, 777, None, 1),
     ("max_nodes", 8, 2, 64, 300, None, 64),
     ("row_groups_384_rows", 48, 8, 128, 700, None, 64),    # 24 tiles: two row groups of 12
